@@ -1,0 +1,186 @@
+/*
+ * moegemv: one mixture-of-experts FFN layer over group-64 affine-quantized
+ * weights, on one AMD Instinct MI355X (gfx950).
+ *
+ * The layer (TurboFieldfare "System design"):
+ *   - weights are MLX-affine: packed 4-bit (experts) or 8-bit (router) codes
+ *     with one BF16 scale and one BF16 bias per group of 64 weights,
+ *     w = scale * q + bias  ("Why the runtime has this shape", 4th bullet);
+ *   - the router normalises x without a learned scale, multiplies by
+ *     router_scale / sqrt(hidden), projects to one score per expert, keeps
+ *     the 8 highest and weights them by a softmax over those 8 times
+ *     per_expert_scale ("Decode", router listing);
+ *   - each selected expert is a GeGLU FFN, down(gelu_tanh(gate x) * up x),
+ *     and the selected outputs are weighted and summed ("Metal execution");
+ *   - a dense shared expert is added without a weight ("Why the runtime has
+ *     this shape", 3rd bullet; "Prefill", last bullet).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless the comment says HOST.
+ *   - The caller owns every buffer.  The library borrows them until the work
+ *     it enqueued on `stream` has finished ("Correctness and safety
+ *     invariants": a queued consumer owns its scratch until completion) and
+ *     allocates no device memory.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *     Calls return once the work is enqueued.
+ *   - All arguments are checked on the host before anything is enqueued.  On
+ *     an error nothing is enqueued and nothing is written; the return value
+ *     is a negative mq_status.  A failed launch returns MQ_ERR_HIP.  Faults
+ *     inside kernels surface at the caller's next synchronisation.
+ *   - Nothing throws across this interface and there is no global mutable
+ *     state: calls on different streams with different workspaces are
+ *     independent.
+ */
+#ifndef MOEGEMV_H
+#define MOEGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MQ_OK = 0,
+    MQ_ERR_NULL = -1,         /* a required pointer is NULL */
+    MQ_ERR_SHAPE = -2,        /* inconsistent or unsupported sizes */
+    MQ_ERR_ALIGN = -3,        /* a pointer, offset or stride is misaligned */
+    MQ_ERR_UNSUPPORTED = -4,  /* bits, group, layout or dtype not supported */
+    MQ_ERR_WORKSPACE = -5,    /* workspace missing or smaller than mq_workspace_bytes */
+    MQ_ERR_HIP = -6,          /* a HIP runtime call failed */
+    MQ_ERR_BUFFER = -7        /* a HOST output buffer is too small */
+} mq_status;
+
+enum { MQ_LAYOUT_CANONICAL = 0, MQ_LAYOUT_DEV_V1 = 1 };
+enum { MQ_DTYPE_BF16 = 0, MQ_DTYPE_F32 = 1 };
+enum { MQ_PATH_AUTO = 0, MQ_PATH_GEMV = 1, MQ_PATH_GROUPED = 2 };
+
+/*
+ * A group-64 affine-quantized matrix W [rows][cols], codes of `bits` bits.
+ *
+ * MQ_LAYOUT_CANONICAL (host side only, the MLX checkpoint form):
+ *   codes  uint32 [rows][cols*bits/32], little-endian; element c of a row is
+ *          in word c/(32/bits) at bit bits*(c % (32/bits)), low bits first;
+ *   scales bf16   [rows][cols/64];  biases bf16 [rows][cols/64].
+ *
+ * MQ_LAYOUT_DEV_V1 (what the kernels read): `codes` points at one packed
+ * region of mq_packed_bytes() bytes, `scales` and `biases` are NULL.  Rows
+ * are padded to a multiple of 64 (padding rows have zero codes, scale and
+ * bias).  The region is a sequence of blocks, row-tile major: block (t, g)
+ * holds rows 64t..64t+63 of group g (columns 64g..64g+63) and sits at byte
+ * (t * cols/64 + g) * BLK:
+ *   bits 4: BLK = 2304 = 2048 B of codes + 256 B of (scale, bias) pairs
+ *   bits 8: BLK = 4352 = 4096 B of codes + 256 B of (scale, bias) pairs
+ * The codes are uint32 words at [j][lane 0..63][i 0..3] (j < 2 for 4-bit,
+ * j < 4 for 8-bit); with a = 4j + i, word (j, lane, i) holds
+ *   4-bit: row 16*(a>>1) + lane%16, columns 32*(a&1) + 8*(lane/16) + 0..7;
+ *          column e of the eight sits at bit 4*(e/2) + 16*(e%2);
+ *   8-bit: row 16*(a>>2) + lane%16, columns 16*(a&3) + 4*(lane/16) + 0..3;
+ *          column e of the four sits at bit 8*e.
+ * The pair area is uint32 [r 0..15][m 0..3] = scale | bias << 16 of row
+ * 16*m + r.  Packing copies every code, scale and bias unchanged; only
+ * their positions move ("Source weights and bounded repack": the repack
+ * changes the layout, never the values).
+ */
+typedef struct {
+    const void* codes;
+    const void* scales;
+    const void* biases;
+    int32_t rows, cols, bits, group, layout;
+} mq_qtensor;
+
+/* Router: 8-bit DEV_V1 matrix [E][H] plus optional per-feature and
+ * per-expert factors (device float arrays; NULL means 1, 1 and 0). */
+typedef struct {
+    mq_qtensor w;
+    const float* router_scale;      /* [H] */
+    const float* per_expert_scale;  /* [E] */
+    const float* logit_bias;        /* [E]: added to the scores before selection */
+    int32_t top_k;                  /* 1 <= top_k <= min(E, 16) */
+    float eps;                      /* RMS-norm epsilon */
+} mq_router;
+
+/* The routed-expert pool: num_experts equally spaced blobs ("The .gturbo
+ * directory": fixed-stride expert blobs whose sub-tensors have their own
+ * offsets; kernels bind sub-regions of one buffer).  Expert e's gate
+ * matrix is DEV_V1 data at base + e*expert_stride + gate_offset, and so on.
+ * gate and up are [inter][hidden], down is [hidden][inter], 4-bit.
+ * expert_stride and the offsets are multiples of 256. */
+typedef struct {
+    const void* base;
+    int64_t expert_stride;
+    int64_t gate_offset, up_offset, down_offset;
+    int32_t num_experts, hidden, inter, bits, group, layout;
+} mq_expert_pool;
+
+/* The dense shared expert: gate, up [shared_inter][hidden], down
+ * [hidden][shared_inter], 4-bit DEV_V1.  Pass NULL for a layer without one. */
+typedef struct {
+    mq_qtensor gate, up, down;
+} mq_shared;
+
+/* Activations [tokens][hidden]; row_stride in elements (>= hidden). */
+typedef struct {
+    void* data;
+    int32_t tokens, hidden, dtype;
+    int64_t row_stride;
+} mq_act;
+
+typedef struct {
+    int32_t path;           /* MQ_PATH_*: AUTO picks by token count */
+    int32_t* topk_ids;      /* optional [T][top_k]: selected experts, highest score first */
+    float* topk_w;          /* optional [T][top_k]: their routing weights */
+    float* logits;          /* optional [T][E]: router scores (incl. logit_bias) */
+    void* workspace;        /* device scratch of workspace_bytes, 256-B aligned */
+    size_t workspace_bytes;
+} mq_opts;
+
+/* Device scratch one call needs for up to max_tokens tokens.  The workspace
+ * must be zero-filled once before its first use (the kernels leave their
+ * counters at zero when they finish).  Returns 0 for invalid arguments. */
+size_t mq_workspace_bytes(const mq_router* router, const mq_expert_pool* pool,
+                          const mq_shared* shared, int32_t max_tokens);
+
+/* out = shared(x) + sum_j w_j * expert_{id_j}(x) for every token of x.
+ * x: bf16 [T][H].  out: bf16 (rounded once, to nearest even) or f32 (the
+ * same sums before that rounding), [T][H].  T = 0 is valid and does nothing. */
+mq_status moe_layer_forward(const mq_act* x, const mq_router* router, const mq_expert_pool* pool,
+                            const mq_shared* shared, mq_act* out, const mq_opts* opts, void* stream);
+
+/* Unit-weight RMS norm between stacked layers: out = bf16(x / sqrt(mean(x^2) + eps)).
+ * x and out bf16 [T][H]; they may alias. */
+mq_status mq_rmsnorm(const mq_act* x, mq_act* out, float eps, void* stream);
+
+/* Bytes of a matrix in `layout` (0 for unsupported arguments). */
+size_t mq_packed_bytes(int32_t rows, int32_t cols, int32_t bits, int32_t group, int32_t layout);
+
+/* HOST: fill *pool's offsets and stride for experts packed back to back as
+ * gate, up, down, each blob rounded up to page_bytes (a power of two >= 256).
+ * base is left as given.  Returns the stride, 0 on invalid arguments. */
+int64_t mq_pool_layout(int32_t hidden, int32_t inter, int32_t bits, int32_t group,
+                       int64_t page_bytes, mq_expert_pool* pool);
+
+/* HOST: canonical -> DEV_V1.  src describes HOST canonical arrays; dst is a
+ * HOST buffer of dst_bytes >= mq_packed_bytes(.., MQ_LAYOUT_DEV_V1).  On
+ * success *dst_desc (may be NULL) describes dst as a DEV_V1 tensor. */
+mq_status mq_pack(const mq_qtensor* src, void* dst, size_t dst_bytes, mq_qtensor* dst_desc);
+
+/* HOST: DEV_V1 -> canonical; the exact inverse of mq_pack.  src->codes is a
+ * HOST copy of the packed region; codes/scales/biases are HOST buffers of
+ * the canonical sizes. */
+mq_status mq_unpack(const mq_qtensor* src, uint32_t* codes, uint16_t* scales, uint16_t* biases);
+
+/* Parity hooks: the GPU's reading of a DEV_V1 tensor.  codes_out uint8
+ * [rows][cols] receives every code; w_out float [rows][cols] receives
+ * scale * q + bias in fp32 (exact when the fp32 product is, e.g. for the
+ * synthetic bias = -2^(bits-1) * scale). */
+mq_status mq_debug_unpack_codes(const mq_qtensor* t, uint8_t* codes_out, void* stream);
+mq_status mq_debug_dequant(const mq_qtensor* t, float* w_out, void* stream);
+
+const char* mq_status_str(mq_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

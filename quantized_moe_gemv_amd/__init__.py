@@ -1,0 +1,273 @@
+"""Python binding of libmoegemv (the MI355X quantized MoE FFN layer).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+behind the C ABI of ``include/moegemv.h``.  PyTorch provides device memory
+and the stream; the library never allocates.  Importing this package fails
+with an ImportError when the HIP library has not been built (run
+``python -m quantized_moe_gemv_amd.build``); there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Optional
+
+import numpy as np
+import torch  # loads the HIP runtime that libmoegemv then shares
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoegemv.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libmoegemv.so is not built: run `python -m quantized_moe_gemv_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+MQ_OK, MQ_ERR_NULL, MQ_ERR_SHAPE, MQ_ERR_ALIGN = 0, -1, -2, -3
+MQ_ERR_UNSUPPORTED, MQ_ERR_WORKSPACE, MQ_ERR_HIP, MQ_ERR_BUFFER = -4, -5, -6, -7
+LAYOUT_CANONICAL, LAYOUT_DEV_V1 = 0, 1
+DTYPE_BF16, DTYPE_F32 = 0, 1
+PATHS = {"auto": 0, "gemv": 1, "grouped": 2}
+GROUP = 64
+EXPORTS = ["moe_layer_forward", "mq_workspace_bytes", "mq_rmsnorm", "mq_packed_bytes", "mq_pool_layout",
+           "mq_pack", "mq_unpack", "mq_debug_unpack_codes", "mq_debug_dequant", "mq_status_str"]
+
+
+class MqQTensor(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
+                ("rows", ctypes.c_int32), ("cols", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("layout", ctypes.c_int32)]
+
+
+class MqRouter(ctypes.Structure):
+    _fields_ = [("w", MqQTensor), ("router_scale", ctypes.c_void_p), ("per_expert_scale", ctypes.c_void_p),
+                ("logit_bias", ctypes.c_void_p), ("top_k", ctypes.c_int32), ("eps", ctypes.c_float)]
+
+
+class MqExpertPool(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("expert_stride", ctypes.c_int64), ("gate_offset", ctypes.c_int64),
+                ("up_offset", ctypes.c_int64), ("down_offset", ctypes.c_int64),
+                ("num_experts", ctypes.c_int32), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("bits", ctypes.c_int32), ("group", ctypes.c_int32), ("layout", ctypes.c_int32)]
+
+
+class MqShared(ctypes.Structure):
+    _fields_ = [("gate", MqQTensor), ("up", MqQTensor), ("down", MqQTensor)]
+
+
+class MqAct(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("tokens", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("row_stride", ctypes.c_int64)]
+
+
+class MqOpts(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("topk_ids", ctypes.c_void_p), ("topk_w", ctypes.c_void_p),
+                ("logits", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+_P = ctypes.c_void_p
+_sig = {
+    "mq_workspace_bytes": (ctypes.c_size_t, [_P, _P, _P, ctypes.c_int32]),
+    "moe_layer_forward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P]),
+    "mq_rmsnorm": (ctypes.c_int, [_P, _P, ctypes.c_float, _P]),
+    "mq_packed_bytes": (ctypes.c_size_t, [ctypes.c_int32] * 5),
+    "mq_pool_layout": (ctypes.c_int64, [ctypes.c_int32] * 4 + [ctypes.c_int64, _P]),
+    "mq_pack": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
+    "mq_unpack": (ctypes.c_int, [_P, _P, _P, _P]),
+    "mq_debug_unpack_codes": (ctypes.c_int, [_P, _P, _P]),
+    "mq_debug_dequant": (ctypes.c_int, [_P, _P, _P]),
+    "mq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+}
+for _name, (_res, _args) in _sig.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s: %s (status %d)" % (what, status_str(status), status))
+        self.status = status
+
+
+def status_str(s: int) -> str:
+    return _lib.mq_status_str(s).decode()
+
+
+def _check(status: int, what: str):
+    if status != MQ_OK:
+        raise MoeError(status, what)
+
+
+def _ref(s) -> Optional[ctypes._Pointer]:
+    return None if s is None else ctypes.byref(s)
+
+
+def _stream_handle(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+# ------------------------------------------------------------------ host packing
+
+def packed_bytes(rows: int, cols: int, bits: int, layout: int = LAYOUT_DEV_V1) -> int:
+    return int(_lib.mq_packed_bytes(rows, cols, bits, GROUP, layout))
+
+
+def _canonical_desc(qt) -> tuple:
+    c = np.ascontiguousarray(qt.codes, dtype=np.uint32)
+    s = np.ascontiguousarray(qt.scales, dtype=np.uint16)
+    b = np.ascontiguousarray(qt.biases, dtype=np.uint16)
+    d = MqQTensor(c.ctypes.data, s.ctypes.data, b.ctypes.data, qt.rows, qt.cols, qt.bits, GROUP, LAYOUT_CANONICAL)
+    return d, (c, s, b)
+
+
+def pack_into(qt, dst: np.ndarray, offset: int = 0) -> int:
+    """Pack a canonical host tensor into dst[offset:] (uint8); returns the byte count."""
+    n = packed_bytes(qt.rows, qt.cols, qt.bits)
+    assert dst.dtype == np.uint8 and dst.flags.c_contiguous and offset + n <= dst.size
+    d, keep = _canonical_desc(qt)
+    _check(_lib.mq_pack(ctypes.byref(d), dst.ctypes.data + offset, n, None), "mq_pack")
+    return n
+
+
+def pack(qt) -> np.ndarray:
+    out = np.empty(packed_bytes(qt.rows, qt.cols, qt.bits), dtype=np.uint8)
+    pack_into(qt, out)
+    return out
+
+
+def unpack(packed: np.ndarray, rows: int, cols: int, bits: int):
+    """DEV_V1 host bytes -> canonical (codes uint32, scales uint16, biases uint16)."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    codes = np.empty((rows, cols * bits // 32), np.uint32)
+    scales = np.empty((rows, cols // GROUP), np.uint16)
+    biases = np.empty((rows, cols // GROUP), np.uint16)
+    d = MqQTensor(packed.ctypes.data, None, None, rows, cols, bits, GROUP, LAYOUT_DEV_V1)
+    _check(_lib.mq_unpack(ctypes.byref(d), codes.ctypes.data, scales.ctypes.data, biases.ctypes.data), "mq_unpack")
+    return codes, scales, biases
+
+
+def pool_layout(hidden: int, inter: int, page_bytes: int = 16384, bits: int = 4) -> MqExpertPool:
+    pool = MqExpertPool()
+    stride = _lib.mq_pool_layout(hidden, inter, bits, GROUP, page_bytes, ctypes.byref(pool))
+    if stride <= 0:
+        raise MoeError(MQ_ERR_SHAPE, "mq_pool_layout")
+    return pool
+
+
+# ------------------------------------------------------------------ device layer
+
+class DeviceLayer:
+    """A layer packed to DEV_V1 and resident in device memory (torch tensors).
+
+    ``src`` is a canonical host layer (``qmoe_synth.Layer`` or anything with
+    the same fields).  The routed experts live in one buffer of
+    num_experts * expert_stride bytes, each blob page-rounded.
+    """
+
+    def __init__(self, src, device="cuda", page_bytes: int = 16384, threads: int = 16):
+        cfg = src.cfg
+        self.hidden, self.num_experts, self.inter = cfg.hidden, cfg.num_experts, cfg.inter
+        self.top_k, self.eps = cfg.top_k, cfg.eps
+        self.shared_inter = 0 if src.shared_gate is None else src.shared_gate.rows
+        E = self.num_experts
+        self.pool = pool_layout(self.hidden, self.inter, page_bytes)
+        stride = self.pool.expert_stride
+        host = np.zeros(E * stride, dtype=np.uint8)
+
+        def pack_expert(e):
+            base = e * stride
+            pack_into(src.gate.select(e), host, base + self.pool.gate_offset)
+            pack_into(src.up.select(e), host, base + self.pool.up_offset)
+            pack_into(src.down.select(e), host, base + self.pool.down_offset)
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(pack_expert, range(E)))
+        self.pool_buf = torch.from_numpy(host).to(device)
+        del host
+        self.pool.base = self.pool_buf.data_ptr()
+        self.pool.num_experts = E
+
+        def dev_tensor(qt):
+            buf = torch.from_numpy(pack(qt)).to(device)
+            return buf, MqQTensor(buf.data_ptr(), None, None, qt.rows, qt.cols, qt.bits, GROUP, LAYOUT_DEV_V1)
+
+        self.router_buf, self.router_w = dev_tensor(src.router)
+        opt = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
+        self.router_scale = opt(src.router_scale)
+        self.per_expert_scale = opt(src.per_expert_scale)
+        self.logit_bias = opt(src.logit_bias)
+        ptr = lambda t: None if t is None else t.data_ptr()
+        self.router = MqRouter(self.router_w, ptr(self.router_scale), ptr(self.per_expert_scale),
+                               ptr(self.logit_bias), self.top_k, self.eps)
+        self.shared = None
+        if src.shared_gate is not None:
+            self.sg_buf, sg = dev_tensor(src.shared_gate)
+            self.su_buf, su = dev_tensor(src.shared_up)
+            self.sd_buf, sd = dev_tensor(src.shared_down)
+            self.shared = MqShared(sg, su, sd)
+
+    def workspace_bytes(self, max_tokens: int) -> int:
+        n = _lib.mq_workspace_bytes(ctypes.byref(self.router), ctypes.byref(self.pool), _ref(self.shared),
+                                    max_tokens)
+        if n == 0:
+            raise MoeError(MQ_ERR_SHAPE, "mq_workspace_bytes")
+        return int(n)
+
+    def new_workspace(self, max_tokens: int, device="cuda") -> torch.Tensor:
+        return torch.zeros(self.workspace_bytes(max_tokens), dtype=torch.uint8, device=device)
+
+    def weight_bytes(self) -> int:
+        n = self.router_buf.numel() + self.pool_buf.numel()
+        if self.shared is not None:
+            n += self.sg_buf.numel() + self.su_buf.numel() + self.sd_buf.numel()
+        return n
+
+
+def _act(t: torch.Tensor) -> MqAct:
+    assert t.dim() == 2 and t.stride(1) == 1
+    dt = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_F32}[t.dtype]
+    return MqAct(t.data_ptr(), t.shape[0], t.shape[1], dt, t.stride(0))
+
+
+def moe_layer_forward(layer: DeviceLayer, x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, path: str = "auto",
+                      out_dtype=torch.bfloat16, topk_ids: Optional[torch.Tensor] = None,
+                      topk_w: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """out = shared(x) + sum_j w_j expert_j(x) on the current (or given) stream."""
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty((T, layer.hidden), dtype=out_dtype, device=x.device)
+    if workspace is None:
+        workspace = layer.new_workspace(T, x.device)
+    xa, oa = _act(x), _act(out)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    opts = MqOpts(PATHS[path], ptr(topk_ids), ptr(topk_w), ptr(logits), workspace.data_ptr(), workspace.numel())
+    st = _lib.moe_layer_forward(ctypes.byref(xa), ctypes.byref(layer.router), ctypes.byref(layer.pool),
+                                _ref(layer.shared), ctypes.byref(oa), ctypes.byref(opts), _stream_handle(stream))
+    _check(st, "moe_layer_forward")
+    return out
+
+
+def rmsnorm(x: torch.Tensor, out: Optional[torch.Tensor] = None, eps: float = 1e-6, stream=None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty_like(x)
+    xa, oa = _act(x), _act(out)
+    _check(_lib.mq_rmsnorm(ctypes.byref(xa), ctypes.byref(oa), eps, _stream_handle(stream)), "mq_rmsnorm")
+    return out
+
+
+def debug_unpack_codes(buf: torch.Tensor, rows: int, cols: int, bits: int, stream=None) -> torch.Tensor:
+    out = torch.empty((rows, cols), dtype=torch.uint8, device=buf.device)
+    d = MqQTensor(buf.data_ptr(), None, None, rows, cols, bits, GROUP, LAYOUT_DEV_V1)
+    _check(_lib.mq_debug_unpack_codes(ctypes.byref(d), out.data_ptr(), _stream_handle(stream)),
+           "mq_debug_unpack_codes")
+    return out
+
+
+def debug_dequant(buf: torch.Tensor, rows: int, cols: int, bits: int, stream=None) -> torch.Tensor:
+    out = torch.empty((rows, cols), dtype=torch.float32, device=buf.device)
+    d = MqQTensor(buf.data_ptr(), None, None, rows, cols, bits, GROUP, LAYOUT_DEV_V1)
+    _check(_lib.mq_debug_dequant(ctypes.byref(d), out.data_ptr(), _stream_handle(stream)), "mq_debug_dequant")
+    return out

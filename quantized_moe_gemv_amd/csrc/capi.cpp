@@ -1,0 +1,301 @@
+// C-ABI entry points: argument checks, workspace carve-up and launches.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include "../../include/moegemv.h"
+#include "layout.h"
+#include "plan.h"
+
+namespace mq {
+__global__ void k_prep(Plan p);
+__global__ void k_router(Plan p);
+__global__ void k_topk(Plan p);
+__global__ void k_gateup(Plan p);
+__global__ void k_down(Plan p);
+__global__ void k_combine(Plan p);
+__global__ void k_rmsnorm(const uint16_t* x, int64_t xs, uint16_t* y, int64_t ys, int H, float eps);
+__global__ void k_debug_read(const uint8_t* data, int rows, int cols, int bits, uint8_t* codes_out, float* w_out);
+mq_status launch_grouped(const Plan& p, hipStream_t s);
+}  // namespace mq
+
+using namespace mq;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct Sizes {
+    int H, E, E_pad, k, I, Is, G_H, G_I, G_s, rsplit, rgroups, ntile, max_tiles;
+};
+
+// Offsets of every workspace region for up to T tokens; returns the total.
+struct Carve {
+    size_t r, rsum8, xsum4, plog, ids, wts, hhi, hlo, hsum, shi, slo, ssum, dpart;
+    size_t x16, counts, offsets, perm, inv, sched, nsched, bitmap, wpre, hg, hs16, ysort, ysh;
+    size_t total;
+};
+
+Carve carve(const Sizes& z, int64_t T) {
+    Carve c;
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
+    c.r = take(T * z.H * 4);
+    c.rsum8 = take(T * z.G_H * 16);
+    c.xsum4 = take(T * z.G_H * 16);
+    c.plog = take((size_t)z.rsplit * T * z.E_pad * 4);
+    c.ids = take(T * z.k * 4);
+    c.wts = take(T * z.k * 4);
+    c.hhi = take(T * z.k * z.I * 2);
+    c.hlo = take(T * z.k * z.I * 2);
+    c.hsum = take(T * z.k * z.G_I * 16);
+    c.shi = take(T * z.Is * 2 + 16);
+    c.slo = take(T * z.Is * 2 + 16);
+    c.ssum = take(T * z.G_s * 16 + 16);
+    c.dpart = take(T * kDownSplits * z.H * 4);
+    c.x16 = take(T * z.H * 2);
+    c.counts = take((size_t)z.E * 4);
+    c.offsets = take((size_t)(z.E + 1) * 4);
+    c.perm = take(T * z.k * 4);
+    c.inv = take(T * z.k * 4);
+    c.sched = take((size_t)z.max_tiles * 4 + 4);
+    c.nsched = take(4);
+    c.bitmap = take((size_t)z.E * ((T + 31) / 32) * 4);
+    c.wpre = take((size_t)z.E * ((T + 31) / 32) * 4);
+    c.hg = take(T * z.k * z.I * 2);
+    c.hs16 = take(T * z.Is * 2 + 16);
+    c.ysort = take(T * z.k * z.H * 4);
+    c.ysh = take(T * z.H * 4);
+    c.total = o;
+    return c;
+}
+
+bool qt_dev_ok(const mq_qtensor& t, int bits) {
+    return t.codes && t.bits == bits && t.group == kGroup && t.layout == MQ_LAYOUT_DEV_V1 && t.rows > 0 &&
+           t.cols > 0 && t.cols % kGroup == 0;
+}
+
+// Checks everything that does not depend on the call's tokens.
+mq_status check_layer(const mq_router* rt, const mq_expert_pool* pool, const mq_shared* sh, Sizes* z) {
+    if (!rt || !pool) return MQ_ERR_NULL;
+    if (!rt->w.codes || !pool->base) return MQ_ERR_NULL;
+    if (rt->w.bits != 8 || rt->w.group != kGroup || rt->w.layout != MQ_LAYOUT_DEV_V1) return MQ_ERR_UNSUPPORTED;
+    if (pool->bits != 4 || pool->group != kGroup || pool->layout != MQ_LAYOUT_DEV_V1) return MQ_ERR_UNSUPPORTED;
+    const int H = pool->hidden, E = pool->num_experts, I = pool->inter;
+    if (H <= 0 || H % kGroup || I <= 0 || I % kGroup || E <= 0 || E > kMaxExperts) return MQ_ERR_SHAPE;
+    if (rt->w.rows != E || rt->w.cols != H) return MQ_ERR_SHAPE;
+    if (rt->top_k < 1 || rt->top_k > E || rt->top_k > kMaxTopK) return MQ_ERR_SHAPE;
+    if (!(rt->eps >= 0.f)) return MQ_ERR_SHAPE;
+    if (!aligned(rt->w.codes, kAlign) || !aligned(pool->base, kAlign)) return MQ_ERR_ALIGN;
+    if (pool->expert_stride % 256 || pool->gate_offset % 256 || pool->up_offset % 256 || pool->down_offset % 256)
+        return MQ_ERR_ALIGN;
+    const int64_t gu = (int64_t)mq_packed_bytes(I, H, 4, kGroup, MQ_LAYOUT_DEV_V1);
+    const int64_t dn = (int64_t)mq_packed_bytes(H, I, 4, kGroup, MQ_LAYOUT_DEV_V1);
+    if (pool->gate_offset < 0 || pool->up_offset < 0 || pool->down_offset < 0 ||
+        pool->gate_offset + gu > pool->expert_stride || pool->up_offset + gu > pool->expert_stride ||
+        pool->down_offset + dn > pool->expert_stride)
+        return MQ_ERR_SHAPE;
+    int Is = 0;
+    if (sh) {
+        if (!qt_dev_ok(sh->gate, 4) || !qt_dev_ok(sh->up, 4) || !qt_dev_ok(sh->down, 4)) {
+            if (!sh->gate.codes || !sh->up.codes || !sh->down.codes) return MQ_ERR_NULL;
+            return MQ_ERR_UNSUPPORTED;
+        }
+        Is = sh->gate.rows;
+        if (Is % kGroup || sh->up.rows != Is || sh->gate.cols != H || sh->up.cols != H || sh->down.rows != H ||
+            sh->down.cols != Is)
+            return MQ_ERR_SHAPE;
+        if (!aligned(sh->gate.codes, kAlign) || !aligned(sh->up.codes, kAlign) || !aligned(sh->down.codes, kAlign))
+            return MQ_ERR_ALIGN;
+    }
+    z->H = H;
+    z->E = E;
+    z->E_pad = (int)pad_rows(E);
+    z->k = rt->top_k;
+    z->I = I;
+    z->Is = Is;
+    z->G_H = H / kGroup;
+    z->G_I = I / kGroup;
+    z->G_s = Is / kGroup;
+    z->rgroups = 4;
+    z->rsplit = (z->G_H + z->rgroups - 1) / z->rgroups;
+    z->ntile = 16;
+    return MQ_OK;
+}
+
+void set_tiles(Sizes* z, int64_t T) {
+    // every expert may add one partial tile to the full ones
+    z->max_tiles = (int)((T * z->k + z->ntile - 1) / z->ntile + z->E);
+}
+
+}  // namespace
+
+extern "C" size_t mq_workspace_bytes(const mq_router* router, const mq_expert_pool* pool, const mq_shared* shared,
+                                     int32_t max_tokens) {
+    Sizes z;
+    if (max_tokens < 0 || check_layer(router, pool, shared, &z) != MQ_OK) return 0;
+    int64_t T = max_tokens > 0 ? max_tokens : 1;
+    set_tiles(&z, T);
+    return carve(z, T).total;
+}
+
+extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router, const mq_expert_pool* pool,
+                                       const mq_shared* shared, mq_act* out, const mq_opts* opts, void* stream) {
+    if (!x || !out || !opts) return MQ_ERR_NULL;
+    Sizes z;
+    mq_status st = check_layer(router, pool, shared, &z);
+    if (st != MQ_OK) return st;
+    const int T = x->tokens;
+    if (T < 0 || out->tokens != T || x->hidden != z.H || out->hidden != z.H) return MQ_ERR_SHAPE;
+    if (x->dtype != MQ_DTYPE_BF16 || (out->dtype != MQ_DTYPE_BF16 && out->dtype != MQ_DTYPE_F32))
+        return MQ_ERR_UNSUPPORTED;
+    if (x->row_stride < x->hidden || out->row_stride < out->hidden) return MQ_ERR_SHAPE;
+    if (opts->path < MQ_PATH_AUTO || opts->path > MQ_PATH_GROUPED) return MQ_ERR_UNSUPPORTED;
+    if (T == 0) return MQ_OK;
+    if (!x->data || !out->data || !opts->workspace) return x->data && out->data ? MQ_ERR_WORKSPACE : MQ_ERR_NULL;
+    if (!aligned(x->data, 16) || x->row_stride % 8) return MQ_ERR_ALIGN;
+    if (!aligned(out->data, 4) || !aligned(opts->workspace, kAlign)) return MQ_ERR_ALIGN;
+    set_tiles(&z, T);
+    Carve c = carve(z, T);
+    if (opts->workspace_bytes < c.total) return MQ_ERR_WORKSPACE;
+
+    uint8_t* ws = (uint8_t*)opts->workspace;
+    Plan p;
+    memset(&p, 0, sizeof(p));
+    p.T = T;
+    p.H = z.H;
+    p.E = z.E;
+    p.E_pad = z.E_pad;
+    p.k = z.k;
+    p.I = z.I;
+    p.Is = z.Is;
+    p.G_H = z.G_H;
+    p.G_I = z.G_I;
+    p.G_s = z.G_s;
+    p.rsplit = z.rsplit;
+    p.rgroups = z.rgroups;
+    p.has_shared = shared != nullptr;
+    p.x = (const uint16_t*)x->data;
+    p.x_stride = x->row_stride;
+    p.router_w = (const uint8_t*)router->w.codes;
+    p.router_scale = router->router_scale;
+    p.pes = router->per_expert_scale;
+    p.logit_bias = router->logit_bias;
+    p.eps = router->eps;
+    p.pool_base = (const uint8_t*)pool->base;
+    p.expert_stride = pool->expert_stride;
+    p.gate_off = pool->gate_offset;
+    p.up_off = pool->up_offset;
+    p.down_off = pool->down_offset;
+    if (shared) {
+        p.sh_gate = (const uint8_t*)shared->gate.codes;
+        p.sh_up = (const uint8_t*)shared->up.codes;
+        p.sh_down = (const uint8_t*)shared->down.codes;
+    }
+    p.out = out->data;
+    p.out_stride = out->row_stride;
+    p.out_f32 = out->dtype == MQ_DTYPE_F32;
+    p.ids_out = opts->topk_ids;
+    p.w_out = opts->topk_w;
+    p.logits_out = opts->logits;
+    p.r = (float*)(ws + c.r);
+    p.rsum8 = (float*)(ws + c.rsum8);
+    p.xsum4 = (float*)(ws + c.xsum4);
+    p.plog = (float*)(ws + c.plog);
+    p.ids = (int32_t*)(ws + c.ids);
+    p.wts = (float*)(ws + c.wts);
+    p.hhi = (uint16_t*)(ws + c.hhi);
+    p.hlo = (uint16_t*)(ws + c.hlo);
+    p.hsum = (float*)(ws + c.hsum);
+    p.shi = (uint16_t*)(ws + c.shi);
+    p.slo = (uint16_t*)(ws + c.slo);
+    p.ssum = (float*)(ws + c.ssum);
+    p.dpart = (float*)(ws + c.dpart);
+    p.counts = (int32_t*)(ws + c.counts);
+    p.offsets = (int32_t*)(ws + c.offsets);
+    p.perm = (int32_t*)(ws + c.perm);
+    p.inv = (int32_t*)(ws + c.inv);
+    p.sched = (int32_t*)(ws + c.sched);
+    p.nsched = (int32_t*)(ws + c.nsched);
+    p.bitmap = (uint32_t*)(ws + c.bitmap);
+    p.wpre = (int32_t*)(ws + c.wpre);
+    p.hg = (_Float16*)(ws + c.hg);
+    p.hs16 = (_Float16*)(ws + c.hs16);
+    p.ysort = (float*)(ws + c.ysort);
+    p.ysh = (float*)(ws + c.ysh);
+    p.max_tiles = z.max_tiles;
+    p.ntile = z.ntile;
+
+    const bool grouped = opts->path == MQ_PATH_GROUPED || (opts->path == MQ_PATH_AUTO && T > 4);
+    if (grouped) p.x16 = (_Float16*)(ws + c.x16);
+
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(k_prep, dim3(T), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(k_router, dim3(z.E_pad / 64, z.rsplit, (T + kRouterTokens - 1) / kRouterTokens), dim3(256),
+                       0, s, p);
+    hipLaunchKernelGGL(k_topk, dim3(T), dim3(64), 0, s, p);
+    if (grouped) {
+        st = launch_grouped(p, s);
+        if (st != MQ_OK) return st;
+    } else {
+        hipLaunchKernelGGL(k_gateup, dim3(T, z.k * (z.I / 64) + z.Is / 64), dim3(256), 0, s, p);
+        hipLaunchKernelGGL(k_down, dim3(T, z.H / 64, kDownSplits), dim3(256), 0, s, p);
+        hipLaunchKernelGGL(k_combine, dim3(T, (z.H + 255) / 256), dim3(256), 0, s, p);
+    }
+    return hipGetLastError() == hipSuccess ? MQ_OK : MQ_ERR_HIP;
+}
+
+extern "C" mq_status mq_rmsnorm(const mq_act* x, mq_act* out, float eps, void* stream) {
+    if (!x || !out) return MQ_ERR_NULL;
+    if (x->dtype != MQ_DTYPE_BF16 || out->dtype != MQ_DTYPE_BF16) return MQ_ERR_UNSUPPORTED;
+    if (x->tokens != out->tokens || x->hidden != out->hidden || x->tokens < 0 || x->hidden <= 0 ||
+        x->row_stride < x->hidden || out->row_stride < out->hidden || !(eps >= 0.f))
+        return MQ_ERR_SHAPE;
+    if (x->tokens == 0) return MQ_OK;
+    if (!x->data || !out->data) return MQ_ERR_NULL;
+    if (!aligned(x->data, 2) || !aligned(out->data, 2)) return MQ_ERR_ALIGN;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(k_rmsnorm, dim3(x->tokens), dim3(256), 0, (hipStream_t)stream, (const uint16_t*)x->data,
+                       x->row_stride, (uint16_t*)out->data, out->row_stride, x->hidden, eps);
+    return hipGetLastError() == hipSuccess ? MQ_OK : MQ_ERR_HIP;
+}
+
+static mq_status debug_read(const mq_qtensor* t, uint8_t* codes_out, float* w_out, void* stream) {
+    if (!t || !t->codes || (!codes_out && !w_out)) return MQ_ERR_NULL;
+    if (!(t->bits == 4 || t->bits == 8) || t->group != kGroup || t->layout != MQ_LAYOUT_DEV_V1)
+        return MQ_ERR_UNSUPPORTED;
+    if (t->rows <= 0 || t->cols <= 0 || t->cols % kGroup) return MQ_ERR_SHAPE;
+    if (!aligned(t->codes, 16)) return MQ_ERR_ALIGN;
+    const int blocks = (int)(pad_rows(t->rows) / kTileRows) * (t->cols / kGroup);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(k_debug_read, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const uint8_t*)t->codes,
+                       t->rows, t->cols, t->bits, codes_out, w_out);
+    return hipGetLastError() == hipSuccess ? MQ_OK : MQ_ERR_HIP;
+}
+
+extern "C" mq_status mq_debug_unpack_codes(const mq_qtensor* t, uint8_t* codes_out, void* stream) {
+    if (!codes_out) return MQ_ERR_NULL;
+    return debug_read(t, codes_out, nullptr, stream);
+}
+
+extern "C" mq_status mq_debug_dequant(const mq_qtensor* t, float* w_out, void* stream) {
+    if (!w_out) return MQ_ERR_NULL;
+    return debug_read(t, nullptr, w_out, stream);
+}
+
+extern "C" const char* mq_status_str(mq_status s) {
+    switch (s) {
+        case MQ_OK: return "ok";
+        case MQ_ERR_NULL: return "required pointer is NULL";
+        case MQ_ERR_SHAPE: return "inconsistent or unsupported sizes";
+        case MQ_ERR_ALIGN: return "misaligned pointer, offset or stride";
+        case MQ_ERR_UNSUPPORTED: return "unsupported bits, group, layout, dtype or path";
+        case MQ_ERR_WORKSPACE: return "workspace missing or too small";
+        case MQ_ERR_HIP: return "HIP runtime error";
+        case MQ_ERR_BUFFER: return "host buffer too small";
+    }
+    return "unknown status";
+}

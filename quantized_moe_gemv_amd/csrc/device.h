@@ -1,0 +1,68 @@
+// Device helpers shared by the HIP kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "layout.h"
+
+namespace mq {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16, round to nearest even (finite values).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// c + a.lo*b.lo + a.hi*b.hi with bf16 pairs, fp32 accumulation.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                           false);
+}
+
+// Pair m (m = 0..3) of a DEV_V1 4-bit word as two bf16 values 128 + q:
+// the nibbles of columns 2m and 2m+1 sit at bits 4m and 16 + 4m, and OR-ing
+// them under the exponent of 128.0 (0x4300) gives 128 + q exactly.
+__device__ __forceinline__ uint32_t q4_pair(uint32_t w, int m) {
+    return ((w >> (4 * m)) & 0x000F000Fu) | 0x43004300u;
+}
+
+// Partial dots of one lane over one 4-bit DEV_V1 block: rows 16*ms + lane%16
+// (ms = 0..3), over the lane's 16 columns 32*ks + 8*(lane/16) + 0..7.
+// xa, xb: the lane's x values for ks = 0 and 1 as bf16 pairs.
+// Adds sum((128 + q) * x) of row ms to d[ms].
+__device__ __forceinline__ void q4_block_dot(const uint4& c0, const uint4& c1, const uint4& xa, const uint4& xb,
+                                             float d[4]) {
+    const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    const uint32_t xk[2][4] = {{xa.x, xa.y, xa.z, xa.w}, {xb.x, xb.y, xb.z, xb.w}};
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) d[a >> 1] = dot2_bf16(q4_pair(w[a], m), xk[a & 1][m], d[a >> 1]);
+    }
+}
+
+// Sum over the four lanes lane%16 + 16*kb (kb = 0..3) of a wave.
+__device__ __forceinline__ float sum_kb(float v) {
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+__device__ __forceinline__ float gelu_tanh(float z) {
+    const float k = 0.7978845608028654f;   // sqrt(2/pi)
+    return 0.5f * z * (1.0f + tanhf(k * (z + 0.044715f * z * z * z)));
+}
+
+template <typename T>
+__device__ __forceinline__ T ld_nt(const T* p) {
+    return __builtin_nontemporal_load(p);
+}
+
+}  // namespace mq

@@ -1,0 +1,75 @@
+// One call's resolved arguments and workspace carve-up, passed by value to
+// every kernel of the call.
+#pragma once
+#include <stdint.h>
+
+namespace mq {
+
+constexpr int kRouterTokens = 4;    // tokens per router workgroup
+constexpr int kMaxTopK = 16;
+constexpr int kMaxExperts = 256;
+constexpr int kDownSplits = 4;      // split of the down-projection source list (GEMV path)
+
+struct Plan {
+    // sizes
+    int T, H, E, E_pad, k, I, Is;
+    int G_H, G_I, G_s;              // groups of 64 along hidden, inter, shared inter
+    int rsplit, rgroups;            // router k-splits and groups per split
+    int has_shared;
+
+    // inputs
+    const uint16_t* x;
+    int64_t x_stride;
+    const uint8_t* router_w;
+    const float* router_scale;
+    const float* pes;
+    const float* logit_bias;
+    float eps;
+    const uint8_t* pool_base;
+    int64_t expert_stride, gate_off, up_off, down_off;
+    const uint8_t* sh_gate;
+    const uint8_t* sh_up;
+    const uint8_t* sh_down;
+
+    // outputs
+    void* out;
+    int64_t out_stride;
+    int out_f32;
+    int32_t* ids_out;
+    float* w_out;
+    float* logits_out;
+
+    // workspace (GEMV path and router)
+    float* r;          // [T][H]      router input, scaled
+    float* rsum8;      // [T][G_H][4] sums of r over each lane's 16 columns (8-bit blocks)
+    float* xsum4;      // [T][G_H][4] sums of x over each lane's 16 columns (4-bit blocks)
+    float* plog;       // [rsplit][T][E_pad] partial router scores
+    int32_t* ids;      // [T][k]
+    float* wts;        // [T][k]
+    uint16_t* hhi;     // [T][k][I]   GeGLU activations, bf16 high part
+    uint16_t* hlo;     // [T][k][I]   bf16 low part (h - hi)
+    float* hsum;       // [T][k][G_I][4]
+    uint16_t* shi;     // [T][Is]
+    uint16_t* slo;     // [T][Is]
+    float* ssum;       // [T][G_s][4]
+    float* dpart;      // [T][kDownSplits][H]
+
+    // workspace (grouped path)
+    _Float16* x16;     // [T][H]
+    int32_t* counts;   // [E]
+    int32_t* offsets;  // [E + 1]
+    int32_t* perm;     // [T*k]  pair p = t*k + j, sorted by expert then token
+    int32_t* inv;      // [T*k]  position of pair p in perm
+    int32_t* sched;    // [max_tiles] (expert << 16 | token tile)
+    int32_t* nsched;   // [1]
+    uint32_t* bitmap;  // [E][ceil(T/32)] tokens that chose each expert
+    int32_t* wpre;     // [E][ceil(T/32)] exclusive popcount prefix of bitmap
+    _Float16* hg;      // [T*k][I]   GeGLU activations in sorted order
+    _Float16* hs16;    // [T][Is]
+    float* ysort;      // [T*k][H]   weighted expert outputs in sorted order
+    float* ysh;        // [T][H]     shared expert outputs
+    int max_tiles;     // upper bound of scheduled (expert, token tile) pairs
+    int ntile;         // tokens per grouped tile
+};
+
+}  // namespace mq

@@ -11,3 +11,18 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: takes more than a few seconds on the CPU")
+
+
+def _ensure_built():
+    """Build the HIP library and the oracle when nothing is built yet."""
+    lib = os.path.join(ROOT, "quantized_moe_gemv_amd", "libmoegemv.so")
+    if not os.path.exists(lib):
+        from quantized_moe_gemv_amd import build as b
+        b.build()
+    import oracle
+    import qmoe_synth
+    qmoe_synth._load()
+    oracle.load()
+
+
+_ensure_built()

@@ -1,0 +1,220 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Integer results (codes, expert ids) must match exactly; floats to the
+tolerances in gpu_util.  Sizes: the tiny layer at several token counts
+(several tiles and ragged tails), and the full Gemma-shaped layer at the
+decode and 128-token prefill shapes, where the oracle checks every routing
+decision and a sample of the outputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import qmoe_synth as S
+from gpu_util import bf16_tensor, bf16_bits, check_output, check_routing, log, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def M():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import quantized_moe_gemv_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def tiny(M):
+    host = S.make_layer(S.CONFIGS["tiny"], S.SEEDS["tiny"])
+    return host, M.DeviceLayer(host)
+
+
+@pytest.fixture(scope="module")
+def decode(M):
+    host = S.make_layer(S.CONFIGS["decode"], S.SEEDS["decode"])
+    return host, M.DeviceLayer(host)
+
+
+@pytest.fixture(scope="module")
+def prefill(M):
+    host = S.make_layer(S.CONFIGS["prefill128"], S.SEEDS["prefill128"])
+    return host, M.DeviceLayer(host)
+
+
+def packed_dev(M, qt):
+    return torch.from_numpy(M.pack(qt)).cuda()
+
+
+@pytest.mark.parametrize("which", ["router", "gate", "down", "shared_gate"])
+@pytest.mark.parametrize("cfg", ["tiny", "decode"])
+def test_codes_and_dequant_bit_exact(M, cfg, which):
+    log("codes/dequant", cfg, which)
+    host = S.make_layer(S.CONFIGS[cfg], S.SEEDS[cfg])
+    qt = getattr(host, which)
+    if qt.codes.ndim == 3:
+        qt = qt.select(3)
+    buf = packed_dev(M, qt)
+    codes = M.debug_unpack_codes(buf, qt.rows, qt.cols, qt.bits).cpu().numpy()
+    w = M.debug_dequant(buf, qt.rows, qt.cols, qt.bits).cpu().numpy()
+    if qt.rows * qt.cols <= 64 * 1024:
+        assert np.array_equal(codes, O.codes(qt))
+    W = O.dequant(qt)
+    assert np.array_equal(w.astype(np.float64), W)        # exact: s*(q - 2^(b-1)) fits fp32
+    # codes through the dequantised values: q = (w - b) / s exactly
+    s = np.repeat(S.bf16_bits_to_f32(qt.scales).astype(np.float64), 64, axis=1)
+    b = np.repeat(S.bf16_bits_to_f32(qt.biases).astype(np.float64), 64, axis=1)
+    assert np.array_equal(codes.astype(np.float64), (W - b) / s)
+
+
+@pytest.mark.parametrize("path", ["gemv", "grouped"])
+@pytest.mark.parametrize("T", [1, 4, 5, 17, 40])
+def test_tiny_layer(M, tiny, path, T):
+    host, dev = tiny
+    log("tiny layer", path, "T=%d" % T)
+    x = S.make_tokens(S.SEEDS["tiny"] + T, T, host.cfg.hidden)
+    ref = O.forward(host, x)
+    got = run_gpu(M, dev, x, path)
+    ok, _ = check_routing(ref, got, host.cfg.top_k)
+    rel = check_output(ref, got, ok)
+    log("  max err / RMS = %.3g" % rel)
+
+
+@pytest.mark.parametrize("path", ["gemv", "grouped"])
+def test_zero_input(M, tiny, path):
+    host, dev = tiny
+    log("zero input", path)
+    x = np.zeros((3, host.cfg.hidden), np.uint16)
+    got = run_gpu(M, dev, x, path)
+    k = host.cfg.top_k
+    assert np.array_equal(got["ids"], np.tile(np.arange(k), (3, 1)))
+    assert np.all(got["w"] == np.float32(1.0 / k))
+    assert np.all(got["out32"] == 0.0) and np.all(got["out16"] == 0)
+
+
+def test_tiny_zipf_and_scales(M):
+    log("tiny layer with router_scale, per_expert_scale and Zipf bias")
+    host = S.make_layer(S.CONFIGS["tiny"], S.SEEDS["tiny"] + 99)
+    rng = np.random.default_rng(5)
+    host.router_scale = rng.uniform(0.5, 1.5, host.cfg.hidden).astype(np.float32)
+    host.per_expert_scale = rng.uniform(0.5, 2.0, host.cfg.num_experts).astype(np.float32)
+    host.logit_bias = S.zipf_logit_bias(3, 0, host.cfg.num_experts)
+    dev = M.DeviceLayer(host)
+    x = S.make_tokens(77, 24, host.cfg.hidden)
+    ref = O.forward(host, x)
+    for path in ("gemv", "grouped"):
+        got = run_gpu(M, dev, x, path)
+        ok, _ = check_routing(ref, got, host.cfg.top_k)
+        check_output(ref, got, ok)
+
+
+def test_no_shared_expert(M):
+    log("tiny layer without shared expert")
+    host = S.make_layer(S.CONFIGS["tiny"], S.SEEDS["tiny"] + 7, shared=False)
+    dev = M.DeviceLayer(host)
+    x = S.make_tokens(78, 9, host.cfg.hidden)
+    ref = O.forward(host, x)
+    for path in ("gemv", "grouped"):
+        got = run_gpu(M, dev, x, path)
+        ok, _ = check_routing(ref, got, host.cfg.top_k)
+        check_output(ref, got, ok)
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_decode_layer(M, decode, T):
+    host, dev = decode
+    log("decode layer (H2816 E128 k8 I704 Is2112)", "T=%d" % T)
+    x = S.make_tokens(S.SEEDS["decode"], T, host.cfg.hidden, batch=T)
+    ref = O.forward(host, x, threads=T, dense_experts=False)
+    got = run_gpu(M, dev, x, "gemv")
+    ok, excused = check_routing(ref, got, host.cfg.top_k)
+    rel = check_output(ref, got, ok)
+    log("  max err / RMS = %.3g, near-ties excused %d" % (rel, excused))
+    got_a = run_gpu(M, dev, x, "auto")
+    assert np.array_equal(got_a["out16"], got["out16"])
+
+
+def test_decode_grouped_path(M, decode):
+    host, dev = decode
+    log("decode layer through the grouped path, T=2")
+    x = S.make_tokens(S.SEEDS["decode"] + 5, 2, host.cfg.hidden)
+    ref = O.forward(host, x, threads=2, dense_experts=False)
+    got = run_gpu(M, dev, x, "grouped")
+    ok, _ = check_routing(ref, got, host.cfg.top_k)
+    check_output(ref, got, ok)
+
+
+def test_prefill128_layer(M, prefill):
+    host, dev = prefill
+    T = 128
+    log("prefill layer T=128 with Zipf routing: every routing decision, 12 sampled outputs")
+    x = S.make_tokens(S.SEEDS["prefill128"], T, host.cfg.hidden)
+    got = run_gpu(M, dev, x, "auto")
+    # all routing decisions from the oracle's router
+    ref_ids = np.empty((T, host.cfg.top_k), np.int32)
+    ref_w = np.empty((T, host.cfg.top_k))
+    ref_lg = np.empty((T, host.cfg.num_experts))
+    for t in range(T):
+        ref_lg[t] = O.router_logits(host, x[t])
+        ref_ids[t], ref_w[t] = O.topk(host, ref_lg[t])
+    ok, excused = check_routing(dict(ids=ref_ids, w=ref_w, logits=ref_lg), got, host.cfg.top_k)
+    counts = np.bincount(got["ids"].ravel(), minlength=host.cfg.num_experts)
+    log("  experts touched %d, max tokens per expert %d, near-ties %d" % ((counts > 0).sum(), counts.max(), excused))
+    sample = np.random.default_rng(1).choice(T, 12, replace=False)
+    sample = np.union1d(sample, [0, T - 1])
+    ref = O.forward(host, x[sample], threads=8, dense_experts=False)
+    sub = {key: got[key][sample] for key in ("ids", "w", "logits", "out32", "out16")}
+    rel = check_output(ref, sub, ok[sample])
+    log("  max err / RMS = %.3g" % rel)
+
+
+def test_grouped_matches_gemv_on_prefill(M, prefill):
+    host, dev = prefill
+    log("prefill layer T=8: grouped vs GEMV path")
+    x = S.make_tokens(S.SEEDS["prefill128"] + 1, 8, host.cfg.hidden)
+    a = run_gpu(M, dev, x, "gemv")
+    b = run_gpu(M, dev, x, "grouped")
+    assert np.array_equal(a["ids"], b["ids"])
+    rms = np.sqrt(np.mean(a["out32"] ** 2))
+    assert np.max(np.abs(a["out32"] - b["out32"])) <= 1e-2 * rms
+
+
+@pytest.mark.parametrize("path", ["gemv", "grouped"])
+def test_deterministic(M, decode, path):
+    host, dev = decode
+    log("determinism", path)
+    x = S.make_tokens(123, 6, host.cfg.hidden)
+    a = run_gpu(M, dev, x, path)
+    b = run_gpu(M, dev, x, path)
+    assert np.array_equal(a["out32"], b["out32"]) and np.array_equal(a["ids"], b["ids"])
+
+
+def test_rmsnorm(M):
+    log("rmsnorm between layers")
+    x = S.make_tokens(5, 7, 2816)
+    want = O.rmsnorm_bf16(x, 1e-6)
+    got = bf16_bits(M.rmsnorm(bf16_tensor(x), eps=1e-6))
+    diff = np.abs(got.astype(np.int32) - want.astype(np.int32))
+    assert diff.max() <= 1 and np.count_nonzero(diff) <= x.size // 1000
+
+
+def test_tiny_stack(M):
+    log("4-layer tiny stack with RMS norm between layers")
+    cfg = S.CONFIGS["tiny"]
+    hosts = [S.make_layer(cfg, S.SEEDS["tiny"], layer=l) for l in range(4)]
+    devs = [M.DeviceLayer(h) for h in hosts]
+    x0 = S.make_tokens(S.SEEDS["tiny"], 2, cfg.hidden)
+    xr, xg = x0, bf16_tensor(x0)
+    for l, (h, d) in enumerate(zip(hosts, devs)):
+        ref = O.forward(h, xr)
+        ids = torch.empty((2, cfg.top_k), dtype=torch.int32, device="cuda")
+        og = M.moe_layer_forward(d, xg, topk_ids=ids)
+        assert np.array_equal(ids.cpu().numpy(), ref["ids"])
+        if l < 3:
+            xr = O.rmsnorm_bf16(ref["out_bf16"], cfg.eps)
+            xg = M.rmsnorm(og, eps=cfg.eps)
+    torch.cuda.synchronize()
+    out = bf16_bits(og).astype(np.uint32) << 16
+    outf = out.view(np.float32).astype(np.float64)
+    rms = np.sqrt(np.mean(ref["out64"] ** 2))
+    assert np.max(np.abs(outf - ref["out64"])) <= 1e-2 * rms + np.max(np.abs(ref["out64"])) * 2 ** -8

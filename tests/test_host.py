@@ -1,0 +1,203 @@
+"""Host-side logic of the C-ABI library, checked without a GPU: exported
+symbols, packed sizes against the pages' byte counts, the DEV_V1 layout
+against its written description, the lossless pack/unpack round trip, and
+argument validation (every rejected call returns before touching the GPU)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import qmoe_synth as S
+import quantized_moe_gemv_amd as M
+from test_oracle_pins import page_constants
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "moegemv.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(mq_\w+|moe_\w+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert set(names) == set(M.EXPORTS)
+    lib = ctypes.CDLL(M.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_expert_blob_sizes_match_pages():
+    pc = page_constants()
+    cfg = S.CONFIGS["decode"]
+    H, I = cfg.hidden, cfg.inter
+    blob = 2 * M.packed_bytes(I, H, 4) + M.packed_bytes(H, I, 4)
+    canon = 2 * M.packed_bytes(I, H, 4, M.LAYOUT_CANONICAL) + M.packed_bytes(H, I, 4, M.LAYOUT_CANONICAL)
+    assert blob == canon == 3345408        # no padding at these shapes
+    pool = M.pool_layout(H, I, page_bytes=pc["page_bytes"])
+    assert pool.expert_stride == pc["page_rounded_expert_blob_bytes"]
+    assert pc["num_layers"] * cfg.num_experts * pool.expert_stride == pc["routed_expert_files_bytes"]
+    assert pool.gate_offset == 0 and pool.up_offset == M.packed_bytes(I, H, 4)
+    assert pool.down_offset == 2 * M.packed_bytes(I, H, 4)
+
+
+def test_packed_bytes_rejects_unsupported():
+    assert M.packed_bytes(64, 100, 4) == 0
+    assert M.packed_bytes(64, 128, 3) == 0
+    assert M._lib.mq_packed_bytes(64, 128, 4, 32, 1) == 0
+    assert M.packed_bytes(0, 128, 4) == 0
+    assert M.packed_bytes(65, 128, 4) == 2 * 2 * 2304      # rows padded to 128
+
+
+def dev_word_expected(q, bits, t, g, j, lane, i):
+    """The DEV_V1 word (j, lane, i) of block (t, g), from the header's description."""
+    a = 4 * j + i
+    if bits == 4:
+        r, c0, n = 16 * (a >> 1) + lane % 16, 32 * (a & 1) + 8 * (lane // 16), 8
+        pos = [4 * (e // 2) + 16 * (e % 2) for e in range(8)]
+    else:
+        r, c0, n = 16 * (a >> 2) + lane % 16, 16 * (a & 3) + 4 * (lane // 16), 4
+        pos = [8 * e for e in range(4)]
+    row = 64 * t + r
+    if row >= q.shape[0]:
+        return 0
+    w = 0
+    for e in range(n):
+        w |= int(q[row, 64 * g + c0 + e]) << pos[e]
+    return w
+
+
+@pytest.mark.parametrize("bits,rows,cols", [(4, 64, 128), (4, 80, 192), (8, 16, 256), (8, 130, 64)])
+def test_dev_layout_matches_description(bits, rows, cols):
+    from test_oracle_pins import qtensor_from_codes
+    rng = np.random.default_rng(rows + bits)
+    q = rng.integers(0, 1 << bits, size=(rows, cols))
+    sc = rng.integers(0, 1 << 16, size=(rows, cols // 64)).astype(np.uint16)
+    bi = rng.integers(0, 1 << 16, size=(rows, cols // 64)).astype(np.uint16)
+    qt = qtensor_from_codes(q, sc, bi, bits)
+    packed = M.pack(qt)
+    blk = 2304 if bits == 4 else 4352
+    ncode = 2048 if bits == 4 else 4096
+    G = cols // 64
+    tiles = (rows + 63) // 64
+    assert packed.size == tiles * G * blk
+    words = packed.view("<u4")
+    for t in range(tiles):
+        for g in range(G):
+            base = (t * G + g) * blk // 4
+            for (j, lane, i) in [(0, 0, 0), (0, 17, 3), (1, 63, 1), (1, 40, 2), (bits // 4 * 2 - 1, 5, 3)]:
+                got = int(words[base + (j * 64 + lane) * 4 + i])
+                assert got == dev_word_expected(q, bits, t, g, j, lane, i)
+            for r16 in (0, 7, 15):
+                for m in range(4):
+                    row = 64 * t + 16 * m + r16
+                    got = int(words[base + ncode // 4 + r16 * 4 + m])
+                    want = 0 if row >= rows else int(sc[row, g]) | (int(bi[row, g]) << 16)
+                    assert got == want
+
+
+@pytest.mark.parametrize("bits,rows,cols", [(4, 704, 2816), (4, 2816, 704), (8, 128, 2816), (4, 100, 64), (8, 16, 256)])
+def test_pack_unpack_round_trip_is_exact(bits, rows, cols):
+    tensor = S.T_GATE_CODES if bits == 4 else S.T_ROUTER_CODES
+    qt = S.make_qtensor(11, 0, 0, tensor, tensor + 1, rows, cols, bits)
+    packed = M.pack(qt)
+    c, s, b = M.unpack(packed, rows, cols, bits)
+    assert np.array_equal(c, qt.codes) and np.array_equal(s, qt.scales) and np.array_equal(b, qt.biases)
+    if bits == 8 and rows % 64 == 0:
+        # 8-bit packing moves whole bytes: the same multiset of bytes
+        canon = np.concatenate([qt.codes.view(np.uint8).ravel(), qt.scales.view(np.uint8).ravel(),
+                                qt.biases.view(np.uint8).ravel()])
+        assert np.array_equal(np.sort(packed), np.sort(canon))
+
+
+# ------------------------------------------------------------------ validation (no GPU involved)
+
+FAKE = 1 << 32   # a 256-aligned address that is never dereferenced
+
+
+def fake_layer(E=16, H=256, I=64, Is=128, k=2, bits=8):
+    pool = M.pool_layout(H, I, page_bytes=4096)
+    pool.base = FAKE
+    pool.num_experts = E
+    rw = M.MqQTensor(FAKE, None, None, E, H, bits, 64, M.LAYOUT_DEV_V1)
+    router = M.MqRouter(rw, None, None, None, k, 1e-6)
+    sh = M.MqShared(M.MqQTensor(FAKE, None, None, Is, H, 4, 64, 1), M.MqQTensor(FAKE, None, None, Is, H, 4, 64, 1),
+                    M.MqQTensor(FAKE, None, None, H, Is, 4, 64, 1))
+    return router, pool, sh
+
+
+def call(router, pool, sh, T=4, H=256, ws_bytes=None, x_ptr=FAKE, out_ptr=FAKE, x_dtype=0, path=0, ws_ptr=FAKE,
+         x_stride=None):
+    x = M.MqAct(x_ptr, T, H, x_dtype, H if x_stride is None else x_stride)
+    out = M.MqAct(out_ptr, T, H, 0, H)
+    if ws_bytes is None:
+        ws_bytes = M._lib.mq_workspace_bytes(ctypes.byref(router), ctypes.byref(pool),
+                                             None if sh is None else ctypes.byref(sh), max(T, 1))
+    opts = M.MqOpts(path, None, None, None, ws_ptr, ws_bytes)
+    return M._lib.moe_layer_forward(ctypes.byref(x), ctypes.byref(router), ctypes.byref(pool),
+                                    None if sh is None else ctypes.byref(sh), ctypes.byref(out),
+                                    ctypes.byref(opts), None)
+
+
+def test_zero_tokens_is_a_no_op():
+    r, p, s = fake_layer()
+    assert call(r, p, s, T=0, x_ptr=None, out_ptr=None, ws_ptr=None) == M.MQ_OK
+
+
+def test_workspace_bytes_grows_with_tokens_and_rejects_bad_layers():
+    r, p, s = fake_layer()
+    f = lambda T: M._lib.mq_workspace_bytes(ctypes.byref(r), ctypes.byref(p), ctypes.byref(s), T)
+    assert 0 < f(1) < f(16) < f(128)
+    r.w.bits = 4
+    assert f(1) == 0
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (lambda r, p, s: setattr(r.w, "bits", 4), M.MQ_ERR_UNSUPPORTED),
+    (lambda r, p, s: setattr(r.w, "group", 32), M.MQ_ERR_UNSUPPORTED),
+    (lambda r, p, s: setattr(r.w, "layout", M.LAYOUT_CANONICAL), M.MQ_ERR_UNSUPPORTED),
+    (lambda r, p, s: setattr(p, "bits", 8), M.MQ_ERR_UNSUPPORTED),
+    (lambda r, p, s: setattr(r, "top_k", 0), M.MQ_ERR_SHAPE),
+    (lambda r, p, s: setattr(r, "top_k", 17), M.MQ_ERR_SHAPE),
+    (lambda r, p, s: setattr(r.w, "rows", 15), M.MQ_ERR_SHAPE),
+    (lambda r, p, s: setattr(p, "inter", 96), M.MQ_ERR_SHAPE),
+    (lambda r, p, s: setattr(p, "num_experts", 300), M.MQ_ERR_SHAPE),
+    (lambda r, p, s: setattr(p, "base", FAKE + 16), M.MQ_ERR_ALIGN),
+    (lambda r, p, s: setattr(r.w, "codes", FAKE + 64), M.MQ_ERR_ALIGN),
+    (lambda r, p, s: setattr(p, "expert_stride", p.expert_stride + 16), M.MQ_ERR_ALIGN),
+    (lambda r, p, s: setattr(p, "expert_stride", 256), M.MQ_ERR_SHAPE),
+    (lambda r, p, s: setattr(p, "base", None), M.MQ_ERR_NULL),
+    (lambda r, p, s: setattr(s.down, "cols", 64), M.MQ_ERR_SHAPE),
+    (lambda r, p, s: setattr(s.gate, "codes", None), M.MQ_ERR_NULL),
+    (lambda r, p, s: setattr(s.up, "codes", FAKE + 32), M.MQ_ERR_ALIGN),
+    (lambda r, p, s: setattr(r, "eps", float("nan")), M.MQ_ERR_SHAPE),
+])
+def test_invalid_layers_are_rejected(mutate, status):
+    r, p, s = fake_layer()
+    ws = M._lib.mq_workspace_bytes(ctypes.byref(r), ctypes.byref(p), ctypes.byref(s), 4)
+    mutate(r, p, s)
+    assert call(r, p, s, ws_bytes=ws) == status
+
+
+def test_invalid_calls_are_rejected():
+    r, p, s = fake_layer()
+    assert call(r, p, s, ws_bytes=1000) == M.MQ_ERR_WORKSPACE
+    assert call(r, p, s, ws_ptr=None) == M.MQ_ERR_WORKSPACE
+    assert call(r, p, s, x_ptr=None) == M.MQ_ERR_NULL
+    assert call(r, p, s, x_dtype=M.DTYPE_F32) == M.MQ_ERR_UNSUPPORTED
+    assert call(r, p, s, H=128) == M.MQ_ERR_SHAPE
+    assert call(r, p, s, x_ptr=FAKE + 2) == M.MQ_ERR_ALIGN
+    assert call(r, p, s, x_stride=260) == M.MQ_ERR_ALIGN
+    assert call(r, p, s, x_stride=100) == M.MQ_ERR_SHAPE
+    assert call(r, p, s, ws_ptr=FAKE + 128) == M.MQ_ERR_ALIGN
+    assert call(r, p, s, path=7) == M.MQ_ERR_UNSUPPORTED
+    assert M._lib.moe_layer_forward(None, None, None, None, None, None, None) == M.MQ_ERR_NULL
+
+
+def test_status_strings():
+    for st in range(-7, 1):
+        assert M.status_str(st) and M.status_str(st) != "unknown status"
+    assert M.status_str(-99) == "unknown status"
