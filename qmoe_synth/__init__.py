@@ -271,12 +271,23 @@ class Layer:
     index: int = 0
 
 
-def make_layer(cfg: LayerConfig, seed: int, layer: int = 0, shared: bool = True) -> Layer:
+def make_expert(cfg: LayerConfig, seed: int, layer: int, expert: int):
+    """(gate, up, down) of one routed expert; the same values make_layer draws for it."""
+    H, I = cfg.hidden, cfg.inter
+    return (make_qtensor(seed, layer, expert, T_GATE_CODES, T_GATE_SCALES, I, H, 4),
+            make_qtensor(seed, layer, expert, T_UP_CODES, T_UP_SCALES, I, H, 4),
+            make_qtensor(seed, layer, expert, T_DOWN_CODES, T_DOWN_SCALES, H, I, 4))
+
+
+def make_layer(cfg: LayerConfig, seed: int, layer: int = 0, shared: bool = True, experts: bool = True) -> Layer:
+    """A full layer; with experts=False the routed experts are left out (None)."""
     H, E, I, Is = cfg.hidden, cfg.num_experts, cfg.inter, cfg.shared_inter
     router = make_qtensor(seed, layer, SHARED_SLOT, T_ROUTER_CODES, T_ROUTER_SCALES, E, H, 8)
-    gate = make_qtensor(seed, layer, 0, T_GATE_CODES, T_GATE_SCALES, I, H, 4, batch=E)
-    up = make_qtensor(seed, layer, 0, T_UP_CODES, T_UP_SCALES, I, H, 4, batch=E)
-    down = make_qtensor(seed, layer, 0, T_DOWN_CODES, T_DOWN_SCALES, H, I, 4, batch=E)
+    gate = up = down = None
+    if experts:
+        gate = make_qtensor(seed, layer, 0, T_GATE_CODES, T_GATE_SCALES, I, H, 4, batch=E)
+        up = make_qtensor(seed, layer, 0, T_UP_CODES, T_UP_SCALES, I, H, 4, batch=E)
+        down = make_qtensor(seed, layer, 0, T_DOWN_CODES, T_DOWN_SCALES, H, I, 4, batch=E)
     sg = su = sd = None
     if shared and Is > 0:
         sg = make_qtensor(seed, layer, SHARED_SLOT, T_SGATE_CODES, T_SGATE_SCALES, Is, H, 4)

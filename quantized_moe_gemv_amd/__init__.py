@@ -8,6 +8,7 @@ with an ImportError when the HIP library has not been built (run
 """
 from __future__ import annotations
 
+import copy
 import ctypes
 import os
 from concurrent.futures import ThreadPoolExecutor
@@ -156,6 +157,14 @@ def pool_layout(hidden: int, inter: int, page_bytes: int = 16384, bits: int = 4)
     return pool
 
 
+def pack_expert_into(pool: MqExpertPool, e: int, gate, up, down, host: np.ndarray) -> None:
+    """Pack one expert's canonical (gate, up, down) into its blob of a host pool buffer."""
+    base = e * pool.expert_stride
+    pack_into(gate, host, base + pool.gate_offset)
+    pack_into(up, host, base + pool.up_offset)
+    pack_into(down, host, base + pool.down_offset)
+
+
 # ------------------------------------------------------------------ device layer
 
 class DeviceLayer:
@@ -166,7 +175,8 @@ class DeviceLayer:
     num_experts * expert_stride bytes, each blob page-rounded.
     """
 
-    def __init__(self, src, device="cuda", page_bytes: int = 16384, threads: int = 16):
+    def __init__(self, src, device="cuda", page_bytes: int = 16384, threads: int = 16,
+                 pool_host: Optional[np.ndarray] = None):
         cfg = src.cfg
         self.hidden, self.num_experts, self.inter = cfg.hidden, cfg.num_experts, cfg.inter
         self.top_k, self.eps = cfg.top_k, cfg.eps
@@ -174,15 +184,17 @@ class DeviceLayer:
         E = self.num_experts
         self.pool = pool_layout(self.hidden, self.inter, page_bytes)
         stride = self.pool.expert_stride
-        host = np.zeros(E * stride, dtype=np.uint8)
+        if pool_host is not None:
+            # experts already packed by the caller (e.g. with pack_pool_into)
+            assert pool_host.dtype == np.uint8 and pool_host.size == E * stride
+            host = pool_host
+        else:
+            host = np.zeros(E * stride, dtype=np.uint8)
 
-        def pack_expert(e):
-            base = e * stride
-            pack_into(src.gate.select(e), host, base + self.pool.gate_offset)
-            pack_into(src.up.select(e), host, base + self.pool.up_offset)
-            pack_into(src.down.select(e), host, base + self.pool.down_offset)
-        with ThreadPoolExecutor(threads) as ex:
-            list(ex.map(pack_expert, range(E)))
+            def pack_expert(e):
+                pack_expert_into(self.pool, e, src.gate.select(e), src.up.select(e), src.down.select(e), host)
+            with ThreadPoolExecutor(threads) as ex:
+                list(ex.map(pack_expert, range(E)))
         self.pool_buf = torch.from_numpy(host).to(device)
         del host
         self.pool.base = self.pool_buf.data_ptr()
@@ -206,6 +218,14 @@ class DeviceLayer:
             self.su_buf, su = dev_tensor(src.shared_up)
             self.sd_buf, sd = dev_tensor(src.shared_down)
             self.shared = MqShared(sg, su, sd)
+
+    def with_logit_bias(self, bias: Optional[torch.Tensor]) -> "DeviceLayer":
+        """The same resident layer with another additive router score bias."""
+        other = copy.copy(self)
+        other.logit_bias = bias
+        other.router = MqRouter(self.router_w, self.router.router_scale, self.router.per_expert_scale,
+                                None if bias is None else bias.data_ptr(), self.top_k, self.eps)
+        return other
 
     def workspace_bytes(self, max_tokens: int) -> int:
         n = _lib.mq_workspace_bytes(ctypes.byref(self.router), ctypes.byref(self.pool), _ref(self.shared),

@@ -23,15 +23,17 @@ inline constexpr int64_t pad_rows(int64_t rows) { return (rows + kTileRows - 1) 
 
 // Canonical 4-bit word (column e of eight at bit 4e) -> device order
 // (column e at bit 4*(e/2) + 16*(e%2)), and back.
-inline uint32_t nib_to_dev(uint32_t w) {
-    uint32_t r = 0;
-    for (int e = 0; e < 8; ++e) r |= ((w >> (4 * e)) & 0xFu) << (4 * (e >> 1) + 16 * (e & 1));
-    return r;
+inline uint32_t compact_nibbles(uint32_t v) {   // low nibbles of the 4 bytes -> bits 0..15
+    v &= 0x0F0F0F0Fu;
+    v = (v | (v >> 4)) & 0x00FF00FFu;
+    return (v | (v >> 8)) & 0x0000FFFFu;
 }
-inline uint32_t nib_from_dev(uint32_t w) {
-    uint32_t r = 0;
-    for (int e = 0; e < 8; ++e) r |= ((w >> (4 * (e >> 1) + 16 * (e & 1))) & 0xFu) << (4 * e);
-    return r;
+inline uint32_t spread_nibbles(uint32_t v) {    // inverse of compact_nibbles
+    v &= 0x0000FFFFu;
+    v = (v | (v << 8)) & 0x00FF00FFu;
+    return (v | (v << 4)) & 0x0F0F0F0Fu;
 }
+inline uint32_t nib_to_dev(uint32_t w) { return compact_nibbles(w) | (compact_nibbles(w >> 4) << 16); }
+inline uint32_t nib_from_dev(uint32_t w) { return spread_nibbles(w) | (spread_nibbles(w >> 16) << 4); }
 
 }  // namespace mq

@@ -218,3 +218,30 @@ def test_tiny_stack(M):
     outf = out.view(np.float32).astype(np.float64)
     rms = np.sqrt(np.mean(ref["out64"] ** 2))
     assert np.max(np.abs(outf - ref["out64"])) <= 1e-2 * rms + np.max(np.abs(ref["out64"])) * 2 ** -8
+
+
+@pytest.mark.parametrize("path", ["gemv", "grouped"])
+def test_graph_replay_matches_eager(M, tiny, path):
+    host, dev = tiny
+    log("hip graph replay vs eager", path)
+    xs = [bf16_tensor(S.make_tokens(900 + i, 5, host.cfg.hidden)) for i in range(3)]
+    ws = dev.new_workspace(5)
+    eager = [M.moe_layer_forward(dev, x, workspace=ws, path=path, out_dtype=torch.float32).clone() for x in xs]
+    outs = [torch.empty((5, host.cfg.hidden), dtype=torch.float32, device="cuda") for _ in xs]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for x, o in zip(xs, outs):
+                M.moe_layer_forward(dev, x, out=o, workspace=ws, path=path)
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        M.moe_layer_forward(dev, xs[rep], workspace=ws, path=path)   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e), "replay %d differs from eager" % rep
