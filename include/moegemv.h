@@ -54,7 +54,11 @@ typedef enum {
 
 enum { MQ_LAYOUT_CANONICAL = 0, MQ_LAYOUT_DEV_V1 = 1 };
 enum { MQ_DTYPE_BF16 = 0, MQ_DTYPE_F32 = 1 };
-enum { MQ_PATH_AUTO = 0, MQ_PATH_GEMV = 1, MQ_PATH_GROUPED = 2 };
+/* Kernel schedule.  AUTO: FUSED for one token, GEMV up to 4 tokens, GROUPED
+ * above.  FUSED (one token only): one launch for the whole layer.  GEMV:
+ * per-(token, expert) dot-product kernels.  GROUPED: tokens sorted by
+ * expert, dequantised weights on the matrix cores. */
+enum { MQ_PATH_AUTO = 0, MQ_PATH_GEMV = 1, MQ_PATH_GROUPED = 2, MQ_PATH_FUSED = 3 };
 
 /*
  * A group-64 affine-quantized matrix W [rows][cols], codes of `bits` bits.

@@ -28,7 +28,7 @@ MQ_OK, MQ_ERR_NULL, MQ_ERR_SHAPE, MQ_ERR_ALIGN = 0, -1, -2, -3
 MQ_ERR_UNSUPPORTED, MQ_ERR_WORKSPACE, MQ_ERR_HIP, MQ_ERR_BUFFER = -4, -5, -6, -7
 LAYOUT_CANONICAL, LAYOUT_DEV_V1 = 0, 1
 DTYPE_BF16, DTYPE_F32 = 0, 1
-PATHS = {"auto": 0, "gemv": 1, "grouped": 2}
+PATHS = {"auto": 0, "gemv": 1, "grouped": 2, "fused": 3}
 GROUP = 64
 EXPORTS = ["moe_layer_forward", "mq_workspace_bytes", "mq_rmsnorm", "mq_packed_bytes", "mq_pool_layout",
            "mq_pack", "mq_unpack", "mq_debug_unpack_codes", "mq_debug_dequant", "mq_status_str"]

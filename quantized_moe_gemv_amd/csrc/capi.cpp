@@ -15,6 +15,7 @@ __global__ void k_down(Plan p);
 __global__ void k_combine(Plan p);
 __global__ void k_rmsnorm(const uint16_t* x, int64_t xs, uint16_t* y, int64_t ys, int H, float eps);
 __global__ void k_debug_read(const uint8_t* data, int rows, int cols, int bits, uint8_t* codes_out, float* w_out);
+__global__ void k_decode(Plan p);
 mq_status launch_grouped(const Plan& p, hipStream_t s);
 }  // namespace mq
 
@@ -29,7 +30,31 @@ inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 struct Sizes {
     int H, E, E_pad, k, I, Is, G_H, G_I, G_s, rsplit, rgroups, ntile, max_tiles;
+    int n_router, n_sg, n_rg, n_src, n_bundles, n_units;
 };
+
+// State of the single-launch decode that persists across calls.  It sits at
+// the start of the workspace, at offsets that do not depend on the token
+// count, and no other kernel writes it.
+struct FusedCarve {
+    size_t logit, hs, h, piece, ctr, bundle, total;
+};
+
+FusedCarve fused_carve(const Sizes& z) {
+    FusedCarve f;
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
+    f.logit = take((size_t)z.E_pad * 8);
+    f.hs = take((size_t)z.Is * 8 + 8);
+    f.h = take((size_t)z.k * z.I * 8);
+    f.piece = take((size_t)z.n_bundles * z.n_src * 128 * 8);
+    f.ctr = take(4 * 4);
+    f.bundle = take((size_t)z.n_bundles * 4);
+    f.total = o;
+    return f;
+}
+
+bool fused_ok(const Sizes& z) { return z.H <= 4096 && z.G_I <= 16; }
 
 // Offsets of every workspace region for up to T tokens; returns the total.
 struct Carve {
@@ -40,7 +65,7 @@ struct Carve {
 
 Carve carve(const Sizes& z, int64_t T) {
     Carve c;
-    size_t o = 0;
+    size_t o = fused_carve(z).total;
     auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
     c.r = take(T * z.H * 4);
     c.rsum8 = take(T * z.G_H * 16);
@@ -122,6 +147,12 @@ mq_status check_layer(const mq_router* rt, const mq_expert_pool* pool, const mq_
     z->rgroups = 4;
     z->rsplit = (z->G_H + z->rgroups - 1) / z->rgroups;
     z->ntile = 16;
+    z->n_router = (E + 15) / 16;
+    z->n_sg = 2 * z->G_s;
+    z->n_rg = 2 * z->k * z->G_I;
+    z->n_src = z->k + (z->G_s + z->G_I - 1) / z->G_I;
+    z->n_bundles = (2 * z->G_H + 3) / 4;
+    z->n_units = z->n_router + z->n_sg + z->n_rg + z->n_bundles * z->n_src;
     return MQ_OK;
 }
 
@@ -152,7 +183,8 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
     if (x->dtype != MQ_DTYPE_BF16 || (out->dtype != MQ_DTYPE_BF16 && out->dtype != MQ_DTYPE_F32))
         return MQ_ERR_UNSUPPORTED;
     if (x->row_stride < x->hidden || out->row_stride < out->hidden) return MQ_ERR_SHAPE;
-    if (opts->path < MQ_PATH_AUTO || opts->path > MQ_PATH_GROUPED) return MQ_ERR_UNSUPPORTED;
+    if (opts->path < MQ_PATH_AUTO || opts->path > MQ_PATH_FUSED) return MQ_ERR_UNSUPPORTED;
+    if (opts->path == MQ_PATH_FUSED && (T > 1 || !fused_ok(z))) return MQ_ERR_UNSUPPORTED;
     if (T == 0) return MQ_OK;
     if (!x->data || !out->data || !opts->workspace) return x->data && out->data ? MQ_ERR_WORKSPACE : MQ_ERR_NULL;
     if (!aligned(x->data, 16) || x->row_stride % 8) return MQ_ERR_ALIGN;
@@ -228,11 +260,38 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
     p.max_tiles = z.max_tiles;
     p.ntile = z.ntile;
 
-    const bool grouped = opts->path == MQ_PATH_GROUPED || (opts->path == MQ_PATH_AUTO && T > 4);
-    if (grouped) p.x16 = (_Float16*)(ws + c.x16);
+    const FusedCarve f = fused_carve(z);
+    p.f_logit = (uint64_t*)(ws + f.logit);
+    p.f_hs = (uint64_t*)(ws + f.hs);
+    p.f_h = (uint64_t*)(ws + f.h);
+    p.f_piece = (uint64_t*)(ws + f.piece);
+    uint32_t* ctr = (uint32_t*)(ws + f.ctr);
+    p.f_queue = ctr;
+    p.f_done = ctr + 1;
+    p.f_epoch = ctr + 2;
+    p.f_err = ctr + 3;
+    p.f_bundle = (uint32_t*)(ws + f.bundle);
+    p.n_units = z.n_units;
+    p.n_router = z.n_router;
+    p.n_sg = shared ? z.n_sg : 0;
+    p.n_rg = z.n_rg;
+    p.n_src = z.n_src;
+    p.n_bundles = z.n_bundles;
 
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
+    const bool fused = opts->path == MQ_PATH_FUSED || (opts->path == MQ_PATH_AUTO && T == 1 && fused_ok(z));
+    if (fused) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            return MQ_ERR_HIP;
+        hipLaunchKernelGGL(k_decode, dim3(cus), dim3(512), 0, s, p);
+        return hipGetLastError() == hipSuccess ? MQ_OK : MQ_ERR_HIP;
+    }
+    const bool grouped = opts->path == MQ_PATH_GROUPED || (opts->path == MQ_PATH_AUTO && T > 4);
+    if (grouped) p.x16 = (_Float16*)(ws + c.x16);
+
     hipLaunchKernelGGL(k_prep, dim3(T), dim3(256), 0, s, p);
     hipLaunchKernelGGL(k_router, dim3(z.E_pad / 64, z.rsplit, (T + kRouterTokens - 1) / kRouterTokens), dim3(256),
                        0, s, p);

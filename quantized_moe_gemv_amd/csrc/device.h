@@ -60,9 +60,12 @@ __device__ __forceinline__ float gelu_tanh(float z) {
     return 0.5f * z * (1.0f + tanhf(k * (z + 0.044715f * z * z * z)));
 }
 
-template <typename T>
-__device__ __forceinline__ T ld_nt(const T* p) {
-    return __builtin_nontemporal_load(p);
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (non-temporal: the weights are read once per call).
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+    const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 }  // namespace mq

@@ -68,6 +68,17 @@ struct Plan {
     _Float16* hs16;    // [T][Is]
     float* ysort;      // [T*k][H]   weighted expert outputs in sorted order
     float* ysh;        // [T][H]     shared expert outputs
+    // single-launch decode: tagged words and counters that persist across calls
+    uint64_t* f_logit;  // [E]            expert scores
+    uint64_t* f_hs;     // [Is]           shared GeGLU activations (bf16 hi | lo)
+    uint64_t* f_h;      // [k][I]         routed GeGLU activations
+    uint64_t* f_piece;  // [n_bundles][n_src][128] partial outputs
+    uint32_t* f_queue;  // work queue counter
+    uint32_t* f_done;   // finished-workgroup counter
+    uint32_t* f_epoch;  // calls completed with this workspace
+    uint32_t* f_err;    // non-zero if a bounded wait gave up
+    uint32_t* f_bundle; // [n_bundles] arrivals per output range
+    int n_units, n_router, n_sg, n_rg, n_src, n_bundles;
     int max_tiles;     // upper bound of scheduled (expert, token tile) pairs
     int ntile;         // tokens per grouped tile
 };

@@ -67,10 +67,12 @@ def test_codes_and_dequant_bit_exact(M, cfg, which):
     assert np.array_equal(codes.astype(np.float64), (W - b) / s)
 
 
-@pytest.mark.parametrize("path", ["gemv", "grouped"])
+@pytest.mark.parametrize("path", ["gemv", "grouped", "fused"])
 @pytest.mark.parametrize("T", [1, 4, 5, 17, 40])
 def test_tiny_layer(M, tiny, path, T):
     host, dev = tiny
+    if path == "fused" and T > 1:
+        pytest.skip("the single-launch path takes one token")
     log("tiny layer", path, "T=%d" % T)
     x = S.make_tokens(S.SEEDS["tiny"] + T, T, host.cfg.hidden)
     ref = O.forward(host, x)
@@ -80,14 +82,15 @@ def test_tiny_layer(M, tiny, path, T):
     log("  max err / RMS = %.3g" % rel)
 
 
-@pytest.mark.parametrize("path", ["gemv", "grouped"])
+@pytest.mark.parametrize("path", ["gemv", "grouped", "fused"])
 def test_zero_input(M, tiny, path):
     host, dev = tiny
     log("zero input", path)
-    x = np.zeros((3, host.cfg.hidden), np.uint16)
+    T = 1 if path == "fused" else 3
+    x = np.zeros((T, host.cfg.hidden), np.uint16)
     got = run_gpu(M, dev, x, path)
     k = host.cfg.top_k
-    assert np.array_equal(got["ids"], np.tile(np.arange(k), (3, 1)))
+    assert np.array_equal(got["ids"], np.tile(np.arange(k), (T, 1)))
     assert np.all(got["w"] == np.float32(1.0 / k))
     assert np.all(got["out32"] == 0.0) and np.all(got["out16"] == 0)
 
@@ -106,6 +109,11 @@ def test_tiny_zipf_and_scales(M):
         got = run_gpu(M, dev, x, path)
         ok, _ = check_routing(ref, got, host.cfg.top_k)
         check_output(ref, got, ok)
+    for t in (0, 5):
+        got = run_gpu(M, dev, x[t:t + 1], "fused")
+        sub = {key: ref[key][t:t + 1] for key in ref}
+        ok, _ = check_routing(sub, got, host.cfg.top_k)
+        check_output(sub, got, ok)
 
 
 def test_no_shared_expert(M):
@@ -118,6 +126,10 @@ def test_no_shared_expert(M):
         got = run_gpu(M, dev, x, path)
         ok, _ = check_routing(ref, got, host.cfg.top_k)
         check_output(ref, got, ok)
+    got = run_gpu(M, dev, x[:1], "fused")
+    sub = {key: ref[key][:1] for key in ref}
+    ok, _ = check_routing(sub, got, host.cfg.top_k)
+    check_output(sub, got, ok)
 
 
 @pytest.mark.parametrize("T", [1, 3])
@@ -130,8 +142,16 @@ def test_decode_layer(M, decode, T):
     ok, excused = check_routing(ref, got, host.cfg.top_k)
     rel = check_output(ref, got, ok)
     log("  max err / RMS = %.3g, near-ties excused %d" % (rel, excused))
-    got_a = run_gpu(M, dev, x, "auto")
-    assert np.array_equal(got_a["out16"], got["out16"])
+    if T == 1:
+        got_f = run_gpu(M, dev, x, "fused")
+        ok, _ = check_routing(ref, got_f, host.cfg.top_k)
+        rel = check_output(ref, got_f, ok)
+        log("  fused: max err / RMS = %.3g" % rel)
+        got_a = run_gpu(M, dev, x, "auto")
+        assert np.array_equal(got_a["out16"], got_f["out16"])
+    else:
+        got_a = run_gpu(M, dev, x, "auto")
+        assert np.array_equal(got_a["out16"], got["out16"])
 
 
 def test_decode_grouped_path(M, decode):
@@ -179,11 +199,11 @@ def test_grouped_matches_gemv_on_prefill(M, prefill):
     assert np.max(np.abs(a["out32"] - b["out32"])) <= 1e-2 * rms
 
 
-@pytest.mark.parametrize("path", ["gemv", "grouped"])
+@pytest.mark.parametrize("path", ["gemv", "grouped", "fused"])
 def test_deterministic(M, decode, path):
     host, dev = decode
     log("determinism", path)
-    x = S.make_tokens(123, 6, host.cfg.hidden)
+    x = S.make_tokens(123, 1 if path == "fused" else 6, host.cfg.hidden)
     a = run_gpu(M, dev, x, path)
     b = run_gpu(M, dev, x, path)
     assert np.array_equal(a["out32"], b["out32"]) and np.array_equal(a["ids"], b["ids"])
@@ -220,14 +240,15 @@ def test_tiny_stack(M):
     assert np.max(np.abs(outf - ref["out64"])) <= 1e-2 * rms + np.max(np.abs(ref["out64"])) * 2 ** -8
 
 
-@pytest.mark.parametrize("path", ["gemv", "grouped"])
+@pytest.mark.parametrize("path", ["gemv", "grouped", "fused"])
 def test_graph_replay_matches_eager(M, tiny, path):
     host, dev = tiny
     log("hip graph replay vs eager", path)
-    xs = [bf16_tensor(S.make_tokens(900 + i, 5, host.cfg.hidden)) for i in range(3)]
+    T = 1 if path == "fused" else 5
+    xs = [bf16_tensor(S.make_tokens(900 + i, T, host.cfg.hidden)) for i in range(3)]
     ws = dev.new_workspace(5)
     eager = [M.moe_layer_forward(dev, x, workspace=ws, path=path, out_dtype=torch.float32).clone() for x in xs]
-    outs = [torch.empty((5, host.cfg.hidden), dtype=torch.float32, device="cuda") for _ in xs]
+    outs = [torch.empty((T, host.cfg.hidden), dtype=torch.float32, device="cuda") for _ in xs]
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
@@ -245,3 +266,26 @@ def test_graph_replay_matches_eager(M, tiny, path):
         torch.cuda.synchronize()
         for o, e in zip(outs, eager):
             assert torch.equal(o, e), "replay %d differs from eager" % rep
+
+
+def test_fused_many_calls_interleaved(M, decode, tiny):
+    """The single-launch path keeps per-workspace state across calls: run it
+    many times, interleaved with the other paths and a second layer sharing
+    the workspace, and check every call against the first result."""
+    host, dev = decode
+    log("fused path: 50 interleaved calls on one workspace")
+    ws = dev.new_workspace(8)
+    xa = bf16_tensor(S.make_tokens(31, 1, host.cfg.hidden))
+    xb = bf16_tensor(S.make_tokens(32, 1, host.cfg.hidden))
+    x8 = bf16_tensor(S.make_tokens(33, 8, host.cfg.hidden))
+    ra = M.moe_layer_forward(dev, xa, workspace=ws, path="fused", out_dtype=torch.float32).clone()
+    rb = M.moe_layer_forward(dev, xb, workspace=ws, path="fused", out_dtype=torch.float32).clone()
+    rg = M.moe_layer_forward(dev, xa, workspace=ws, path="gemv", out_dtype=torch.float32).clone()
+    for i in range(50):
+        a = M.moe_layer_forward(dev, xa if i % 2 == 0 else xb, workspace=ws, path="fused", out_dtype=torch.float32)
+        assert torch.equal(a, ra if i % 2 == 0 else rb), "call %d" % i
+        if i % 10 == 3:
+            M.moe_layer_forward(dev, x8, workspace=ws, path="grouped")
+    torch.cuda.synchronize()
+    rms = float(torch.sqrt(torch.mean(rg.double() ** 2)))
+    assert float(torch.max(torch.abs(ra.double() - rg.double()))) <= 1e-4 * rms
