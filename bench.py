@@ -122,7 +122,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=60)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=16)
+    ap.add_argument("--cpu-tokens", type=int, default=64)
+    ap.add_argument("--path", default="auto", choices=["auto", "fused", "gemv", "grouped"])
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the layer runs on a single MI355X and has no multi-GPU path "
@@ -151,7 +152,7 @@ def main():
     def decode_call(i):
         dev = layers[i % len(layers)]
         x = xdev[i % n_tok:i % n_tok + 1]
-        return lambda: M.moe_layer_forward(dev, x, out=out, workspace=ws)
+        return lambda: M.moe_layer_forward(dev, x, out=out, workspace=ws, path=args.path)
     calls = [decode_call(i) for i in range(args.steps)]
     ms, _ = time_graph(torch, calls, args.steps, args.warmup)
     ms_eager = time_eager(torch, calls, min(args.steps, 300))

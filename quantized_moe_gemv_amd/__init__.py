@@ -4,7 +4,7 @@ Argument marshalling only: every step of the layer runs in the HIP kernels
 behind the C ABI of ``include/moegemv.h``.  PyTorch provides device memory
 and the stream; the library never allocates.  Importing this package fails
 with an ImportError when the HIP library has not been built (run
-``python -m quantized_moe_gemv_amd.build``); there is no CPU fallback.
+``python quantized_moe_gemv_amd/build.py``); there is no CPU fallback.
 """
 from __future__ import annotations
 
@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoegemv.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError("libmoegemv.so is not built: run `python -m quantized_moe_gemv_amd.build`")
+    raise ImportError("libmoegemv.so is not built: run `python quantized_moe_gemv_amd/build.py`")
 _lib = ctypes.CDLL(LIB_PATH)
 
 MQ_OK, MQ_ERR_NULL, MQ_ERR_SHAPE, MQ_ERR_ALIGN = 0, -1, -2, -3

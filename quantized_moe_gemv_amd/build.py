@@ -1,6 +1,8 @@
 """Build libmoegemv.so (HIP for gfx950) in the package directory.
 
-    python -m quantized_moe_gemv_amd.build
+    python quantized_moe_gemv_amd/build.py
+
+(Run it as a file: importing the package needs the library it builds.)
 """
 from __future__ import annotations
 

@@ -17,8 +17,8 @@ def _ensure_built():
     """Build the HIP library and the oracle when nothing is built yet."""
     lib = os.path.join(ROOT, "quantized_moe_gemv_amd", "libmoegemv.so")
     if not os.path.exists(lib):
-        from quantized_moe_gemv_amd import build as b
-        b.build()
+        import __graft_entry__
+        __graft_entry__._build_module().build()
     import oracle
     import qmoe_synth
     qmoe_synth._load()
