@@ -30,36 +30,35 @@ inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 struct Sizes {
     int H, E, E_pad, k, I, Is, G_H, G_I, G_s, rsplit, rgroups, ntile, max_tiles;
-    int rq, gq, n_router, n_sg, n_sd, n_sc, n_rg, n_rd, n_src, n_ctr;
+    int n_router, n_sg, n_sd, n_sc, n_rg, n_rd, n_src;
 };
 
 // State of the single-launch decode that persists across calls.  It sits at
 // the start of the workspace, at offsets that do not depend on the token
 // count, and no other kernel writes it.
 struct FusedCarve {
-    size_t rpart, sgpart, rgpart, act, ids, piece, ctr, total;
-    int64_t h_stride, ids_stride;   // in 8-byte words
+    size_t rpart, sgpart, rgpart, act, piece, ctr, total;
+    int64_t h_stride, rpart_stride;   // in 8-byte words
 };
 
 FusedCarve fused_carve(const Sizes& z) {
     FusedCarve f;
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
-    f.rpart = take((size_t)(z.E + 15) / 16 * z.rq * 16 * 8);
-    f.sgpart = take((size_t)2 * z.G_s * z.gq * 64 * 8 + 8);
-    f.rgpart = take((size_t)z.k * 2 * z.G_I * z.gq * 64 * 8);
-    // one copy per XCD of the activations (shared then routed) and of the ids
+    f.rpart_stride = (int64_t)up((size_t)(z.E + 15) / 16 * 8 * 16 * 8) / 8;
+    f.rpart = take((size_t)8 * f.rpart_stride * 8);
+    f.sgpart = take((size_t)2 * z.G_s * kFusedPieces * 64 * 8 + 8);
+    f.rgpart = take((size_t)z.k * 2 * z.G_I * kFusedPieces * 64 * 8);
+    // one copy per XCD of the activations (shared then routed)
     f.h_stride = (int64_t)up(((size_t)z.Is + (size_t)z.k * z.I) * 8 + 8) / 8;
     f.act = take((size_t)8 * f.h_stride * 8);
-    f.ids_stride = 32;
-    f.ids = take((size_t)8 * f.ids_stride * 8);
     f.piece = take((size_t)z.G_H * z.n_src * 64 * 8);
-    f.ctr = take((size_t)(z.n_ctr + 2) * kCtrStride * 4);
+    f.ctr = take((size_t)3 * kCtrStride * 4);   // c_done, epoch, error flag
     f.total = o;
     return f;
 }
 
-bool fused_ok(const Sizes& z) { return z.H <= 4096 && z.G_I <= 12 && z.n_src <= 32; }
+bool fused_ok(const Sizes& z) { return z.G_H <= 48 && z.G_I <= 12 && z.n_src <= 32; }
 
 // Offsets of every workspace region for up to T tokens; returns the total.
 struct Carve {
@@ -152,16 +151,15 @@ mq_status check_layer(const mq_router* rt, const mq_expert_pool* pool, const mq_
     z->rgroups = 4;
     z->rsplit = (z->G_H + z->rgroups - 1) / z->rgroups;
     z->ntile = 16;
-    z->rq = z->G_H < 8 ? z->G_H : 8;
-    z->gq = (z->G_H + 11) / 12 > (z->G_H < 4 ? z->G_H : 4) ? (z->G_H + 11) / 12 : (z->G_H < 4 ? z->G_H : 4);
-    z->n_router = (E + 15) / 16 * z->rq;
-    z->n_sg = 2 * z->G_s * z->gq;
+    // single-launch decode: router slices of 16 experts in kRouterPieces column
+    // pieces, gate/up half tiles in kFusedPieces (short rows give empty pieces)
+    z->n_router = (E + 15) / 16 * kRouterPieces;
+    z->n_sg = 2 * z->G_s * kFusedPieces;
     z->n_sc = (z->G_s + z->G_I - 1) / z->G_I;
     z->n_sd = z->G_H * z->n_sc;
-    z->n_rg = 2 * z->k * z->G_I * z->gq;
+    z->n_rg = 2 * z->k * z->G_I * kFusedPieces;
     z->n_rd = z->G_H * z->k;
     z->n_src = z->k + z->n_sc;
-    z->n_ctr = 3 + z->k;
     return MQ_OK;
 }
 
@@ -275,20 +273,13 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
     p.f_rgpart = (uint64_t*)(ws + f.rgpart);
     p.f_hs = (uint64_t*)(ws + f.act);
     p.f_h = p.f_hs + z.Is;
-    p.f_ids = (uint64_t*)(ws + f.ids);
     p.h_stride = f.h_stride;
-    p.ids_stride = f.ids_stride;
+    p.rpart_stride = f.rpart_stride;
     p.f_piece = (uint64_t*)(ws + f.piece);
     uint32_t* ctr = (uint32_t*)(ws + f.ctr);
-    p.c_base = ctr;
-    p.c_router = ctr;
-    p.c_hs = ctr + kCtrStride;
-    p.c_done = ctr + 2 * kCtrStride;
-    p.c_h = ctr + 3 * kCtrStride;
-    p.f_epoch = ctr + z.n_ctr * kCtrStride;
-    p.f_err = ctr + (z.n_ctr + 1) * kCtrStride;
-    p.rq = z.rq;
-    p.gq = z.gq;
+    p.c_done = ctr;
+    p.f_epoch = ctr + kCtrStride;
+    p.f_err = ctr + 2 * kCtrStride;
     p.n_router = z.n_router;
     p.n_sg = z.n_sg;
     p.n_sd = z.n_sd;
@@ -296,7 +287,6 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
     p.n_rg = z.n_rg;
     p.n_rd = z.n_rd;
     p.n_src = z.n_src;
-    p.n_ctr = z.n_ctr;
 
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
@@ -315,7 +305,7 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
     hipLaunchKernelGGL(k_prep, dim3(T), dim3(256), 0, s, p);
     hipLaunchKernelGGL(k_router, dim3(z.E_pad / 64, z.rsplit, (T + kRouterTokens - 1) / kRouterTokens), dim3(256),
                        0, s, p);
-    hipLaunchKernelGGL(k_topk, dim3(T), dim3(64), 0, s, p);
+    hipLaunchKernelGGL(k_topk, dim3(T), dim3(256), 0, s, p);
     if (grouped) {
         st = launch_grouped(p, s);
         if (st != MQ_OK) return st;

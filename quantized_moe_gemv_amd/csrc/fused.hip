@@ -6,21 +6,24 @@
 // increasing order):
 //   router pieces   16 experts x a column range      -> partial scores
 //   shared gate/up  32 rows x a column range          -> partial g, u
-//   shared down     64 output rows x a chunk of Is    -> partial outputs
 //   routed gate/up  (slot j, 32 rows, column range)   -> partial g, u
+//   shared down     64 output rows x a chunk of Is    -> partial outputs
 //   routed down     (64 output rows, slot j)          -> partial outputs
 // Every dependency points to an earlier unit, so with all workgroups
 // resident every wait ends; each wait is also bounded.  Partial results are
-// 64-bit words carrying the call's epoch in their high half.  An arrival
-// counter per target tells its last contributor to reduce (in a fixed
-// order, so results repeat bit for bit), and one thread per consumer
-// workgroup polls a single done-counter before the data is read, which
-// keeps polling light.  Each workgroup issues the loads of its next unit
-// before it computes the current one.
+// 64-bit words carrying the call's epoch in their high half: a reader
+// issues all of its loads, then re-reads only the words whose tag is not yet
+// current.  Each sum has a fixed reducer (the highest-indexed contributor),
+// which sums in a fixed order, so results repeat bit for bit.  Each
+// workgroup issues the loads of its next unit before it computes the
+// current one.
 //
-// Results that many workgroups read (expert ids, GeGLU activations) are
-// written once per XCD (eight copies) and each reader takes the copy of its
-// own XCD, so the readers do not all queue on the same memory channels.
+// Results that many workgroups read (partial router scores, GeGLU
+// activations) are written once per XCD (eight copies) and each reader takes
+// the copy of its own XCD, so the readers do not all queue on the same
+// memory channels.  Every workgroup that runs routed units sums the router
+// scores and selects the experts itself, which costs less than waiting for
+// one workgroup to publish them.
 //
 // The shared expert and the router do not depend on each other, so the
 // shared branch streams while the routing decision is made ("Decode",
@@ -37,6 +40,8 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kItems = 3;           // 16-byte code loads per lane per unit
 constexpr int kSpinLimit = 1 << 20;
 constexpr int kCopies = 8;         // replicas of broadcast results, one per XCD
+constexpr int kRq = kRouterPieces;
+constexpr int kGq = kFusedPieces;
 
 // ----------------------------------------------------------------- words and counters
 
@@ -66,21 +71,6 @@ __device__ __forceinline__ uint32_t wait_word(const uint64_t* p, uint32_t tag, u
     return (uint32_t)v;
 }
 
-// One thread waits until *ctr >= target; then the workgroup proceeds together.
-__device__ __forceinline__ void wait_ctr(const uint32_t* ctr, uint32_t target, uint32_t* err) {
-    if (threadIdx.x == 0) {
-        int spins = 0;
-        while (ld_ctr(ctr) < target) {
-            if (++spins > kSpinLimit || ((spins & 63) == 0 && ld_ctr(err))) {
-                atomicOr(err, 1u);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(4);
-        }
-    }
-    __syncthreads();
-}
-
 // Payloads of words base[0 .. n) into dst, for n <= 4 * kThreads: every
 // load is issued before any is checked, so the gather costs one round trip.
 __device__ __forceinline__ void gather_words(const uint64_t* base, int n, uint32_t tag, uint32_t* err,
@@ -102,9 +92,6 @@ __device__ __forceinline__ void gather_words(const uint64_t* base, int n, uint32
     __syncthreads();
 }
 
-__device__ __forceinline__ void bump(uint32_t* ctr) {
-    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // ----------------------------------------------------------------- units
 
@@ -118,18 +105,23 @@ struct Unit {
 };
 
 struct Shared {
-    uint16_t x[4096];
+    // arrays read with 16-byte LDS accesses come first and stay 16-byte aligned
+    alignas(16) uint16_t x[4096];
+    alignas(16) uint16_t hhi[16 * 64];   // one source's activations, bf16 high and low parts
+    alignas(16) uint16_t hlo[16 * 64];
+    alignas(16) float lg[256];           // expert scores (padding: -inf)
+    alignas(16) float xr[4096];          // router input numerator x * router_scale
+    alignas(16) float selv[kMaxTopK];    // selected scores (padding: -inf)
+    alignas(16) uint32_t gbuf[2048];     // gathered payloads (partial results of other units)
     float xsum[64 * 4];       // x summed over each lane's 16 columns of a group (4-bit blocks)
     float rsum[64 * 4];       // router input summed over each lane's 16 columns (8-bit blocks)
-    float rc;                 // router input scale 1/sqrt(mean(x^2)+eps)/sqrt(H)
+    float c8[512];            // per 8-column chunk: sum of x
+    float c4[1024];           // per 4-column quarter: sum of x * router_scale
     float red[kWaves][64];
-    uint16_t hhi[16 * 64];    // one source's activations, bf16 high and low parts
-    uint16_t hlo[16 * 64];
     float hsum[16 * 4];
-    uint32_t gbuf[2048];      // gathered payloads (partial results of other units)
-    float lg[256];            // expert scores
     int32_t ids[kMaxTopK];
     float wts[kMaxTopK];
+    float rc;                 // router input scale 1/sqrt(mean(x^2)+eps)/sqrt(H)
     uint32_t flag;
 };
 
@@ -145,20 +137,30 @@ __device__ __forceinline__ Unit decode_unit(const Plan& p, int u) {
     x.a = x.b = x.q = x.g0 = x.ng = 0;
     if (u < p.n_router) {
         x.kind = U_ROUTER;
-        x.a = u / p.rq;
-        x.q = u % p.rq;
-        krange(p.G_H, p.rq, x.q, &x.g0, &x.ng);
+        x.a = u / kRq;
+        x.q = u % kRq;
+        krange(p.G_H, kRq, x.q, &x.g0, &x.ng);
         return x;
     }
     u -= p.n_router;
     if (u < p.n_sg) {
         x.kind = U_SG;
-        x.a = u / p.gq;
-        x.q = u % p.gq;
-        krange(p.G_H, p.gq, x.q, &x.g0, &x.ng);
+        x.a = u / kGq;
+        x.q = u % kGq;
+        krange(p.G_H, kGq, x.q, &x.g0, &x.ng);
         return x;
     }
     u -= p.n_sg;
+    if (u < p.n_rg) {
+        x.kind = U_RG;
+        const int per = 2 * p.G_I * kGq;
+        x.a = u / per;
+        x.b = (u % per) / kGq;
+        x.q = u % kGq;
+        krange(p.G_H, kGq, x.q, &x.g0, &x.ng);
+        return x;
+    }
+    u -= p.n_rg;
     if (u < p.n_sd) {
         x.kind = U_SD;
         x.a = u / p.n_sc;
@@ -168,16 +170,6 @@ __device__ __forceinline__ Unit decode_unit(const Plan& p, int u) {
         return x;
     }
     u -= p.n_sd;
-    if (u < p.n_rg) {
-        x.kind = U_RG;
-        const int per = 2 * p.G_I * p.gq;
-        x.a = u / per;
-        x.b = (u % per) / p.gq;
-        x.q = u % p.gq;
-        krange(p.G_H, p.gq, x.q, &x.g0, &x.ng);
-        return x;
-    }
-    u -= p.n_rg;
     if (u < p.n_rd) {
         x.kind = U_RD;
         x.a = u / p.k;
@@ -253,130 +245,127 @@ __device__ __forceinline__ void issue_loads(const Plan& p, const Shared& sh, con
 
 // ----------------------------------------------------------------- setup
 
+__device__ __forceinline__ float sum8_bf16(const uint4& v) {
+    return ((bf16_lo(v.x) + bf16_hi(v.x)) + (bf16_lo(v.y) + bf16_hi(v.y))) +
+           ((bf16_lo(v.z) + bf16_hi(v.z)) + (bf16_lo(v.w) + bf16_hi(v.w)));
+}
+
+// The token into LDS, the router input scale, and the column sums the block
+// dots need: thread c holds columns 8c .. 8c+7 and contributes its partial
+// sums; each lane set is then a sum of two (4-bit) or four (8-bit) of them.
 __device__ __forceinline__ void stage_token(const Plan& p, Shared& sh) {
     const int t = threadIdx.x;
-    if (t < p.H / 8) *(uint4*)(sh.x + 8 * t) = *(const uint4*)(p.x + 8 * t);
-    __syncthreads();
+    const int nch = p.H / 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
     float ss = 0.f;
-    for (int i = t; i < p.H; i += kThreads) {
-        const float v = bf16_to_f32(sh.x[i]);
-        ss += v * v;
+    if (t < nch) {
+        v = *(const uint4*)(p.x + 8 * t);
+        *(uint4*)(sh.x + 8 * t) = v;
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        float q0 = 0.f, q1 = 0.f;   // sums of columns 8t..8t+3 and 8t+4..8t+7 (times router_scale)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float a0 = bf16_lo(w[i]), a1 = bf16_hi(w[i]);
+            ss += a0 * a0 + a1 * a1;
+            const float r0 = p.router_scale ? p.router_scale[8 * t + 2 * i] : 1.0f;
+            const float r1 = p.router_scale ? p.router_scale[8 * t + 2 * i + 1] : 1.0f;
+            if (i < 2) q0 += a0 * r0 + a1 * r1; else q1 += a0 * r0 + a1 * r1;
+        }
+        float4* xr = (float4*)(sh.xr + 8 * t);
+        float rs[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rs[e] = p.router_scale ? p.router_scale[8 * t + e] : 1.0f;
+        xr[0] = make_float4(bf16_lo(v.x) * rs[0], bf16_hi(v.x) * rs[1], bf16_lo(v.y) * rs[2], bf16_hi(v.y) * rs[3]);
+        xr[1] = make_float4(bf16_lo(v.z) * rs[4], bf16_hi(v.z) * rs[5], bf16_lo(v.w) * rs[6], bf16_hi(v.w) * rs[7]);
+        sh.c8[t] = sum8_bf16(v);
+        sh.c4[2 * t] = q0;
+        sh.c4[2 * t + 1] = q1;
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
     if ((t & 63) == 0) sh.red[t >> 6][0] = ss;
     __syncthreads();
-    if (t == 0) {
-        float s = 0.f;
-        for (int w = 0; w < kWaves; ++w) s += sh.red[w][0];
-        sh.rc = (1.0f / sqrtf(s / (float)p.H + p.eps)) * (1.0f / sqrtf((float)p.H));
-    }
-    __syncthreads();
-    const float rc = sh.rc;
-    for (int q = t; q < p.G_H * 4; q += kThreads) {
-        const int g = q >> 2, kb = q & 3;
-        float s4 = 0.f, s8 = 0.f;
-        for (int ks = 0; ks < 2; ++ks)
-            for (int e = 0; e < 8; ++e) s4 += bf16_to_f32(sh.x[64 * g + 32 * ks + 8 * kb + e]);
-        for (int ks = 0; ks < 4; ++ks)
-            for (int e = 0; e < 4; ++e) {
-                const int i = 64 * g + 16 * ks + 4 * kb + e;
-                s8 += bf16_to_f32(sh.x[i]) * rc * (p.router_scale ? p.router_scale[i] : 1.0f);
-            }
-        sh.xsum[q] = s4;
-        sh.rsum[q] = s8;
+    if (t < p.G_H * 4) {
+        float tot = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) tot += sh.red[w][0];
+        const float rc = (1.0f / sqrtf(tot / (float)p.H + p.eps)) * (1.0f / sqrtf((float)p.H));
+        if (t == 0) sh.rc = rc;
+        const int g = t >> 2, kb = t & 3;
+        // 4-bit lane set: chunks 8g + kb (columns 32*0 + 8kb) and 8g + 4 + kb
+        sh.xsum[t] = sh.c8[8 * g + kb] + sh.c8[8 * g + 4 + kb];
+        // 8-bit lane set: quarters (16 ks + 4 kb) for ks = 0..3, quarter index = 16g + 4ks + kb
+        const float r = (sh.c4[16 * g + kb] + sh.c4[16 * g + 4 + kb]) + (sh.c4[16 * g + 8 + kb] + sh.c4[16 * g + 12 + kb]);
+        sh.rsum[t] = r * rc;
     }
     __syncthreads();
 }
 
-// The last router piece: sum the partial scores of every piece in order,
-// select the top k (higher score first, ties to the lower expert index),
-// softmax over the selected scores times per_expert_scale, and publish
-// ids and weights (every copy) and the caller's optional outputs.
-__device__ __forceinline__ void reduce_topk(const Plan& p, Shared& sh, uint32_t tag) {
-    wait_ctr(p.c_router, (uint32_t)p.n_router, p.f_err);
-    const int nslice = (p.E + 15) / 16;
-    gather_words(p.f_rpart, nslice * p.rq * 16, tag, p.f_err, sh.gbuf);
-    for (int e = threadIdx.x; e < p.E; e += kThreads) {
-        const int slice = e >> 4, r = e & 15;
-        float s = 0.f;
-        for (int q = 0; q < p.rq; ++q) s += __uint_as_float(sh.gbuf[(slice * p.rq + q) * 16 + r]);
-        if (p.logit_bias) s += p.logit_bias[e];
-        if (p.logits_out) p.logits_out[e] = s;
+// Expert ids and weights, computed by every workgroup that needs them from
+// its XCD's copy of the partial scores: sum the pieces of each score in
+// order, rank every expert (the number of scores that beat it: higher, or
+// equal with a lower index), keep ranks < k in rank order, then the softmax
+// over the selected scores times per_expert_scale.  One workgroup reports
+// the scores, ids and weights to the caller's optional outputs.
+__device__ __forceinline__ void fetch_ids(const Plan& p, Shared& sh, uint32_t tag) {
+    const int nslice = (p.E + 15) / 16, epad = (p.E + 31) & ~31;
+    gather_words(p.f_rpart + (blockIdx.x % kCopies) * p.rpart_stride, nslice * kRq * 16, tag, p.f_err, sh.gbuf);
+    // the workgroup of the first routed gate/up unit (it always fetches the ids)
+    const bool reporter = (int)blockIdx.x == (p.n_router + p.n_sg) % (int)gridDim.x;
+    for (int e = threadIdx.x; e < epad; e += kThreads) {
+        float s = -INFINITY;
+        if (e < p.E) {
+            const int slice = e >> 4, r = e & 15;
+            float a[kRq];
+#pragma unroll
+            for (int q = 0; q < kRq; ++q) a[q] = __uint_as_float(sh.gbuf[(slice * kRq + q) * 16 + r]);
+            s = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+            if (p.logit_bias) s += p.logit_bias[e];
+            if (reporter && p.logits_out) p.logits_out[e] = s;
+            if (!(s == s)) s = -INFINITY;   // a NaN score ranks last; ids stay distinct
+        }
         sh.lg[e] = s;
     }
+    if (threadIdx.x < kMaxTopK) sh.selv[threadIdx.x] = -INFINITY;
     __syncthreads();
-    if (threadIdx.x < 64) {
-        const int lane = threadIdx.x;
-        float v[4];
-        bool live[4];
+    for (int e = threadIdx.x; e < p.E; e += kThreads) {
+        const float v = sh.lg[e];
+        int rank = 0;
+        for (int c = 0; c < epad; c += 32) {
+            float4 w[8];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int e = lane + 64 * m;
-            live[m] = e < p.E;
-            float s = live[m] ? sh.lg[e] : -INFINITY;
-            if (!(s == s)) s = -INFINITY;
-            v[m] = s;
-        }
-        float selv[kMaxTopK];
-        int seli[kMaxTopK];
+            for (int m = 0; m < 8; ++m) w[m] = *(const float4*)(sh.lg + c + 4 * m);
 #pragma unroll
-        for (int j = 0; j < kMaxTopK; ++j) {
-            if (j < p.k) {
-                float bv = -INFINITY;
-                int bi = 0x7FFFFFFF;
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int e = lane + 64 * m;
-                    if (live[m] && (v[m] > bv || (v[m] == bv && e < bi))) { bv = v[m]; bi = e; }
-                }
-#pragma unroll
-                for (int o = 32; o >= 1; o >>= 1) {
-                    const float ov = __shfl_xor(bv, o, 64);
-                    const int oi = __shfl_xor(bi, o, 64);
-                    if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-                }
-                selv[j] = bv;
-                seli[j] = bi;
-#pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    if (lane + 64 * m == bi) live[m] = false;
+            for (int m = 0; m < 8; ++m) {
+                const int o = c + 4 * m;
+                rank += (w[m].x > v) + (w[m].x == v && o < e);
+                rank += (w[m].y > v) + (w[m].y == v && o + 1 < e);
+                rank += (w[m].z > v) + (w[m].z == v && o + 2 < e);
+                rank += (w[m].w > v) + (w[m].w == v && o + 3 < e);
             }
         }
-        if (lane == 0) {
-            float den = 0.f;
-#pragma unroll
-            for (int j = 0; j < kMaxTopK; ++j)
-                if (j < p.k) den += expf(selv[j] - selv[0]);
-#pragma unroll
-            for (int j = 0; j < kMaxTopK; ++j)
-                if (j < p.k) {
-                    const float w = expf(selv[j] - selv[0]) / den * (p.pes ? p.pes[seli[j]] : 1.0f);
-                    sh.ids[j] = seli[j];
-                    sh.wts[j] = w;
-                    if (p.ids_out) p.ids_out[j] = seli[j];
-                    if (p.w_out) p.w_out[j] = w;
-                }
+        if (rank < p.k) {
+            sh.ids[rank] = e;
+            sh.selv[rank] = v;
         }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < kCopies * 2 * p.k; i += kThreads) {
-        const int c = i / (2 * p.k), j = (i % (2 * p.k)) >> 1;
-        const uint32_t payload = (i & 1) ? __float_as_uint(sh.wts[j]) : (uint32_t)sh.ids[j];
-        st_word(p.f_ids + c * p.ids_stride + (i % (2 * p.k)), tag, payload);
-    }
-    __syncthreads();
-}
-
-// Expert ids and weights from this XCD's copy.
-__device__ __forceinline__ void fetch_ids(const Plan& p, Shared& sh, uint32_t tag) {
-    const uint64_t* src = p.f_ids + (blockIdx.x % kCopies) * p.ids_stride;
-    if (threadIdx.x < 2 * p.k) {
-        const uint32_t v = wait_word(src + threadIdx.x, tag, p.f_err);
-        if (threadIdx.x & 1)
-            sh.wts[threadIdx.x >> 1] = __uint_as_float(v);
-        else
-            sh.ids[threadIdx.x >> 1] = (int32_t)v;
+    if (threadIdx.x < p.k) {
+        const int j = threadIdx.x;
+        float4 sv[kMaxTopK / 4];
+#pragma unroll
+        for (int m = 0; m < kMaxTopK / 4; ++m) sv[m] = *(const float4*)(sh.selv + 4 * m);
+        const float top = sv[0].x;
+        float den = 0.f;
+#pragma unroll
+        for (int m = 0; m < kMaxTopK / 4; ++m)
+            den += (expf(sv[m].x - top) + expf(sv[m].y - top)) + (expf(sv[m].z - top) + expf(sv[m].w - top));
+        const float w = expf(sh.selv[j] - top) / den * (p.pes ? p.pes[sh.ids[j]] : 1.0f);
+        sh.wts[j] = w;
+        if (reporter) {
+            if (p.ids_out) p.ids_out[j] = sh.ids[j];
+            if (p.w_out) p.w_out[j] = w;
+        }
     }
     __syncthreads();
 }
@@ -392,13 +381,11 @@ __device__ __forceinline__ void stage_h(const Plan& p, Shared& sh, const uint64_
     __syncthreads();
     for (int q = threadIdx.x; q < ng * 4; q += kThreads) {
         const int gl = q >> 2, qb = q & 3;
-        float s = 0.f;
-        for (int ks = 0; ks < 2; ++ks)
-            for (int e = 0; e < 8; ++e) {
-                const int i = 64 * gl + 32 * ks + 8 * qb + e;
-                s += bf16_to_f32(sh.hhi[i]) + bf16_to_f32(sh.hlo[i]);
-            }
-        sh.hsum[q] = s;
+        const uint4 a0 = *(const uint4*)(sh.hhi + 64 * gl + 8 * qb);
+        const uint4 a1 = *(const uint4*)(sh.hhi + 64 * gl + 32 + 8 * qb);
+        const uint4 b0 = *(const uint4*)(sh.hlo + 64 * gl + 8 * qb);
+        const uint4 b1 = *(const uint4*)(sh.hlo + 64 * gl + 32 + 8 * qb);
+        sh.hsum[q] = (sum8_bf16(a0) + sum8_bf16(a1)) + (sum8_bf16(b0) + sum8_bf16(b1));
     }
     __syncthreads();
 }
@@ -446,25 +433,22 @@ __device__ __forceinline__ void run_router(const Plan& p, Shared& sh, const Unit
             float d = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int col = 64 * g + 16 * i + 4 * kb;
-                const uint2 xv = *(const uint2*)(sh.x + col);
-                float r[4] = {bf16_lo(xv.x), bf16_hi(xv.x), bf16_lo(xv.y), bf16_hi(xv.y)};
-                if (p.router_scale)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) r[e] *= p.router_scale[col + e];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) d = fmaf((float)((cw[i] >> (8 * e)) & 0xFFu), r[e], d);
+                const float4 r = *(const float4*)(sh.xr + 64 * g + 16 * i + 4 * kb);
+                d = fmaf((float)(cw[i] & 0xFFu), r.x, d);
+                d = fmaf((float)((cw[i] >> 8) & 0xFFu), r.y, d);
+                d = fmaf((float)((cw[i] >> 16) & 0xFFu), r.z, d);
+                d = fmaf((float)(cw[i] >> 24), r.w, d);
             }
             acc = fmaf(bf16_lo(L.s[m].x), d * sh.rc, fmaf(bf16_hi(L.s[m].x), sh.rsum[g * 4 + kb], acc));
         }
     }
     reduce_rows(sh, &acc, 1);
-    if (threadIdx.x < 16)
-        st_word(p.f_rpart + ((int64_t)(x.a * p.rq + x.q) * 16 + threadIdx.x), tag,
-                __float_as_uint(row_total(sh, threadIdx.x)));
+    if (threadIdx.x < 16 * kCopies) {
+        const int r = threadIdx.x & 15, c = threadIdx.x >> 4;
+        st_word(p.f_rpart + c * p.rpart_stride + (int64_t)(x.a * kRq + x.q) * 16 + r, tag,
+                __float_as_uint(row_total(sh, r)));
+    }
     __syncthreads();
-    if (threadIdx.x == 0) bump(p.c_router);
-    if (x.a * p.rq + x.q == p.n_router - 1) reduce_topk(p, sh, tag);
 }
 
 // Gate/up piece: 32 rows x a column range -> partial (g, u).  The last of
@@ -493,17 +477,18 @@ __device__ __forceinline__ void run_gateup(const Plan& p, Shared& sh, const Unit
     reduce_rows(sh, acc, 4);
     const bool shared = x.kind == U_SG;
     const int ht = shared ? x.a : x.b;
-    uint64_t* base = shared ? p.f_sgpart + (int64_t)ht * p.gq * 64
-                            : p.f_rgpart + ((int64_t)x.a * 2 * p.G_I + ht) * p.gq * 64;
+    uint64_t* base = shared ? p.f_sgpart + (int64_t)ht * kGq * 64
+                            : p.f_rgpart + ((int64_t)x.a * 2 * p.G_I + ht) * kGq * 64;
     if (threadIdx.x < 64) st_word(base + x.q * 64 + threadIdx.x, tag, __float_as_uint(row_total(sh, threadIdx.x)));
     __syncthreads();
-    if (x.q != p.gq - 1) return;
+    if (x.q != kGq - 1) return;
     // the last piece of the half tile: sum all pieces in order, then GeGLU
-    gather_words(base, p.gq * 64, tag, p.f_err, sh.gbuf);
+    gather_words(base, kGq * 64, tag, p.f_err, sh.gbuf);
     if (threadIdx.x < 32) {
         const int r = threadIdx.x;
         float gv = 0.f, uv = 0.f;
-        for (int q = 0; q < p.gq; ++q) {
+#pragma unroll
+        for (int q = 0; q < kGq; ++q) {
             gv += __uint_as_float(sh.gbuf[q * 64 + r]);
             uv += __uint_as_float(sh.gbuf[q * 64 + 32 + r]);
         }
@@ -515,7 +500,6 @@ __device__ __forceinline__ void run_gateup(const Plan& p, Shared& sh, const Unit
         for (int c = 0; c < kCopies; ++c) st_word(hout + c * p.h_stride + r, tag, ((uint32_t)h1 << 16) | h2);
     }
     __syncthreads();
-    if (threadIdx.x == 0) bump(shared ? p.c_hs : p.c_h + x.a * kCtrStride);
 }
 
 // Down piece: one 64-row output tile from one source -> partial outputs.  The
@@ -554,9 +538,17 @@ __device__ __forceinline__ void run_down(const Plan& p, Shared& sh, const Unit& 
     if (shared || x.b != p.k - 1) return;
     // the last source of this output tile: sum every source in order
     gather_words(tilep, p.n_src * 64, tag, p.f_err, sh.gbuf);
+    for (int i = p.n_src * 64 + threadIdx.x; i < ((p.n_src + 3) & ~3) * 64; i += kThreads) sh.gbuf[i] = 0u;
+    __syncthreads();
     if (threadIdx.x < 64) {
         float v = 0.f;
-        for (int s2 = 0; s2 < p.n_src; ++s2) v += __uint_as_float(sh.gbuf[s2 * 64 + threadIdx.x]);
+        for (int s2 = 0; s2 < p.n_src; s2 += 4) {
+            const float a0 = __uint_as_float(sh.gbuf[s2 * 64 + threadIdx.x]);
+            const float a1 = __uint_as_float(sh.gbuf[(s2 + 1) * 64 + threadIdx.x]);
+            const float a2 = __uint_as_float(sh.gbuf[(s2 + 2) * 64 + threadIdx.x]);
+            const float a3 = __uint_as_float(sh.gbuf[(s2 + 3) * 64 + threadIdx.x]);
+            v += ((a0 + a1) + a2) + a3;
+        }
         const int row = 64 * x.a + threadIdx.x;
         if (p.out_f32)
             ((float*)p.out)[row] = v;
@@ -576,12 +568,10 @@ __device__ __forceinline__ void run_unit(const Plan& p, Shared& sh, const Unit& 
             run_gateup(p, sh, x, L, tag);
             break;
         case U_SD:
-            wait_ctr(p.c_hs, (uint32_t)(2 * p.G_s), p.f_err);
             stage_h(p, sh, p.f_hs + (blockIdx.x % kCopies) * p.h_stride, x.g0, x.ng, tag);
             run_down(p, sh, x, L, tag);
             break;
         case U_RD:
-            wait_ctr(p.c_h + x.b * kCtrStride, (uint32_t)(2 * p.G_I), p.f_err);
             stage_h(p, sh, p.f_h + (blockIdx.x % kCopies) * p.h_stride + (int64_t)x.b * p.I, 0, x.ng, tag);
             run_down(p, sh, x, L, tag);
             break;
@@ -592,47 +582,61 @@ __device__ __forceinline__ void run_unit(const Plan& p, Shared& sh, const Unit& 
 
 // ----------------------------------------------------------------- the kernel
 
+// One step of a workgroup's unit sequence: make sure the current unit's
+// loads are out, put the next unit's loads out when their addresses are
+// known, then run the current unit.  The two load buffers swap roles from
+// step to step (the caller alternates them), so loads still in flight are
+// never copied between registers, which would make the copy wait for them.
+__device__ __forceinline__ void step(const Plan& p, Shared& sh, const Unit& cur, Loads& lc, bool& ic, const Unit& nxt,
+                                     Loads& ln, bool& in, bool& have, uint32_t tag) {
+    if (!ic) {
+        if (!have) {
+            fetch_ids(p, sh, tag);
+            have = true;
+        }
+        issue_loads(p, sh, cur, lc);
+        ic = true;
+    }
+    if (!in && nxt.kind != U_NONE && (!needs_ids(nxt) || have)) {
+        issue_loads(p, sh, nxt, ln);
+        in = true;
+    }
+    run_unit(p, sh, cur, lc, tag);
+}
+
 __global__ __launch_bounds__(kThreads) void k_decode(Plan p) {
     __shared__ Shared sh;
     const uint32_t tag = ld_ctr(p.f_epoch) + 1;
     const int nwg = gridDim.x;
-    // Units u, u + nwg, u + 2 nwg are in flight: their loads are issued as soon
-    // as their addresses are known (routed units need the expert ids first).
-    // Every branch below is taken by all waves alike: `have` lives in registers
-    // and changes only where every wave passes.
+    // Every branch below is taken by all waves alike: the flags live in
+    // registers and change only where every wave passes.
     int u = blockIdx.x;
-    Unit u0 = decode_unit(p, u), u1 = decode_unit(p, u + nwg), u2 = decode_unit(p, u + 2 * nwg);
-    Loads l0, l1, l2;
-    bool i0 = false, i1 = false, i2 = false, have = false;
-    if (u0.kind != U_NONE && !needs_ids(u0)) { issue_loads(p, sh, u0, l0); i0 = true; }
-    if (u1.kind != U_NONE && !needs_ids(u1)) { issue_loads(p, sh, u1, l1); i1 = true; }
+    Unit ua = decode_unit(p, u), ub = decode_unit(p, u + nwg);
+    Loads la, lb;
+    bool ia = false, ib = false, have = false;
+    if (ua.kind != U_NONE && !needs_ids(ua)) { issue_loads(p, sh, ua, la); ia = true; }
+    if (ub.kind != U_NONE && !needs_ids(ub)) { issue_loads(p, sh, ub, lb); ib = true; }
     stage_token(p, sh);
-    while (u0.kind != U_NONE) {
-        if (!i0) {
-            if (!have) {
-                fetch_ids(p, sh, tag);
-                have = true;
-            }
-            issue_loads(p, sh, u0, l0);
-        }
-        if (!i1 && u1.kind != U_NONE && (!needs_ids(u1) || have)) { issue_loads(p, sh, u1, l1); i1 = true; }
-        if (!i2 && u2.kind != U_NONE && (!needs_ids(u2) || have)) { issue_loads(p, sh, u2, l2); i2 = true; }
-        run_unit(p, sh, u0, l0, tag);
-        if (u0.kind == U_ROUTER && u0.a * p.rq + u0.q == p.n_router - 1) have = true;   // it ran the top-k
+    while (ua.kind != U_NONE) {
+        step(p, sh, ua, la, ia, ub, lb, ib, have, tag);
         u += nwg;
-        u0 = u1; l0 = l1; i0 = i1;
-        u1 = u2; l1 = l2; i1 = i2;
-        u2 = decode_unit(p, u + 2 * nwg);
-        i2 = false;
+        if (ub.kind == U_NONE) break;
+        ua = decode_unit(p, u + nwg);
+        ia = false;
+        step(p, sh, ub, lb, ib, ua, la, ia, have, tag);
+        u += nwg;
+        ub = decode_unit(p, u + nwg);
+        ib = false;
     }
     // The last workgroup to finish clears every counter and advances the epoch.
     __syncthreads();
     if (threadIdx.x == 0) sh.flag = atomicAdd(p.c_done, 1u) + 1 == (uint32_t)nwg;
     __syncthreads();
     if (sh.flag) {
-        for (int i = threadIdx.x; i < p.n_ctr; i += kThreads)
-            __hip_atomic_store(p.c_base + i * kCtrStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (threadIdx.x == 0) __hip_atomic_store(p.f_epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (threadIdx.x == 0) {
+            __hip_atomic_store(p.c_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(p.f_epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 

@@ -117,58 +117,42 @@ __global__ __launch_bounds__(256) void k_router(Plan p) {
 }
 
 // Scores, top-k (higher score first, ties to the lower expert) and the
-// softmax weights over the selected scores times per_expert_scale.  One wave per token.
-__global__ __launch_bounds__(64) void k_topk(Plan p) {
-    const int t = blockIdx.x, lane = threadIdx.x;
-    float v[4];
-    bool live[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int e = lane + 64 * m;
-        live[m] = e < p.E;
+// softmax weights over the selected scores times per_expert_scale.  One
+// workgroup per token: each expert's rank is the number of scores that beat
+// it, and the experts of rank < k are the selection, in rank order.
+__global__ __launch_bounds__(256) void k_topk(Plan p) {
+    const int t = blockIdx.x;
+    __shared__ float lg[kMaxExperts];
+    __shared__ float selv[kMaxTopK];
+    __shared__ int seli[kMaxTopK];
+    for (int e = threadIdx.x; e < p.E; e += 256) {
         float s = 0.f;
-        if (live[m]) {
-            for (int sp = 0; sp < p.rsplit; ++sp) s += p.plog[((int64_t)sp * p.T + t) * p.E_pad + e];
-            if (p.logit_bias) s += p.logit_bias[e];
-            if (p.logits_out) p.logits_out[(int64_t)t * p.E + e] = s;
-            if (!(s == s)) s = -INFINITY;   // a NaN score ranks last; ids stay distinct
-        }
-        v[m] = s;
+        for (int sp = 0; sp < p.rsplit; ++sp) s += p.plog[((int64_t)sp * p.T + t) * p.E_pad + e];
+        if (p.logit_bias) s += p.logit_bias[e];
+        if (p.logits_out) p.logits_out[(int64_t)t * p.E + e] = s;
+        lg[e] = (s == s) ? s : -INFINITY;   // a NaN score ranks last; ids stay distinct
     }
-    float selv[kMaxTopK];
-    int seli[kMaxTopK];
-    for (int j = 0; j < p.k; ++j) {
-        float bv = -INFINITY;
-        int bi = 0x7FFFFFFF;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int e = lane + 64 * m;
-            if (live[m] && (v[m] > bv || (v[m] == bv && e < bi))) { bv = v[m]; bi = e; }
+    __syncthreads();
+    for (int e = threadIdx.x; e < p.E; e += 256) {
+        const float v = lg[e];
+        int rank = 0;
+        for (int o = 0; o < p.E; ++o) rank += (lg[o] > v) || (lg[o] == v && o < e);
+        if (rank < p.k) {
+            selv[rank] = v;
+            seli[rank] = e;
         }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            float ov = __shfl_xor(bv, o, 64);
-            int oi = __shfl_xor(bi, o, 64);
-            if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-        }
-        selv[j] = bv;
-        seli[j] = bi;
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-            if (lane + 64 * m == bi) live[m] = false;
     }
-    if (lane == 0) {
-        const float mx = selv[0];
+    __syncthreads();
+    if (threadIdx.x < p.k) {
+        const int j = threadIdx.x;
         float den = 0.f;
-        for (int j = 0; j < p.k; ++j) den += expf(selv[j] - mx);
-        for (int j = 0; j < p.k; ++j) {
-            const int e = seli[j];
-            float w = expf(selv[j] - mx) / den * (p.pes ? p.pes[e] : 1.0f);
-            p.ids[t * p.k + j] = e;
-            p.wts[t * p.k + j] = w;
-            if (p.ids_out) p.ids_out[t * p.k + j] = e;
-            if (p.w_out) p.w_out[t * p.k + j] = w;
-        }
+        for (int i = 0; i < p.k; ++i) den += expf(selv[i] - selv[0]);
+        const int e = seli[j];
+        const float w = expf(selv[j] - selv[0]) / den * (p.pes ? p.pes[e] : 1.0f);
+        p.ids[t * p.k + j] = e;
+        p.wts[t * p.k + j] = w;
+        if (p.ids_out) p.ids_out[t * p.k + j] = e;
+        if (p.w_out) p.w_out[t * p.k + j] = w;
     }
 }
 

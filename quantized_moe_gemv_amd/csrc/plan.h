@@ -9,6 +9,8 @@ constexpr int kRouterTokens = 4;    // tokens per router workgroup
 constexpr int kMaxTopK = 16;
 constexpr int kMaxExperts = 256;
 constexpr int kDownSplits = 4;      // split of the down-projection source list (GEMV path)
+constexpr int kRouterPieces = 8;   // single-launch decode: column pieces of a 16-expert router slice
+constexpr int kFusedPieces = 4;    // and of a gate/up half tile
 constexpr int kCtrStride = 64;      // counters of the single-launch decode sit 256 bytes apart
 
 struct Plan {
@@ -70,23 +72,17 @@ struct Plan {
     float* ysort;      // [T*k][H]   weighted expert outputs in sorted order
     float* ysh;        // [T][H]     shared expert outputs
     // single-launch decode: tagged words and counters that persist across calls
-    uint64_t* f_rpart;   // [E/16][rq][16]      partial router scores
-    uint64_t* f_sgpart;  // [2 G_s][gq][64]     partial shared gate (32) and up (32) rows
-    uint64_t* f_rgpart;  // [k][2 G_I][gq][64]  partial routed gate/up rows
+    uint64_t* f_rpart;   // [copies][E/16][8][16] partial router scores, rpart_stride apart
+    uint64_t* f_sgpart;  // [2 G_s][4][64]      partial shared gate (32) and up (32) rows
+    uint64_t* f_rgpart;  // [k][2 G_I][4][64]   partial routed gate/up rows
     uint64_t* f_hs;      // [copies][Is]        shared GeGLU activations (bf16 hi | lo), h_stride apart
     uint64_t* f_h;       // [copies][k][I]      routed GeGLU activations, h_stride apart
-    uint64_t* f_ids;     // [copies][2k]        expert ids and weights, ids_stride apart
-    int64_t h_stride, ids_stride;
+    int64_t h_stride, rpart_stride;
     uint64_t* f_piece;   // [G_H][n_src][64]    partial outputs per output tile and source
-    uint32_t* c_base;    // counters (kCtrStride apart) cleared at the end of every call:
-    uint32_t* c_router;  //   router pieces done
-    uint32_t* c_hs;      //   shared half tiles published
-    uint32_t* c_done;    //   workgroups finished
-    uint32_t* c_h;       //   [k] routed half tiles published per slot
+    uint32_t* c_done;    // workgroups finished (cleared at the end of every call)
     uint32_t* f_epoch;   // calls completed with this workspace
     uint32_t* f_err;     // non-zero once a bounded wait has given up
-    int rq, gq;          // column splits of router pieces and gate/up pieces
-    int n_router, n_sg, n_sd, n_sc, n_rg, n_rd, n_src, n_ctr;
+    int n_router, n_sg, n_sd, n_sc, n_rg, n_rd, n_src;
     int max_tiles;     // upper bound of scheduled (expert, token tile) pairs
     int ntile;         // tokens per grouped tile
 };
