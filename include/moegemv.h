@@ -98,7 +98,7 @@ typedef struct {
  * per-expert factors (device float arrays; NULL means 1, 1 and 0). */
 typedef struct {
     mq_qtensor w;
-    const float* router_scale;      /* [H] */
+    const float* router_scale;      /* [H], 16-byte aligned */
     const float* per_expert_scale;  /* [E] */
     const float* logit_bias;        /* [E]: added to the scores before selection */
     int32_t top_k;                  /* 1 <= top_k <= min(E, 16) */

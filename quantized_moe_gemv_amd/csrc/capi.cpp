@@ -58,7 +58,23 @@ FusedCarve fused_carve(const Sizes& z) {
     return f;
 }
 
-bool fused_ok(const Sizes& z) { return z.G_H <= 48 && z.G_I <= 12 && z.n_src <= 32; }
+// The single-launch decode holds every unit's loads in registers: at most
+// kFusedSlotsA units without expert ids and kFusedSlotsB with them per
+// workgroup, one workgroup per compute unit.
+constexpr int kFusedSlotsA = 2, kFusedSlotsB = 5;
+
+bool fused_ok(const Sizes& z, int cus) {
+    return z.G_H <= 48 && z.G_I <= 12 && z.n_src <= 32 && z.n_router + z.n_sg + z.n_sd <= kFusedSlotsA * cus &&
+           z.n_rg + z.n_rd <= kFusedSlotsB * cus;
+}
+
+int device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    return cus;
+}
 
 // Offsets of every workspace region for up to T tokens; returns the total.
 struct Carve {
@@ -118,6 +134,7 @@ mq_status check_layer(const mq_router* rt, const mq_expert_pool* pool, const mq_
     if (rt->top_k < 1 || rt->top_k > E || rt->top_k > kMaxTopK) return MQ_ERR_SHAPE;
     if (!(rt->eps >= 0.f)) return MQ_ERR_SHAPE;
     if (!aligned(rt->w.codes, kAlign) || !aligned(pool->base, kAlign)) return MQ_ERR_ALIGN;
+    if (rt->router_scale && !aligned(rt->router_scale, 16)) return MQ_ERR_ALIGN;
     if (pool->expert_stride % 256 || pool->gate_offset % 256 || pool->up_offset % 256 || pool->down_offset % 256)
         return MQ_ERR_ALIGN;
     const int64_t gu = (int64_t)mq_packed_bytes(I, H, 4, kGroup, MQ_LAYOUT_DEV_V1);
@@ -191,7 +208,7 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
         return MQ_ERR_UNSUPPORTED;
     if (x->row_stride < x->hidden || out->row_stride < out->hidden) return MQ_ERR_SHAPE;
     if (opts->path < MQ_PATH_AUTO || opts->path > MQ_PATH_FUSED) return MQ_ERR_UNSUPPORTED;
-    if (opts->path == MQ_PATH_FUSED && (T > 1 || !fused_ok(z))) return MQ_ERR_UNSUPPORTED;
+    if (opts->path == MQ_PATH_FUSED && T > 1) return MQ_ERR_UNSUPPORTED;
     if (T == 0) return MQ_OK;
     if (!x->data || !out->data || !opts->workspace) return x->data && out->data ? MQ_ERR_WORKSPACE : MQ_ERR_NULL;
     if (!aligned(x->data, 16) || x->row_stride % 8) return MQ_ERR_ALIGN;
@@ -290,12 +307,14 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
 
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
-    const bool fused = opts->path == MQ_PATH_FUSED || (opts->path == MQ_PATH_AUTO && T == 1 && fused_ok(z));
+    int cus = 0;
+    if (opts->path == MQ_PATH_FUSED || (opts->path == MQ_PATH_AUTO && T == 1)) {
+        cus = device_cus();
+        if (cus <= 0) return MQ_ERR_HIP;
+        if (opts->path == MQ_PATH_FUSED && !fused_ok(z, cus)) return MQ_ERR_UNSUPPORTED;
+    }
+    const bool fused = opts->path == MQ_PATH_FUSED || (opts->path == MQ_PATH_AUTO && T == 1 && fused_ok(z, cus));
     if (fused) {
-        int dev = 0, cus = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-            return MQ_ERR_HIP;
         hipLaunchKernelGGL(k_decode, dim3(cus), dim3(512), 0, s, p);
         return hipGetLastError() == hipSuccess ? MQ_OK : MQ_ERR_HIP;
     }

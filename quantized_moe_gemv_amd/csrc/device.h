@@ -9,6 +9,12 @@ namespace mq {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar)
+// value: branches on it are scalar branches, not exec-masked ones, so a
+// load under such a branch never shares its destination registers with a
+// masked write that would have to wait for it.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }

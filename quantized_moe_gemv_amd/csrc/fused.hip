@@ -1,22 +1,21 @@
 // Single-launch decode of one token through the whole layer.
 //
-// The layer is cut into ~25 KB units of weight streaming, listed in
-// dependency order and dealt round-robin to one workgroup per compute unit
-// (unit u runs on workgroup u % grid; each workgroup runs its units in
-// increasing order):
-//   router pieces   16 experts x a column range      -> partial scores
-//   shared gate/up  32 rows x a column range          -> partial g, u
-//   routed gate/up  (slot j, 32 rows, column range)   -> partial g, u
-//   shared down     64 output rows x a chunk of Is    -> partial outputs
-//   routed down     (64 output rows, slot j)          -> partial outputs
-// Every dependency points to an earlier unit, so with all workgroups
-// resident every wait ends; each wait is also bounded.  Partial results are
+// The layer is cut into ~25 KB units of weight streaming, in two lists
+// dealt round-robin to one workgroup per compute unit (unit i of a list runs
+// on workgroup i % grid):
+//   without expert ids: router pieces    16 experts x a column range  -> partial scores
+//                       shared gate/up   32 rows x a column range     -> partial g, u
+//                       shared down      64 output rows x a chunk of Is -> partial outputs
+//   with expert ids:    routed gate/up   (slot j, 32 rows, column range) -> partial g, u
+//                       routed down      (64 output rows, slot j)     -> partial outputs
+// A workgroup puts out the loads of all its units of the first list at
+// once, and those of the second list as soon as it knows the expert ids, so
+// the memory system has the whole remaining stream in flight; the units are
+// computed as their data lands.  Each wait is bounded.  Partial results are
 // 64-bit words carrying the call's epoch in their high half: a reader
 // issues all of its loads, then re-reads only the words whose tag is not yet
 // current.  Each sum has a fixed reducer (the highest-indexed contributor),
-// which sums in a fixed order, so results repeat bit for bit.  Each
-// workgroup issues the loads of its next unit before it computes the
-// current one.
+// which sums in a fixed order, so results repeat bit for bit.
 //
 // Results that many workgroups read (partial router scores, GeGLU
 // activations) are written once per XCD (eight copies) and each reader takes
@@ -40,6 +39,8 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kItems = 3;           // 16-byte code loads per lane per unit
 constexpr int kSpinLimit = 1 << 20;
 constexpr int kCopies = 8;         // replicas of broadcast results, one per XCD
+constexpr int kSlotsA = 2;         // units per workgroup that need no expert ids
+constexpr int kSlotsB = 5;         // units per workgroup that do
 constexpr int kRq = kRouterPieces;
 constexpr int kGq = kFusedPieces;
 
@@ -75,11 +76,15 @@ __device__ __forceinline__ uint32_t wait_word(const uint64_t* p, uint32_t tag, u
 // load is issued before any is checked, so the gather costs one round trip.
 __device__ __forceinline__ void gather_words(const uint64_t* base, int n, uint32_t tag, uint32_t* err,
                                              uint32_t* dst) {
+    if (n <= 0) {
+        __syncthreads();
+        return;
+    }
     uint64_t v[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         const int i = threadIdx.x + kThreads * m;
-        v[m] = i < n ? ld_word(base + i) : 0;
+        v[m] = ld_word(base + (i < n ? i : n - 1));   // unconditional: see issue_loads
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -110,8 +115,11 @@ struct Shared {
     alignas(16) uint16_t hhi[16 * 64];   // one source's activations, bf16 high and low parts
     alignas(16) uint16_t hlo[16 * 64];
     alignas(16) float lg[256];           // expert scores (padding: -inf)
+    alignas(16) uint64_t key[256];       // selection keys (padding: 0)
     alignas(16) float xr[4096];          // router input numerator x * router_scale
     alignas(16) float selv[kMaxTopK];    // selected scores (padding: -inf)
+    float pes[256];           // per_expert_scale (1 when absent)
+    float lbias[256];         // logit_bias (0 when absent)
     alignas(16) uint32_t gbuf[2048];     // gathered payloads (partial results of other units)
     float xsum[64 * 4];       // x summed over each lane's 16 columns of a group (4-bit blocks)
     float rsum[64 * 4];       // router input summed over each lane's 16 columns (8-bit blocks)
@@ -181,8 +189,6 @@ __device__ __forceinline__ Unit decode_unit(const Plan& p, int u) {
     return x;
 }
 
-__device__ __forceinline__ bool needs_ids(const Unit& x) { return x.kind == U_RG || x.kind == U_RD; }
-
 // A unit's weight loads, issued before the unit waits or computes.
 struct Loads {
     uint4 c[kItems];
@@ -193,53 +199,66 @@ __device__ __forceinline__ const uint8_t* tile4(const uint8_t* m, int tile, int 
     return m + (int64_t)tile * G * kBlk4;
 }
 
+// The loads of one unit.  Within a unit, item it of wave w (it = w + 8m)
+// reads the block base[it & 1] + (it >> 1) * step, so each wave needs two
+// uniform base pointers, fixed for the unit, and one scalar add per item:
+//   router:  it -> 8-bit block (slice rows, group g0 + it)
+//   gate/up: even it -> gate, odd it -> up, group g0 + it/2, one half tile
+//   down:    group g0 + it/2, rows of half (it & 1) of the output tile
+// Every item issues its two loads unconditionally (items past the unit's
+// end read the router's first block and are skipped when computed): a
+// register that a load may still be filling is never written on another
+// path, which would make that write wait for the load.
 __device__ __forceinline__ void issue_loads(const Plan& p, const Shared& sh, const Unit& x, Loads& L) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = wave_id(), lane = threadIdx.x & 63, par = wave & 1;
+    const uint8_t* b0 = p.router_w;
+    const uint8_t* b1 = p.router_w;
+    int64_t step = 0;
+    int n = 0, oc = 0, os = kCodes4;
+    if (x.kind == U_ROUTER) {
+        const int tile = x.a >> 2, j = x.a & 3;
+        b0 = p.router_w + ((int64_t)tile * p.G_H + x.g0) * kBlk8;
+        b1 = b0 + kBlk8;
+        step = 2 * kBlk8;
+        n = x.ng;
+        oc = j * 1024;
+        os = kCodes8 + 8 * (j >> 1);   // pair j is .x (j even) or .y
+    } else if (x.kind == U_SG || x.kind == U_RG) {
+        const int ht = x.kind == U_SG ? x.a : x.b;
+        const uint8_t* g;
+        const uint8_t* u;
+        if (x.kind == U_SG) {
+            g = p.sh_gate;
+            u = p.sh_up;
+        } else {
+            const uint8_t* blob = p.pool_base + (int64_t)sh.ids[x.a] * p.expert_stride;
+            g = blob + p.gate_off;
+            u = blob + p.up_off;
+        }
+        const int64_t o = ((int64_t)(ht >> 1) * p.G_H + x.g0) * kBlk4;
+        b0 = g + o;
+        b1 = u + o;
+        step = kBlk4;
+        n = 2 * x.ng;
+        oc = (ht & 1) * 1024;
+        os = kCodes4 + 8 * (ht & 1);
+    } else if (x.kind == U_SD || x.kind == U_RD) {
+        const uint8_t* m0 = x.kind == U_SD ? p.sh_down + ((int64_t)x.a * p.G_s + x.g0) * kBlk4
+                                           : p.pool_base + (int64_t)sh.ids[x.b] * p.expert_stride + p.down_off +
+                                                 (int64_t)x.a * p.G_I * kBlk4;
+        b0 = b1 = m0;
+        step = kBlk4;
+        n = 2 * x.ng;
+        oc = par * 1024;
+        os = kCodes4 + 8 * par;
+    }
+    const uint8_t* wb = (par ? b1 : b0) + (int64_t)(wave >> 1) * step;
+    const int lc = oc + lane * 16, ls = os + (lane & 15) * 16;
 #pragma unroll
     for (int m = 0; m < kItems; ++m) {
-        const int it = wave + kWaves * m;
-        L.c[m] = make_uint4(0, 0, 0, 0);
-        L.s[m] = make_uint2(0, 0);
-        if (x.kind == U_ROUTER) {
-            if (it < x.ng) {
-                const int tile = x.a >> 2, j = x.a & 3;
-                const uint8_t* blk = p.router_w + ((int64_t)tile * p.G_H + x.g0 + it) * kBlk8;
-                L.c[m] = ld_stream16(blk + (j * 64 + lane) * 16);
-                L.s[m].x = *(const uint32_t*)(blk + kCodes8 + (lane & 15) * 16 + 4 * j);
-            }
-        } else if (x.kind == U_SG || x.kind == U_RG) {
-            // items: (group, matrix), gate for even items and up for odd ones
-            if (it < 2 * x.ng) {
-                const int g = x.g0 + (it >> 1);
-                const uint8_t* m0;
-                int ht;
-                if (x.kind == U_SG) {
-                    ht = x.a;
-                    m0 = (it & 1) ? p.sh_up : p.sh_gate;
-                } else {
-                    ht = x.b;
-                    const uint8_t* blob = p.pool_base + (int64_t)sh.ids[x.a] * p.expert_stride;
-                    m0 = blob + ((it & 1) ? p.up_off : p.gate_off);
-                }
-                const int jh = ht & 1;
-                const uint8_t* blk = tile4(m0, ht >> 1, p.G_H) + (int64_t)g * kBlk4;
-                L.c[m] = ld_stream16(blk + jh * 1024 + lane * 16);
-                L.s[m] = *(const uint2*)(blk + kCodes4 + (lane & 15) * 16 + 8 * jh);
-            }
-        } else if (x.kind == U_SD || x.kind == U_RD) {
-            // items: (group, half of the 64-row output tile)
-            if (it < 2 * x.ng) {
-                const int gl = it >> 1, half = it & 1;
-                const uint8_t* blk;
-                if (x.kind == U_SD)
-                    blk = tile4(p.sh_down, x.a, p.G_s) + (int64_t)(x.g0 + gl) * kBlk4;
-                else
-                    blk = tile4(p.pool_base + (int64_t)sh.ids[x.b] * p.expert_stride + p.down_off, x.a, p.G_I) +
-                          (int64_t)gl * kBlk4;
-                L.c[m] = ld_stream16(blk + half * 1024 + lane * 16);
-                L.s[m] = *(const uint2*)(blk + kCodes4 + (lane & 15) * 16 + 8 * half);
-            }
-        }
+        const uint8_t* blk = wave + kWaves * m < n ? wb + (int64_t)(kWaves / 2) * m * step : p.router_w;
+        L.c[m] = ld_stream16(blk + lc);
+        L.s[m] = *(const uint2*)(blk + ls);
     }
 }
 
@@ -250,33 +269,60 @@ __device__ __forceinline__ float sum8_bf16(const uint4& v) {
            ((bf16_lo(v.z) + bf16_hi(v.z)) + (bf16_lo(v.w) + bf16_hi(v.w)));
 }
 
+// The token and the small per-expert vectors, loaded into registers before
+// any weight so that they head the memory queues.
+struct TokenLoads {
+    uint4 x;
+    float4 r0, r1;   // router_scale of the thread's 8 columns
+    float pes, lb;   // per_expert_scale and logit_bias of expert threadIdx.x
+};
+
+__device__ __forceinline__ void load_token(const Plan& p, TokenLoads& t) {
+    const int c = threadIdx.x;
+    t.x = make_uint4(0, 0, 0, 0);
+    t.r0 = t.r1 = make_float4(1.f, 1.f, 1.f, 1.f);
+    t.pes = 1.f;
+    t.lb = 0.f;
+    if (c < p.H / 8) {
+        t.x = *(const uint4*)(p.x + 8 * c);
+        if (p.router_scale) {
+            t.r0 = *(const float4*)(p.router_scale + 8 * c);
+            t.r1 = *(const float4*)(p.router_scale + 8 * c + 4);
+        }
+    }
+    if (c < p.E) {
+        if (p.pes) t.pes = p.pes[c];
+        if (p.logit_bias) t.lb = p.logit_bias[c];
+    }
+}
+
 // The token into LDS, the router input scale, and the column sums the block
 // dots need: thread c holds columns 8c .. 8c+7 and contributes its partial
 // sums; each lane set is then a sum of two (4-bit) or four (8-bit) of them.
-__device__ __forceinline__ void stage_token(const Plan& p, Shared& sh) {
+__device__ __forceinline__ void stage_token(const Plan& p, Shared& sh, const TokenLoads& tl) {
     const int t = threadIdx.x;
     const int nch = p.H / 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
+    const uint4 v = tl.x;
+    if (t < p.E) {
+        sh.pes[t] = tl.pes;
+        sh.lbias[t] = tl.lb;
+    }
     float ss = 0.f;
     if (t < nch) {
-        v = *(const uint4*)(p.x + 8 * t);
         *(uint4*)(sh.x + 8 * t) = v;
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        const float a[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                            bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+        const float rs[8] = {tl.r0.x, tl.r0.y, tl.r0.z, tl.r0.w, tl.r1.x, tl.r1.y, tl.r1.z, tl.r1.w};
         float q0 = 0.f, q1 = 0.f;   // sums of columns 8t..8t+3 and 8t+4..8t+7 (times router_scale)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float a0 = bf16_lo(w[i]), a1 = bf16_hi(w[i]);
-            ss += a0 * a0 + a1 * a1;
-            const float r0 = p.router_scale ? p.router_scale[8 * t + 2 * i] : 1.0f;
-            const float r1 = p.router_scale ? p.router_scale[8 * t + 2 * i + 1] : 1.0f;
-            if (i < 2) q0 += a0 * r0 + a1 * r1; else q1 += a0 * r0 + a1 * r1;
+            ss += a[2 * i] * a[2 * i] + a[2 * i + 1] * a[2 * i + 1];
+            const float r = a[2 * i] * rs[2 * i] + a[2 * i + 1] * rs[2 * i + 1];
+            if (i < 2) q0 += r; else q1 += r;
         }
         float4* xr = (float4*)(sh.xr + 8 * t);
-        float rs[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) rs[e] = p.router_scale ? p.router_scale[8 * t + e] : 1.0f;
-        xr[0] = make_float4(bf16_lo(v.x) * rs[0], bf16_hi(v.x) * rs[1], bf16_lo(v.y) * rs[2], bf16_hi(v.y) * rs[3]);
-        xr[1] = make_float4(bf16_lo(v.z) * rs[4], bf16_hi(v.z) * rs[5], bf16_lo(v.w) * rs[6], bf16_hi(v.w) * rs[7]);
+        xr[0] = make_float4(a[0] * rs[0], a[1] * rs[1], a[2] * rs[2], a[3] * rs[3]);
+        xr[1] = make_float4(a[4] * rs[4], a[5] * rs[5], a[6] * rs[6], a[7] * rs[7]);
         sh.c8[t] = sum8_bf16(v);
         sh.c4[2 * t] = q0;
         sh.c4[2 * t + 1] = q1;
@@ -310,43 +356,53 @@ __device__ __forceinline__ void stage_token(const Plan& p, Shared& sh) {
 __device__ __forceinline__ void fetch_ids(const Plan& p, Shared& sh, uint32_t tag) {
     const int nslice = (p.E + 15) / 16, epad = (p.E + 31) & ~31;
     gather_words(p.f_rpart + (blockIdx.x % kCopies) * p.rpart_stride, nslice * kRq * 16, tag, p.f_err, sh.gbuf);
-    // the workgroup of the first routed gate/up unit (it always fetches the ids)
-    const bool reporter = (int)blockIdx.x == (p.n_router + p.n_sg) % (int)gridDim.x;
+    // workgroup 0 runs the first routed unit, so it always fetches the ids
+    const bool reporter = blockIdx.x == 0;
+    // Selection key of expert e: the score's bits made order-preserving as an
+    // unsigned integer (NaN as -inf, -0 as +0) above 0xFFFF - e, so that keys
+    // compare as (score, then lower index); padding keys are 0, below all.
     for (int e = threadIdx.x; e < epad; e += kThreads) {
         float s = -INFINITY;
+        uint64_t key = 0;
         if (e < p.E) {
             const int slice = e >> 4, r = e & 15;
             float a[kRq];
 #pragma unroll
             for (int q = 0; q < kRq; ++q) a[q] = __uint_as_float(sh.gbuf[(slice * kRq + q) * 16 + r]);
             s = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
-            if (p.logit_bias) s += p.logit_bias[e];
+            s += sh.lbias[e];
             if (reporter && p.logits_out) p.logits_out[e] = s;
             if (!(s == s)) s = -INFINITY;   // a NaN score ranks last; ids stay distinct
+            if (s == 0.f) s = 0.f;
+            uint32_t u = __float_as_uint(s);
+            u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+            key = ((uint64_t)u << 32) | (uint32_t)(0xFFFF - e);
         }
         sh.lg[e] = s;
+        sh.key[e] = key;
     }
     if (threadIdx.x < kMaxTopK) sh.selv[threadIdx.x] = -INFINITY;
     __syncthreads();
-    for (int e = threadIdx.x; e < p.E; e += kThreads) {
-        const float v = sh.lg[e];
+    // Rank of expert e = the number of keys above its key.  Each expert's
+    // comparisons are split over nparts adjacent lanes, summed by shuffles.
+    {
+        const int lg2 = epad <= 128 ? 2 : 1, nparts = 1 << lg2;
+        const int e = threadIdx.x >> lg2, part = threadIdx.x & (nparts - 1), len = epad >> lg2;
         int rank = 0;
-        for (int c = 0; c < epad; c += 32) {
-            float4 w[8];
-#pragma unroll
-            for (int m = 0; m < 8; ++m) w[m] = *(const float4*)(sh.lg + c + 4 * m);
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const int o = c + 4 * m;
-                rank += (w[m].x > v) + (w[m].x == v && o < e);
-                rank += (w[m].y > v) + (w[m].y == v && o + 1 < e);
-                rank += (w[m].z > v) + (w[m].z == v && o + 2 < e);
-                rank += (w[m].w > v) + (w[m].w == v && o + 3 < e);
+        if (e < p.E) {
+            const uint64_t me = sh.key[e];
+            const uint64_t* kp = sh.key + part * len;
+            for (int o = 0; o < len; o += 4) {
+                const ulonglong2 k0 = *(const ulonglong2*)(kp + o);
+                const ulonglong2 k1 = *(const ulonglong2*)(kp + o + 2);
+                rank += (int)(k0.x > me) + (int)(k0.y > me) + (int)(k1.x > me) + (int)(k1.y > me);
             }
         }
-        if (rank < p.k) {
+        rank += __shfl_xor(rank, 1, 64);
+        if (lg2 == 2) rank += __shfl_xor(rank, 2, 64);
+        if (e < p.E && part == 0 && rank < p.k) {
             sh.ids[rank] = e;
-            sh.selv[rank] = v;
+            sh.selv[rank] = sh.lg[e];
         }
     }
     __syncthreads();
@@ -360,7 +416,7 @@ __device__ __forceinline__ void fetch_ids(const Plan& p, Shared& sh, uint32_t ta
 #pragma unroll
         for (int m = 0; m < kMaxTopK / 4; ++m)
             den += (expf(sv[m].x - top) + expf(sv[m].y - top)) + (expf(sv[m].z - top) + expf(sv[m].w - top));
-        const float w = expf(sh.selv[j] - top) / den * (p.pes ? p.pes[sh.ids[j]] : 1.0f);
+        const float w = expf(sh.selv[j] - top) / den * sh.pes[sh.ids[j]];
         sh.wts[j] = w;
         if (reporter) {
             if (p.ids_out) p.ids_out[j] = sh.ids[j];
@@ -407,7 +463,7 @@ __device__ __forceinline__ void half_block_dot(const uint4& c, const uint4& xa, 
 // Row totals over the lanes and waves: v[r] holds rows 16*r + lane%16; after
 // the call sh.red[w][row] holds wave w's part of each row.
 __device__ __forceinline__ void reduce_rows(Shared& sh, const float* v, int nr) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = wave_id(), lane = threadIdx.x & 63;
     for (int r = 0; r < nr; ++r) {
         const float s = sum_kb(v[r]);
         if (lane < 16) sh.red[wave][16 * r + lane] = s;
@@ -421,8 +477,17 @@ __device__ __forceinline__ float row_total(const Shared& sh, int row) {
     return v;
 }
 
+// Row (0..63) of a unit whose even waves hold rows 0..31 and odd waves
+// rows 32..63 (gate/up: gate and up rows; down: the two halves of a tile).
+__device__ __forceinline__ float row_total_par(const Shared& sh, int row) {
+    const int par = row >> 5, r = row & 31;
+    float v = 0.f;
+    for (int w = par; w < kWaves; w += 2) v += sh.red[w][r];
+    return v;
+}
+
 __device__ __forceinline__ void run_router(const Plan& p, Shared& sh, const Unit& x, const Loads& L, uint32_t tag) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, kb = lane >> 4;
+    const int wave = wave_id(), lane = threadIdx.x & 63, kb = lane >> 4;
     float acc = 0.f;
 #pragma unroll
     for (int m = 0; m < kItems; ++m) {
@@ -439,11 +504,12 @@ __device__ __forceinline__ void run_router(const Plan& p, Shared& sh, const Unit
                 d = fmaf((float)((cw[i] >> 16) & 0xFFu), r.z, d);
                 d = fmaf((float)(cw[i] >> 24), r.w, d);
             }
-            acc = fmaf(bf16_lo(L.s[m].x), d * sh.rc, fmaf(bf16_hi(L.s[m].x), sh.rsum[g * 4 + kb], acc));
+            const uint32_t sw = (x.a & 1) ? L.s[m].y : L.s[m].x;
+            acc = fmaf(bf16_lo(sw), d * sh.rc, fmaf(bf16_hi(sw), sh.rsum[g * 4 + kb], acc));
         }
     }
     reduce_rows(sh, &acc, 1);
-    if (threadIdx.x < 16 * kCopies) {
+    if (wave_id() < 16 * kCopies / 64) {
         const int r = threadIdx.x & 15, c = threadIdx.x >> 4;
         st_word(p.f_rpart + c * p.rpart_stride + (int64_t)(x.a * kRq + x.q) * 16 + r, tag,
                 __float_as_uint(row_total(sh, r)));
@@ -454,13 +520,13 @@ __device__ __forceinline__ void run_router(const Plan& p, Shared& sh, const Unit
 // Gate/up piece: 32 rows x a column range -> partial (g, u).  The last of
 // the gq pieces of a half tile reduces them and publishes h = gelu(g) * u.
 __device__ __forceinline__ void run_gateup(const Plan& p, Shared& sh, const Unit& x, const Loads& L, uint32_t tag) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, kb = lane >> 4;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};    // rows 16*r + lane%16: r = 0, 1 gate, 2, 3 up
+    const int wave = wave_id(), lane = threadIdx.x & 63, kb = lane >> 4;
+    float acc[2] = {0.f, 0.f};    // rows 16*r + lane%16 of the wave's matrix (gate: even waves, up: odd)
 #pragma unroll
     for (int m = 0; m < kItems; ++m) {
         const int it = wave + kWaves * m;
         if (it < 2 * x.ng) {
-            const int g = x.g0 + (it >> 1), mat = it & 1;
+            const int g = x.g0 + (it >> 1);
             const uint4 xa = *(const uint4*)(sh.x + 64 * g + 8 * kb);
             const uint4 xb = *(const uint4*)(sh.x + 64 * g + 32 + 8 * kb);
             const float xs = sh.xsum[g * 4 + kb];
@@ -468,23 +534,20 @@ __device__ __forceinline__ void run_gateup(const Plan& p, Shared& sh, const Unit
             half_block_dot(L.c[m], xa, xb, d);
             const uint32_t sw[2] = {L.s[m].x, L.s[m].y};
 #pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const float v = fmaf(bf16_lo(sw[r]), fmaf(-128.f, xs, d[r]), bf16_hi(sw[r]) * xs);
-                if (mat == 0) acc[r] += v; else acc[2 + r] += v;
-            }
+            for (int r = 0; r < 2; ++r) acc[r] += fmaf(bf16_lo(sw[r]), fmaf(-128.f, xs, d[r]), bf16_hi(sw[r]) * xs);
         }
     }
-    reduce_rows(sh, acc, 4);
+    reduce_rows(sh, acc, 2);
     const bool shared = x.kind == U_SG;
     const int ht = shared ? x.a : x.b;
     uint64_t* base = shared ? p.f_sgpart + (int64_t)ht * kGq * 64
                             : p.f_rgpart + ((int64_t)x.a * 2 * p.G_I + ht) * kGq * 64;
-    if (threadIdx.x < 64) st_word(base + x.q * 64 + threadIdx.x, tag, __float_as_uint(row_total(sh, threadIdx.x)));
+    if (wave_id() == 0) st_word(base + x.q * 64 + threadIdx.x, tag, __float_as_uint(row_total_par(sh, threadIdx.x)));
     __syncthreads();
     if (x.q != kGq - 1) return;
     // the last piece of the half tile: sum all pieces in order, then GeGLU
     gather_words(base, kGq * 64, tag, p.f_err, sh.gbuf);
-    if (threadIdx.x < 32) {
+    if (wave_id() == 0 && threadIdx.x < 32) {
         const int r = threadIdx.x;
         float gv = 0.f, uv = 0.f;
 #pragma unroll
@@ -505,15 +568,15 @@ __device__ __forceinline__ void run_gateup(const Plan& p, Shared& sh, const Unit
 // Down piece: one 64-row output tile from one source -> partial outputs.  The
 // last of the n_src pieces of a tile sums them in source order into out.
 __device__ __forceinline__ void run_down(const Plan& p, Shared& sh, const Unit& x, const Loads& L, uint32_t tag) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, kb = lane >> 4;
+    const int wave = wave_id(), lane = threadIdx.x & 63, kb = lane >> 4;
     const bool shared = x.kind == U_SD;
     const float wf = shared ? 1.0f : sh.wts[x.b];
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};    // rows 16*r + lane%16 of the output tile
+    float acc[2] = {0.f, 0.f};    // rows 32*(wave & 1) + 16*r + lane%16 of the output tile
 #pragma unroll
     for (int m = 0; m < kItems; ++m) {
         const int it = wave + kWaves * m;
         if (it < 2 * x.ng) {
-            const int gl = it >> 1, half = it & 1;
+            const int gl = it >> 1;
             const uint4 ha = *(const uint4*)(sh.hhi + 64 * gl + 8 * kb);
             const uint4 hb = *(const uint4*)(sh.hhi + 64 * gl + 32 + 8 * kb);
             const uint4 la = *(const uint4*)(sh.hlo + 64 * gl + 8 * kb);
@@ -524,23 +587,20 @@ __device__ __forceinline__ void run_down(const Plan& p, Shared& sh, const Unit& 
             half_block_dot(L.c[m], la, lb, d);
             const uint32_t sw[2] = {L.s[m].x, L.s[m].y};
 #pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const float v = wf * fmaf(bf16_lo(sw[r]), fmaf(-128.f, hs, d[r]), bf16_hi(sw[r]) * hs);
-                if (half == 0) acc[r] += v; else acc[2 + r] += v;
-            }
+            for (int r = 0; r < 2; ++r) acc[r] += wf * fmaf(bf16_lo(sw[r]), fmaf(-128.f, hs, d[r]), bf16_hi(sw[r]) * hs);
         }
     }
-    reduce_rows(sh, acc, 4);
+    reduce_rows(sh, acc, 2);
     const int src = shared ? p.k + x.b : x.b;
     uint64_t* tilep = p.f_piece + (int64_t)x.a * p.n_src * 64;
-    if (threadIdx.x < 64) st_word(tilep + src * 64 + threadIdx.x, tag, __float_as_uint(row_total(sh, threadIdx.x)));
+    if (wave_id() == 0) st_word(tilep + src * 64 + threadIdx.x, tag, __float_as_uint(row_total_par(sh, threadIdx.x)));
     __syncthreads();
     if (shared || x.b != p.k - 1) return;
     // the last source of this output tile: sum every source in order
     gather_words(tilep, p.n_src * 64, tag, p.f_err, sh.gbuf);
     for (int i = p.n_src * 64 + threadIdx.x; i < ((p.n_src + 3) & ~3) * 64; i += kThreads) sh.gbuf[i] = 0u;
     __syncthreads();
-    if (threadIdx.x < 64) {
+    if (wave_id() == 0) {
         float v = 0.f;
         for (int s2 = 0; s2 < p.n_src; s2 += 4) {
             const float a0 = __uint_as_float(sh.gbuf[s2 * 64 + threadIdx.x]);
@@ -558,75 +618,81 @@ __device__ __forceinline__ void run_down(const Plan& p, Shared& sh, const Unit& 
     __syncthreads();
 }
 
-__device__ __forceinline__ void run_unit(const Plan& p, Shared& sh, const Unit& x, const Loads& L, uint32_t tag) {
-    switch (x.kind) {
-        case U_ROUTER:
-            run_router(p, sh, x, L, tag);
-            break;
-        case U_SG:
-        case U_RG:
-            run_gateup(p, sh, x, L, tag);
-            break;
-        case U_SD:
-            stage_h(p, sh, p.f_hs + (blockIdx.x % kCopies) * p.h_stride, x.g0, x.ng, tag);
-            run_down(p, sh, x, L, tag);
-            break;
-        case U_RD:
-            stage_h(p, sh, p.f_h + (blockIdx.x % kCopies) * p.h_stride + (int64_t)x.b * p.I, 0, x.ng, tag);
-            run_down(p, sh, x, L, tag);
-            break;
-        default:
-            break;
-    }
-}
-
 // ----------------------------------------------------------------- the kernel
 
-// One step of a workgroup's unit sequence: make sure the current unit's
-// loads are out, put the next unit's loads out when their addresses are
-// known, then run the current unit.  The two load buffers swap roles from
-// step to step (the caller alternates them), so loads still in flight are
-// never copied between registers, which would make the copy wait for them.
-__device__ __forceinline__ void step(const Plan& p, Shared& sh, const Unit& cur, Loads& lc, bool& ic, const Unit& nxt,
-                                     Loads& ln, bool& in, bool& have, uint32_t tag) {
-    if (!ic) {
-        if (!have) {
-            fetch_ids(p, sh, tag);
-            have = true;
-        }
-        issue_loads(p, sh, cur, lc);
-        ic = true;
-    }
-    if (!in && nxt.kind != U_NONE && (!needs_ids(nxt) || have)) {
-        issue_loads(p, sh, nxt, ln);
-        in = true;
-    }
-    run_unit(p, sh, cur, lc, tag);
+// Units that need no expert ids, in dependency order: router pieces, shared
+// gate/up pieces, shared down pieces.
+__device__ __forceinline__ Unit unit_a(const Plan& p, int i) {
+    if (i < p.n_router + p.n_sg) return decode_unit(p, i);
+    if (i < p.n_router + p.n_sg + p.n_sd) return decode_unit(p, i + p.n_rg);
+    return decode_unit(p, 1 << 30);
 }
 
+// Units that need them: routed gate/up pieces, then routed down pieces.
+__device__ __forceinline__ Unit unit_b(const Plan& p, int i) {
+    const int a0 = p.n_router + p.n_sg;
+    if (i < p.n_rg) return decode_unit(p, a0 + i);
+    if (i < p.n_rg + p.n_rd) return decode_unit(p, a0 + p.n_sd + i);
+    return decode_unit(p, 1 << 30);
+}
+
+// Phases of a workgroup (every branch below is taken by all of its waves):
+//   1. the token's loads, then the weight loads of every unit that needs no
+//      expert ids;
+//   2. the router and shared gate/up pieces (they wait for nothing);
+//   3. the expert ids (waits for the router pieces), then the weight loads of
+//      every routed unit, all in flight at once;
+//   4. the shared down pieces (wait for the shared activations), then the
+//      routed units in order.
+// Every wait is for a unit earlier in the order router < shared gate/up <
+// ids < shared down < routed gate/up < routed down, and each workgroup runs
+// its units in that order, so with all workgroups resident every wait ends.
 __global__ __launch_bounds__(kThreads) void k_decode(Plan p) {
     __shared__ Shared sh;
     const uint32_t tag = ld_ctr(p.f_epoch) + 1;
     const int nwg = gridDim.x;
-    // Every branch below is taken by all waves alike: the flags live in
-    // registers and change only where every wave passes.
-    int u = blockIdx.x;
-    Unit ua = decode_unit(p, u), ub = decode_unit(p, u + nwg);
-    Loads la, lb;
-    bool ia = false, ib = false, have = false;
-    if (ua.kind != U_NONE && !needs_ids(ua)) { issue_loads(p, sh, ua, la); ia = true; }
-    if (ub.kind != U_NONE && !needs_ids(ub)) { issue_loads(p, sh, ub, lb); ib = true; }
-    stage_token(p, sh);
-    while (ua.kind != U_NONE) {
-        step(p, sh, ua, la, ia, ub, lb, ib, have, tag);
-        u += nwg;
-        if (ub.kind == U_NONE) break;
-        ua = decode_unit(p, u + nwg);
-        ia = false;
-        step(p, sh, ub, lb, ib, ua, la, ia, have, tag);
-        u += nwg;
-        ub = decode_unit(p, u + nwg);
-        ib = false;
+    TokenLoads tl;
+    load_token(p, tl);
+    Unit ua[kSlotsA];
+    Loads la[kSlotsA];
+#pragma unroll
+    for (int i = 0; i < kSlotsA; ++i) {
+        ua[i] = unit_a(p, blockIdx.x + i * nwg);
+        issue_loads(p, sh, ua[i], la[i]);
+    }
+    stage_token(p, sh, tl);
+#pragma unroll
+    for (int i = 0; i < kSlotsA; ++i) {
+        if (ua[i].kind == U_ROUTER)
+            run_router(p, sh, ua[i], la[i], tag);
+        else if (ua[i].kind == U_SG)
+            run_gateup(p, sh, ua[i], la[i], tag);
+    }
+    Unit ub[kSlotsB];
+    Loads lb[kSlotsB];
+    bool routed = false;
+#pragma unroll
+    for (int i = 0; i < kSlotsB; ++i) {
+        ub[i] = unit_b(p, blockIdx.x + i * nwg);
+        routed |= ub[i].kind != U_NONE;
+    }
+    if (routed) fetch_ids(p, sh, tag);
+#pragma unroll
+    for (int i = 0; i < kSlotsB; ++i) issue_loads(p, sh, ub[i], lb[i]);
+#pragma unroll
+    for (int i = 0; i < kSlotsA; ++i)
+        if (ua[i].kind == U_SD) {
+            stage_h(p, sh, p.f_hs + (blockIdx.x % kCopies) * p.h_stride, ua[i].g0, ua[i].ng, tag);
+            run_down(p, sh, ua[i], la[i], tag);
+        }
+#pragma unroll
+    for (int i = 0; i < kSlotsB; ++i) {
+        if (ub[i].kind == U_RG) {
+            run_gateup(p, sh, ub[i], lb[i], tag);
+        } else if (ub[i].kind == U_RD) {
+            stage_h(p, sh, p.f_h + (blockIdx.x % kCopies) * p.h_stride + (int64_t)ub[i].b * p.I, 0, ub[i].ng, tag);
+            run_down(p, sh, ub[i], lb[i], tag);
+        }
     }
     // The last workgroup to finish clears every counter and advances the epoch.
     __syncthreads();

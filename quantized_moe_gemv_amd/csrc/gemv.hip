@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void k_prep(Plan p) {
 // ceil(T / kRouterTokens) token chunks), 4 waves splitting the groups.
 __global__ __launch_bounds__(256) void k_router(Plan p) {
     const int tile = blockIdx.x, split = blockIdx.y, t0 = blockIdx.z * kRouterTokens;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, kb = lane >> 4;
+    const int wave = wave_id(), lane = threadIdx.x & 63, kb = lane >> 4;
     const int g0 = split * p.rgroups, g1 = min(p.G_H, g0 + p.rgroups);
     const int nt = min(kRouterTokens, p.T - t0);
     float acc[kRouterTokens][4];
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(256) void k_topk(Plan p) {
 // grid (T, k * I/64 + Is/64).
 __global__ __launch_bounds__(256) void k_gateup(Plan p) {
     const int t = blockIdx.x, item = blockIdx.y;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, kb = lane >> 4;
+    const int wave = wave_id(), lane = threadIdx.x & 63, kb = lane >> 4;
     const int It = p.I / 64, routed = p.k * It;
     const uint8_t *gw, *uw;
     uint16_t *hi, *lo;
@@ -245,7 +245,7 @@ __global__ __launch_bounds__(256) void k_gateup(Plan p) {
 // grid (T, H/64, kDownSplits).
 __global__ __launch_bounds__(256) void k_down(Plan p) {
     const int t = blockIdx.x, rt = blockIdx.y, split = blockIdx.z;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, kb = lane >> 4;
+    const int wave = wave_id(), lane = threadIdx.x & 63, kb = lane >> 4;
     const int nr = p.k * p.G_I, nb = nr + (p.has_shared ? p.G_s : 0);
     const int b0 = split * nb / kDownSplits, b1 = (split + 1) * nb / kDownSplits;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};

@@ -114,7 +114,7 @@ __device__ __forceinline__ float4_t mma_tile(const uint8_t* tile, int G, int ms,
 // Gate/up + GeGLU for one (expert, token tile) or, with shared = 1, for the
 // shared expert over a tile of all tokens.  grid (I/64, tiles), block 256.
 __global__ __launch_bounds__(256) void k_gg_gateup(Plan p, int shared) {
-    const int rt = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int rt = blockIdx.x, wave = wave_id(), lane = threadIdx.x & 63;
     const int n = lane & 15;
     int count, first;   // tokens of this tile, position of its first pair
     const uint8_t *gw, *uw;
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) void k_gg_gateup(Plan p, int shared) {
 // Down projection for one (expert, token tile): ysort[pos] = w_pair * (W_down . h),
 // or with shared = 1 the shared expert: ysh[t] = W_sdown . hs.  grid (H/64, tiles).
 __global__ __launch_bounds__(256) void k_gg_down(Plan p, int shared) {
-    const int rt = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int rt = blockIdx.x, wave = wave_id(), lane = threadIdx.x & 63;
     const int n = lane & 15;
     int count, first, G, K;
     const uint8_t* dw;
