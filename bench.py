@@ -1,23 +1,36 @@
 """Benchmark of the quantized MoE FFN layer on one MI355X.
 
-One step = one call of the whole layer (router, top-k, routed experts,
-shared expert, combine) for one decode token of a Gemma-4-26B-A4B-shaped
-layer (hidden 2816, 128 experts, top-8, expert intermediate 704, shared
-intermediate 2112; 8-bit router, 4-bit experts, group 64).  Calls rotate
-over --layers distinct resident layers with a fresh token each, so the
-256 MB Infinity Cache cannot hold the working set.  The timed calls are
+The headline line is decode: one call of the whole layer (router, top-k,
+routed experts, shared expert, combine) for one token of a Gemma-4-26B-A4B-
+shaped layer (hidden 2816, 128 experts, top-8, expert intermediate 704,
+shared intermediate 2112; 8-bit router, 4-bit experts, group 64).  Calls
+rotate over --layers distinct resident layers with a fresh token each, so
+the 256 MB Infinity Cache cannot hold the working set.  The timed calls are
 replayed from a HIP graph (one capture of K calls); inputs are resident in
-HBM before the timer starts.
+HBM before the timer starts.  The single-launch decode kernel's own duration
+is the timed region's event interval over the launches in it (one launch
+per call); the roofline figure divides the call's algorithmic bytes by it.
 
-Also reported: the 128-token prefill chunk with Zipf(1.1)-skewed routing
-(same layers), and the fp64 CPU oracle timed on a bounded sample of decode
-tokens.  Prints one JSON line.
+Also reported (extra fields of the same JSON line): the 128-token prefill
+chunk with Zipf(1.1)-skewed routing, the 30-layer stack (one token through
+30 layers with an RMSNorm between them), the 4096-token prefill (the
+matrix-core regime, reported in TFLOP/s), and the fp64 CPU oracle timed on
+a bounded sample of decode tokens.  Prints one JSON line on stdout.
+
+Profiling helpers (not part of the default run):
+  --profile decode       runs decode calls back to back, then a copy kernel of
+                         known size, for rocprofv3 counter runs;
+  --traffic-summary F W  turns the FETCH_SIZE / WRITE_SIZE counter CSVs of
+                         those runs into the traffic summary under profiles/.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 from concurrent.futures import ThreadPoolExecutor
@@ -27,12 +40,26 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, vendor figure
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
+MFMA_PEAK_TFLOPS = 2500.0    # MI355X dense fp16/bf16 matrix peak, vendor figure
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (% of peak), decode and 128-tok prefill"
+DECODE_KERNEL = "k_decode"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_decode_decode_h2816_e128_traffic.txt")
+COPY_BYTES = 256 << 20       # each direction of the reference copy kernel
+# Sources whose change invalidates the recorded counter traffic of the decode kernel.
+KERNEL_SOURCES = ["fused.hip", "device.h", "plan.h", "layout.h"]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "quantized_moe_gemv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def build_layers(M, S, cfg, seed, n_layers, threads):
@@ -55,15 +82,18 @@ def build_layers(M, S, cfg, seed, n_layers, threads):
     return layers
 
 
-def decode_bytes(dev, cfg):
-    """Algorithmic HBM bytes of one decode call: router, the k selected experts,
-    the shared expert, the input row and the bf16 output row."""
+def layer_bytes(M, cfg):
+    """Algorithmic bytes: one routed expert, the router, the shared expert."""
     H, I, Is = cfg.hidden, cfg.inter, cfg.shared_inter
-    import quantized_moe_gemv_amd as M
     expert = 2 * M.packed_bytes(I, H, 4) + M.packed_bytes(H, I, 4)
     shared = 2 * M.packed_bytes(Is, H, 4) + M.packed_bytes(H, Is, 4)
     router = M.packed_bytes(cfg.num_experts, H, 8)
-    return router + cfg.top_k * expert + shared + 2 * H * 2, expert, router, shared
+    return expert, router, shared
+
+
+def flops_per_token(cfg):
+    H, E, k, I, Is = cfg.hidden, cfg.num_experts, cfg.top_k, cfg.inter, cfg.shared_inter
+    return 2 * E * H + k * 6 * I * H + 6 * Is * H
 
 
 def time_graph(torch, calls, steps, warmup):
@@ -82,7 +112,6 @@ def time_graph(torch, calls, steps, warmup):
     g.replay()                      # untimed replay
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     ev0.record()
     g.replay()
     ev1.record()
@@ -101,6 +130,20 @@ def time_eager(torch, calls, steps):
     return ev0.elapsed_time(ev1) / steps
 
 
+def recorded_traffic():
+    """HBM bytes per decode launch from the committed counter summary, or None
+    when it is missing or was taken from other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            txt = f.read()
+    except OSError:
+        return None, "no counter summary"
+    kv = dict(re.findall(r"^(\w+):\s*(\S+)\s*$", txt, re.M))
+    if kv.get("source_sha256") != kernel_source_hash():
+        return None, "kernel changed since the counters were taken"
+    return float(kv["traffic_bytes_per_launch"]), "rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel"
+
+
 def cpu_baseline(S, cfg, seed, tokens, threads):
     import oracle as O
     host = S.make_layer(cfg, seed, layer=0)
@@ -109,9 +152,96 @@ def cpu_baseline(S, cfg, seed, tokens, threads):
     O.forward(host, x, threads=threads, dense_experts=False)
     dt = time.time() - t0
     return dict(value=tokens / dt, unit="tokens/s", cores=threads, kind="oracle",
-                sample="%d decode tokens of layer 0 (fp64 C oracle, token-parallel over %d threads), %.1f s wall"
-                       % (tokens, threads, dt))
+                sample="%d decode tokens of one layer of the decode workload (fp64 C oracle, tokens split over "
+                       "%d threads), %.1f s wall" % (tokens, threads, dt))
 
+
+def host_threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 4
+    return max(1, min(16, n))
+
+
+# ------------------------------------------------------------------ profiling helpers
+
+def profile_decode(args):
+    """Back-to-back decode calls, then a copy kernel of COPY_BYTES each way."""
+    import torch
+    import qmoe_synth as S
+    import quantized_moe_gemv_amd as M
+    torch.cuda.set_device(0)
+    cfg, seed = S.CONFIGS["decode"], S.SEEDS["stack30"]
+    layers = build_layers(M, S, cfg, seed, args.layers, host_threads())
+    xs = torch.from_numpy(S.make_tokens(seed, args.steps, cfg.hidden, batch=1).view(np.int16)).view(torch.bfloat16)
+    xs = xs.cuda()
+    ws = layers[0].new_workspace(1)
+    out = torch.empty((1, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+    for i in range(args.steps):
+        M.moe_layer_forward(layers[i % len(layers)], xs[i:i + 1], out=out, workspace=ws, path="fused")
+    torch.cuda.synchronize()
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log("profile run done: %d decode calls, 5 copies of %d B" % (args.steps, COPY_BYTES))
+
+
+def read_counter(path, counter):
+    """Per-dispatch values of `counter` for the decode kernel and the copy kernel."""
+    dec, cop = [], []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"])
+            if DECODE_KERNEL in r["Kernel_Name"]:
+                dec.append(v)
+            elif "elementwise_kernel" in r["Kernel_Name"] and int(r["Grid_Size"]) >= COPY_BYTES // 64:
+                cop.append(v)
+    if not dec or not cop:
+        raise SystemExit("%s: no %s rows for the decode or the copy kernel" % (path, counter))
+    return float(np.median(dec)), float(np.median(cop)), len(dec)
+
+
+def traffic_summary(fetch_csv, write_csv, out_path):
+    f_dec, f_cop, n = read_counter(fetch_csv, "FETCH_SIZE")
+    w_dec, w_cop, _ = read_counter(write_csv, "WRITE_SIZE")
+    ff = COPY_BYTES / (f_cop * 1024.0)     # bytes per KiB of counter reading
+    fw = COPY_BYTES / (w_cop * 1024.0)
+    fetch = f_dec * 1024.0 * ff
+    write = w_dec * 1024.0 * fw
+    lines = [
+        "# HBM traffic of the single-launch decode kernel (k_decode)",
+        "# workload: decode, 1 token per call, H2816 E128 top8 I704 Is2112, rotated over 30 resident layers",
+        "# commands (run from /tmp with TMPDIR=/tmp):",
+        "#   rocprofv3 --pmc FETCH_SIZE -d <dir> -o fetch --output-format csv -- python3 <repo>/bench.py --profile decode --steps 200",
+        "#   rocprofv3 --pmc WRITE_SIZE -d <dir> -o write --output-format csv -- python3 <repo>/bench.py --profile decode --steps 200",
+        "#   python3 <repo>/bench.py --traffic-summary <dir>/fetch_counter_collection.csv <dir>/write_counter_collection.csv",
+        "# The copy kernel (torch.neg over %d B, fp32) reads and writes %d B per launch; its counter" % (COPY_BYTES, COPY_BYTES),
+        "# readings give the scale from KiB of counter to bytes of HBM traffic.",
+        "kernel: %s" % DECODE_KERNEL,
+        "source_sha256: %s" % kernel_source_hash(),
+        "dispatches: %d" % n,
+        "fetch_kib_per_dispatch: %.1f" % f_dec,
+        "write_kib_per_dispatch: %.1f" % w_dec,
+        "copy_fetch_kib: %.1f" % f_cop,
+        "copy_write_kib: %.1f" % w_cop,
+        "fetch_scale: %.4f" % ff,
+        "write_scale: %.4f" % fw,
+        "fetch_bytes_per_launch: %.0f" % fetch,
+        "write_bytes_per_launch: %.0f" % write,
+        "traffic_bytes_per_launch: %.0f" % (fetch + write),
+        "algorithmic_bytes_per_launch: 37193728",
+    ]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+# ------------------------------------------------------------------ main run
 
 def main():
     ap = argparse.ArgumentParser()
@@ -121,14 +251,24 @@ def main():
     ap.add_argument("--layers", type=int, default=30)
     ap.add_argument("--prefill-steps", type=int, default=60)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--no-large", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=64)
+    ap.add_argument("--cpu-tokens", type=int, default=640)
     ap.add_argument("--path", default="auto", choices=["auto", "fused", "gemv", "grouped"])
+    ap.add_argument("--profile", choices=["decode"])
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(args.traffic_summary[0], args.traffic_summary[1], TRAFFIC_FILE)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the layer runs on a single MI355X and has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.profile:
+        profile_decode(args)
+        return
 
     import torch
     import qmoe_synth as S
@@ -137,10 +277,11 @@ def main():
     torch.cuda.set_device(0)
     cfg = S.CONFIGS["decode"]
     seed = S.SEEDS["stack30"]
-    threads = min(16, os.cpu_count() or 4)
+    threads = host_threads()
     layers = build_layers(M, S, cfg, seed, args.layers, threads)
     H, k = cfg.hidden, cfg.top_k
-    per_call, expert_b, router_b, shared_b = decode_bytes(layers[0], cfg)
+    expert_b, router_b, shared_b = layer_bytes(M, cfg)
+    per_call = router_b + k * expert_b + shared_b + 2 * H * 2
 
     # ---------------------------------------------------------------- decode
     n_tok = args.steps
@@ -156,8 +297,10 @@ def main():
     calls = [decode_call(i) for i in range(args.steps)]
     ms, _ = time_graph(torch, calls, args.steps, args.warmup)
     ms_eager = time_eager(torch, calls, min(args.steps, 300))
+    # one launch of the decode kernel per call: the timed region's events over its launches
     gbs = per_call / (ms * 1e-3) / 1e9
     log("decode: %.2f us/call (graph), %.2f us/call (eager), %.0f GB/s" % (ms * 1e3, ms_eager * 1e3, gbs))
+    traffic, traffic_note = recorded_traffic() if args.path in ("auto", "fused") else (None, "not the fused kernel")
 
     result = {
         "metric": METRIC,
@@ -171,17 +314,20 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic (seeded random 4-bit/8-bit group-64 affine codes, bf16 N(0,1) tokens)",
+        "data": "synthetic (seeded uniform 4-bit/8-bit group-64 affine codes, bf16 scale/bias, bf16 N(0,1) tokens)",
         "config": {
-            "workload": "decode, 1 token per call, Gemma-4-26B-A4B MoE layer (H2816 E128 top8 I704 Is2112, "
-                        "8-bit router, 4-bit experts, group 64), rotated over %d resident layers" % len(layers),
+            "workload": "decode, 1 token per call, Gemma-4-26B-A4B-shaped MoE layer (hidden 2816, 128 experts, "
+                        "top-8, expert intermediate 704, shared intermediate 2112; 8-bit router, 4-bit experts, "
+                        "group 64), rotated over %d resident layers" % len(layers),
             "tokens_per_call": 1, "resident_layers": len(layers), "launch": "hip graph of %d calls" % args.steps,
             "weights": "int4/int8 affine group-64, bf16 scale+bias", "accumulate": "fp32", "output": "bf16",
+            "path": args.path,
         },
         "roofline": {
-            "bound": "hbm", "kernel": "moe_layer_forward (whole call)", "achieved": gbs, "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-            "bytes_per_call": per_call,
+            "bound": "hbm", "kernel": DECODE_KERNEL if args.path in ("auto", "fused") else "whole call",
+            "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+            "traffic": traffic, "traffic_source": traffic_note,
+            "algorithmic_bytes_per_launch": per_call, "launch_ms": ms,
         },
         "decode_eager_ms_per_call": ms_eager,
     }
@@ -212,7 +358,52 @@ def main():
             "tokens_per_s": T / (pms * 1e-3), "ms_per_call": pms, "achieved_GBs": pgbs,
             "frac_hbm_peak": pgbs / HBM_PEAK_GBS, "experts_touched_mean": float(touched.mean()),
             "bytes_per_call": float(pbytes), "calls": args.prefill_steps,
+            "workload": "128-token prefill chunk, Zipf(1.1) logit bias, same layers",
         }
+
+    # ---------------------------------------------------------------- 30-layer stack
+    if not args.no_stack and len(layers) >= 2:
+        ntk = 8
+        xa = torch.from_numpy(S.make_tokens(seed, ntk, H, batch=3).view(np.int16)).view(torch.bfloat16).cuda()
+        bufs = [torch.empty((1, H), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+
+        def token_calls(t):
+            seq = []
+            for l, dev in enumerate(layers):
+                src = xa[t:t + 1] if l == 0 else bufs[l % 2]
+                dst = bufs[(l + 1) % 2]
+                seq.append(lambda dev=dev, src=src, dst=dst: M.moe_layer_forward(dev, src, out=dst, workspace=ws))
+                seq.append(lambda dst=dst: M.rmsnorm(dst, out=dst))
+            return seq
+        scalls = [c for t in range(ntk) for c in token_calls(t)]
+        sms, _ = time_graph(torch, scalls, len(scalls), 0)
+        per_tok = sms * len(scalls) / ntk
+        sgbs = len(layers) * per_call / (per_tok * 1e-3) / 1e9
+        log("stack%d: %.2f us/token, %.0f tokens/s, %.0f GB/s" % (len(layers), per_tok * 1e3, 1.0 / (per_tok * 1e-3), sgbs))
+        result["stack"] = {
+            "layers": len(layers), "tokens_per_s": 1.0 / (per_tok * 1e-3), "ms_per_token": per_tok,
+            "achieved_GBs": sgbs, "frac_hbm_peak": sgbs / HBM_PEAK_GBS, "tokens": ntk,
+            "workload": "one decode token through %d resident layers, unit-weight RMSNorm between layers" % len(layers),
+        }
+
+    # ---------------------------------------------------------------- prefill 4096
+    if not args.no_large:
+        T = 4096
+        xl = torch.from_numpy(S.make_tokens(seed, T, H, batch=4).view(np.int16)).view(torch.bfloat16).cuda()
+        zb = torch.from_numpy(S.zipf_logit_bias(seed, 0, cfg.num_experts)).cuda()
+        dev = layers[0].with_logit_bias(zb)
+        wsl = dev.new_workspace(T)
+        outl = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        lcall = [lambda: M.moe_layer_forward(dev, xl, out=outl, workspace=wsl)]
+        lms, _ = time_graph(torch, lcall, 3, 1)
+        tf = T * flops_per_token(cfg) / (lms * 1e-3) / 1e12
+        log("prefill4096: %.3f ms/call, %.0f tokens/s, %.1f TFLOP/s" % (lms, T / (lms * 1e-3), tf))
+        result["prefill4096"] = {
+            "tokens_per_s": T / (lms * 1e-3), "ms_per_call": lms, "TFLOPs": tf,
+            "frac_mfma_peak": tf / MFMA_PEAK_TFLOPS, "flops_per_call": T * flops_per_token(cfg),
+            "workload": "4096-token prefill, Zipf(1.1) logit bias, one layer",
+        }
+        del wsl
 
     # ---------------------------------------------------------------- CPU oracle
     if not args.no_cpu_baseline:

@@ -42,6 +42,12 @@ def prefill(M):
     return host, M.DeviceLayer(host)
 
 
+@pytest.fixture(scope="module")
+def large(M):
+    host = S.make_layer(S.CONFIGS["prefill4096"], S.SEEDS["prefill4096"])
+    return host, M.DeviceLayer(host)
+
+
 def packed_dev(M, qt):
     return torch.from_numpy(M.pack(qt)).cuda()
 
@@ -182,6 +188,29 @@ def test_prefill128_layer(M, prefill):
     log("  experts touched %d, max tokens per expert %d, near-ties %d" % ((counts > 0).sum(), counts.max(), excused))
     sample = np.random.default_rng(1).choice(T, 12, replace=False)
     sample = np.union1d(sample, [0, T - 1])
+    ref = O.forward(host, x[sample], threads=8, dense_experts=False)
+    sub = {key: got[key][sample] for key in ("ids", "w", "logits", "out32", "out16")}
+    rel = check_output(ref, sub, ok[sample])
+    log("  max err / RMS = %.3g" % rel)
+
+
+def test_prefill4096_layer(M, large):
+    """The large-batch prefill at its full size (the matrix-core regime): every
+    routing decision and a sample of the outputs."""
+    host, dev = large
+    T = 4096
+    log("prefill layer T=4096 with Zipf routing: every routing decision, 16 sampled outputs")
+    x = S.make_tokens(S.SEEDS["prefill4096"], T, host.cfg.hidden)
+    got = run_gpu(M, dev, x, "auto")
+    ref_lg = np.stack([O.router_logits(host, x[t]) for t in range(T)])
+    ref_ids = np.empty((T, host.cfg.top_k), np.int32)
+    ref_w = np.empty((T, host.cfg.top_k))
+    for t in range(T):
+        ref_ids[t], ref_w[t] = O.topk(host, ref_lg[t])
+    ok, excused = check_routing(dict(ids=ref_ids, w=ref_w, logits=ref_lg), got, host.cfg.top_k)
+    counts = np.bincount(got["ids"].ravel(), minlength=host.cfg.num_experts)
+    log("  experts touched %d, max tokens per expert %d, near-ties %d" % ((counts > 0).sum(), counts.max(), excused))
+    sample = np.union1d(np.random.default_rng(2).choice(T, 14, replace=False), [0, T - 1])
     ref = O.forward(host, x[sample], threads=8, dense_experts=False)
     sub = {key: got[key][sample] for key in ("ids", "w", "logits", "out32", "out16")}
     rel = check_output(ref, sub, ok[sample])
