@@ -30,14 +30,14 @@ inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 struct Sizes {
     int H, E, E_pad, k, I, Is, G_H, G_I, G_s, rsplit, rgroups, ntile, max_tiles;
-    int n_router, n_sg, n_sd, n_sc, n_rg, n_rd, n_src;
+    int n_router, n_sg, n_sd, n_sc, n_rh, n_rd, n_src;
 };
 
 // State of the single-launch decode that persists across calls.  It sits at
 // the start of the workspace, at offsets that do not depend on the token
 // count, and no other kernel writes it.
 struct FusedCarve {
-    size_t rpart, sgpart, rgpart, act, piece, ctr, total;
+    size_t rpart, sgpart, act, piece, ctr, total;
     int64_t h_stride, rpart_stride;   // in 8-byte words
 };
 
@@ -48,7 +48,6 @@ FusedCarve fused_carve(const Sizes& z) {
     f.rpart_stride = (int64_t)up((size_t)(z.E + 15) / 16 * 8 * 16 * 8) / 8;
     f.rpart = take((size_t)8 * f.rpart_stride * 8);
     f.sgpart = take((size_t)2 * z.G_s * kFusedPieces * 64 * 8 + 8);
-    f.rgpart = take((size_t)z.k * 2 * z.G_I * kFusedPieces * 64 * 8);
     // one copy per XCD of the activations (shared then routed)
     f.h_stride = (int64_t)up(((size_t)z.Is + (size_t)z.k * z.I) * 8 + 8) / 8;
     f.act = take((size_t)8 * f.h_stride * 8);
@@ -58,14 +57,17 @@ FusedCarve fused_carve(const Sizes& z) {
     return f;
 }
 
-// The single-launch decode holds every unit's loads in registers: at most
-// kFusedSlotsA units without expert ids and kFusedSlotsB with them per
-// workgroup, one workgroup per compute unit.
-constexpr int kFusedSlotsA = 2, kFusedSlotsB = 5;
+// The single-launch decode holds every unit's loads in registers, one
+// workgroup per compute unit: at most kFusedSlotsA units without expert ids
+// per workgroup; one full-row routed gate/up unit (2 G_H <= 8 waves x 12
+// loads) on each of the first n_rh workgroups; kFusedSlotsL down pieces on
+// each of the others and kFusedSlotsX on each of the first n_rh.
+constexpr int kFusedSlotsA = 2, kFusedSlotsL = 3, kFusedSlotsX = 2;
 
 bool fused_ok(const Sizes& z, int cus) {
-    return z.G_H <= 48 && z.G_I <= 12 && z.n_src <= 32 && z.n_router + z.n_sg + z.n_sd <= kFusedSlotsA * cus &&
-           z.n_rg + z.n_rd <= kFusedSlotsB * cus;
+    const int64_t m = (int64_t)cus - z.n_rh;
+    return z.G_H <= 48 && z.G_I <= 12 && z.n_src <= 32 && z.n_router + z.n_sg <= kFusedSlotsA * cus && m >= 0 &&
+           z.n_sd + z.n_rd <= m * kFusedSlotsL + (int64_t)z.n_rh * kFusedSlotsX;
 }
 
 int device_cus() {
@@ -174,7 +176,7 @@ mq_status check_layer(const mq_router* rt, const mq_expert_pool* pool, const mq_
     z->n_sg = 2 * z->G_s * kFusedPieces;
     z->n_sc = (z->G_s + z->G_I - 1) / z->G_I;
     z->n_sd = z->G_H * z->n_sc;
-    z->n_rg = 2 * z->k * z->G_I * kFusedPieces;
+    z->n_rh = 2 * z->k * z->G_I;
     z->n_rd = z->G_H * z->k;
     z->n_src = z->k + z->n_sc;
     return MQ_OK;
@@ -287,7 +289,6 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
     const FusedCarve f = fused_carve(z);
     p.f_rpart = (uint64_t*)(ws + f.rpart);
     p.f_sgpart = (uint64_t*)(ws + f.sgpart);
-    p.f_rgpart = (uint64_t*)(ws + f.rgpart);
     p.f_hs = (uint64_t*)(ws + f.act);
     p.f_h = p.f_hs + z.Is;
     p.h_stride = f.h_stride;
@@ -301,7 +302,7 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
     p.n_sg = z.n_sg;
     p.n_sd = z.n_sd;
     p.n_sc = z.n_sc;
-    p.n_rg = z.n_rg;
+    p.n_rh = z.n_rh;
     p.n_rd = z.n_rd;
     p.n_src = z.n_src;
 

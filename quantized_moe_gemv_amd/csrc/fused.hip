@@ -39,8 +39,10 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kItems = 3;           // 16-byte code loads per lane per unit
 constexpr int kSpinLimit = 1 << 20;
 constexpr int kCopies = 8;         // replicas of broadcast results, one per XCD
+constexpr int kItemsRH = 12;       // 16-byte code loads per lane of a full-row routed gate/up unit
 constexpr int kSlotsA = 2;         // units per workgroup that need no expert ids
-constexpr int kSlotsB = 5;         // units per workgroup that do
+constexpr int kSlotsL = 3;         // down pieces of a workgroup without a full-row unit
+constexpr int kSlotsX = 2;         // down pieces of a workgroup with one
 constexpr int kRq = kRouterPieces;
 constexpr int kGq = kFusedPieces;
 
@@ -100,11 +102,11 @@ __device__ __forceinline__ void gather_words(const uint64_t* base, int n, uint32
 
 // ----------------------------------------------------------------- units
 
-enum { U_ROUTER = 0, U_SG = 1, U_SD = 2, U_RG = 3, U_RD = 4, U_NONE = 5 };
+enum { U_ROUTER = 0, U_SG = 1, U_SD = 2, U_RH = 3, U_RD = 4, U_NONE = 5 };
 
 struct Unit {
     int kind;
-    int a, b;         // router: slice; SG: half tile; SD: out tile, chunk; RG: slot, half tile; RD: out tile, slot
+    int a, b;         // router: slice; SG: half tile; SD: out tile, chunk; RH: slot, half tile; RD: out tile, slot
     int q;            // piece index of the column range (router, gate/up)
     int g0, ng;       // column-group range
 };
@@ -140,60 +142,86 @@ __device__ __forceinline__ void krange(int G, int nq, int q, int* g0, int* ng) {
     *ng = b - a;
 }
 
-__device__ __forceinline__ Unit decode_unit(const Plan& p, int u) {
+__device__ __forceinline__ Unit no_unit() {
     Unit x;
-    x.a = x.b = x.q = x.g0 = x.ng = 0;
-    if (u < p.n_router) {
-        x.kind = U_ROUTER;
-        x.a = u / kRq;
-        x.q = u % kRq;
-        krange(p.G_H, kRq, x.q, &x.g0, &x.ng);
-        return x;
-    }
-    u -= p.n_router;
-    if (u < p.n_sg) {
-        x.kind = U_SG;
-        x.a = u / kGq;
-        x.q = u % kGq;
-        krange(p.G_H, kGq, x.q, &x.g0, &x.ng);
-        return x;
-    }
-    u -= p.n_sg;
-    if (u < p.n_rg) {
-        x.kind = U_RG;
-        const int per = 2 * p.G_I * kGq;
-        x.a = u / per;
-        x.b = (u % per) / kGq;
-        x.q = u % kGq;
-        krange(p.G_H, kGq, x.q, &x.g0, &x.ng);
-        return x;
-    }
-    u -= p.n_rg;
-    if (u < p.n_sd) {
-        x.kind = U_SD;
-        x.a = u / p.n_sc;
-        x.b = u % p.n_sc;
-        x.g0 = x.b * p.G_I;
-        x.ng = min(p.G_I, p.G_s - x.g0);
-        return x;
-    }
-    u -= p.n_sd;
-    if (u < p.n_rd) {
-        x.kind = U_RD;
-        x.a = u / p.k;
-        x.b = u % p.k;
-        x.ng = p.G_I;
-        return x;
-    }
     x.kind = U_NONE;
+    x.a = x.b = x.q = x.g0 = x.ng = 0;
     return x;
 }
 
+// Unit i of the list that needs no expert ids: router pieces, then shared
+// gate/up pieces.
+__device__ __forceinline__ Unit unit_a(const Plan& p, int i) {
+    Unit x = no_unit();
+    if (i < p.n_router) {
+        x.kind = U_ROUTER;
+        x.a = i / kRq;
+        x.q = i % kRq;
+        krange(p.G_H, kRq, x.q, &x.g0, &x.ng);
+    } else if (i < p.n_router + p.n_sg) {
+        i -= p.n_router;
+        x.kind = U_SG;
+        x.a = i / kGq;
+        x.q = i % kGq;
+        krange(p.G_H, kGq, x.q, &x.g0, &x.ng);
+    }
+    return x;
+}
+
+// Full-row routed gate/up unit w: slot w / (2 G_I), half tile w % (2 G_I),
+// every column group.
+__device__ __forceinline__ Unit unit_rh(const Plan& p, int w) {
+    Unit x = no_unit();
+    if (w < p.n_rh) {
+        x.kind = U_RH;
+        x.a = w / (2 * p.G_I);
+        x.b = w % (2 * p.G_I);
+        x.ng = p.G_H;
+    }
+    return x;
+}
+
+// Down piece i: shared down pieces (output tile, chunk of Is), then routed
+// down pieces (output tile, slot), each tile's slots in order.
+__device__ __forceinline__ Unit unit_down(const Plan& p, int i) {
+    Unit x = no_unit();
+    if (i < p.n_sd) {
+        x.kind = U_SD;
+        x.a = i / p.n_sc;
+        x.b = i % p.n_sc;
+        x.g0 = x.b * p.G_I;
+        x.ng = min(p.G_I, p.G_s - x.g0);
+    } else if (i < p.n_sd + p.n_rd) {
+        i -= p.n_sd;
+        x.kind = U_RD;
+        x.a = i / p.k;
+        x.b = i % p.k;
+        x.ng = p.G_I;
+    }
+    return x;
+}
+
+// Down piece of slot s of workgroup w.  The workgroups without a full-row
+// unit take the first pieces, kSlotsL each, round-robin; the rest go to the
+// workgroups with one, kSlotsX each.  Either way a workgroup's pieces come in
+// increasing order.
+__device__ __forceinline__ int down_piece(const Plan& p, int w, int nwg, int s) {
+    const int m = nwg - p.n_rh, nd = p.n_sd + p.n_rd, nfirst = min(nd, m * kSlotsL);
+    if (w >= p.n_rh) {
+        const int i = (w - p.n_rh) + m * s;
+        return i < nfirst ? i : nd;
+    }
+    const int i = nfirst + w + p.n_rh * s;
+    return i < nd ? i : nd;
+}
+
 // A unit's weight loads, issued before the unit waits or computes.
-struct Loads {
-    uint4 c[kItems];
-    uint2 s[kItems];
+template <int N>
+struct LoadsN {
+    uint4 c[N];
+    uint2 s[N];
 };
+typedef LoadsN<kItems> Loads;
 
 __device__ __forceinline__ const uint8_t* tile4(const uint8_t* m, int tile, int G) {
     return m + (int64_t)tile * G * kBlk4;
@@ -209,7 +237,8 @@ __device__ __forceinline__ const uint8_t* tile4(const uint8_t* m, int tile, int 
 // end read the router's first block and are skipped when computed): a
 // register that a load may still be filling is never written on another
 // path, which would make that write wait for the load.
-__device__ __forceinline__ void issue_loads(const Plan& p, const Shared& sh, const Unit& x, Loads& L) {
+template <int N>
+__device__ __forceinline__ void issue_loads(const Plan& p, const Shared& sh, const Unit& x, LoadsN<N>& L) {
     const int wave = wave_id(), lane = threadIdx.x & 63, par = wave & 1;
     const uint8_t* b0 = p.router_w;
     const uint8_t* b1 = p.router_w;
@@ -223,7 +252,7 @@ __device__ __forceinline__ void issue_loads(const Plan& p, const Shared& sh, con
         n = x.ng;
         oc = j * 1024;
         os = kCodes8 + 8 * (j >> 1);   // pair j is .x (j even) or .y
-    } else if (x.kind == U_SG || x.kind == U_RG) {
+    } else if (x.kind == U_SG || x.kind == U_RH) {
         const int ht = x.kind == U_SG ? x.a : x.b;
         const uint8_t* g;
         const uint8_t* u;
@@ -255,7 +284,7 @@ __device__ __forceinline__ void issue_loads(const Plan& p, const Shared& sh, con
     const uint8_t* wb = (par ? b1 : b0) + (int64_t)(wave >> 1) * step;
     const int lc = oc + lane * 16, ls = os + (lane & 15) * 16;
 #pragma unroll
-    for (int m = 0; m < kItems; ++m) {
+    for (int m = 0; m < N; ++m) {
         const uint8_t* blk = wave + kWaves * m < n ? wb + (int64_t)(kWaves / 2) * m * step : p.router_w;
         L.c[m] = ld_stream16(blk + lc);
         L.s[m] = *(const uint2*)(blk + ls);
@@ -392,6 +421,7 @@ __device__ __forceinline__ void fetch_ids(const Plan& p, Shared& sh, uint32_t ta
         if (e < p.E) {
             const uint64_t me = sh.key[e];
             const uint64_t* kp = sh.key + part * len;
+#pragma unroll 8
             for (int o = 0; o < len; o += 4) {
                 const ulonglong2 k0 = *(const ulonglong2*)(kp + o);
                 const ulonglong2 k1 = *(const ulonglong2*)(kp + o + 2);
@@ -406,21 +436,20 @@ __device__ __forceinline__ void fetch_ids(const Plan& p, Shared& sh, uint32_t ta
         }
     }
     __syncthreads();
-    if (threadIdx.x < p.k) {
-        const int j = threadIdx.x;
-        float4 sv[kMaxTopK / 4];
+    // softmax over the selected scores (padding entries are -inf, so 0)
+    if (wave_id() == 0) {
+        const int j = threadIdx.x & (kMaxTopK - 1);
+        const float ej = expf(sh.selv[j] - sh.selv[0]);
+        float den = ej;
 #pragma unroll
-        for (int m = 0; m < kMaxTopK / 4; ++m) sv[m] = *(const float4*)(sh.selv + 4 * m);
-        const float top = sv[0].x;
-        float den = 0.f;
-#pragma unroll
-        for (int m = 0; m < kMaxTopK / 4; ++m)
-            den += (expf(sv[m].x - top) + expf(sv[m].y - top)) + (expf(sv[m].z - top) + expf(sv[m].w - top));
-        const float w = expf(sh.selv[j] - top) / den * sh.pes[sh.ids[j]];
-        sh.wts[j] = w;
-        if (reporter) {
-            if (p.ids_out) p.ids_out[j] = sh.ids[j];
-            if (p.w_out) p.w_out[j] = w;
+        for (int o = 1; o < kMaxTopK; o <<= 1) den += __shfl_xor(den, o, 64);
+        if (threadIdx.x < p.k) {
+            const float w = ej / den * sh.pes[sh.ids[j]];
+            sh.wts[j] = w;
+            if (reporter) {
+                if (p.ids_out) p.ids_out[j] = sh.ids[j];
+                if (p.w_out) p.w_out[j] = w;
+            }
         }
     }
     __syncthreads();
@@ -517,8 +546,8 @@ __device__ __forceinline__ void run_router(const Plan& p, Shared& sh, const Unit
     __syncthreads();
 }
 
-// Gate/up piece: 32 rows x a column range -> partial (g, u).  The last of
-// the gq pieces of a half tile reduces them and publishes h = gelu(g) * u.
+// Shared gate/up piece: 32 rows x a column range -> partial (g, u).  The
+// last of the pieces of a half tile reduces them and publishes h = gelu(g) * u.
 __device__ __forceinline__ void run_gateup(const Plan& p, Shared& sh, const Unit& x, const Loads& L, uint32_t tag) {
     const int wave = wave_id(), lane = threadIdx.x & 63, kb = lane >> 4;
     float acc[2] = {0.f, 0.f};    // rows 16*r + lane%16 of the wave's matrix (gate: even waves, up: odd)
@@ -538,10 +567,8 @@ __device__ __forceinline__ void run_gateup(const Plan& p, Shared& sh, const Unit
         }
     }
     reduce_rows(sh, acc, 2);
-    const bool shared = x.kind == U_SG;
-    const int ht = shared ? x.a : x.b;
-    uint64_t* base = shared ? p.f_sgpart + (int64_t)ht * kGq * 64
-                            : p.f_rgpart + ((int64_t)x.a * 2 * p.G_I + ht) * kGq * 64;
+    const int ht = x.a;
+    uint64_t* base = p.f_sgpart + (int64_t)ht * kGq * 64;
     if (wave_id() == 0) st_word(base + x.q * 64 + threadIdx.x, tag, __float_as_uint(row_total_par(sh, threadIdx.x)));
     __syncthreads();
     if (x.q != kGq - 1) return;
@@ -558,9 +585,44 @@ __device__ __forceinline__ void run_gateup(const Plan& p, Shared& sh, const Unit
         const float h = gelu_tanh(gv) * uv;
         const uint16_t h1 = f32_to_bf16(h);
         const uint16_t h2 = f32_to_bf16(h - bf16_to_f32(h1));
-        uint64_t* hout = shared ? p.f_hs + 32 * ht : p.f_h + (int64_t)x.a * p.I + 32 * ht;
+        uint64_t* hout = p.f_hs + 32 * ht;
 #pragma unroll
         for (int c = 0; c < kCopies; ++c) st_word(hout + c * p.h_stride + r, tag, ((uint32_t)h1 << 16) | h2);
+    }
+    __syncthreads();
+}
+
+// Full-row routed gate/up unit: 32 rows of gate and up of one selected
+// expert over every column group, so the workgroup holds complete sums and
+// publishes h = gelu(g) * u for its 32 rows without any partial exchange.
+__device__ __forceinline__ void run_rh(const Plan& p, Shared& sh, const Unit& x, const LoadsN<kItemsRH>& L,
+                                       uint32_t tag) {
+    const int wave = wave_id(), lane = threadIdx.x & 63, kb = lane >> 4;
+    float acc[2] = {0.f, 0.f};    // rows 16*r + lane%16 of the wave's matrix (gate: even waves, up: odd)
+#pragma unroll
+    for (int m = 0; m < kItemsRH; ++m) {
+        const int it = wave + kWaves * m;
+        if (it < 2 * x.ng) {
+            const int g = it >> 1;
+            const uint4 xa = *(const uint4*)(sh.x + 64 * g + 8 * kb);
+            const uint4 xb = *(const uint4*)(sh.x + 64 * g + 32 + 8 * kb);
+            const float xs = sh.xsum[g * 4 + kb];
+            float d[2] = {0.f, 0.f};
+            half_block_dot(L.c[m], xa, xb, d);
+            const uint32_t sw[2] = {L.s[m].x, L.s[m].y};
+#pragma unroll
+            for (int r = 0; r < 2; ++r) acc[r] += fmaf(bf16_lo(sw[r]), fmaf(-128.f, xs, d[r]), bf16_hi(sw[r]) * xs);
+        }
+    }
+    reduce_rows(sh, acc, 2);
+    if (wave_id() == 0 && threadIdx.x < 32) {
+        const int r = threadIdx.x;
+        const float h = gelu_tanh(row_total_par(sh, r)) * row_total_par(sh, 32 + r);
+        const uint16_t h1 = f32_to_bf16(h);
+        const uint16_t h2 = f32_to_bf16(h - bf16_to_f32(h1));
+        uint64_t* hout = p.f_h + (int64_t)x.a * p.I + 32 * x.b + r;
+#pragma unroll
+        for (int c = 0; c < kCopies; ++c) st_word(hout + c * p.h_stride, tag, ((uint32_t)h1 << 16) | h2);
     }
     __syncthreads();
 }
@@ -618,37 +680,51 @@ __device__ __forceinline__ void run_down(const Plan& p, Shared& sh, const Unit& 
     __syncthreads();
 }
 
+// A shared or routed down piece with its activations staged; nothing for
+// an empty slot.
+__device__ __forceinline__ void run_down_unit(const Plan& p, Shared& sh, const Unit& x, const Loads& L, uint32_t tag) {
+    if (x.kind == U_SD) {
+        stage_h(p, sh, p.f_hs + (blockIdx.x % kCopies) * p.h_stride, x.g0, x.ng, tag);
+        run_down(p, sh, x, L, tag);
+    } else if (x.kind == U_RD) {
+        stage_h(p, sh, p.f_h + (blockIdx.x % kCopies) * p.h_stride + (int64_t)x.b * p.I, 0, x.ng, tag);
+        run_down(p, sh, x, L, tag);
+    }
+}
+
 // ----------------------------------------------------------------- the kernel
 
-// Units that need no expert ids, in dependency order: router pieces, shared
-// gate/up pieces, shared down pieces.
-__device__ __forceinline__ Unit unit_a(const Plan& p, int i) {
-    if (i < p.n_router + p.n_sg) return decode_unit(p, i);
-    if (i < p.n_router + p.n_sg + p.n_sd) return decode_unit(p, i + p.n_rg);
-    return decode_unit(p, 1 << 30);
-}
-
-// Units that need them: routed gate/up pieces, then routed down pieces.
-__device__ __forceinline__ Unit unit_b(const Plan& p, int i) {
-    const int a0 = p.n_router + p.n_sg;
-    if (i < p.n_rg) return decode_unit(p, a0 + i);
-    if (i < p.n_rg + p.n_rd) return decode_unit(p, a0 + p.n_sd + i);
-    return decode_unit(p, 1 << 30);
-}
-
 // Phases of a workgroup (every branch below is taken by all of its waves):
-//   1. the token's loads, then the weight loads of every unit that needs no
-//      expert ids;
-//   2. the router and shared gate/up pieces (they wait for nothing);
+//   1. the token's loads, then the weight loads of its units that need no
+//      expert ids (router pieces, shared gate/up pieces);
+//   2. those units;
 //   3. the expert ids (waits for the router pieces), then the weight loads of
-//      every routed unit, all in flight at once;
-//   4. the shared down pieces (wait for the shared activations), then the
-//      routed units in order.
+//      all its remaining units at once: one full-row routed gate/up unit
+//      (workgroups 0 .. n_rh-1) and its down pieces;
+//   4. those units in order.
 // Every wait is for a unit earlier in the order router < shared gate/up <
-// ids < shared down < routed gate/up < routed down, and each workgroup runs
-// its units in that order, so with all workgroups resident every wait ends.
+// ids < routed gate/up < shared down < routed down (a tile's slots in
+// order), and each workgroup runs its units in that order, so with all
+// workgroups resident every wait ends.
+
+// Touch every field of the argument block the kernel reads, in one batch.
+// Left alone, the compiler fetches the block field by field near each first
+// use: a chain of dependent scalar-cache misses before the first weight load.
+// Once the lines are cached, later reads of the fields hit.
+__device__ __forceinline__ void prefetch_args(const Plan& p) {
+    asm volatile("" ::"s"(p.x), "s"(p.router_w), "s"(p.router_scale), "s"(p.pes), "s"(p.logit_bias),
+                 "s"(p.f_epoch), "s"(p.pool_base), "s"(p.sh_gate), "s"(p.sh_up), "s"(p.sh_down));
+    asm volatile("" ::"s"(p.f_rpart), "s"(p.f_sgpart), "s"(p.f_hs), "s"(p.f_h), "s"(p.f_piece),
+                 "s"(p.f_err), "s"(p.c_done), "s"(p.out), "s"(p.ids_out), "s"(p.w_out), "s"(p.logits_out));
+    asm volatile("" ::"s"(p.E), "s"(p.k), "s"(p.H), "s"(p.I), "s"(p.G_H), "s"(p.G_I), "s"(p.G_s), "s"(p.n_src),
+                 "s"(p.n_sg), "s"(p.n_router), "s"(p.n_rh), "s"(p.n_sd), "s"(p.n_sc), "s"(p.n_rd), "s"(p.eps));
+    asm volatile("" ::"s"(p.h_stride), "s"(p.rpart_stride), "s"(p.expert_stride), "s"(p.gate_off), "s"(p.up_off),
+                 "s"(p.down_off), "s"(p.out_f32), "s"(gridDim.x));
+}
+
 __global__ __launch_bounds__(kThreads) void k_decode(Plan p) {
     __shared__ Shared sh;
+    prefetch_args(p);
     const uint32_t tag = ld_ctr(p.f_epoch) + 1;
     const int nwg = gridDim.x;
     TokenLoads tl;
@@ -668,31 +744,32 @@ __global__ __launch_bounds__(kThreads) void k_decode(Plan p) {
         else if (ua[i].kind == U_SG)
             run_gateup(p, sh, ua[i], la[i], tag);
     }
-    Unit ub[kSlotsB];
-    Loads lb[kSlotsB];
-    bool routed = false;
+    const int w = blockIdx.x;
+    const Unit rh = unit_rh(p, w);
+    if (rh.kind == U_RH || down_piece(p, w, nwg, 0) < p.n_sd + p.n_rd) fetch_ids(p, sh, tag);
+    if (rh.kind == U_RH) {
+        LoadsN<kItemsRH> lr;
+        Unit ux[kSlotsX];
+        Loads lx[kSlotsX];
+        issue_loads(p, sh, rh, lr);
 #pragma unroll
-    for (int i = 0; i < kSlotsB; ++i) {
-        ub[i] = unit_b(p, blockIdx.x + i * nwg);
-        routed |= ub[i].kind != U_NONE;
-    }
-    if (routed) fetch_ids(p, sh, tag);
+        for (int i = 0; i < kSlotsX; ++i) {
+            ux[i] = unit_down(p, down_piece(p, w, nwg, i));
+            issue_loads(p, sh, ux[i], lx[i]);
+        }
+        run_rh(p, sh, rh, lr, tag);
 #pragma unroll
-    for (int i = 0; i < kSlotsB; ++i) issue_loads(p, sh, ub[i], lb[i]);
+        for (int i = 0; i < kSlotsX; ++i) run_down_unit(p, sh, ux[i], lx[i], tag);
+    } else {
+        Unit ul[kSlotsL];
+        Loads ll[kSlotsL];
 #pragma unroll
-    for (int i = 0; i < kSlotsA; ++i)
-        if (ua[i].kind == U_SD) {
-            stage_h(p, sh, p.f_hs + (blockIdx.x % kCopies) * p.h_stride, ua[i].g0, ua[i].ng, tag);
-            run_down(p, sh, ua[i], la[i], tag);
+        for (int i = 0; i < kSlotsL; ++i) {
+            ul[i] = unit_down(p, down_piece(p, w, nwg, i));
+            issue_loads(p, sh, ul[i], ll[i]);
         }
 #pragma unroll
-    for (int i = 0; i < kSlotsB; ++i) {
-        if (ub[i].kind == U_RG) {
-            run_gateup(p, sh, ub[i], lb[i], tag);
-        } else if (ub[i].kind == U_RD) {
-            stage_h(p, sh, p.f_h + (blockIdx.x % kCopies) * p.h_stride + (int64_t)ub[i].b * p.I, 0, ub[i].ng, tag);
-            run_down(p, sh, ub[i], lb[i], tag);
-        }
+        for (int i = 0; i < kSlotsL; ++i) run_down_unit(p, sh, ul[i], ll[i], tag);
     }
     // The last workgroup to finish clears every counter and advances the epoch.
     __syncthreads();
