@@ -2,6 +2,8 @@
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/moegemv.h"
 #include "layout.h"
 #include "plan.h"
@@ -30,7 +32,7 @@ inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 struct Sizes {
     int H, E, E_pad, k, I, Is, G_H, G_I, G_s, rsplit, rgroups, ntile, max_tiles;
-    int n_router, n_sg, n_sd, n_sc, n_rh, n_rd, n_src;
+    int n_router, n_sg, n_sd, n_sc, n_rh, n_src;
 };
 
 // State of the single-launch decode that persists across calls.  It sits at
@@ -59,15 +61,23 @@ FusedCarve fused_carve(const Sizes& z) {
 
 // The single-launch decode holds every unit's loads in registers, one
 // workgroup per compute unit: at most kFusedSlotsA units without expert ids
-// per workgroup; one full-row routed gate/up unit (2 G_H <= 8 waves x 12
-// loads) on each of the first n_rh workgroups; kFusedSlotsL down pieces on
-// each of the others and kFusedSlotsX on each of the first n_rh.
-constexpr int kFusedSlotsA = 2, kFusedSlotsL = 3, kFusedSlotsX = 2;
+// per workgroup; a full-row routed gate/up unit (2 G_H <= 8 waves x 12 loads)
+// and at most one shared down piece on each of the first n_rh workgroups;
+// one routed down unit (one slot, at most kFusedTilesD output tiles) on each
+// of the next k * n_rng; the remaining shared down pieces after those; the
+// sum of output tile a on workgroup a.
+constexpr int kFusedSlotsA = 2, kFusedTilesD = 5;
+
+int fused_ranges(const Sizes& z, int cus) {
+    const int m = cus - z.n_rh;
+    return m < z.k ? 0 : std::min(m / z.k, z.G_H);
+}
 
 bool fused_ok(const Sizes& z, int cus) {
-    const int64_t m = (int64_t)cus - z.n_rh;
-    return z.G_H <= 48 && z.G_I <= 12 && z.n_src <= 32 && z.n_router + z.n_sg <= kFusedSlotsA * cus && m >= 0 &&
-           z.n_sd + z.n_rd <= m * kFusedSlotsL + (int64_t)z.n_rh * kFusedSlotsX;
+    const int r = fused_ranges(z, cus);
+    if (z.G_H > 48 || z.G_I > 12 || z.n_src > 32 || z.n_router + z.n_sg > kFusedSlotsA * cus || r < 1) return false;
+    const int spare = cus - z.n_rh - z.k * r;
+    return (z.G_H + r - 1) / r <= kFusedTilesD && z.n_sd <= z.n_rh + spare && z.G_H <= cus;
 }
 
 int device_cus() {
@@ -177,7 +187,6 @@ mq_status check_layer(const mq_router* rt, const mq_expert_pool* pool, const mq_
     z->n_sc = (z->G_s + z->G_I - 1) / z->G_I;
     z->n_sd = z->G_H * z->n_sc;
     z->n_rh = 2 * z->k * z->G_I;
-    z->n_rd = z->G_H * z->k;
     z->n_src = z->k + z->n_sc;
     return MQ_OK;
 }
@@ -303,7 +312,6 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
     p.n_sd = z.n_sd;
     p.n_sc = z.n_sc;
     p.n_rh = z.n_rh;
-    p.n_rd = z.n_rd;
     p.n_src = z.n_src;
 
     hipStream_t s = (hipStream_t)stream;
@@ -315,6 +323,7 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
         if (opts->path == MQ_PATH_FUSED && !fused_ok(z, cus)) return MQ_ERR_UNSUPPORTED;
     }
     const bool fused = opts->path == MQ_PATH_FUSED || (opts->path == MQ_PATH_AUTO && T == 1 && fused_ok(z, cus));
+    p.n_rng = fused ? fused_ranges(z, cus) : 0;
     if (fused) {
         hipLaunchKernelGGL(k_decode, dim3(cus), dim3(512), 0, s, p);
         return hipGetLastError() == hipSuccess ? MQ_OK : MQ_ERR_HIP;

@@ -54,6 +54,24 @@ __device__ __forceinline__ void q4_block_dot(const uint4& c0, const uint4& c1, c
     }
 }
 
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// c + a.lo*b.lo + a.hi*b.hi with fp16 pairs, fp32 accumulation.
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
+}
+
+// Pair m of a DEV_V1 4-bit word as two fp16 values 1024 + q (the fp16
+// exponent of 1024.0 is 0x6400; its ten mantissa bits hold q exactly).
+__device__ __forceinline__ uint32_t q4_pair16(uint32_t w, int m) {
+    return ((w >> (4 * m)) & 0x000F000Fu) | 0x64006400u;
+}
+
+// fp32 -> fp16 bits, round to nearest even.
+__device__ __forceinline__ uint16_t f32_to_f16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+__device__ __forceinline__ float f16_lo(uint32_t v) { return (float)__builtin_bit_cast(f16x2_t, v)[0]; }
+__device__ __forceinline__ float f16_hi(uint32_t v) { return (float)__builtin_bit_cast(f16x2_t, v)[1]; }
+
 // Sum over the four lanes lane%16 + 16*kb (kb = 0..3) of a wave.
 __device__ __forceinline__ float sum_kb(float v) {
     v += __shfl_xor(v, 16, 64);

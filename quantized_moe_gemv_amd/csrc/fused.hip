@@ -6,8 +6,9 @@
 //   without expert ids: router pieces    16 experts x a column range  -> partial scores
 //                       shared gate/up   32 rows x a column range     -> partial g, u
 //                       shared down      64 output rows x a chunk of Is -> partial outputs
-//   with expert ids:    routed gate/up   (slot j, 32 rows, column range) -> partial g, u
-//                       routed down      (64 output rows, slot j)     -> partial outputs
+//   with expert ids:    routed gate/up   (slot j, 32 rows, all columns) -> h
+//                       routed down      (slot j, a range of output tiles) -> partial outputs
+//                       output sums      (64 output rows, every source) -> out
 // A workgroup puts out the loads of all its units of the first list at
 // once, and those of the second list as soon as it knows the expert ids, so
 // the memory system has the whole remaining stream in flight; the units are
@@ -41,8 +42,8 @@ constexpr int kSpinLimit = 1 << 20;
 constexpr int kCopies = 8;         // replicas of broadcast results, one per XCD
 constexpr int kItemsRH = 12;       // 16-byte code loads per lane of a full-row routed gate/up unit
 constexpr int kSlotsA = 2;         // units per workgroup that need no expert ids
-constexpr int kSlotsL = 3;         // down pieces of a workgroup without a full-row unit
-constexpr int kSlotsX = 2;         // down pieces of a workgroup with one
+constexpr int kTilesD = 5;         // output tiles of a routed down unit
+constexpr int kItemsD = 3 * kTilesD;   // 16-byte code loads per lane of a routed down unit
 constexpr int kRq = kRouterPieces;
 constexpr int kGq = kFusedPieces;
 
@@ -102,11 +103,11 @@ __device__ __forceinline__ void gather_words(const uint64_t* base, int n, uint32
 
 // ----------------------------------------------------------------- units
 
-enum { U_ROUTER = 0, U_SG = 1, U_SD = 2, U_RH = 3, U_RD = 4, U_NONE = 5 };
+enum { U_ROUTER = 0, U_SG = 1, U_SD = 2, U_RH = 3, U_NONE = 4 };
 
 struct Unit {
     int kind;
-    int a, b;         // router: slice; SG: half tile; SD: out tile, chunk; RH: slot, half tile; RD: out tile, slot
+    int a, b;         // router: slice; SG: half tile; SD: out tile, chunk; RH: slot, half tile
     int q;            // piece index of the column range (router, gate/up)
     int g0, ng;       // column-group range
 };
@@ -114,8 +115,7 @@ struct Unit {
 struct Shared {
     // arrays read with 16-byte LDS accesses come first and stay 16-byte aligned
     alignas(16) uint16_t x[4096];
-    alignas(16) uint16_t hhi[16 * 64];   // one source's activations, bf16 high and low parts
-    alignas(16) uint16_t hlo[16 * 64];
+    alignas(16) uint16_t h16[16 * 64];   // one source's GeGLU activations, fp16
     alignas(16) float lg[256];           // expert scores (padding: -inf)
     alignas(16) uint64_t key[256];       // selection keys (padding: 0)
     alignas(16) float xr[4096];          // router input numerator x * router_scale
@@ -128,6 +128,7 @@ struct Shared {
     float c8[512];            // per 8-column chunk: sum of x
     float c4[1024];           // per 4-column quarter: sum of x * router_scale
     float red[kWaves][64];
+    float red2[kWaves][kTilesD][32];   // per-wave row sums of a routed down unit
     float hsum[16 * 4];
     int32_t ids[kMaxTopK];
     float wts[kMaxTopK];
@@ -181,38 +182,46 @@ __device__ __forceinline__ Unit unit_rh(const Plan& p, int w) {
     return x;
 }
 
-// Down piece i: shared down pieces (output tile, chunk of Is), then routed
-// down pieces (output tile, slot), each tile's slots in order.
-__device__ __forceinline__ Unit unit_down(const Plan& p, int i) {
+// Shared down piece i: output tile i / n_sc, chunk i % n_sc of Is.
+__device__ __forceinline__ Unit unit_sd(const Plan& p, int i) {
     Unit x = no_unit();
-    if (i < p.n_sd) {
+    if (i >= 0 && i < p.n_sd) {
         x.kind = U_SD;
         x.a = i / p.n_sc;
         x.b = i % p.n_sc;
         x.g0 = x.b * p.G_I;
         x.ng = min(p.G_I, p.G_s - x.g0);
-    } else if (i < p.n_sd + p.n_rd) {
-        i -= p.n_sd;
-        x.kind = U_RD;
-        x.a = i / p.k;
-        x.b = i % p.k;
-        x.ng = p.G_I;
     }
     return x;
 }
 
-// Down piece of slot s of workgroup w.  The workgroups without a full-row
-// unit take the first pieces, kSlotsL each, round-robin; the rest go to the
-// workgroups with one, kSlotsX each.  Either way a workgroup's pieces come in
-// increasing order.
-__device__ __forceinline__ int down_piece(const Plan& p, int w, int nwg, int s) {
-    const int m = nwg - p.n_rh, nd = p.n_sd + p.n_rd, nfirst = min(nd, m * kSlotsL);
-    if (w >= p.n_rh) {
-        const int i = (w - p.n_rh) + m * s;
-        return i < nfirst ? i : nd;
+// Routed down unit v (0 <= v < k * n_rng): one selected expert (slot
+// v / n_rng) over the output tiles of range v % n_rng, so its activations are
+// staged once for all those tiles.
+struct DownUnit {
+    int b, t0, nt;
+};
+
+__device__ __forceinline__ DownUnit unit_rdu(const Plan& p, int v) {
+    DownUnit d;
+    d.b = d.t0 = d.nt = 0;
+    if (v >= 0 && v < p.k * p.n_rng) {
+        const int r = v % p.n_rng;
+        d.b = v / p.n_rng;
+        d.t0 = r * p.G_H / p.n_rng;
+        d.nt = (r + 1) * p.G_H / p.n_rng - d.t0;
     }
-    const int i = nfirst + w + p.n_rh * s;
-    return i < nd ? i : nd;
+    return d;
+}
+
+// Workgroups: 0 .. n_rh-1 run one full-row routed gate/up unit each (and
+// shared down piece w if there is one); the next k * n_rng run one routed
+// down unit each; any after them run the remaining shared down pieces.
+__device__ __forceinline__ int sd_piece_of(const Plan& p, int w) {
+    if (w < p.n_rh) return w < p.n_sd ? w : -1;
+    const int first = p.n_rh + p.k * p.n_rng;
+    const int i = p.n_rh + (w - first);
+    return (w >= first && i < p.n_sd) ? i : -1;
 }
 
 // A unit's weight loads, issued before the unit waits or computes.
@@ -271,11 +280,8 @@ __device__ __forceinline__ void issue_loads(const Plan& p, const Shared& sh, con
         n = 2 * x.ng;
         oc = (ht & 1) * 1024;
         os = kCodes4 + 8 * (ht & 1);
-    } else if (x.kind == U_SD || x.kind == U_RD) {
-        const uint8_t* m0 = x.kind == U_SD ? p.sh_down + ((int64_t)x.a * p.G_s + x.g0) * kBlk4
-                                           : p.pool_base + (int64_t)sh.ids[x.b] * p.expert_stride + p.down_off +
-                                                 (int64_t)x.a * p.G_I * kBlk4;
-        b0 = b1 = m0;
+    } else if (x.kind == U_SD) {
+        b0 = b1 = p.sh_down + ((int64_t)x.a * p.G_s + x.g0) * kBlk4;
         step = kBlk4;
         n = 2 * x.ng;
         oc = par * 1024;
@@ -455,22 +461,21 @@ __device__ __forceinline__ void fetch_ids(const Plan& p, Shared& sh, uint32_t ta
     __syncthreads();
 }
 
-// One source's activations (64 tagged words per group, from group g0) into
-// LDS as bf16 high/low parts, with each lane's column sums.
+// One source's activations (64 tagged words per group, from group g0, fp16
+// in the low half of the payload) into LDS, with each lane's column sums.
 __device__ __forceinline__ void stage_h(const Plan& p, Shared& sh, const uint64_t* h, int g0, int ng, uint32_t tag) {
     gather_words(h + 64 * g0, ng * 64, tag, p.f_err, sh.gbuf);
-    for (int q = threadIdx.x; q < ng * 64; q += kThreads) {
-        sh.hhi[q] = (uint16_t)(sh.gbuf[q] >> 16);
-        sh.hlo[q] = (uint16_t)(sh.gbuf[q] & 0xFFFFu);
-    }
+    for (int q = threadIdx.x; q < ng * 64; q += kThreads) sh.h16[q] = (uint16_t)sh.gbuf[q];
     __syncthreads();
     for (int q = threadIdx.x; q < ng * 4; q += kThreads) {
         const int gl = q >> 2, qb = q & 3;
-        const uint4 a0 = *(const uint4*)(sh.hhi + 64 * gl + 8 * qb);
-        const uint4 a1 = *(const uint4*)(sh.hhi + 64 * gl + 32 + 8 * qb);
-        const uint4 b0 = *(const uint4*)(sh.hlo + 64 * gl + 8 * qb);
-        const uint4 b1 = *(const uint4*)(sh.hlo + 64 * gl + 32 + 8 * qb);
-        sh.hsum[q] = (sum8_bf16(a0) + sum8_bf16(a1)) + (sum8_bf16(b0) + sum8_bf16(b1));
+        const uint4 a0 = *(const uint4*)(sh.h16 + 64 * gl + 8 * qb);
+        const uint4 a1 = *(const uint4*)(sh.h16 + 64 * gl + 32 + 8 * qb);
+        const uint32_t w[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        float v = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v += f16_lo(w[i]) + f16_hi(w[i]);
+        sh.hsum[q] = v;
     }
     __syncthreads();
 }
@@ -487,6 +492,16 @@ __device__ __forceinline__ void half_block_dot(const uint4& c, const uint4& xa, 
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) d[i >> 1] = dot2_bf16(q4_pair(w[i], q), xk[i & 1][q], d[i >> 1]);
+}
+
+// The same with fp16 activations: adds sum((1024 + q) * h) to d[r].
+__device__ __forceinline__ void half_block_dot16(const uint4& c, const uint4& ha, const uint4& hb, float d[2]) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    const uint32_t hk[2][4] = {{ha.x, ha.y, ha.z, ha.w}, {hb.x, hb.y, hb.z, hb.w}};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) d[i >> 1] = dot2_f16(q4_pair16(w[i], q), hk[i & 1][q], d[i >> 1]);
 }
 
 // Row totals over the lanes and waves: v[r] holds rows 16*r + lane%16; after
@@ -583,11 +598,10 @@ __device__ __forceinline__ void run_gateup(const Plan& p, Shared& sh, const Unit
             uv += __uint_as_float(sh.gbuf[q * 64 + 32 + r]);
         }
         const float h = gelu_tanh(gv) * uv;
-        const uint16_t h1 = f32_to_bf16(h);
-        const uint16_t h2 = f32_to_bf16(h - bf16_to_f32(h1));
+        const uint32_t h16 = f32_to_f16(h);
         uint64_t* hout = p.f_hs + 32 * ht;
 #pragma unroll
-        for (int c = 0; c < kCopies; ++c) st_word(hout + c * p.h_stride + r, tag, ((uint32_t)h1 << 16) | h2);
+        for (int c = 0; c < kCopies; ++c) st_word(hout + c * p.h_stride + r, tag, h16);
     }
     __syncthreads();
 }
@@ -618,78 +632,124 @@ __device__ __forceinline__ void run_rh(const Plan& p, Shared& sh, const Unit& x,
     if (wave_id() == 0 && threadIdx.x < 32) {
         const int r = threadIdx.x;
         const float h = gelu_tanh(row_total_par(sh, r)) * row_total_par(sh, 32 + r);
-        const uint16_t h1 = f32_to_bf16(h);
-        const uint16_t h2 = f32_to_bf16(h - bf16_to_f32(h1));
+        const uint32_t h16 = f32_to_f16(h);
         uint64_t* hout = p.f_h + (int64_t)x.a * p.I + 32 * x.b + r;
 #pragma unroll
-        for (int c = 0; c < kCopies; ++c) st_word(hout + c * p.h_stride, tag, ((uint32_t)h1 << 16) | h2);
+        for (int c = 0; c < kCopies; ++c) st_word(hout + c * p.h_stride, tag, h16);
     }
     __syncthreads();
 }
 
-// Down piece: one 64-row output tile from one source -> partial outputs.  The
-// last of the n_src pieces of a tile sums them in source order into out.
-__device__ __forceinline__ void run_down(const Plan& p, Shared& sh, const Unit& x, const Loads& L, uint32_t tag) {
+// Shared down piece: one 64-row output tile from one chunk of the shared
+// activations -> partial outputs (source k + chunk).
+__device__ __forceinline__ void run_sd_piece(const Plan& p, Shared& sh, const Unit& x, const Loads& L, uint32_t tag) {
+    stage_h(p, sh, p.f_hs + (blockIdx.x % kCopies) * p.h_stride, x.g0, x.ng, tag);
     const int wave = wave_id(), lane = threadIdx.x & 63, kb = lane >> 4;
-    const bool shared = x.kind == U_SD;
-    const float wf = shared ? 1.0f : sh.wts[x.b];
     float acc[2] = {0.f, 0.f};    // rows 32*(wave & 1) + 16*r + lane%16 of the output tile
 #pragma unroll
     for (int m = 0; m < kItems; ++m) {
         const int it = wave + kWaves * m;
         if (it < 2 * x.ng) {
             const int gl = it >> 1;
-            const uint4 ha = *(const uint4*)(sh.hhi + 64 * gl + 8 * kb);
-            const uint4 hb = *(const uint4*)(sh.hhi + 64 * gl + 32 + 8 * kb);
-            const uint4 la = *(const uint4*)(sh.hlo + 64 * gl + 8 * kb);
-            const uint4 lb = *(const uint4*)(sh.hlo + 64 * gl + 32 + 8 * kb);
+            const uint4 ha = *(const uint4*)(sh.h16 + 64 * gl + 8 * kb);
+            const uint4 hb = *(const uint4*)(sh.h16 + 64 * gl + 32 + 8 * kb);
             const float hs = sh.hsum[gl * 4 + kb];
             float d[2] = {0.f, 0.f};
-            half_block_dot(L.c[m], ha, hb, d);
-            half_block_dot(L.c[m], la, lb, d);
+            half_block_dot16(L.c[m], ha, hb, d);
             const uint32_t sw[2] = {L.s[m].x, L.s[m].y};
 #pragma unroll
-            for (int r = 0; r < 2; ++r) acc[r] += wf * fmaf(bf16_lo(sw[r]), fmaf(-128.f, hs, d[r]), bf16_hi(sw[r]) * hs);
+            for (int r = 0; r < 2; ++r) acc[r] += fmaf(bf16_lo(sw[r]), fmaf(-1024.f, hs, d[r]), bf16_hi(sw[r]) * hs);
         }
     }
     reduce_rows(sh, acc, 2);
-    const int src = shared ? p.k + x.b : x.b;
-    uint64_t* tilep = p.f_piece + (int64_t)x.a * p.n_src * 64;
-    if (wave_id() == 0) st_word(tilep + src * 64 + threadIdx.x, tag, __float_as_uint(row_total_par(sh, threadIdx.x)));
+    uint64_t* dst = p.f_piece + ((int64_t)x.a * p.n_src + p.k + x.b) * 64;
+    if (wave_id() == 0) st_word(dst + threadIdx.x, tag, __float_as_uint(row_total_par(sh, threadIdx.x)));
     __syncthreads();
-    if (shared || x.b != p.k - 1) return;
-    // the last source of this output tile: sum every source in order
-    gather_words(tilep, p.n_src * 64, tag, p.f_err, sh.gbuf);
-    for (int i = p.n_src * 64 + threadIdx.x; i < ((p.n_src + 3) & ~3) * 64; i += kThreads) sh.gbuf[i] = 0u;
+}
+
+// Loads of a routed down unit: for each of its tiles, wave w takes groups
+// w/2, w/2 + 4, w/2 + 8 of the expert's intermediate, half w % 2 of the tile.
+__device__ __forceinline__ void issue_rdu(const Plan& p, const Shared& sh, const DownUnit& d, LoadsN<kItemsD>& L) {
+    const int wave = wave_id(), lane = threadIdx.x & 63, par = wave & 1;
+    const uint8_t* base = p.pool_base + (int64_t)sh.ids[d.b] * p.expert_stride + p.down_off +
+                          ((int64_t)d.t0 * p.G_I + (wave >> 1)) * kBlk4;
+    const int lc = par * 1024 + lane * 16, ls = kCodes4 + 8 * par + (lane & 15) * 16;
+#pragma unroll
+    for (int t = 0; t < kTilesD; ++t)
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            if (t < d.nt && (wave >> 1) + 4 * j < p.G_I) {
+                const uint8_t* blk = base + ((int64_t)t * p.G_I + 4 * j) * kBlk4;
+                L.c[3 * t + j] = ld_stream16(blk + lc);
+                L.s[3 * t + j] = *(const uint2*)(blk + ls);
+            }
+}
+
+// Routed down unit: the weighted partial outputs of one selected expert for
+// each of its tiles (source = slot).
+__device__ __forceinline__ void run_rdu(const Plan& p, Shared& sh, const DownUnit& d, const LoadsN<kItemsD>& L,
+                                        uint32_t tag) {
+    stage_h(p, sh, p.f_h + (blockIdx.x % kCopies) * p.h_stride + (int64_t)d.b * p.I, 0, p.G_I, tag);
+    const int wave = wave_id(), lane = threadIdx.x & 63, kb = lane >> 4;
+    const float wf = sh.wts[d.b];
+    float acc[kTilesD][2];
+#pragma unroll
+    for (int t = 0; t < kTilesD; ++t) acc[t][0] = acc[t][1] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int g = (wave >> 1) + 4 * j;
+        if (g < p.G_I) {
+            const uint4 ha = *(const uint4*)(sh.h16 + 64 * g + 8 * kb);
+            const uint4 hb = *(const uint4*)(sh.h16 + 64 * g + 32 + 8 * kb);
+            const float hs = sh.hsum[g * 4 + kb];
+#pragma unroll
+            for (int t = 0; t < kTilesD; ++t)
+                if (t < d.nt) {
+                    const int m = 3 * t + j;
+                    float dd[2] = {0.f, 0.f};
+                    half_block_dot16(L.c[m], ha, hb, dd);
+                    const uint32_t sw[2] = {L.s[m].x, L.s[m].y};
+#pragma unroll
+                    for (int r = 0; r < 2; ++r)
+                        acc[t][r] += wf * fmaf(bf16_lo(sw[r]), fmaf(-1024.f, hs, dd[r]), bf16_hi(sw[r]) * hs);
+                }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < kTilesD; ++t)
+        if (t < d.nt)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const float v = sum_kb(acc[t][r]);
+                if (lane < 16) sh.red2[wave][t][16 * r + lane] = v;
+            }
     __syncthreads();
     if (wave_id() == 0) {
-        float v = 0.f;
-        for (int s2 = 0; s2 < p.n_src; s2 += 4) {
-            const float a0 = __uint_as_float(sh.gbuf[s2 * 64 + threadIdx.x]);
-            const float a1 = __uint_as_float(sh.gbuf[(s2 + 1) * 64 + threadIdx.x]);
-            const float a2 = __uint_as_float(sh.gbuf[(s2 + 2) * 64 + threadIdx.x]);
-            const float a3 = __uint_as_float(sh.gbuf[(s2 + 3) * 64 + threadIdx.x]);
-            v += ((a0 + a1) + a2) + a3;
+        const int row = threadIdx.x, par = row >> 5;
+        for (int t = 0; t < d.nt; ++t) {
+            float v = 0.f;
+            for (int w2 = par; w2 < kWaves; w2 += 2) v += sh.red2[w2][t][row & 31];
+            st_word(p.f_piece + ((int64_t)(d.t0 + t) * p.n_src + d.b) * 64 + row, tag, __float_as_uint(v));
         }
-        const int row = 64 * x.a + threadIdx.x;
+    }
+    __syncthreads();
+}
+
+// Output tile a: every source's partial outputs summed in source order
+// (routed slots, then shared chunks), rounded once.
+__device__ __forceinline__ void run_reduce(const Plan& p, Shared& sh, int a, uint32_t tag) {
+    const uint64_t* tilep = p.f_piece + (int64_t)a * p.n_src * 64;
+    gather_words(tilep, p.n_src * 64, tag, p.f_err, sh.gbuf);
+    if (wave_id() == 0) {
+        float v = 0.f;
+        for (int s2 = 0; s2 < p.n_src; ++s2) v += __uint_as_float(sh.gbuf[s2 * 64 + threadIdx.x]);
+        const int row = 64 * a + threadIdx.x;
         if (p.out_f32)
             ((float*)p.out)[row] = v;
         else
             ((uint16_t*)p.out)[row] = f32_to_bf16(v);
     }
     __syncthreads();
-}
-
-// A shared or routed down piece with its activations staged; nothing for
-// an empty slot.
-__device__ __forceinline__ void run_down_unit(const Plan& p, Shared& sh, const Unit& x, const Loads& L, uint32_t tag) {
-    if (x.kind == U_SD) {
-        stage_h(p, sh, p.f_hs + (blockIdx.x % kCopies) * p.h_stride, x.g0, x.ng, tag);
-        run_down(p, sh, x, L, tag);
-    } else if (x.kind == U_RD) {
-        stage_h(p, sh, p.f_h + (blockIdx.x % kCopies) * p.h_stride + (int64_t)x.b * p.I, 0, x.ng, tag);
-        run_down(p, sh, x, L, tag);
-    }
 }
 
 // ----------------------------------------------------------------- the kernel
@@ -699,13 +759,13 @@ __device__ __forceinline__ void run_down_unit(const Plan& p, Shared& sh, const U
 //      expert ids (router pieces, shared gate/up pieces);
 //   2. those units;
 //   3. the expert ids (waits for the router pieces), then the weight loads of
-//      all its remaining units at once: one full-row routed gate/up unit
-//      (workgroups 0 .. n_rh-1) and its down pieces;
-//   4. those units in order.
+//      its remaining units at once: a full-row routed gate/up unit and a
+//      shared down piece, or a routed down unit, or a shared down piece;
+//   4. those units, then (workgroup a < G_H) the sum of output tile a.
 // Every wait is for a unit earlier in the order router < shared gate/up <
-// ids < routed gate/up < shared down < routed down (a tile's slots in
-// order), and each workgroup runs its units in that order, so with all
-// workgroups resident every wait ends.
+// ids < routed gate/up < shared down < routed down < output sums, and each
+// workgroup runs its units in that order, so with all workgroups resident
+// every wait ends.
 
 // Touch every field of the argument block the kernel reads, in one batch.
 // Left alone, the compiler fetches the block field by field near each first
@@ -717,7 +777,7 @@ __device__ __forceinline__ void prefetch_args(const Plan& p) {
     asm volatile("" ::"s"(p.f_rpart), "s"(p.f_sgpart), "s"(p.f_hs), "s"(p.f_h), "s"(p.f_piece),
                  "s"(p.f_err), "s"(p.c_done), "s"(p.out), "s"(p.ids_out), "s"(p.w_out), "s"(p.logits_out));
     asm volatile("" ::"s"(p.E), "s"(p.k), "s"(p.H), "s"(p.I), "s"(p.G_H), "s"(p.G_I), "s"(p.G_s), "s"(p.n_src),
-                 "s"(p.n_sg), "s"(p.n_router), "s"(p.n_rh), "s"(p.n_sd), "s"(p.n_sc), "s"(p.n_rd), "s"(p.eps));
+                 "s"(p.n_sg), "s"(p.n_router), "s"(p.n_rh), "s"(p.n_sd), "s"(p.n_sc), "s"(p.n_rng), "s"(p.eps));
     asm volatile("" ::"s"(p.h_stride), "s"(p.rpart_stride), "s"(p.expert_stride), "s"(p.gate_off), "s"(p.up_off),
                  "s"(p.down_off), "s"(p.out_f32), "s"(gridDim.x));
 }
@@ -746,31 +806,26 @@ __global__ __launch_bounds__(kThreads) void k_decode(Plan p) {
     }
     const int w = blockIdx.x;
     const Unit rh = unit_rh(p, w);
-    if (rh.kind == U_RH || down_piece(p, w, nwg, 0) < p.n_sd + p.n_rd) fetch_ids(p, sh, tag);
+    const DownUnit du = unit_rdu(p, w - p.n_rh);
+    const Unit sd = unit_sd(p, sd_piece_of(p, w));
+    if (rh.kind == U_RH || du.nt > 0) fetch_ids(p, sh, tag);
     if (rh.kind == U_RH) {
         LoadsN<kItemsRH> lr;
-        Unit ux[kSlotsX];
-        Loads lx[kSlotsX];
+        Loads ls;
         issue_loads(p, sh, rh, lr);
-#pragma unroll
-        for (int i = 0; i < kSlotsX; ++i) {
-            ux[i] = unit_down(p, down_piece(p, w, nwg, i));
-            issue_loads(p, sh, ux[i], lx[i]);
-        }
+        issue_loads(p, sh, sd, ls);
         run_rh(p, sh, rh, lr, tag);
-#pragma unroll
-        for (int i = 0; i < kSlotsX; ++i) run_down_unit(p, sh, ux[i], lx[i], tag);
-    } else {
-        Unit ul[kSlotsL];
-        Loads ll[kSlotsL];
-#pragma unroll
-        for (int i = 0; i < kSlotsL; ++i) {
-            ul[i] = unit_down(p, down_piece(p, w, nwg, i));
-            issue_loads(p, sh, ul[i], ll[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < kSlotsL; ++i) run_down_unit(p, sh, ul[i], ll[i], tag);
+        if (sd.kind == U_SD) run_sd_piece(p, sh, sd, ls, tag);
+    } else if (du.nt > 0) {
+        LoadsN<kItemsD> ld;
+        issue_rdu(p, sh, du, ld);
+        run_rdu(p, sh, du, ld, tag);
+    } else if (sd.kind == U_SD) {
+        Loads ls;
+        issue_loads(p, sh, sd, ls);
+        run_sd_piece(p, sh, sd, ls, tag);
     }
+    if (w < p.G_H) run_reduce(p, sh, w, tag);
     // The last workgroup to finish clears every counter and advances the epoch.
     __syncthreads();
     if (threadIdx.x == 0) sh.flag = atomicAdd(p.c_done, 1u) + 1 == (uint32_t)nwg;

@@ -317,4 +317,6 @@ def test_fused_many_calls_interleaved(M, decode, tiny):
             M.moe_layer_forward(dev, x8, workspace=ws, path="grouped")
     torch.cuda.synchronize()
     rms = float(torch.sqrt(torch.mean(rg.double() ** 2)))
-    assert float(torch.max(torch.abs(ra.double() - rg.double()))) <= 1e-4 * rms
+    # the single-launch path hands the GeGLU activations to the down projection
+    # as fp16 (relative rounding <= 2^-11); the GEMV path keeps 16 significant bits
+    assert float(torch.max(torch.abs(ra.double() - rg.double()))) <= 4 * 2.0 ** -11 * rms
