@@ -32,14 +32,14 @@ inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 struct Sizes {
     int H, E, E_pad, k, I, Is, G_H, G_I, G_s, rsplit, rgroups, ntile, max_tiles;
-    int n_router, n_sg, n_sd, n_sc, n_rh, n_src;
+    int n_router, n_sd, n_sc, n_rh, n_src;
 };
 
 // State of the single-launch decode that persists across calls.  It sits at
 // the start of the workspace, at offsets that do not depend on the token
 // count, and no other kernel writes it.
 struct FusedCarve {
-    size_t rpart, sgpart, act, piece, ctr, total;
+    size_t rpart, act, piece, ctr, total;
     int64_t h_stride, rpart_stride;   // in 8-byte words
 };
 
@@ -49,7 +49,6 @@ FusedCarve fused_carve(const Sizes& z) {
     auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
     f.rpart_stride = (int64_t)up((size_t)(z.E + 15) / 16 * 8 * 16 * 8) / 8;
     f.rpart = take((size_t)8 * f.rpart_stride * 8);
-    f.sgpart = take((size_t)2 * z.G_s * kFusedPieces * 64 * 8 + 8);
     // one copy per XCD of the activations (shared then routed)
     f.h_stride = (int64_t)up(((size_t)z.Is + (size_t)z.k * z.I) * 8 + 8) / 8;
     f.act = take((size_t)8 * f.h_stride * 8);
@@ -60,24 +59,26 @@ FusedCarve fused_carve(const Sizes& z) {
 }
 
 // The single-launch decode holds every unit's loads in registers, one
-// workgroup per compute unit: at most kFusedSlotsA units without expert ids
-// per workgroup; a full-row routed gate/up unit (2 G_H <= 8 waves x 12 loads)
-// and at most one shared down piece on each of the first n_rh workgroups;
-// one routed down unit (one slot, at most kFusedTilesD output tiles) on each
-// of the next k * n_rng; the remaining shared down pieces after those; the
-// sum of output tile a on workgroup a.
-constexpr int kFusedSlotsA = 2, kFusedTilesD = 5;
+// workgroup per compute unit.  Workgroups 0 .. n_rh-1 each run a full-row
+// routed gate/up unit (2 G_H <= 8 waves x 12 loads); the m = cus - n_rh
+// others run one full-row shared gate/up unit each (the first 2 G_s of them)
+// and at most kFusedSlotsSD shared down pieces each; routed down work runs
+// one tile per routed workgroup for the first S = n_rh / G_H slots and in
+// n_rng ranges of at most kFusedTilesD tiles on the shared workgroups for
+// the others; router piece i on workgroup i; output tile a's sum on
+// workgroup a.
+constexpr int kFusedSlotsSD = 2, kFusedTilesD = 3;
 
 int fused_ranges(const Sizes& z, int cus) {
-    const int m = cus - z.n_rh;
-    return m < z.k ? 0 : std::min(m / z.k, z.G_H);
+    const int S = std::min(z.n_rh / z.G_H, z.k), m = cus - z.n_rh;
+    return S >= z.k ? 1 : std::min(m / (z.k - S), z.G_H);
 }
 
 bool fused_ok(const Sizes& z, int cus) {
-    const int r = fused_ranges(z, cus);
-    if (z.G_H > 48 || z.G_I > 12 || z.n_src > 32 || z.n_router + z.n_sg > kFusedSlotsA * cus || r < 1) return false;
-    const int spare = cus - z.n_rh - z.k * r;
-    return (z.G_H + r - 1) / r <= kFusedTilesD && z.n_sd <= z.n_rh + spare && z.G_H <= cus;
+    const int m = cus - z.n_rh, r = fused_ranges(z, cus);
+    if (z.G_H > 48 || z.G_I > 12 || z.n_src > 32 || m < 1 || r < 1) return false;
+    return (z.G_H + r - 1) / r <= kFusedTilesD && 2 * z.G_s <= m && (std::max(z.n_sd - z.n_rh, 0) + m - 1) / m <= kFusedSlotsSD &&
+           z.n_router <= cus && z.G_H <= cus;
 }
 
 int device_cus() {
@@ -180,10 +181,8 @@ mq_status check_layer(const mq_router* rt, const mq_expert_pool* pool, const mq_
     z->rgroups = 4;
     z->rsplit = (z->G_H + z->rgroups - 1) / z->rgroups;
     z->ntile = 16;
-    // single-launch decode: router slices of 16 experts in kRouterPieces column
-    // pieces, gate/up half tiles in kFusedPieces (short rows give empty pieces)
+    // single-launch decode: router slices of 16 experts in kRouterPieces column pieces
     z->n_router = (E + 15) / 16 * kRouterPieces;
-    z->n_sg = 2 * z->G_s * kFusedPieces;
     z->n_sc = (z->G_s + z->G_I - 1) / z->G_I;
     z->n_sd = z->G_H * z->n_sc;
     z->n_rh = 2 * z->k * z->G_I;
@@ -297,7 +296,6 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
 
     const FusedCarve f = fused_carve(z);
     p.f_rpart = (uint64_t*)(ws + f.rpart);
-    p.f_sgpart = (uint64_t*)(ws + f.sgpart);
     p.f_hs = (uint64_t*)(ws + f.act);
     p.f_h = p.f_hs + z.Is;
     p.h_stride = f.h_stride;
@@ -308,7 +306,6 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
     p.f_epoch = ctr + kCtrStride;
     p.f_err = ctr + 2 * kCtrStride;
     p.n_router = z.n_router;
-    p.n_sg = z.n_sg;
     p.n_sd = z.n_sd;
     p.n_sc = z.n_sc;
     p.n_rh = z.n_rh;

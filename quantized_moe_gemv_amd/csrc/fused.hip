@@ -1,22 +1,23 @@
 // Single-launch decode of one token through the whole layer.
 //
-// The layer is cut into ~25 KB units of weight streaming, in two lists
-// dealt round-robin to one workgroup per compute unit (unit i of a list runs
-// on workgroup i % grid):
+// The layer is cut into units of weight streaming, given to one workgroup
+// per compute unit:
 //   without expert ids: router pieces    16 experts x a column range  -> partial scores
-//                       shared gate/up   32 rows x a column range     -> partial g, u
+//                       shared gate/up   32 rows x all columns         -> h (shared)
 //                       shared down      64 output rows x a chunk of Is -> partial outputs
 //   with expert ids:    routed gate/up   (slot j, 32 rows, all columns) -> h
 //                       routed down      (slot j, a range of output tiles) -> partial outputs
 //                       output sums      (64 output rows, every source) -> out
-// A workgroup puts out the loads of all its units of the first list at
-// once, and those of the second list as soon as it knows the expert ids, so
-// the memory system has the whole remaining stream in flight; the units are
-// computed as their data lands.  Each wait is bounded.  Partial results are
+// Full-row gate/up units hold complete sums, so only the router scores, the
+// activations and the partial outputs cross between workgroups.  A
+// workgroup puts out the loads of all its units that need no expert ids at
+// once, and those of the rest as soon as it knows the ids, so the memory
+// system has its whole remaining stream in flight; the units are computed as
+// their data lands.  Each wait is bounded.  Partial results are
 // 64-bit words carrying the call's epoch in their high half: a reader
 // issues all of its loads, then re-reads only the words whose tag is not yet
-// current.  Each sum has a fixed reducer (the highest-indexed contributor),
-// which sums in a fixed order, so results repeat bit for bit.
+// current.  Each sum has a fixed reducer which sums in a fixed order, so
+// results repeat bit for bit.
 //
 // Results that many workgroups read (partial router scores, GeGLU
 // activations) are written once per XCD (eight copies) and each reader takes
@@ -26,7 +27,7 @@
 // one workgroup to publish them.
 //
 // The shared expert and the router do not depend on each other, so the
-// shared branch streams while the routing decision is made ("Decode",
+// shared gate/up streams while the routing decision is made ("Decode",
 // phase table: the shared expert overlaps the wait for the expert ids).
 #include <math.h>
 
@@ -41,11 +42,10 @@ constexpr int kItems = 3;           // 16-byte code loads per lane per unit
 constexpr int kSpinLimit = 1 << 20;
 constexpr int kCopies = 8;         // replicas of broadcast results, one per XCD
 constexpr int kItemsRH = 12;       // 16-byte code loads per lane of a full-row routed gate/up unit
-constexpr int kSlotsA = 2;         // units per workgroup that need no expert ids
-constexpr int kTilesD = 5;         // output tiles of a routed down unit
+constexpr int kSlotsSD = 2;        // shared down pieces of a shared workgroup
+constexpr int kTilesD = 3;         // output tiles of a routed down unit
 constexpr int kItemsD = 3 * kTilesD;   // 16-byte code loads per lane of a routed down unit
 constexpr int kRq = kRouterPieces;
-constexpr int kGq = kFusedPieces;
 
 // ----------------------------------------------------------------- words and counters
 
@@ -103,11 +103,11 @@ __device__ __forceinline__ void gather_words(const uint64_t* base, int n, uint32
 
 // ----------------------------------------------------------------- units
 
-enum { U_ROUTER = 0, U_SG = 1, U_SD = 2, U_RH = 3, U_NONE = 4 };
+enum { U_ROUTER = 0, U_SH = 1, U_SD = 2, U_RH = 3, U_NONE = 4 };
 
 struct Unit {
     int kind;
-    int a, b;         // router: slice; SG: half tile; SD: out tile, chunk; RH: slot, half tile
+    int a, b;         // router: slice; SH: half tile; SD: out tile, chunk; RH: slot, half tile
     int q;            // piece index of the column range (router, gate/up)
     int g0, ng;       // column-group range
 };
@@ -150,21 +150,26 @@ __device__ __forceinline__ Unit no_unit() {
     return x;
 }
 
-// Unit i of the list that needs no expert ids: router pieces, then shared
-// gate/up pieces.
-__device__ __forceinline__ Unit unit_a(const Plan& p, int i) {
+// Router piece i: 16 experts (slice i / 8) x column range i % 8.
+__device__ __forceinline__ Unit unit_router(const Plan& p, int i) {
     Unit x = no_unit();
     if (i < p.n_router) {
         x.kind = U_ROUTER;
         x.a = i / kRq;
         x.q = i % kRq;
         krange(p.G_H, kRq, x.q, &x.g0, &x.ng);
-    } else if (i < p.n_router + p.n_sg) {
-        i -= p.n_router;
-        x.kind = U_SG;
-        x.a = i / kGq;
-        x.q = i % kGq;
-        krange(p.G_H, kGq, x.q, &x.g0, &x.ng);
+    }
+    return x;
+}
+
+// Full-row shared gate/up unit i: half tile i of the shared expert, every
+// column group.
+__device__ __forceinline__ Unit unit_sh(const Plan& p, int i) {
+    Unit x = no_unit();
+    if (i >= 0 && i < 2 * p.G_s) {
+        x.kind = U_SH;
+        x.a = i;
+        x.ng = p.G_H;
     }
     return x;
 }
@@ -195,33 +200,48 @@ __device__ __forceinline__ Unit unit_sd(const Plan& p, int i) {
     return x;
 }
 
-// Routed down unit v (0 <= v < k * n_rng): one selected expert (slot
-// v / n_rng) over the output tiles of range v % n_rng, so its activations are
-// staged once for all those tiles.
+// A routed down unit: one selected expert (slot b) over output tiles
+// t0 .. t0+nt-1, so its activations are staged once for all those tiles.
 struct DownUnit {
     int b, t0, nt;
 };
 
-__device__ __forceinline__ DownUnit unit_rdu(const Plan& p, int v) {
+// Workgroup roles.  Workgroups 0 .. n_rh-1 ("routed") run one full-row
+// routed gate/up unit and shared down piece w each; the m = grid - n_rh
+// others ("shared") run the full-row shared gate/up units (one each, the
+// first 2 G_s of them) and any further shared down pieces.  Routed down
+// work: the first S = min(n_rh / G_H, k) slots one tile per routed
+// workgroup, the other slots in n_rng tile ranges each on the shared
+// workgroups.  Router piece i runs on workgroup i and the sum of output tile
+// a on workgroup a, after all its other work.
+__device__ __forceinline__ DownUnit unit_rdu(const Plan& p, int w, int nwg) {
     DownUnit d;
     d.b = d.t0 = d.nt = 0;
-    if (v >= 0 && v < p.k * p.n_rng) {
+    const int S = min(p.n_rh / p.G_H, p.k);
+    if (w < p.n_rh) {
+        if (w < S * p.G_H) {
+            d.b = w / p.G_H;
+            d.t0 = w % p.G_H;
+            d.nt = 1;
+        }
+        return d;
+    }
+    const int v = w - p.n_rh;
+    if (S < p.k && v < (p.k - S) * p.n_rng) {
         const int r = v % p.n_rng;
-        d.b = v / p.n_rng;
+        d.b = S + v / p.n_rng;
         d.t0 = r * p.G_H / p.n_rng;
         d.nt = (r + 1) * p.G_H / p.n_rng - d.t0;
     }
     return d;
 }
 
-// Workgroups: 0 .. n_rh-1 run one full-row routed gate/up unit each (and
-// shared down piece w if there is one); the next k * n_rng run one routed
-// down unit each; any after them run the remaining shared down pieces.
-__device__ __forceinline__ int sd_piece_of(const Plan& p, int w) {
-    if (w < p.n_rh) return w < p.n_sd ? w : -1;
-    const int first = p.n_rh + p.k * p.n_rng;
-    const int i = p.n_rh + (w - first);
-    return (w >= first && i < p.n_sd) ? i : -1;
+// Shared down piece s of workgroup w: piece w on the routed workgroups, the
+// rest (j = n_rh + v + m s for shared workgroup v) on the shared ones.
+__device__ __forceinline__ Unit sd_piece(const Plan& p, int w, int nwg, int s) {
+    if (w < p.n_rh) return s == 0 ? unit_sd(p, w) : no_unit();
+    const int m = nwg - p.n_rh, j = p.n_rh + (w - p.n_rh) + m * s;
+    return unit_sd(p, j);
 }
 
 // A unit's weight loads, issued before the unit waits or computes.
@@ -261,11 +281,11 @@ __device__ __forceinline__ void issue_loads(const Plan& p, const Shared& sh, con
         n = x.ng;
         oc = j * 1024;
         os = kCodes8 + 8 * (j >> 1);   // pair j is .x (j even) or .y
-    } else if (x.kind == U_SG || x.kind == U_RH) {
-        const int ht = x.kind == U_SG ? x.a : x.b;
+    } else if (x.kind == U_SH || x.kind == U_RH) {
+        const int ht = x.kind == U_SH ? x.a : x.b;
         const uint8_t* g;
         const uint8_t* u;
-        if (x.kind == U_SG) {
+        if (x.kind == U_SH) {
             g = p.sh_gate;
             u = p.sh_up;
         } else {
@@ -561,54 +581,10 @@ __device__ __forceinline__ void run_router(const Plan& p, Shared& sh, const Unit
     __syncthreads();
 }
 
-// Shared gate/up piece: 32 rows x a column range -> partial (g, u).  The
-// last of the pieces of a half tile reduces them and publishes h = gelu(g) * u.
-__device__ __forceinline__ void run_gateup(const Plan& p, Shared& sh, const Unit& x, const Loads& L, uint32_t tag) {
-    const int wave = wave_id(), lane = threadIdx.x & 63, kb = lane >> 4;
-    float acc[2] = {0.f, 0.f};    // rows 16*r + lane%16 of the wave's matrix (gate: even waves, up: odd)
-#pragma unroll
-    for (int m = 0; m < kItems; ++m) {
-        const int it = wave + kWaves * m;
-        if (it < 2 * x.ng) {
-            const int g = x.g0 + (it >> 1);
-            const uint4 xa = *(const uint4*)(sh.x + 64 * g + 8 * kb);
-            const uint4 xb = *(const uint4*)(sh.x + 64 * g + 32 + 8 * kb);
-            const float xs = sh.xsum[g * 4 + kb];
-            float d[2] = {0.f, 0.f};
-            half_block_dot(L.c[m], xa, xb, d);
-            const uint32_t sw[2] = {L.s[m].x, L.s[m].y};
-#pragma unroll
-            for (int r = 0; r < 2; ++r) acc[r] += fmaf(bf16_lo(sw[r]), fmaf(-128.f, xs, d[r]), bf16_hi(sw[r]) * xs);
-        }
-    }
-    reduce_rows(sh, acc, 2);
-    const int ht = x.a;
-    uint64_t* base = p.f_sgpart + (int64_t)ht * kGq * 64;
-    if (wave_id() == 0) st_word(base + x.q * 64 + threadIdx.x, tag, __float_as_uint(row_total_par(sh, threadIdx.x)));
-    __syncthreads();
-    if (x.q != kGq - 1) return;
-    // the last piece of the half tile: sum all pieces in order, then GeGLU
-    gather_words(base, kGq * 64, tag, p.f_err, sh.gbuf);
-    if (wave_id() == 0 && threadIdx.x < 32) {
-        const int r = threadIdx.x;
-        float gv = 0.f, uv = 0.f;
-#pragma unroll
-        for (int q = 0; q < kGq; ++q) {
-            gv += __uint_as_float(sh.gbuf[q * 64 + r]);
-            uv += __uint_as_float(sh.gbuf[q * 64 + 32 + r]);
-        }
-        const float h = gelu_tanh(gv) * uv;
-        const uint32_t h16 = f32_to_f16(h);
-        uint64_t* hout = p.f_hs + 32 * ht;
-#pragma unroll
-        for (int c = 0; c < kCopies; ++c) st_word(hout + c * p.h_stride + r, tag, h16);
-    }
-    __syncthreads();
-}
-
-// Full-row routed gate/up unit: 32 rows of gate and up of one selected
-// expert over every column group, so the workgroup holds complete sums and
-// publishes h = gelu(g) * u for its 32 rows without any partial exchange.
+// Full-row gate/up unit (routed: one selected expert; shared: the shared
+// expert): 32 rows of gate and up over every column group, so the workgroup
+// holds complete sums and publishes h = gelu(g) * u for its 32 rows without
+// any partial exchange.
 __device__ __forceinline__ void run_rh(const Plan& p, Shared& sh, const Unit& x, const LoadsN<kItemsRH>& L,
                                        uint32_t tag) {
     const int wave = wave_id(), lane = threadIdx.x & 63, kb = lane >> 4;
@@ -633,7 +609,7 @@ __device__ __forceinline__ void run_rh(const Plan& p, Shared& sh, const Unit& x,
         const int r = threadIdx.x;
         const float h = gelu_tanh(row_total_par(sh, r)) * row_total_par(sh, 32 + r);
         const uint32_t h16 = f32_to_f16(h);
-        uint64_t* hout = p.f_h + (int64_t)x.a * p.I + 32 * x.b + r;
+        uint64_t* hout = x.kind == U_SH ? p.f_hs + 32 * x.a + r : p.f_h + (int64_t)x.a * p.I + 32 * x.b + r;
 #pragma unroll
         for (int c = 0; c < kCopies; ++c) st_word(hout + c * p.h_stride, tag, h16);
     }
@@ -755,12 +731,13 @@ __device__ __forceinline__ void run_reduce(const Plan& p, Shared& sh, int a, uin
 // ----------------------------------------------------------------- the kernel
 
 // Phases of a workgroup (every branch below is taken by all of its waves):
-//   1. the token's loads, then the weight loads of its units that need no
-//      expert ids (router pieces, shared gate/up pieces);
+//   1. the token's loads, then the weight loads of its router piece and
+//      shared gate/up pieces;
 //   2. those units;
 //   3. the expert ids (waits for the router pieces), then the weight loads of
-//      its remaining units at once: a full-row routed gate/up unit and a
-//      shared down piece, or a routed down unit, or a shared down piece;
+//      its remaining units at once: a full-row routed gate/up unit (routed
+//      workgroups) or shared down pieces (shared workgroups), and a routed
+//      down unit;
 //   4. those units, then (workgroup a < G_H) the sum of output tile a.
 // Every wait is for a unit earlier in the order router < shared gate/up <
 // ids < routed gate/up < shared down < routed down < output sums, and each
@@ -774,10 +751,10 @@ __device__ __forceinline__ void run_reduce(const Plan& p, Shared& sh, int a, uin
 __device__ __forceinline__ void prefetch_args(const Plan& p) {
     asm volatile("" ::"s"(p.x), "s"(p.router_w), "s"(p.router_scale), "s"(p.pes), "s"(p.logit_bias),
                  "s"(p.f_epoch), "s"(p.pool_base), "s"(p.sh_gate), "s"(p.sh_up), "s"(p.sh_down));
-    asm volatile("" ::"s"(p.f_rpart), "s"(p.f_sgpart), "s"(p.f_hs), "s"(p.f_h), "s"(p.f_piece),
+    asm volatile("" ::"s"(p.f_rpart), "s"(p.f_hs), "s"(p.f_h), "s"(p.f_piece),
                  "s"(p.f_err), "s"(p.c_done), "s"(p.out), "s"(p.ids_out), "s"(p.w_out), "s"(p.logits_out));
     asm volatile("" ::"s"(p.E), "s"(p.k), "s"(p.H), "s"(p.I), "s"(p.G_H), "s"(p.G_I), "s"(p.G_s), "s"(p.n_src),
-                 "s"(p.n_sg), "s"(p.n_router), "s"(p.n_rh), "s"(p.n_sd), "s"(p.n_sc), "s"(p.n_rng), "s"(p.eps));
+                 "s"(p.n_router), "s"(p.n_rh), "s"(p.n_sd), "s"(p.n_sc), "s"(p.n_rng), "s"(p.eps));
     asm volatile("" ::"s"(p.h_stride), "s"(p.rpart_stride), "s"(p.expert_stride), "s"(p.gate_off), "s"(p.up_off),
                  "s"(p.down_off), "s"(p.out_f32), "s"(gridDim.x));
 }
@@ -786,45 +763,45 @@ __global__ __launch_bounds__(kThreads) void k_decode(Plan p) {
     __shared__ Shared sh;
     prefetch_args(p);
     const uint32_t tag = ld_ctr(p.f_epoch) + 1;
-    const int nwg = gridDim.x;
+    const int nwg = gridDim.x, w = blockIdx.x;
     TokenLoads tl;
     load_token(p, tl);
-    Unit ua[kSlotsA];
-    Loads la[kSlotsA];
-#pragma unroll
-    for (int i = 0; i < kSlotsA; ++i) {
-        ua[i] = unit_a(p, blockIdx.x + i * nwg);
-        issue_loads(p, sh, ua[i], la[i]);
-    }
+    const Unit ur = unit_router(p, w);
+    const Unit us = unit_sh(p, w - p.n_rh);
+    Loads lrt;
+    LoadsN<kItemsRH> lsh;
+    issue_loads(p, sh, ur, lrt);
+    issue_loads(p, sh, us, lsh);
     stage_token(p, sh, tl);
-#pragma unroll
-    for (int i = 0; i < kSlotsA; ++i) {
-        if (ua[i].kind == U_ROUTER)
-            run_router(p, sh, ua[i], la[i], tag);
-        else if (ua[i].kind == U_SG)
-            run_gateup(p, sh, ua[i], la[i], tag);
-    }
-    const int w = blockIdx.x;
+    if (ur.kind == U_ROUTER) run_router(p, sh, ur, lrt, tag);
+    if (us.kind == U_SH) run_rh(p, sh, us, lsh, tag);
     const Unit rh = unit_rh(p, w);
-    const DownUnit du = unit_rdu(p, w - p.n_rh);
-    const Unit sd = unit_sd(p, sd_piece_of(p, w));
+    const DownUnit du = unit_rdu(p, w, nwg);
     if (rh.kind == U_RH || du.nt > 0) fetch_ids(p, sh, tag);
+    LoadsN<kItemsD> ld;
     if (rh.kind == U_RH) {
         LoadsN<kItemsRH> lr;
-        Loads ls;
+        Loads lsd;
+        const Unit usd = sd_piece(p, w, nwg, 0);
         issue_loads(p, sh, rh, lr);
-        issue_loads(p, sh, sd, ls);
+        issue_loads(p, sh, usd, lsd);
+        if (du.nt > 0) issue_rdu(p, sh, du, ld);
         run_rh(p, sh, rh, lr, tag);
-        if (sd.kind == U_SD) run_sd_piece(p, sh, sd, ls, tag);
-    } else if (du.nt > 0) {
-        LoadsN<kItemsD> ld;
-        issue_rdu(p, sh, du, ld);
-        run_rdu(p, sh, du, ld, tag);
-    } else if (sd.kind == U_SD) {
-        Loads ls;
-        issue_loads(p, sh, sd, ls);
-        run_sd_piece(p, sh, sd, ls, tag);
+        if (usd.kind == U_SD) run_sd_piece(p, sh, usd, lsd, tag);
+    } else {
+        Unit usd[kSlotsSD];
+        Loads lsd[kSlotsSD];
+#pragma unroll
+        for (int s = 0; s < kSlotsSD; ++s) {
+            usd[s] = sd_piece(p, w, nwg, s);
+            issue_loads(p, sh, usd[s], lsd[s]);
+        }
+        if (du.nt > 0) issue_rdu(p, sh, du, ld);
+#pragma unroll
+        for (int s = 0; s < kSlotsSD; ++s)
+            if (usd[s].kind == U_SD) run_sd_piece(p, sh, usd[s], lsd[s], tag);
     }
+    if (du.nt > 0) run_rdu(p, sh, du, ld, tag);
     if (w < p.G_H) run_reduce(p, sh, w, tag);
     // The last workgroup to finish clears every counter and advances the epoch.
     __syncthreads();

@@ -10,7 +10,6 @@ constexpr int kMaxTopK = 16;
 constexpr int kMaxExperts = 256;
 constexpr int kDownSplits = 4;      // split of the down-projection source list (GEMV path)
 constexpr int kRouterPieces = 8;   // single-launch decode: column pieces of a 16-expert router slice
-constexpr int kFusedPieces = 4;    // and of a gate/up half tile
 constexpr int kCtrStride = 64;      // counters of the single-launch decode sit 256 bytes apart
 
 struct Plan {
@@ -73,7 +72,6 @@ struct Plan {
     float* ysh;        // [T][H]     shared expert outputs
     // single-launch decode: tagged words and counters that persist across calls
     uint64_t* f_rpart;   // [copies][E/16][8][16] partial router scores, rpart_stride apart
-    uint64_t* f_sgpart;  // [2 G_s][4][64]      partial shared gate (32) and up (32) rows
     uint64_t* f_hs;      // [copies][Is]        shared GeGLU activations (fp16 payload), h_stride apart
     uint64_t* f_h;       // [copies][k][I]      routed GeGLU activations, h_stride apart
     int64_t h_stride, rpart_stride;
@@ -81,7 +79,7 @@ struct Plan {
     uint32_t* c_done;    // workgroups finished (cleared at the end of every call)
     uint32_t* f_epoch;   // calls completed with this workspace
     uint32_t* f_err;     // non-zero once a bounded wait has given up
-    int n_router, n_sg, n_sd, n_sc, n_rh, n_rng, n_src;   // n_rng: tile ranges per routed down slot
+    int n_router, n_sd, n_sc, n_rh, n_rng, n_src;   // n_rng: tile ranges per routed down slot
     int max_tiles;     // upper bound of scheduled (expert, token tile) pairs
     int ntile;         // tokens per grouped tile
 };
