@@ -60,7 +60,7 @@ FusedCarve fused_carve(const Sizes& z) {
 
 // The single-launch decode holds every unit's loads in registers, one
 // workgroup per compute unit.  Workgroups 0 .. n_rh-1 each run a full-row
-// routed gate/up unit (2 G_H <= 8 waves x 12 loads); the m = cus - n_rh
+// routed gate/up unit (2 G_H <= 16 waves x 6 loads); the m = cus - n_rh
 // others run one full-row shared gate/up unit each (the first 2 G_s of them)
 // and at most kFusedSlotsSD shared down pieces each; routed down work runs
 // one tile per routed workgroup for the first S = n_rh / G_H slots and in
@@ -322,7 +322,7 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
     const bool fused = opts->path == MQ_PATH_FUSED || (opts->path == MQ_PATH_AUTO && T == 1 && fused_ok(z, cus));
     p.n_rng = fused ? fused_ranges(z, cus) : 0;
     if (fused) {
-        hipLaunchKernelGGL(k_decode, dim3(cus), dim3(512), 0, s, p);
+        hipLaunchKernelGGL(k_decode, dim3(cus), dim3(1024), 0, s, p);
         return hipGetLastError() == hipSuccess ? MQ_OK : MQ_ERR_HIP;
     }
     const bool grouped = opts->path == MQ_PATH_GROUPED || (opts->path == MQ_PATH_AUTO && T > 4);

@@ -36,15 +36,18 @@
 
 namespace mq {
 
-constexpr int kThreads = 512;
+// 1024 threads: four waves per SIMD, so the dependent chains of one wave
+// (dequantisation, dot steps, reductions) are hidden behind the others.
+constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kItems = 3;           // 16-byte code loads per lane per unit
+constexpr int kItems = 2;           // 16-byte code loads per lane per unit (<= 32 items)
 constexpr int kSpinLimit = 1 << 20;
 constexpr int kCopies = 8;         // replicas of broadcast results, one per XCD
-constexpr int kItemsRH = 12;       // 16-byte code loads per lane of a full-row routed gate/up unit
+constexpr int kItemsRH = 6;        // 16-byte code loads per lane of a full-row gate/up unit (2 G_H <= 96)
 constexpr int kSlotsSD = 2;        // shared down pieces of a shared workgroup
 constexpr int kTilesD = 3;         // output tiles of a routed down unit
-constexpr int kItemsD = 3 * kTilesD;   // 16-byte code loads per lane of a routed down unit
+constexpr int kGroupsD = 2;        // column groups per wave pair and tile of a routed down unit (G_I <= 16)
+constexpr int kItemsD = kGroupsD * kTilesD;   // 16-byte code loads per lane of a routed down unit
 constexpr int kRq = kRouterPieces;
 
 // ----------------------------------------------------------------- words and counters
@@ -441,7 +444,7 @@ __device__ __forceinline__ void fetch_ids(const Plan& p, Shared& sh, uint32_t ta
     // Rank of expert e = the number of keys above its key.  Each expert's
     // comparisons are split over nparts adjacent lanes, summed by shuffles.
     {
-        const int lg2 = epad <= 128 ? 2 : 1, nparts = 1 << lg2;
+        const int lg2 = epad <= 128 ? 3 : 2, nparts = 1 << lg2;   // nparts * epad <= kThreads
         const int e = threadIdx.x >> lg2, part = threadIdx.x & (nparts - 1), len = epad >> lg2;
         int rank = 0;
         if (e < p.E) {
@@ -455,7 +458,8 @@ __device__ __forceinline__ void fetch_ids(const Plan& p, Shared& sh, uint32_t ta
             }
         }
         rank += __shfl_xor(rank, 1, 64);
-        if (lg2 == 2) rank += __shfl_xor(rank, 2, 64);
+        rank += __shfl_xor(rank, 2, 64);
+        if (lg2 == 3) rank += __shfl_xor(rank, 4, 64);
         if (e < p.E && part == 0 && rank < p.k) {
             sh.ids[rank] = e;
             sh.selv[rank] = sh.lg[e];
@@ -644,7 +648,7 @@ __device__ __forceinline__ void run_sd_piece(const Plan& p, Shared& sh, const Un
 }
 
 // Loads of a routed down unit: for each of its tiles, wave w takes groups
-// w/2, w/2 + 4, w/2 + 8 of the expert's intermediate, half w % 2 of the tile.
+// w/2, w/2 + kWaves/2 of the expert's intermediate, half w % 2 of the tile.
 __device__ __forceinline__ void issue_rdu(const Plan& p, const Shared& sh, const DownUnit& d, LoadsN<kItemsD>& L) {
     const int wave = wave_id(), lane = threadIdx.x & 63, par = wave & 1;
     const uint8_t* base = p.pool_base + (int64_t)sh.ids[d.b] * p.expert_stride + p.down_off +
@@ -653,11 +657,11 @@ __device__ __forceinline__ void issue_rdu(const Plan& p, const Shared& sh, const
 #pragma unroll
     for (int t = 0; t < kTilesD; ++t)
 #pragma unroll
-        for (int j = 0; j < 3; ++j)
-            if (t < d.nt && (wave >> 1) + 4 * j < p.G_I) {
-                const uint8_t* blk = base + ((int64_t)t * p.G_I + 4 * j) * kBlk4;
-                L.c[3 * t + j] = ld_stream16(blk + lc);
-                L.s[3 * t + j] = *(const uint2*)(blk + ls);
+        for (int j = 0; j < kGroupsD; ++j)
+            if (t < d.nt && (wave >> 1) + (kWaves / 2) * j < p.G_I) {
+                const uint8_t* blk = base + ((int64_t)t * p.G_I + (kWaves / 2) * j) * kBlk4;
+                L.c[kGroupsD * t + j] = ld_stream16(blk + lc);
+                L.s[kGroupsD * t + j] = *(const uint2*)(blk + ls);
             }
 }
 
@@ -672,8 +676,8 @@ __device__ __forceinline__ void run_rdu(const Plan& p, Shared& sh, const DownUni
 #pragma unroll
     for (int t = 0; t < kTilesD; ++t) acc[t][0] = acc[t][1] = 0.f;
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-        const int g = (wave >> 1) + 4 * j;
+    for (int j = 0; j < kGroupsD; ++j) {
+        const int g = (wave >> 1) + (kWaves / 2) * j;
         if (g < p.G_I) {
             const uint4 ha = *(const uint4*)(sh.h16 + 64 * g + 8 * kb);
             const uint4 hb = *(const uint4*)(sh.h16 + 64 * g + 32 + 8 * kb);
@@ -681,7 +685,7 @@ __device__ __forceinline__ void run_rdu(const Plan& p, Shared& sh, const DownUni
 #pragma unroll
             for (int t = 0; t < kTilesD; ++t)
                 if (t < d.nt) {
-                    const int m = 3 * t + j;
+                    const int m = kGroupsD * t + j;
                     float dd[2] = {0.f, 0.f};
                     half_block_dot16(L.c[m], ha, hb, dd);
                     const uint32_t sw[2] = {L.s[m].x, L.s[m].y};
