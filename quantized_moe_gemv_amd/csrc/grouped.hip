@@ -19,11 +19,33 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
+// Prefix sum of v[0 .. n) (n <= 1024) in LDS, one value per thread: the
+// thread's exclusive prefix in *excl_out, the total as the return value.
+// Every thread of the block must call it.
+__device__ __forceinline__ int block_scan_total(int* buf, int n, int v, int* excl_out) {
+    const int t = threadIdx.x;
+    buf[t] = t < n ? v : 0;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+        const int add = t >= d ? buf[t - d] : 0;
+        __syncthreads();
+        buf[t] += add;
+        __syncthreads();
+    }
+    const int total = buf[1023];
+    *excl_out = buf[t] - (t < n ? v : 0);
+    __syncthreads();
+    return total;
+}
+
 // Stable counting sort of the (token, slot) pairs by expert, one workgroup.
 // The selected experts of one token are distinct, so the rank of pair
 // (t, j) among the pairs of expert e is the number of tokens before t that
-// chose e: a popcount over a per-expert token bitmap.
+// chose e: a popcount over a per-expert token bitmap.  Expert offsets and
+// the tile schedule (expert << 16 | tile) come from block-wide prefix sums.
 __global__ __launch_bounds__(1024) void k_permute(Plan p) {
+    __shared__ int scan[1024];
+    __shared__ int offs[kMaxExperts + 1];
     uint32_t* bitmap = p.bitmap;
     int32_t* wpre = p.wpre;
     const int T = p.T, k = p.k, E = p.E, W = (T + 31) / 32;
@@ -35,32 +57,36 @@ __global__ __launch_bounds__(1024) void k_permute(Plan p) {
         atomicOr(&bitmap[e * W + (t >> 5)], 1u << (t & 31));
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += 1024) {
-        int run = 0;
+    int cnt = 0;
+    if (threadIdx.x < E) {
+        const int e = threadIdx.x;
         for (int w = 0; w < W; ++w) {
-            wpre[e * W + w] = run;
-            run += __popc(bitmap[e * W + w]);
+            wpre[e * W + w] = cnt;
+            cnt += __popc(bitmap[e * W + w]);
         }
-        p.counts[e] = run;
+        p.counts[e] = cnt;
     }
-    __syncthreads();
+    int off;
+    block_scan_total(scan, E, cnt, &off);   // E <= kMaxExperts <= 1024
+    if (threadIdx.x < E) {
+        offs[threadIdx.x] = off;
+        p.offsets[threadIdx.x] = off;
+    }
     if (threadIdx.x == 0) {
-        int off = 0, nt = 0;
-        for (int e = 0; e < E; ++e) {
-            p.offsets[e] = off;
-            const int c = p.counts[e];
-            for (int tile = 0; tile * p.ntile < c; ++tile) p.sched[nt++] = (e << 16) | tile;
-            off += c;
-        }
-        p.offsets[E] = off;
-        *p.nsched = nt;
+        offs[E] = P;
+        p.offsets[E] = P;
     }
-    __syncthreads();
+    const int ntiles = threadIdx.x < E ? (cnt + p.ntile - 1) / p.ntile : 0;
+    int toff;
+    const int nsched = block_scan_total(scan, E, ntiles, &toff);
+    if (threadIdx.x < E)
+        for (int tile = 0; tile < ntiles; ++tile) p.sched[toff + tile] = (threadIdx.x << 16) | tile;
+    if (threadIdx.x == 0) *p.nsched = nsched;
     for (int q = threadIdx.x; q < P; q += 1024) {
         const int t = q / k, e = p.ids[q];
         const uint32_t word = bitmap[e * W + (t >> 5)];
         const int rank = wpre[e * W + (t >> 5)] + __popc(word & ((1u << (t & 31)) - 1u));
-        const int pos = p.offsets[e] + rank;
+        const int pos = offs[e] + rank;
         p.perm[pos] = q;
         p.inv[q] = pos;
     }
@@ -86,29 +112,77 @@ __device__ __forceinline__ void sb_half2(uint32_t pr, half2_t* s2, half2_t* b2) 
     *b2 = (half2_t){b, b};
 }
 
-// One 16-row slice (wave) x 16 tokens of W . X^T over K = 64 * G columns.
-// Wave `ms` owns rows 16*ms .. 16*ms+15 of the 64-row tile at `tile`.
-// xrow: this lane's token row (fp16, K long), or nullptr for a padding token.
-__device__ __forceinline__ float4_t mma_tile(const uint8_t* tile, int G, int ms, int lane, const _Float16* xrow,
-                                             float4_t acc) {
-    const int kb = lane >> 4;
-    const uint8_t* wbase = tile + ((ms >> 1) * 64 + lane) * 16 + 8 * (ms & 1);
-    const uint8_t* sbase = tile + kCodes4 + (lane & 15) * 16 + 4 * ms;
-    for (int g = 0; g < G; ++g) {
-        const uint8_t* blk = (const uint8_t*)((const char*)wbase + (int64_t)g * kBlk4);
-        const uint2 cw = *(const uint2*)blk;
-        const uint32_t pr = *(const uint32_t*)(sbase + (int64_t)g * kBlk4);
-        half2_t s2, b2;
-        sb_half2(pr, &s2, &b2);
-        half8_t b0 = {}, b1 = {};
-        if (xrow) {
-            b0 = *(const half8_t*)(xrow + 64 * g + 8 * kb);
-            b1 = *(const half8_t*)(xrow + 64 * g + 32 + 8 * kb);
+// One 16-row slice (wave ms) x 16 tokens of W . X^T over K = 64 * G
+// columns, for NM matrices at once (gate and up share the token operand).
+// The column-group loop is software-pipelined: the loads of the next kBatch
+// groups are in flight while the current kBatch groups are dequantised and
+// multiplied, so a wave keeps up to 2 kBatch groups of loads outstanding
+// instead of waiting for each group's loads in turn.
+// xrow: this lane's token row (fp16, K long); lanes past the tile's tokens
+// read a valid row too and their results are not stored, so every load is
+// unconditional.
+constexpr int kBatch = 4;
+
+template <int NM>
+struct TileLoads {
+    uint2 c[NM][kBatch];
+    uint32_t s[NM][kBatch];
+    half8_t x0[kBatch], x1[kBatch];
+};
+
+template <int NM>
+__device__ __forceinline__ void tile_load(TileLoads<NM>& L, const uint8_t* const* wbase, const uint8_t* const* sbase,
+                                          const _Float16* xrow, int kb, int g0, int G) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+        const int g = g0 + u;
+        if (g < G) {
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                L.c[m][u] = *(const uint2*)(wbase[m] + (int64_t)g * kBlk4);
+                L.s[m][u] = *(const uint32_t*)(sbase[m] + (int64_t)g * kBlk4);
+            }
+            L.x0[u] = *(const half8_t*)(xrow + 64 * g + 8 * kb);
+            L.x1[u] = *(const half8_t*)(xrow + 64 * g + 32 + 8 * kb);
         }
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8(cw.x, s2, b2), b0, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8(cw.y, s2, b2), b1, acc, 0, 0, 0);
     }
-    return acc;
+}
+
+template <int NM>
+__device__ __forceinline__ void tile_mma(const TileLoads<NM>& L, float4_t* acc, int g0, int G) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+        if (g0 + u < G) {
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                half2_t s2, b2;
+                sb_half2(L.s[m][u], &s2, &b2);
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8(L.c[m][u].x, s2, b2), L.x0[u], acc[m], 0, 0, 0);
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8(L.c[m][u].y, s2, b2), L.x1[u], acc[m], 0, 0, 0);
+            }
+        }
+    }
+}
+
+template <int NM>
+__device__ __forceinline__ void mma_tiles(const uint8_t* const* tiles, int G, int ms, int lane, const _Float16* xrow,
+                                          float4_t* acc) {
+    const int kb = lane >> 4;
+    const uint8_t* wbase[NM];
+    const uint8_t* sbase[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+        wbase[m] = tiles[m] + ((ms >> 1) * 64 + lane) * 16 + 8 * (ms & 1);
+        sbase[m] = tiles[m] + kCodes4 + (lane & 15) * 16 + 4 * ms;
+    }
+    TileLoads<NM> A, B;
+    tile_load(A, wbase, sbase, xrow, kb, 0, G);
+    for (int g0 = 0; g0 < G; g0 += 2 * kBatch) {
+        tile_load(B, wbase, sbase, xrow, kb, g0 + kBatch, G);
+        tile_mma(A, acc, g0, G);
+        tile_load(A, wbase, sbase, xrow, kb, g0 + 2 * kBatch, G);
+        tile_mma(B, acc, g0 + kBatch, G);
+    }
 }
 
 // Gate/up + GeGLU for one (expert, token tile) or, with shared = 1, for the
@@ -135,14 +209,14 @@ __global__ __launch_bounds__(256) void k_gg_gateup(Plan p, int shared) {
         uw = blob + p.up_off + (int64_t)rt * p.G_H * kBlk4;
         rows = p.I;
     }
-    const _Float16* xrow = nullptr;
-    if (n < count) {
-        const int tok = shared ? first + n : p.perm[first + n] / p.k;
-        xrow = p.x16 + (int64_t)tok * p.H;
-    }
-    float4_t ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
-    ag = mma_tile(gw, p.G_H, wave, lane, xrow, ag);
-    au = mma_tile(uw, p.G_H, wave, lane, xrow, au);
+    // lanes past the tile's tokens use the tile's first token (not stored)
+    const int nn = n < count ? n : 0;
+    const int tok = shared ? first + nn : p.perm[first + nn] / p.k;
+    const _Float16* xrow = p.x16 + (int64_t)tok * p.H;
+    float4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    const uint8_t* tiles[2] = {gw, uw};
+    mma_tiles<2>(tiles, p.G_H, wave, lane, xrow, acc);
+    const float4_t ag = acc[0], au = acc[1];
     if (n < count) {
         _Float16* dst = shared ? p.hs16 + (int64_t)(first + n) * p.Is : p.hg + (int64_t)(first + n) * p.I;
         const int r0 = rt * 64 + 16 * wave + 4 * (lane >> 4);
@@ -177,9 +251,11 @@ __global__ __launch_bounds__(256) void k_gg_down(Plan p, int shared) {
         G = p.G_I;
         K = p.I;
     }
-    const _Float16* hrow = n < count ? hbase + (int64_t)(first + n) * K : nullptr;
-    float4_t acc = {0.f, 0.f, 0.f, 0.f};
-    acc = mma_tile(dw, G, wave, lane, hrow, acc);
+    const _Float16* hrow = hbase + (int64_t)(first + (n < count ? n : 0)) * K;   // padding lanes: not stored
+    float4_t accv[1] = {{0.f, 0.f, 0.f, 0.f}};
+    const uint8_t* tiles[1] = {dw};
+    mma_tiles<1>(tiles, G, wave, lane, hrow, accv);
+    const float4_t acc = accv[0];
     if (n < count) {
         const int r0 = rt * 64 + 16 * wave + 4 * (lane >> 4);
         if (shared) {
