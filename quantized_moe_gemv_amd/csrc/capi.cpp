@@ -31,7 +31,7 @@ inline size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 struct Sizes {
-    int H, E, E_pad, k, I, Is, G_H, G_I, G_s, rsplit, rgroups, ntile, max_tiles;
+    int H, E, E_pad, k, I, Is, G_H, G_I, G_s, rsplit, rgroups, ntile, max_tiles, n_vs;
     int n_router, n_sd, n_sc, n_rh, n_src;
 };
 
@@ -92,7 +92,7 @@ int device_cus() {
 // Offsets of every workspace region for up to T tokens; returns the total.
 struct Carve {
     size_t r, rsum8, xsum4, plog, ids, wts, hhi, hlo, hsum, shi, slo, ssum, dpart;
-    size_t x16, counts, offsets, perm, inv, sched, nsched, bitmap, wpre, hg, hs16, ysort, ysh;
+    size_t x16, counts, offsets, perm, inv, sched, nsched, bitmap, wpre, hg, ysort;
     size_t total;
 };
 
@@ -118,14 +118,15 @@ Carve carve(const Sizes& z, int64_t T) {
     c.offsets = take((size_t)(z.E + 1) * 4);
     c.perm = take(T * z.k * 4);
     c.inv = take(T * z.k * 4);
-    c.sched = take((size_t)z.max_tiles * 4 + 4);
+    // sized for the smallest chunk so that the carve grows with T whatever
+    // chunk size set_tiles picks
+    c.sched = take(((size_t)(T * z.k + 31) / 32 + z.E + (size_t)z.n_vs * ((T + 31) / 32)) * 4 + 4);
     c.nsched = take(4);
     c.bitmap = take((size_t)z.E * ((T + 31) / 32) * 4);
     c.wpre = take((size_t)z.E * ((T + 31) / 32) * 4);
-    c.hg = take(T * z.k * z.I * 2);
-    c.hs16 = take(T * z.Is * 2 + 16);
-    c.ysort = take(T * z.k * z.H * 4);
-    c.ysh = take(T * z.H * 4);
+    const size_t rows = T * (z.k + z.n_vs);
+    c.hg = take(rows * z.I * 2);
+    c.ysort = take(rows * z.H * 4);
     c.total = o;
     return c;
 }
@@ -180,7 +181,6 @@ mq_status check_layer(const mq_router* rt, const mq_expert_pool* pool, const mq_
     z->G_s = Is / kGroup;
     z->rgroups = 4;
     z->rsplit = (z->G_H + z->rgroups - 1) / z->rgroups;
-    z->ntile = 16;
     // single-launch decode: router slices of 16 experts in kRouterPieces column pieces
     z->n_router = (E + 15) / 16 * kRouterPieces;
     z->n_sc = (z->G_s + z->G_I - 1) / z->G_I;
@@ -190,9 +190,14 @@ mq_status check_layer(const mq_router* rt, const mq_expert_pool* pool, const mq_
     return MQ_OK;
 }
 
-void set_tiles(Sizes* z, int64_t T) {
-    // every expert may add one partial tile to the full ones
-    z->max_tiles = (int)((T * z->k + z->ntile - 1) / z->ntile + z->E);
+void set_tiles(Sizes* z, int64_t T, bool has_shared) {
+    // Tokens per grouped work item: 32 while experts average at most 32
+    // tokens (many small items, little weight reuse to gain), else 128.
+    z->ntile = T * z->k <= (int64_t)32 * z->E ? 32 : 128;
+    z->n_vs = has_shared ? z->n_sc : 0;
+    // every expert may add one partial chunk to the full ones
+    const int64_t nch = (T + z->ntile - 1) / z->ntile;
+    z->max_tiles = (int)((T * z->k + z->ntile - 1) / z->ntile + z->E + z->n_vs * nch);
 }
 
 }  // namespace
@@ -202,7 +207,7 @@ extern "C" size_t mq_workspace_bytes(const mq_router* router, const mq_expert_po
     Sizes z;
     if (max_tokens < 0 || check_layer(router, pool, shared, &z) != MQ_OK) return 0;
     int64_t T = max_tokens > 0 ? max_tokens : 1;
-    set_tiles(&z, T);
+    set_tiles(&z, T, shared != nullptr);
     return carve(z, T).total;
 }
 
@@ -223,7 +228,7 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
     if (!x->data || !out->data || !opts->workspace) return x->data && out->data ? MQ_ERR_WORKSPACE : MQ_ERR_NULL;
     if (!aligned(x->data, 16) || x->row_stride % 8) return MQ_ERR_ALIGN;
     if (!aligned(out->data, 4) || !aligned(opts->workspace, kAlign)) return MQ_ERR_ALIGN;
-    set_tiles(&z, T);
+    set_tiles(&z, T, shared != nullptr);
     Carve c = carve(z, T);
     if (opts->workspace_bytes < c.total) return MQ_ERR_WORKSPACE;
 
@@ -288,11 +293,10 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
     p.bitmap = (uint32_t*)(ws + c.bitmap);
     p.wpre = (int32_t*)(ws + c.wpre);
     p.hg = (_Float16*)(ws + c.hg);
-    p.hs16 = (_Float16*)(ws + c.hs16);
     p.ysort = (float*)(ws + c.ysort);
-    p.ysh = (float*)(ws + c.ysh);
     p.max_tiles = z.max_tiles;
     p.ntile = z.ntile;
+    p.n_vs = z.n_vs;
 
     const FusedCarve f = fused_carve(z);
     p.f_rpart = (uint64_t*)(ws + f.rpart);

@@ -18,6 +18,7 @@ namespace mq {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // Prefix sum of v[0 .. n) (n <= 1024) in LDS, one value per thread: the
 // thread's exclusive prefix in *excl_out, the total as the return value.
@@ -42,7 +43,7 @@ __device__ __forceinline__ int block_scan_total(int* buf, int n, int v, int* exc
 // The selected experts of one token are distinct, so the rank of pair
 // (t, j) among the pairs of expert e is the number of tokens before t that
 // chose e: a popcount over a per-expert token bitmap.  Expert offsets and
-// the tile schedule (expert << 16 | tile) come from block-wide prefix sums.
+// the schedule (expert << 16 | chunk) come from block-wide prefix sums.
 __global__ __launch_bounds__(1024) void k_permute(Plan p) {
     __shared__ int scan[1024];
     __shared__ int offs[kMaxExperts + 1];
@@ -81,7 +82,10 @@ __global__ __launch_bounds__(1024) void k_permute(Plan p) {
     const int nsched = block_scan_total(scan, E, ntiles, &toff);
     if (threadIdx.x < E)
         for (int tile = 0; tile < ntiles; ++tile) p.sched[toff + tile] = (threadIdx.x << 16) | tile;
-    if (threadIdx.x == 0) *p.nsched = nsched;
+    // then the chunks of the shared expert's virtual experts E .. E+n_vs-1
+    const int nch = (T + p.ntile - 1) / p.ntile;
+    for (int q = threadIdx.x; q < p.n_vs * nch; q += 1024) p.sched[nsched + q] = ((E + q / nch) << 16) | (q % nch);
+    if (threadIdx.x == 0) *p.nsched = nsched + p.n_vs * nch;
     for (int q = threadIdx.x; q < P; q += 1024) {
         const int t = q / k, e = p.ids[q];
         const uint32_t word = bitmap[e * W + (t >> 5)];
@@ -112,62 +116,110 @@ __device__ __forceinline__ void sb_half2(uint32_t pr, half2_t* s2, half2_t* b2) 
     *b2 = (half2_t){b, b};
 }
 
-// One 16-row slice (wave ms) x 16 tokens of W . X^T over K = 64 * G
-// columns, for NM matrices at once (gate and up share the token operand).
-// The column-group loop is software-pipelined: the loads of the next kBatch
-// groups are in flight while the current kBatch groups are dequantised and
-// multiplied, so a wave keeps up to 2 kBatch groups of loads outstanding
-// instead of waiting for each group's loads in turn.
-// xrow: this lane's token row (fp16, K long); lanes past the tile's tokens
-// read a valid row too and their results are not stored, so every load is
-// unconditional.
-constexpr int kBatch = 4;
+// Grouped dequant-GEMM.  A work item is (64-row tile of one matrix, chunk
+// of up to p.ntile tokens of one expert).  The shared expert takes part as
+// n_sc virtual experts of I rows each (its gate/up rows, and the matching
+// column slices of its down projection), applied to every token with
+// weight 1, so it fills the machine together with the routed work.
+//
+// Wave ms owns rows 16 ms .. 16 ms + 15 of the tile.  The token operand (x
+// for gate/up, h for down) is staged in LDS kKB column groups at a time for
+// every token of the chunk; each dequantised weight fragment then feeds the
+// MFMAs of all the chunk's 16-token tiles.  The weights and the token rows
+// of the next batch are loaded into registers while the current batch is
+// multiplied.
+constexpr int kKB = 4;                    // most column groups per staged batch
+constexpr int kXPitch = kKB * 64 + 8;     // LDS row pitch in halves (rows fall on different banks)
 
-template <int NM>
-struct TileLoads {
-    uint2 c[NM][kBatch];
-    uint32_t s[NM][kBatch];
-    half8_t x0[kBatch], x1[kBatch];
+template <int NM, int KB>
+struct WLoads {
+    uint2 c[NM][KB];
+    uint32_t s[NM][KB];
 };
 
-template <int NM>
-__device__ __forceinline__ void tile_load(TileLoads<NM>& L, const uint8_t* const* wbase, const uint8_t* const* sbase,
-                                          const _Float16* xrow, int kb, int g0, int G) {
+// Weight words of column groups g0 .. g0+KB-1.  A group past the end is
+// read from group G-1 with its scale and bias forced to zero, so its
+// dequantised fragment is exactly zero; no load is predicated.
+template <int NM, int KB>
+__device__ __forceinline__ void w_load(WLoads<NM, KB>& L, const uint8_t* const* wbase, const uint8_t* const* sbase,
+                                       int g0, int G) {
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-        const int g = g0 + u;
-        if (g < G) {
+    for (int u = 0; u < KB; ++u) {
+        const int g = min(g0 + u, G - 1);
 #pragma unroll
-            for (int m = 0; m < NM; ++m) {
-                L.c[m][u] = *(const uint2*)(wbase[m] + (int64_t)g * kBlk4);
-                L.s[m][u] = *(const uint32_t*)(sbase[m] + (int64_t)g * kBlk4);
-            }
-            L.x0[u] = *(const half8_t*)(xrow + 64 * g + 8 * kb);
-            L.x1[u] = *(const half8_t*)(xrow + 64 * g + 32 + 8 * kb);
+        for (int m = 0; m < NM; ++m) {
+            L.c[m][u] = *(const uint2*)(wbase[m] + (int64_t)g * kBlk4);
+            const uint32_t sv = *(const uint32_t*)(sbase[m] + (int64_t)g * kBlk4);
+            L.s[m][u] = g0 + u < G ? sv : 0u;
         }
     }
 }
 
-template <int NM>
-__device__ __forceinline__ void tile_mma(const TileLoads<NM>& L, float4_t* acc, int g0, int G) {
+// Token-operand pieces (16 bytes) of one batch held by this thread: piece i
+// is row tid / (8 KB) + (32 / KB) i, columns (tid % (8 KB)) * 8 .. + 7 of the
+// batch.  Rows past the chunk repeat its last row and groups past the end
+// repeat group G-1 (their weights are zero), so every load is in bounds and
+// unmasked.
+template <int NTT, int KB>
+struct XLoads {
+    u32x4_t v[NTT * KB / 2];
+};
+
+template <int NTT, int KB>
+__device__ __forceinline__ void x_load(XLoads<NTT, KB>& X, const _Float16* src, int64_t stride, const int* rows,
+                                       int count, int g0, int G) {
+    const int q = threadIdx.x % (8 * KB), g = min(g0 + (q >> 3), G - 1);
+    const int col = g * 64 + (q & 7) * 8;
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-        if (g0 + u < G) {
+    for (int i = 0; i < NTT * KB / 2; ++i) {
+        const int n = min((int)threadIdx.x / (8 * KB) + (32 / KB) * i, count - 1);
+        X.v[i] = *(const u32x4_t*)(src + (int64_t)rows[n] * stride + col);
+    }
+}
+
+template <int NTT, int KB>
+__device__ __forceinline__ void x_store(const XLoads<NTT, KB>& X, _Float16 (*xs)[kXPitch]) {
+    const int q = threadIdx.x % (8 * KB);
+#pragma unroll
+    for (int i = 0; i < NTT * KB / 2; ++i)
+        *(u32x4_t*)&xs[threadIdx.x / (8 * KB) + (32 / KB) * i][q * 8] = X.v[i];
+}
+
+template <int NM, int NTT, int MAXT, int KB>
+__device__ __forceinline__ void w_mma(const WLoads<NM, KB>& L, _Float16 (*xs)[kXPitch], float4_t (*acc)[MAXT],
+                                      int lane) {
+    const int kb = lane >> 4, n = lane & 15;
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+        half8_t a0[NM], a1[NM];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            half2_t s2, b2;
+            sb_half2(L.s[m][u], &s2, &b2);
+            a0[m] = dequant8(L.c[m][u].x, s2, b2);
+            a1[m] = dequant8(L.c[m][u].y, s2, b2);
+        }
+#pragma unroll
+        for (int t = 0; t < NTT; ++t) {
+            const half8_t b0 = *(const half8_t*)&xs[16 * t + n][64 * u + 8 * kb];
+            const half8_t b1 = *(const half8_t*)&xs[16 * t + n][64 * u + 32 + 8 * kb];
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
-                half2_t s2, b2;
-                sb_half2(L.s[m][u], &s2, &b2);
-                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8(L.c[m][u].x, s2, b2), L.x0[u], acc[m], 0, 0, 0);
-                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant8(L.c[m][u].y, s2, b2), L.x1[u], acc[m], 0, 0, 0);
+                acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[m], b0, acc[m][t], 0, 0, 0);
+                acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1[m], b1, acc[m][t], 0, 0, 0);
             }
         }
     }
 }
 
-template <int NM>
-__device__ __forceinline__ void mma_tiles(const uint8_t* const* tiles, int G, int ms, int lane, const _Float16* xrow,
-                                          float4_t* acc) {
-    const int kb = lane >> 4;
+// One work item over all G column groups: acc[m][t] holds rows
+// 16 ms + 4 (lane / 16) + i, token 16 t + lane % 16 of matrix m.
+template <int NM, int NTT, int MAXT>
+__device__ __forceinline__ void gg_tile_n(const uint8_t* const* tiles, int G, const _Float16* src, int64_t stride,
+                                          const int* rows, int count, _Float16 (*xs)[kXPitch],
+                                          float4_t (*acc)[MAXT]) {
+    constexpr int KB = NTT <= 4 ? kKB : kKB / 2;   // keeps the prefetched rows within the register budget
+    const int ms = wave_id(), lane = threadIdx.x & 63;
     const uint8_t* wbase[NM];
     const uint8_t* sbase[NM];
 #pragma unroll
@@ -175,108 +227,173 @@ __device__ __forceinline__ void mma_tiles(const uint8_t* const* tiles, int G, in
         wbase[m] = tiles[m] + ((ms >> 1) * 64 + lane) * 16 + 8 * (ms & 1);
         sbase[m] = tiles[m] + kCodes4 + (lane & 15) * 16 + 4 * ms;
     }
-    TileLoads<NM> A, B;
-    tile_load(A, wbase, sbase, xrow, kb, 0, G);
-    for (int g0 = 0; g0 < G; g0 += 2 * kBatch) {
-        tile_load(B, wbase, sbase, xrow, kb, g0 + kBatch, G);
-        tile_mma(A, acc, g0, G);
-        tile_load(A, wbase, sbase, xrow, kb, g0 + 2 * kBatch, G);
-        tile_mma(B, acc, g0 + kBatch, G);
+    WLoads<NM, KB> A, B;
+    XLoads<NTT, KB> X;
+    x_load(X, src, stride, rows, count, 0, G);
+    w_load(A, wbase, sbase, 0, G);
+    // The loads for the batch after the last one re-read (clamped) groups
+    // just read, which keeps every load unconditional.
+    for (int g0 = 0;; g0 += 2 * KB) {
+        x_store(X, xs);
+        __syncthreads();
+        x_load(X, src, stride, rows, count, g0 + KB, G);
+        w_load(B, wbase, sbase, g0 + KB, G);
+        w_mma<NM, NTT, MAXT, KB>(A, xs, acc, lane);
+        __syncthreads();
+        if (g0 + KB >= G) break;
+        x_store(X, xs);
+        __syncthreads();
+        x_load(X, src, stride, rows, count, g0 + 2 * KB, G);
+        w_load(A, wbase, sbase, g0 + 2 * KB, G);
+        w_mma<NM, NTT, MAXT, KB>(B, xs, acc, lane);
+        __syncthreads();
+        if (g0 + 2 * KB >= G) break;
     }
 }
 
-// Gate/up + GeGLU for one (expert, token tile) or, with shared = 1, for the
-// shared expert over a tile of all tokens.  grid (I/64, tiles), block 256.
-__global__ __launch_bounds__(256) void k_gg_gateup(Plan p, int shared) {
-    const int rt = blockIdx.x, wave = wave_id(), lane = threadIdx.x & 63;
-    const int n = lane & 15;
-    int count, first;   // tokens of this tile, position of its first pair
-    const uint8_t *gw, *uw;
-    int rows;
-    if (shared) {
-        first = blockIdx.y * p.ntile;
-        count = min(p.ntile, p.T - first);
-        gw = p.sh_gate + (int64_t)rt * p.G_H * kBlk4;
-        uw = p.sh_up + (int64_t)rt * p.G_H * kBlk4;
-        rows = p.Is;
+// Dispatch on the chunk's number of 16-token tiles so that every MFMA
+// sequence is straight-line code.
+template <int NM, int MAXT>
+__device__ __forceinline__ void gg_tile(const uint8_t* const* tiles, int G, const _Float16* src, int64_t stride,
+                                        const int* rows, int count, _Float16 (*xs)[kXPitch], float4_t (*acc)[MAXT]) {
+    const int ntt = (count + 15) / 16;
+    if constexpr (MAXT <= 2) {
+        if (ntt == 1) gg_tile_n<NM, 1, MAXT>(tiles, G, src, stride, rows, count, xs, acc);
+        else gg_tile_n<NM, MAXT, MAXT>(tiles, G, src, stride, rows, count, xs, acc);
     } else {
-        if ((int)blockIdx.y >= *p.nsched) return;
-        const int sc = p.sched[blockIdx.y], e = sc >> 16, tile = sc & 0xFFFF;
-        first = p.offsets[e] + tile * p.ntile;
-        count = min(p.ntile, p.offsets[e + 1] - first);
-        const uint8_t* blob = p.pool_base + (int64_t)e * p.expert_stride;
-        gw = blob + p.gate_off + (int64_t)rt * p.G_H * kBlk4;
-        uw = blob + p.up_off + (int64_t)rt * p.G_H * kBlk4;
-        rows = p.I;
-    }
-    // lanes past the tile's tokens use the tile's first token (not stored)
-    const int nn = n < count ? n : 0;
-    const int tok = shared ? first + nn : p.perm[first + nn] / p.k;
-    const _Float16* xrow = p.x16 + (int64_t)tok * p.H;
-    float4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    const uint8_t* tiles[2] = {gw, uw};
-    mma_tiles<2>(tiles, p.G_H, wave, lane, xrow, acc);
-    const float4_t ag = acc[0], au = acc[1];
-    if (n < count) {
-        _Float16* dst = shared ? p.hs16 + (int64_t)(first + n) * p.Is : p.hg + (int64_t)(first + n) * p.I;
-        const int r0 = rt * 64 + 16 * wave + 4 * (lane >> 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (r0 + i < rows) dst[r0 + i] = (_Float16)(gelu_tanh(ag[i]) * au[i]);
-    }
-}
-
-// Down projection for one (expert, token tile): ysort[pos] = w_pair * (W_down . h),
-// or with shared = 1 the shared expert: ysh[t] = W_sdown . hs.  grid (H/64, tiles).
-__global__ __launch_bounds__(256) void k_gg_down(Plan p, int shared) {
-    const int rt = blockIdx.x, wave = wave_id(), lane = threadIdx.x & 63;
-    const int n = lane & 15;
-    int count, first, G, K;
-    const uint8_t* dw;
-    const _Float16* hbase;
-    if (shared) {
-        first = blockIdx.y * p.ntile;
-        count = min(p.ntile, p.T - first);
-        dw = p.sh_down + (int64_t)rt * p.G_s * kBlk4;
-        hbase = p.hs16;
-        G = p.G_s;
-        K = p.Is;
-    } else {
-        if ((int)blockIdx.y >= *p.nsched) return;
-        const int sc = p.sched[blockIdx.y], e = sc >> 16, tile = sc & 0xFFFF;
-        first = p.offsets[e] + tile * p.ntile;
-        count = min(p.ntile, p.offsets[e + 1] - first);
-        dw = p.pool_base + (int64_t)e * p.expert_stride + p.down_off + (int64_t)rt * p.G_I * kBlk4;
-        hbase = p.hg;
-        G = p.G_I;
-        K = p.I;
-    }
-    const _Float16* hrow = hbase + (int64_t)(first + (n < count ? n : 0)) * K;   // padding lanes: not stored
-    float4_t accv[1] = {{0.f, 0.f, 0.f, 0.f}};
-    const uint8_t* tiles[1] = {dw};
-    mma_tiles<1>(tiles, G, wave, lane, hrow, accv);
-    const float4_t acc = accv[0];
-    if (n < count) {
-        const int r0 = rt * 64 + 16 * wave + 4 * (lane >> 4);
-        if (shared) {
-            float* dst = p.ysh + (int64_t)(first + n) * p.H;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dst[r0 + i] = acc[i];
-        } else {
-            const float w = p.wts[p.perm[first + n]];
-            float* dst = p.ysort + (int64_t)(first + n) * p.H;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dst[r0 + i] = w * acc[i];
+        switch (ntt) {
+            case 1: gg_tile_n<NM, 1, MAXT>(tiles, G, src, stride, rows, count, xs, acc); break;
+            case 2: gg_tile_n<NM, 2, MAXT>(tiles, G, src, stride, rows, count, xs, acc); break;
+            case 3: gg_tile_n<NM, 3, MAXT>(tiles, G, src, stride, rows, count, xs, acc); break;
+            case 4: gg_tile_n<NM, 4, MAXT>(tiles, G, src, stride, rows, count, xs, acc); break;
+            case 5: gg_tile_n<NM, 5, MAXT>(tiles, G, src, stride, rows, count, xs, acc); break;
+            case 6: gg_tile_n<NM, 6, MAXT>(tiles, G, src, stride, rows, count, xs, acc); break;
+            case 7: gg_tile_n<NM, 7, MAXT>(tiles, G, src, stride, rows, count, xs, acc); break;
+            default: gg_tile_n<NM, MAXT, MAXT>(tiles, G, src, stride, rows, count, xs, acc); break;
         }
     }
 }
 
-// out[t] = shared + sum_j ysort[inv[t][j]] (slot order), rounded once.  grid (T, ceil(H/256)).
+// The work item of this workgroup: blockIdx.y indexes the schedule
+// (expert << 16 | chunk), blockIdx.x the 64-row tile.  Experts E .. E+n_vs-1
+// are the shared expert's virtual experts.  Returns false when the
+// workgroup has nothing to do.
+struct Item {
+    int count;          // tokens of the chunk
+    int pos0;           // row of chunk token 0 in hg / ysort
+    int shared;         // 1 for a virtual shared expert
+    int tok0;           // shared: first token of the chunk
+    int G;              // column groups of the operand
+    const uint8_t* w[2];
+};
+
+__device__ __forceinline__ bool gg_item(const Plan& p, bool down, Item* it) {
+    if ((int)blockIdx.y >= *p.nsched) return false;
+    const int sc = p.sched[blockIdx.y], ex = sc >> 16, c = sc & 0xFFFF, rt = blockIdx.x;
+    if (ex < p.E) {
+        const int first = p.offsets[ex] + c * p.ntile;
+        it->count = min(p.ntile, p.offsets[ex + 1] - first);
+        it->pos0 = first;
+        it->shared = 0;
+        it->tok0 = 0;
+        const uint8_t* base = p.pool_base + (int64_t)ex * p.expert_stride;
+        if (down) {
+            it->G = p.G_I;
+            it->w[0] = it->w[1] = base + p.down_off + (int64_t)rt * p.G_I * kBlk4;
+        } else {
+            it->G = p.G_H;
+            it->w[0] = base + p.gate_off + (int64_t)rt * p.G_H * kBlk4;
+            it->w[1] = base + p.up_off + (int64_t)rt * p.G_H * kBlk4;
+        }
+    } else {
+        const int j = ex - p.E;
+        it->tok0 = c * p.ntile;
+        it->count = min(p.ntile, p.T - it->tok0);
+        it->pos0 = p.T * p.k + j * p.T + it->tok0;
+        it->shared = 1;
+        if (down) {
+            it->G = min(p.G_I, p.G_s - j * p.G_I);
+            it->w[0] = it->w[1] = p.sh_down + ((int64_t)rt * p.G_s + (int64_t)j * p.G_I) * kBlk4;
+        } else {
+            if (rt * 64 >= p.Is - j * p.I) return false;   // the last virtual expert may be shorter
+            it->G = p.G_H;
+            it->w[0] = p.sh_gate + (int64_t)(j * p.G_I + rt) * p.G_H * kBlk4;
+            it->w[1] = p.sh_up + (int64_t)(j * p.G_I + rt) * p.G_H * kBlk4;
+        }
+    }
+    return true;
+}
+
+// Gate/up + GeGLU: hg[pos] = gelu(gate x) * (up x) in fp16.
+// grid (I / 64, max_tiles), block 256.
+template <int MAXT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gg_gateup(Plan p) {
+    __shared__ __attribute__((aligned(16))) _Float16 xs[MAXT * 16][kXPitch];
+    __shared__ int rows[MAXT * 16];
+    Item it;
+    if (!gg_item(p, false, &it)) return;
+    const int rt = blockIdx.x, wave = wave_id(), lane = threadIdx.x & 63;
+    if ((int)threadIdx.x < it.count)
+        rows[threadIdx.x] = it.shared ? it.tok0 + threadIdx.x : p.perm[it.pos0 + threadIdx.x] / p.k;
+    __syncthreads();
+    float4_t acc[2][MAXT];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int t = 0; t < MAXT; ++t) acc[m][t] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    gg_tile<2, MAXT>(it.w, it.G, p.x16, p.H, rows, it.count, xs, acc);
+    const int r0 = rt * 64 + 16 * wave + 4 * (lane >> 4);
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) {
+        const int n = 16 * t + (lane & 15);
+        if (n < it.count) {
+            _Float16* dst = p.hg + (int64_t)(it.pos0 + n) * p.I + r0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[i] = (_Float16)(gelu_tanh(acc[0][t][i]) * acc[1][t][i]);
+        }
+    }
+}
+
+// Down projection: ysort[pos] = w_pair * (W_down . h), weight 1 for the
+// shared expert's slices.  grid (H / 64, max_tiles), block 256.
+template <int MAXT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gg_down(Plan p) {
+    __shared__ __attribute__((aligned(16))) _Float16 xs[MAXT * 16][kXPitch];
+    __shared__ int rows[MAXT * 16];
+    __shared__ float wrow[MAXT * 16];
+    Item it;
+    if (!gg_item(p, true, &it)) return;
+    const int rt = blockIdx.x, wave = wave_id(), lane = threadIdx.x & 63;
+    if ((int)threadIdx.x < it.count) {
+        rows[threadIdx.x] = it.pos0 + threadIdx.x;
+        wrow[threadIdx.x] = it.shared ? 1.f : p.wts[p.perm[it.pos0 + threadIdx.x]];
+    }
+    __syncthreads();
+    float4_t acc[1][MAXT];
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) acc[0][t] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    gg_tile<1, MAXT>(it.w, it.G, p.hg, p.I, rows, it.count, xs, acc);
+    const int r0 = rt * 64 + 16 * wave + 4 * (lane >> 4);
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) {
+        const int n = 16 * t + (lane & 15);
+        if (n < it.count) {
+            const float w = wrow[n];
+            float* dst = p.ysort + (int64_t)(it.pos0 + n) * p.H + r0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[i] = w * acc[0][t][i];
+        }
+    }
+}
+
+// out[t] = sum_j ysort[inv[t][j]] (slot order) + the shared expert's
+// slices, rounded once.  grid (T, ceil(H/256)).
 __global__ __launch_bounds__(256) void k_gg_combine(Plan p) {
     const int t = blockIdx.x, i = blockIdx.y * 256 + threadIdx.x;
     if (i >= p.H) return;
-    float v = p.has_shared ? p.ysh[(int64_t)t * p.H + i] : 0.f;
+    float v = 0.f;
     for (int j = 0; j < p.k; ++j) v += p.ysort[(int64_t)p.inv[t * p.k + j] * p.H + i];
+    for (int j = 0; j < p.n_vs; ++j) v += p.ysort[((int64_t)p.T * p.k + (int64_t)j * p.T + t) * p.H + i];
     if (p.out_f32)
         ((float*)p.out)[(int64_t)t * p.out_stride + i] = v;
     else
@@ -285,11 +402,14 @@ __global__ __launch_bounds__(256) void k_gg_combine(Plan p) {
 
 mq_status launch_grouped(const Plan& p, hipStream_t s) {
     hipLaunchKernelGGL(k_permute, dim3(1), dim3(1024), 0, s, p);
-    const int tshared = (p.T + p.ntile - 1) / p.ntile;
-    hipLaunchKernelGGL(k_gg_gateup, dim3(p.I / 64, p.max_tiles), dim3(256), 0, s, p, 0);
-    if (p.has_shared) hipLaunchKernelGGL(k_gg_gateup, dim3(p.Is / 64, tshared), dim3(256), 0, s, p, 1);
-    hipLaunchKernelGGL(k_gg_down, dim3(p.H / 64, p.max_tiles), dim3(256), 0, s, p, 0);
-    if (p.has_shared) hipLaunchKernelGGL(k_gg_down, dim3(p.H / 64, tshared), dim3(256), 0, s, p, 1);
+    const dim3 gu(p.I / 64, p.max_tiles), dn(p.H / 64, p.max_tiles);
+    if (p.ntile <= 32) {
+        hipLaunchKernelGGL(k_gg_gateup<2>, gu, dim3(256), 0, s, p);
+        hipLaunchKernelGGL(k_gg_down<2>, dn, dim3(256), 0, s, p);
+    } else {
+        hipLaunchKernelGGL(k_gg_gateup<8>, gu, dim3(256), 0, s, p);
+        hipLaunchKernelGGL(k_gg_down<8>, dn, dim3(256), 0, s, p);
+    }
     hipLaunchKernelGGL(k_gg_combine, dim3(p.T, (p.H + 255) / 256), dim3(256), 0, s, p);
     return MQ_OK;
 }

@@ -62,14 +62,14 @@ struct Plan {
     int32_t* offsets;  // [E + 1]
     int32_t* perm;     // [T*k]  pair p = t*k + j, sorted by expert then token
     int32_t* inv;      // [T*k]  position of pair p in perm
-    int32_t* sched;    // [max_tiles] (expert << 16 | token tile)
+    int32_t* sched;    // [max_tiles] (expert << 16 | token chunk)
     int32_t* nsched;   // [1]
     uint32_t* bitmap;  // [E][ceil(T/32)] tokens that chose each expert
     int32_t* wpre;     // [E][ceil(T/32)] exclusive popcount prefix of bitmap
-    _Float16* hg;      // [T*k][I]   GeGLU activations in sorted order
-    _Float16* hs16;    // [T][Is]
-    float* ysort;      // [T*k][H]   weighted expert outputs in sorted order
-    float* ysh;        // [T][H]     shared expert outputs
+    // rows T*k + j*T + t of hg / ysort belong to token t and the shared
+    // expert's virtual expert j (its rows j*I .. j*I + I - 1)
+    _Float16* hg;      // [T*k + n_vs*T][I]  GeGLU activations in sorted order
+    float* ysort;      // [T*k + n_vs*T][H]  weighted expert outputs in sorted order
     // single-launch decode: tagged words and counters that persist across calls
     uint64_t* f_rpart;   // [copies][E/16][8][16] partial router scores, rpart_stride apart
     uint64_t* f_hs;      // [copies][Is]        shared GeGLU activations (fp16 payload), h_stride apart
@@ -80,8 +80,9 @@ struct Plan {
     uint32_t* f_epoch;   // calls completed with this workspace
     uint32_t* f_err;     // non-zero once a bounded wait has given up
     int n_router, n_sd, n_sc, n_rh, n_rng, n_src;   // n_rng: tile ranges per routed down slot
-    int max_tiles;     // upper bound of scheduled (expert, token tile) pairs
-    int ntile;         // tokens per grouped tile
+    int max_tiles;     // upper bound of scheduled (expert, token chunk) pairs
+    int ntile;         // tokens per grouped chunk (32 or 128)
+    int n_vs;          // virtual experts of the shared expert (0 without one)
 };
 
 }  // namespace mq
