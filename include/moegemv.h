@@ -46,7 +46,7 @@ typedef enum {
     MQ_ERR_NULL = -1,         /* a required pointer is NULL */
     MQ_ERR_SHAPE = -2,        /* inconsistent or unsupported sizes */
     MQ_ERR_ALIGN = -3,        /* a pointer, offset or stride is misaligned */
-    MQ_ERR_UNSUPPORTED = -4,  /* bits, group, layout or dtype not supported */
+    MQ_ERR_UNSUPPORTED = -4,  /* bits, group, layout, dtype, path or size not supported */
     MQ_ERR_WORKSPACE = -5,    /* workspace missing or smaller than mq_workspace_bytes */
     MQ_ERR_HIP = -6,          /* a HIP runtime call failed */
     MQ_ERR_BUFFER = -7        /* a HOST output buffer is too small */
@@ -57,7 +57,9 @@ enum { MQ_DTYPE_BF16 = 0, MQ_DTYPE_F32 = 1 };
 /* Kernel schedule.  AUTO: FUSED for one token, GEMV up to 4 tokens, GROUPED
  * above.  FUSED (one token only): one launch for the whole layer.  GEMV:
  * per-(token, expert) dot-product kernels.  GROUPED: tokens sorted by
- * expert, dequantised weights on the matrix cores. */
+ * expert, dequantised weights on the matrix cores; it takes at most 32640
+ * tokens per call and an expert intermediate size of at most 2496
+ * (MQ_ERR_UNSUPPORTED otherwise, before any work is queued). */
 enum { MQ_PATH_AUTO = 0, MQ_PATH_GEMV = 1, MQ_PATH_GROUPED = 2, MQ_PATH_FUSED = 3 };
 
 /*

@@ -19,6 +19,7 @@ __global__ void k_rmsnorm(const uint16_t* x, int64_t xs, uint16_t* y, int64_t ys
 __global__ void k_debug_read(const uint8_t* data, int rows, int cols, int bits, uint8_t* codes_out, float* w_out);
 __global__ void k_decode(Plan p);
 mq_status launch_grouped(const Plan& p, hipStream_t s);
+bool grouped_ok(int H, int I, int64_t T);
 }  // namespace mq
 
 using namespace mq;
@@ -39,7 +40,7 @@ struct Sizes {
 // the start of the workspace, at offsets that do not depend on the token
 // count, and no other kernel writes it.
 struct FusedCarve {
-    size_t rpart, act, piece, ctr, total;
+    size_t rpart, act, piece, ctr, fcnt, total;
     int64_t h_stride, rpart_stride;   // in 8-byte words
 };
 
@@ -54,6 +55,7 @@ FusedCarve fused_carve(const Sizes& z) {
     f.act = take((size_t)8 * f.h_stride * 8);
     f.piece = take((size_t)z.G_H * z.n_src * 64 * 8);
     f.ctr = take((size_t)3 * kCtrStride * 4);   // c_done, epoch, error flag
+    f.fcnt = take((size_t)(kFrontMaxGroups + 1) * 4);   // grouped-path front counters
     f.total = o;
     return f;
 }
@@ -191,9 +193,7 @@ mq_status check_layer(const mq_router* rt, const mq_expert_pool* pool, const mq_
 }
 
 void set_tiles(Sizes* z, int64_t T, bool has_shared) {
-    // Tokens per grouped work item: 32 while experts average at most 32
-    // tokens (many small items, little weight reuse to gain), else 128.
-    z->ntile = T * z->k <= (int64_t)32 * z->E ? 32 : 128;
+    z->ntile = 128;   // tokens per grouped work item
     z->n_vs = has_shared ? z->n_sc : 0;
     // every expert may add one partial chunk to the full ones
     const int64_t nch = (T + z->ntile - 1) / z->ntile;
@@ -309,6 +309,7 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
     p.c_done = ctr;
     p.f_epoch = ctr + kCtrStride;
     p.f_err = ctr + 2 * kCtrStride;
+    p.fcnt = (uint32_t*)(ws + f.fcnt);
     p.n_router = z.n_router;
     p.n_sd = z.n_sd;
     p.n_sc = z.n_sc;
@@ -330,16 +331,17 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
         return hipGetLastError() == hipSuccess ? MQ_OK : MQ_ERR_HIP;
     }
     const bool grouped = opts->path == MQ_PATH_GROUPED || (opts->path == MQ_PATH_AUTO && T > 4);
+    if (grouped && !grouped_ok(z.H, z.I, T)) return MQ_ERR_UNSUPPORTED;
     if (grouped) p.x16 = (_Float16*)(ws + c.x16);
 
-    hipLaunchKernelGGL(k_prep, dim3(T), dim3(256), 0, s, p);
-    hipLaunchKernelGGL(k_router, dim3(z.E_pad / 64, z.rsplit, (T + kRouterTokens - 1) / kRouterTokens), dim3(256),
-                       0, s, p);
-    hipLaunchKernelGGL(k_topk, dim3(T), dim3(256), 0, s, p);
     if (grouped) {
         st = launch_grouped(p, s);
         if (st != MQ_OK) return st;
     } else {
+        hipLaunchKernelGGL(k_prep, dim3(T), dim3(256), 0, s, p);
+        hipLaunchKernelGGL(k_router, dim3(z.E_pad / 64, z.rsplit, (T + kRouterTokens - 1) / kRouterTokens),
+                           dim3(256), 0, s, p);
+        hipLaunchKernelGGL(k_topk, dim3(T), dim3(256), 0, s, p);
         hipLaunchKernelGGL(k_gateup, dim3(T, z.k * (z.I / 64) + z.Is / 64), dim3(256), 0, s, p);
         hipLaunchKernelGGL(k_down, dim3(T, z.H / 64, kDownSplits), dim3(256), 0, s, p);
         hipLaunchKernelGGL(k_combine, dim3(T, (z.H + 255) / 256), dim3(256), 0, s, p);
