@@ -94,7 +94,7 @@ int device_cus() {
 // Offsets of every workspace region for up to T tokens; returns the total.
 struct Carve {
     size_t r, rsum8, xsum4, plog, ids, wts, hhi, hlo, hsum, shi, slo, ssum, dpart;
-    size_t x16, counts, offsets, perm, inv, sched, nsched, bitmap, wpre, hg, ysort;
+    size_t x16, counts, offsets, perm, inv, sched, nsched, hg, ysort;
     size_t total;
 };
 
@@ -124,8 +124,6 @@ Carve carve(const Sizes& z, int64_t T) {
     // chunk size set_tiles picks
     c.sched = take(((size_t)(T * z.k + 31) / 32 + z.E + (size_t)z.n_vs * ((T + 31) / 32)) * 4 + 4);
     c.nsched = take(4);
-    c.bitmap = take((size_t)z.E * ((T + 31) / 32) * 4);
-    c.wpre = take((size_t)z.E * ((T + 31) / 32) * 4);
     const size_t rows = T * (z.k + z.n_vs);
     c.hg = take(rows * z.I * 2);
     c.ysort = take(rows * z.H * 4);
@@ -290,8 +288,6 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
     p.inv = (int32_t*)(ws + c.inv);
     p.sched = (int32_t*)(ws + c.sched);
     p.nsched = (int32_t*)(ws + c.nsched);
-    p.bitmap = (uint32_t*)(ws + c.bitmap);
-    p.wpre = (int32_t*)(ws + c.wpre);
     p.hg = (_Float16*)(ws + c.hg);
     p.ysort = (float*)(ws + c.ysort);
     p.max_tiles = z.max_tiles;

@@ -64,12 +64,10 @@ struct Plan {
     _Float16* x16;     // [T][H]
     int32_t* counts;   // [E]
     int32_t* offsets;  // [E + 1]
-    int32_t* perm;     // [T*k]  pair p = t*k + j, sorted by expert then token
+    int32_t* perm;     // [T*k]  pair p = t*k + j, sorted by expert (any order within one)
     int32_t* inv;      // [T*k]  position of pair p in perm
     int32_t* sched;    // [max_tiles] (expert << 16 | token chunk)
     int32_t* nsched;   // [1]
-    uint32_t* bitmap;  // [E][ceil(T/32)] tokens that chose each expert
-    int32_t* wpre;     // [E][ceil(T/32)] exclusive popcount prefix of bitmap
     // rows T*k + j*T + t of hg / ysort belong to token t and the shared
     // expert's virtual expert j (its rows j*I .. j*I + I - 1)
     _Float16* hg;      // [T*k + n_vs*T][I]  GeGLU activations in sorted order
