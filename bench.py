@@ -21,7 +21,11 @@ Profiling helpers (not part of the default run):
   --profile decode       runs decode calls back to back, then a copy kernel of
                          known size, for rocprofv3 counter runs;
   --traffic-summary F W  turns the FETCH_SIZE / WRITE_SIZE counter CSVs of
-                         those runs into the traffic summary under profiles/.
+                         those runs into the traffic summary under profiles/;
+  --stats-summary S J    turns the kernel statistics CSV of a rocprofv3
+                         --kernel-trace --stats run of the default benchmark,
+                         and the JSON line that run printed, into the kernel
+                         table under profiles/.
 """
 from __future__ import annotations
 
@@ -45,6 +49,7 @@ MFMA_PEAK_TFLOPS = 2500.0    # MI355X dense fp16/bf16 matrix peak, vendor figure
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (% of peak), decode and 128-tok prefill"
 DECODE_KERNEL = "k_decode"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_decode_decode_h2816_e128_traffic.txt")
+STATS_FILE = os.path.join(ROOT, "profiles", "kernel_stats_bench_decode_prefill128_stack30_prefill4096.txt")
 COPY_BYTES = 256 << 20       # each direction of the reference copy kernel
 # Sources whose change invalidates the recorded counter traffic of the decode kernel.
 KERNEL_SOURCES = ["fused.hip", "device.h", "plan.h", "layout.h"]
@@ -241,6 +246,43 @@ def traffic_summary(fetch_csv, write_csv, out_path):
     print("\n".join(lines))
 
 
+def stats_summary(stats_csv, bench_json, out_path):
+    with open(stats_csv) as f:
+        rows = list(csv.DictReader(f))
+    with open(bench_json) as f:
+        res = json.loads([l for l in f if l.strip().startswith("{")][-1])
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = [
+        "# rocprofv3 kernel statistics of the default benchmark run",
+        "# workloads: decode (graph of %d calls + eager calls, %d resident layers), 128-token prefill (graph),"
+        % (res["steps"], res["config"].get("resident_layers", 30)),
+        "#            30-layer stack with RMSNorm, 4096-token prefill (graph); warm-up calls included",
+        "# command (from /tmp with TMPDIR=/tmp):",
+        "#   rocprofv3 --kernel-trace --stats -d <dir> -o bench --output-format csv -- python3 <repo>/bench.py > <dir>/bench.json",
+        "#   python3 <repo>/bench.py --stats-summary <dir>/bench_kernel_stats.csv <dir>/bench.json",
+        "# bench.py in the same run: decode %.2f us/call (graph)" % (res["ms_per_step"] * 1000.0),
+    ]
+    extra = []
+    if isinstance(res.get("prefill128"), dict):
+        extra.append("prefill128 %.2f us/call" % (res["prefill128"]["ms_per_call"] * 1e3))
+    if isinstance(res.get("stack"), dict):
+        extra.append("stack%d %.2f us/token" % (res["stack"]["layers"], res["stack"]["ms_per_token"] * 1e3))
+    if isinstance(res.get("prefill4096"), dict):
+        extra.append("prefill4096 %.3f ms/call" % res["prefill4096"]["ms_per_call"])
+    if extra:
+        lines.append("#   " + ", ".join(extra))
+    lines += ["", "%-62s %6s %12s %10s %10s %10s" % ("kernel", "calls", "total_ms", "avg_us", "min_us", "max_us")]
+    for r in rows:
+        name = r["Name"]
+        name = name if len(name) <= 60 else name[:57] + "..."
+        lines.append("%-62s %6d %12.3f %10.2f %10.2f %10.2f" % (
+            name, int(r["Calls"]), float(r["TotalDurationNs"]) / 1e6, float(r["AverageNs"]) / 1e3,
+            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 # ------------------------------------------------------------------ main run
 
 def main():
@@ -258,9 +300,13 @@ def main():
     ap.add_argument("--path", default="auto", choices=["auto", "fused", "gemv", "grouped"])
     ap.add_argument("--profile", choices=["decode"])
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--stats-summary", nargs=2, metavar=("STATS_CSV", "BENCH_JSON"))
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(args.traffic_summary[0], args.traffic_summary[1], TRAFFIC_FILE)
+        return
+    if args.stats_summary:
+        stats_summary(args.stats_summary[0], args.stats_summary[1], STATS_FILE)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: the layer runs on a single MI355X and has no multi-GPU path "
