@@ -443,18 +443,19 @@ __device__ __forceinline__ void fetch_ids(const Plan& p, Shared& sh, uint32_t ta
     __syncthreads();
     // Rank of expert e = the number of keys above its key.  Each expert's
     // comparisons are split over nparts adjacent lanes, summed by shuffles.
+    // Part q reads the key pairs q, q + nparts, ...: the parts of a wave read
+    // adjacent 16-byte pieces, on distinct LDS banks.
     {
         const int lg2 = epad <= 128 ? 3 : 2, nparts = 1 << lg2;   // nparts * epad <= kThreads
         const int e = threadIdx.x >> lg2, part = threadIdx.x & (nparts - 1), len = epad >> lg2;
         int rank = 0;
         if (e < p.E) {
             const uint64_t me = sh.key[e];
-            const uint64_t* kp = sh.key + part * len;
+            const uint64_t* kp = sh.key + 2 * part;
 #pragma unroll 8
-            for (int o = 0; o < len; o += 4) {
-                const ulonglong2 k0 = *(const ulonglong2*)(kp + o);
-                const ulonglong2 k1 = *(const ulonglong2*)(kp + o + 2);
-                rank += (int)(k0.x > me) + (int)(k0.y > me) + (int)(k1.x > me) + (int)(k1.y > me);
+            for (int o = 0; o < len; o += 2) {
+                const ulonglong2 k0 = *(const ulonglong2*)(kp + o * nparts);
+                rank += (int)(k0.x > me) + (int)(k0.y > me);
             }
         }
         rank += __shfl_xor(rank, 1, 64);
