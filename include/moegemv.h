@@ -154,6 +154,15 @@ size_t mq_workspace_bytes(const mq_router* router, const mq_expert_pool* pool,
 mq_status moe_layer_forward(const mq_act* x, const mq_router* router, const mq_expert_pool* pool,
                             const mq_shared* shared, mq_act* out, const mq_opts* opts, void* stream);
 
+/* HOST result: the sticky error bits that the single-launch path (FUSED)
+ * keeps in a workspace.  Bit 0: a bounded wait for another workgroup's
+ * partial result gave up, so the calls since the bits were last clear may
+ * have wrong results (it happens only if the workgroups of a launch are not
+ * all resident at once).  Copies the bits into *errors after the work queued
+ * on `stream` has finished (the call synchronises the stream).  The bits stay
+ * set until the workspace is zero-filled again.  workspace_bytes >= 1024. */
+mq_status mq_workspace_errors(const void* workspace, size_t workspace_bytes, uint32_t* errors, void* stream);
+
 /* Unit-weight RMS norm between stacked layers: out = bf16(x / sqrt(mean(x^2) + eps)).
  * x and out bf16 [T][H]; they may alias. */
 mq_status mq_rmsnorm(const mq_act* x, mq_act* out, float eps, void* stream);

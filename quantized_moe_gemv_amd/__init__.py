@@ -30,7 +30,7 @@ LAYOUT_CANONICAL, LAYOUT_DEV_V1 = 0, 1
 DTYPE_BF16, DTYPE_F32 = 0, 1
 PATHS = {"auto": 0, "gemv": 1, "grouped": 2, "fused": 3}
 GROUP = 64
-EXPORTS = ["moe_layer_forward", "mq_workspace_bytes", "mq_rmsnorm", "mq_packed_bytes", "mq_pool_layout",
+EXPORTS = ["moe_layer_forward", "mq_workspace_bytes", "mq_workspace_errors", "mq_rmsnorm", "mq_packed_bytes", "mq_pool_layout",
            "mq_pack", "mq_unpack", "mq_debug_unpack_codes", "mq_debug_dequant", "mq_status_str"]
 
 
@@ -71,6 +71,7 @@ _sig = {
     "mq_workspace_bytes": (ctypes.c_size_t, [_P, _P, _P, ctypes.c_int32]),
     "moe_layer_forward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P]),
     "mq_rmsnorm": (ctypes.c_int, [_P, _P, ctypes.c_float, _P]),
+    "mq_workspace_errors": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
     "mq_packed_bytes": (ctypes.c_size_t, [ctypes.c_int32] * 5),
     "mq_pool_layout": (ctypes.c_int64, [ctypes.c_int32] * 4 + [ctypes.c_int64, _P]),
     "mq_pack": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
@@ -268,6 +269,14 @@ def moe_layer_forward(layer: DeviceLayer, x: torch.Tensor, out: Optional[torch.T
                                 _ref(layer.shared), ctypes.byref(oa), ctypes.byref(opts), _stream_handle(stream))
     _check(st, "moe_layer_forward")
     return out
+
+
+def workspace_errors(workspace: torch.Tensor, stream=None) -> int:
+    """Sticky error bits of the single-launch path in `workspace` (0: none)."""
+    v = ctypes.c_uint32(0)
+    _check(_lib.mq_workspace_errors(workspace.data_ptr(), workspace.numel(), ctypes.byref(v), _stream_handle(stream)),
+           "mq_workspace_errors")
+    return int(v.value)
 
 
 def rmsnorm(x: torch.Tensor, out: Optional[torch.Tensor] = None, eps: float = 1e-6, stream=None) -> torch.Tensor:

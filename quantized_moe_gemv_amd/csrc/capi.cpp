@@ -48,13 +48,13 @@ FusedCarve fused_carve(const Sizes& z) {
     FusedCarve f;
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
+    f.ctr = take((size_t)3 * kCtrStride * 4);   // c_done, epoch, error flag: first, at fixed offsets
     f.rpart_stride = (int64_t)up((size_t)(z.E + 15) / 16 * 8 * 16 * 8) / 8;
     f.rpart = take((size_t)8 * f.rpart_stride * 8);
     // one copy per XCD of the activations (shared then routed)
     f.h_stride = (int64_t)up(((size_t)z.Is + (size_t)z.k * z.I) * 8 + 8) / 8;
     f.act = take((size_t)8 * f.h_stride * 8);
     f.piece = take((size_t)z.G_H * z.n_src * 64 * 8);
-    f.ctr = take((size_t)3 * kCtrStride * 4);   // c_done, epoch, error flag
     f.fcnt = take((size_t)(kFrontMaxGroups + 1) * 4);   // grouped-path front counters
     f.total = o;
     return f;
@@ -343,6 +343,22 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
         hipLaunchKernelGGL(k_combine, dim3(T, (z.H + 255) / 256), dim3(256), 0, s, p);
     }
     return hipGetLastError() == hipSuccess ? MQ_OK : MQ_ERR_HIP;
+}
+
+extern "C" mq_status mq_workspace_errors(const void* workspace, size_t workspace_bytes, uint32_t* errors,
+                                         void* stream) {
+    if (!workspace || !errors) return MQ_ERR_NULL;
+    if (!aligned(workspace, kAlign)) return MQ_ERR_ALIGN;
+    // the error flag sits at a fixed offset at the start of every workspace
+    const size_t at = 2 * kCtrStride * sizeof(uint32_t);
+    if (workspace_bytes < at + sizeof(uint32_t)) return MQ_ERR_WORKSPACE;
+    (void)hipGetLastError();
+    hipStream_t s = (hipStream_t)stream;
+    if (hipMemcpyAsync(errors, (const uint8_t*)workspace + at, sizeof(uint32_t), hipMemcpyDeviceToHost, s) !=
+            hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return MQ_ERR_HIP;
+    return MQ_OK;
 }
 
 extern "C" mq_status mq_rmsnorm(const mq_act* x, mq_act* out, float eps, void* stream) {

@@ -50,6 +50,15 @@ constexpr int kGroupsD = 2;        // column groups per wave pair and tile of a 
 constexpr int kItemsD = kGroupsD * kTilesD;   // 16-byte code loads per lane of a routed down unit
 constexpr int kRq = kRouterPieces;
 
+// The copy of a broadcast result that this workgroup reads: the one of the
+// XCD it runs on (XCC_ID).  Every copy holds the same words, so the choice
+// only decides which memory channels serve the read.
+__device__ __forceinline__ int xcc_copy() {
+    uint32_t v;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+    return (int)(v & (kCopies - 1));
+}
+
 // ----------------------------------------------------------------- words and counters
 
 __device__ __forceinline__ uint64_t ld_word(const uint64_t* p) {
@@ -413,7 +422,7 @@ __device__ __forceinline__ void stage_token(const Plan& p, Shared& sh, const Tok
 // the scores, ids and weights to the caller's optional outputs.
 __device__ __forceinline__ void fetch_ids(const Plan& p, Shared& sh, uint32_t tag) {
     const int nslice = (p.E + 15) / 16, epad = (p.E + 31) & ~31;
-    gather_words(p.f_rpart + (blockIdx.x % kCopies) * p.rpart_stride, nslice * kRq * 16, tag, p.f_err, sh.gbuf);
+    gather_words(p.f_rpart + xcc_copy() * p.rpart_stride, nslice * kRq * 16, tag, p.f_err, sh.gbuf);
     // workgroup 0 runs the first routed unit, so it always fetches the ids
     const bool reporter = blockIdx.x == 0;
     // Selection key of expert e: the score's bits made order-preserving as an
@@ -624,7 +633,7 @@ __device__ __forceinline__ void run_rh(const Plan& p, Shared& sh, const Unit& x,
 // Shared down piece: one 64-row output tile from one chunk of the shared
 // activations -> partial outputs (source k + chunk).
 __device__ __forceinline__ void run_sd_piece(const Plan& p, Shared& sh, const Unit& x, const Loads& L, uint32_t tag) {
-    stage_h(p, sh, p.f_hs + (blockIdx.x % kCopies) * p.h_stride, x.g0, x.ng, tag);
+    stage_h(p, sh, p.f_hs + xcc_copy() * p.h_stride, x.g0, x.ng, tag);
     const int wave = wave_id(), lane = threadIdx.x & 63, kb = lane >> 4;
     float acc[2] = {0.f, 0.f};    // rows 32*(wave & 1) + 16*r + lane%16 of the output tile
 #pragma unroll
@@ -670,7 +679,7 @@ __device__ __forceinline__ void issue_rdu(const Plan& p, const Shared& sh, const
 // each of its tiles (source = slot).
 __device__ __forceinline__ void run_rdu(const Plan& p, Shared& sh, const DownUnit& d, const LoadsN<kItemsD>& L,
                                         uint32_t tag) {
-    stage_h(p, sh, p.f_h + (blockIdx.x % kCopies) * p.h_stride + (int64_t)d.b * p.I, 0, p.G_I, tag);
+    stage_h(p, sh, p.f_h + xcc_copy() * p.h_stride + (int64_t)d.b * p.I, 0, p.G_I, tag);
     const int wave = wave_id(), lane = threadIdx.x & 63, kb = lane >> 4;
     const float wf = sh.wts[d.b];
     float acc[kTilesD][2];

@@ -53,6 +53,7 @@ def run_gpu(M, dev, x_bits, path="auto", ws=None):
                               logits=lg)
     o16 = M.moe_layer_forward(dev, x, workspace=ws, path=path, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
+    assert M.workspace_errors(ws) == 0, "a bounded wait of the single-launch path gave up"
     return dict(ids=ids.cpu().numpy(), w=w.cpu().numpy(), logits=lg.cpu().numpy(),
                 out32=o32.cpu().numpy().astype(np.float64), out16=bf16_bits(o16))
 

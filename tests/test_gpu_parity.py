@@ -295,6 +295,7 @@ def test_graph_replay_matches_eager(M, tiny, path):
         torch.cuda.synchronize()
         for o, e in zip(outs, eager):
             assert torch.equal(o, e), "replay %d differs from eager" % rep
+    assert M.workspace_errors(ws) == 0
 
 
 def test_fused_many_calls_interleaved(M, decode, tiny):
@@ -316,6 +317,7 @@ def test_fused_many_calls_interleaved(M, decode, tiny):
         if i % 10 == 3:
             M.moe_layer_forward(dev, x8, workspace=ws, path="grouped")
     torch.cuda.synchronize()
+    assert M.workspace_errors(ws) == 0
     rms = float(torch.sqrt(torch.mean(rg.double() ** 2)))
     # the single-launch path hands the GeGLU activations to the down projection
     # as fp16 (relative rounding <= 2^-11); the GEMV path keeps 16 significant bits

@@ -201,3 +201,13 @@ def test_status_strings():
     for st in range(-7, 1):
         assert M.status_str(st) and M.status_str(st) != "unknown status"
     assert M.status_str(-99) == "unknown status"
+
+
+def test_workspace_errors_rejects_bad_arguments():
+    """Argument checks of mq_workspace_errors run before any device access."""
+    v = ctypes.c_uint32(0)
+    lib = M._lib
+    assert lib.mq_workspace_errors(None, 4096, ctypes.byref(v), None) == M.MQ_ERR_NULL
+    assert lib.mq_workspace_errors(256, 4096, None, None) == M.MQ_ERR_NULL
+    assert lib.mq_workspace_errors(256 + 8, 4096, ctypes.byref(v), None) == M.MQ_ERR_ALIGN
+    assert lib.mq_workspace_errors(256, 16, ctypes.byref(v), None) == M.MQ_ERR_WORKSPACE
