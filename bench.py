@@ -20,6 +20,8 @@ a bounded sample of decode tokens.  Prints one JSON line on stdout.
 Profiling helpers (not part of the default run):
   --profile decode       runs decode calls back to back, then a copy kernel of
                          known size, for rocprofv3 counter runs;
+  --profile prefill      runs 128-token prefill calls (Zipf-skewed routing)
+                         back to back, for counter runs on the grouped kernels;
   --traffic-summary F W  turns the FETCH_SIZE / WRITE_SIZE counter CSVs of
                          those runs into the traffic summary under profiles/;
   --stats-summary S J    turns the kernel statistics CSV of a rocprofv3
@@ -194,6 +196,27 @@ def profile_decode(args):
     log("profile run done: %d decode calls, 5 copies of %d B" % (args.steps, COPY_BYTES))
 
 
+def profile_prefill(args):
+    """Back-to-back 128-token prefill calls over the resident layers."""
+    import torch
+    import qmoe_synth as S
+    import quantized_moe_gemv_amd as M
+    torch.cuda.set_device(0)
+    cfg, seed, T = S.CONFIGS["decode"], S.SEEDS["stack30"], 128
+    layers = build_layers(M, S, cfg, seed, args.layers, host_threads())
+    zl = [d.with_logit_bias(torch.from_numpy(S.zipf_logit_bias(seed, l, cfg.num_experts)).cuda())
+          for l, d in enumerate(layers)]
+    nb = max(1, min(args.steps, 2 * len(layers)))
+    xp = torch.from_numpy(S.make_tokens(seed, nb * T, cfg.hidden, batch=2).view(np.int16)).view(torch.bfloat16)
+    xp = xp.cuda().view(nb, T, cfg.hidden)
+    ws = layers[0].new_workspace(T)
+    out = torch.empty((T, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+    for i in range(args.steps):
+        M.moe_layer_forward(zl[i % len(zl)], xp[i % nb], out=out, workspace=ws)
+    torch.cuda.synchronize()
+    log("profile run done: %d prefill calls of %d tokens" % (args.steps, T))
+
+
 def read_counter(path, counter):
     """Per-dispatch values of `counter` for the decode kernel and the copy kernel."""
     dec, cop = [], []
@@ -298,7 +321,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=640)
     ap.add_argument("--path", default="auto", choices=["auto", "fused", "gemv", "grouped"])
-    ap.add_argument("--profile", choices=["decode"])
+    ap.add_argument("--profile", choices=["decode", "prefill"])
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--stats-summary", nargs=2, metavar=("STATS_CSV", "BENCH_JSON"))
     args = ap.parse_args()
@@ -312,8 +335,11 @@ def main():
         print("bench.py measures one GPU: the layer runs on a single MI355X and has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
-    if args.profile:
+    if args.profile == "decode":
         profile_decode(args)
+        return
+    if args.profile == "prefill":
+        profile_prefill(args)
         return
 
     import torch

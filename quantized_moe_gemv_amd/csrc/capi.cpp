@@ -19,7 +19,7 @@ __global__ void k_rmsnorm(const uint16_t* x, int64_t xs, uint16_t* y, int64_t ys
 __global__ void k_debug_read(const uint8_t* data, int rows, int cols, int bits, uint8_t* codes_out, float* w_out);
 __global__ void k_decode(Plan p);
 mq_status launch_grouped(const Plan& p, hipStream_t s);
-bool grouped_ok(int H, int I, int64_t T);
+bool grouped_ok(int H, int I, int64_t T, int rows_per_token);
 }  // namespace mq
 
 using namespace mq;
@@ -94,7 +94,7 @@ int device_cus() {
 // Offsets of every workspace region for up to T tokens; returns the total.
 struct Carve {
     size_t r, rsum8, xsum4, plog, ids, wts, hhi, hlo, hsum, shi, slo, ssum, dpart;
-    size_t x16, counts, offsets, perm, inv, sched, nsched, hg, ysort;
+    size_t x16, xso, counts, offsets, perm, inv, sched, nsched, hg, hso, ysort;
     size_t total;
 };
 
@@ -116,16 +116,18 @@ Carve carve(const Sizes& z, int64_t T) {
     c.ssum = take(T * z.G_s * 16 + 16);
     c.dpart = take(T * kDownSplits * z.H * 4);
     c.x16 = take(T * z.H * 2);
+    c.xso = take(T * z.G_H * 8);
     c.counts = take((size_t)z.E * 4);
     c.offsets = take((size_t)(z.E + 1) * 4);
     c.perm = take(T * z.k * 4);
     c.inv = take(T * z.k * 4);
     // sized for the smallest chunk so that the carve grows with T whatever
     // chunk size set_tiles picks
-    c.sched = take(((size_t)(T * z.k + 31) / 32 + z.E + (size_t)z.n_vs * ((T + 31) / 32)) * 4 + 4);
+    c.sched = take(((size_t)(T * z.k + 31) / 32 + z.E + (size_t)z.n_vs * ((T + 31) / 32)) * 8 + 8);
     c.nsched = take(4);
     const size_t rows = T * (z.k + z.n_vs);
     c.hg = take(rows * z.I * 2);
+    c.hso = take(rows * z.G_I * 8);
     c.ysort = take(rows * z.H * 4);
     c.total = o;
     return c;
@@ -191,7 +193,10 @@ mq_status check_layer(const mq_router* rt, const mq_expert_pool* pool, const mq_
 }
 
 void set_tiles(Sizes* z, int64_t T, bool has_shared) {
-    z->ntile = 128;   // tokens per grouped work item
+    // tokens per grouped work item: 64 up to 1024 tokens, so that no work
+    // item outlasts the call's weight streaming, 128 above (fewer re-reads
+    // of the weights where the matrix cores bound the call)
+    z->ntile = T <= 1024 ? 64 : 128;
     z->n_vs = has_shared ? z->n_sc : 0;
     // every expert may add one partial chunk to the full ones
     const int64_t nch = (T + z->ntile - 1) / z->ntile;
@@ -286,9 +291,10 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
     p.offsets = (int32_t*)(ws + c.offsets);
     p.perm = (int32_t*)(ws + c.perm);
     p.inv = (int32_t*)(ws + c.inv);
-    p.sched = (int32_t*)(ws + c.sched);
+    p.sched = (int2*)(ws + c.sched);
     p.nsched = (int32_t*)(ws + c.nsched);
     p.hg = (_Float16*)(ws + c.hg);
+    p.hso = (float*)(ws + c.hso);
     p.ysort = (float*)(ws + c.ysort);
     p.max_tiles = z.max_tiles;
     p.ntile = z.ntile;
@@ -327,8 +333,11 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
         return hipGetLastError() == hipSuccess ? MQ_OK : MQ_ERR_HIP;
     }
     const bool grouped = opts->path == MQ_PATH_GROUPED || (opts->path == MQ_PATH_AUTO && T > 4);
-    if (grouped && !grouped_ok(z.H, z.I, T)) return MQ_ERR_UNSUPPORTED;
-    if (grouped) p.x16 = (_Float16*)(ws + c.x16);
+    if (grouped && !grouped_ok(z.H, z.I, T, z.k + z.n_vs)) return MQ_ERR_UNSUPPORTED;
+    if (grouped) {
+        p.x16 = (_Float16*)(ws + c.x16);
+        p.xso = (float*)(ws + c.xso);
+    }
 
     if (grouped) {
         st = launch_grouped(p, s);

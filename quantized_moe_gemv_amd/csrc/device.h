@@ -72,6 +72,13 @@ __device__ __forceinline__ uint16_t f32_to_f16(float f) { return __builtin_bit_c
 __device__ __forceinline__ float f16_lo(uint32_t v) { return (float)__builtin_bit_cast(f16x2_t, v)[0]; }
 __device__ __forceinline__ float f16_hi(uint32_t v) { return (float)__builtin_bit_cast(f16x2_t, v)[1]; }
 
+// Sum over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
 // Sum over the four lanes lane%16 + 16*kb (kb = 0..3) of a wave.
 __device__ __forceinline__ float sum_kb(float v) {
     v += __shfl_xor(v, 16, 64);

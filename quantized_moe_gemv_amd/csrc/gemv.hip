@@ -12,11 +12,6 @@
 
 namespace mq {
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
 
 // Per token: scaled router input r = x / sqrt(mean(x^2) + eps) * router_scale / sqrt(H),
 // and the per-lane column sums used by the 8-bit (r) and 4-bit (x) block dots.
@@ -38,7 +33,6 @@ __global__ __launch_bounds__(256) void k_prep(Plan p) {
     for (int i = threadIdx.x; i < p.H; i += 256) {
         float rs = p.router_scale ? p.router_scale[i] : 1.0f;
         r[i] = bf16_to_f32(x[i]) * c * rs;
-        if (p.x16) p.x16[(int64_t)t * p.H + i] = (_Float16)bf16_to_f32(x[i]);
     }
     for (int q = threadIdx.x; q < p.G_H * 4; q += 256) {
         const int g = q >> 2, kb = q & 3;

@@ -1,13 +1,11 @@
 // Grouped path (many tokens per call): token -> expert permutation, grouped
 // dequant-GEMMs on the matrix cores, and the combine.
 //
-// The weight operand of each MFMA is dequantised in registers from one
-// DEV_V1 word per lane: the word holds the eight 4-bit codes of one row and
-// eight consecutive columns, which is exactly the A fragment of
-// v_mfma_f32_16x16x32_f16 for lane (row % 16, column block lane / 16).
-// Codes become fp16 through the exponent trick (0x6400 | q = 1024 + q),
-// then w = s * q + b in fp16 (bounded FP16 staging of dequantised weights,
-// as the staged-affine prefill of the pages does), and accumulation is fp32.
+// One DEV_V1 word per lane holds the eight 4-bit codes of one row and
+// eight consecutive columns, which is exactly a weight fragment of
+// v_mfma_f32_16x16x32_f16 for lane (row % 16, column block lane / 16), as
+// the A operand (D[row][token]) or as the B operand (D[token][row]).
+// Accumulation is fp32 throughout.
 #include "device.h"
 #include "plan.h"
 
@@ -58,23 +56,35 @@ __device__ __forceinline__ int block_scan_total(int* buf, int n, int v, int* exc
 // writes the schedule.  Device-scope fences order the stores before the
 // counter and the loads after it.
 constexpr int kFrontStatic = 16 * 1024;   // bytes of static LDS in k_front (upper bound)
+// Units with at most this many tokens take the code-operand path of the
+// grouped GEMMs, the others the dequantised-weight path for all their
+// chunks: the choice is per unit, so a token's arithmetic does not depend
+// on which chunk of its expert it lands in.
+constexpr int kSmallTokens = 16;
 
-// Schedule entries (unit << 16 | tiles << 8 | chunk), tiles = the chunk's
-// 16-token tiles, heaviest chunks first: the full chunks of every unit (the
-// experts, then the shared expert's virtual experts E .. E+n_vs-1 over all T
-// tokens), then the partial last chunks by decreasing number of tiles.
-// Items are independent, so the order within a class does not matter.
-// cnt: this thread's expert count (thread u < E); every thread calls it.
-__device__ __forceinline__ void build_schedule(const Plan& p, int cnt, int* scan) {
+// Schedule entries, heaviest chunks first: the full chunks of every unit
+// (the experts, then the shared expert's virtual experts E .. E+n_vs-1 over
+// all T tokens), then the partial last chunks by decreasing number of
+// 16-token tiles.  Entry .x = unit << 16 | big << 12 | tiles << 8 | chunk
+// (big: the unit has more than kSmallTokens tokens), .y = first sorted row
+// of the chunk (in hg / ysort) | its token count << 24.  Items are
+// independent, so the order within a class does not matter.
+// cnt, off: this thread's expert count and first sorted row (thread u < E);
+// every thread calls it.
+__device__ __forceinline__ void build_schedule(const Plan& p, int cnt, int off, int* scan) {
     __shared__ int ccount[17], cfill[17];
     const int T = p.T, E = p.E, nu = E + p.n_vs;   // nu <= kMaxExperts + a few <= 1024
     const int u = threadIdx.x;
     const int ucnt = u < E ? cnt : (u < nu ? T : 0);
+    const int row0 = u < E ? off : T * p.k + (u - E) * T;
     const int nfull = ucnt / p.ntile, rem = ucnt - nfull * p.ntile;
     const int cls = rem > 0 ? (rem + 15) / 16 : 0;   // 1 .. ntile / 16
+    const int big = (ucnt > kSmallTokens) << 12;
     int foff;
     const int tfull = block_scan_total(scan, nu, nfull, &foff);
-    for (int c = 0; c < nfull; ++c) p.sched[foff + c] = (u << 16) | ((p.ntile / 16) << 8) | c;
+    for (int c = 0; c < nfull; ++c)
+        p.sched[foff + c] =
+            make_int2((u << 16) | big | ((p.ntile / 16) << 8) | c, (row0 + c * p.ntile) | (p.ntile << 24));
     if (threadIdx.x < 17) ccount[threadIdx.x] = cfill[threadIdx.x] = 0;
     __syncthreads();
     if (cls > 0) atomicAdd(&ccount[cls], 1);
@@ -82,7 +92,8 @@ __device__ __forceinline__ void build_schedule(const Plan& p, int cnt, int* scan
     if (cls > 0) {
         int before = 0;   // partial chunks of heavier classes
         for (int q = cls + 1; q <= 16; ++q) before += ccount[q];
-        p.sched[tfull + before + atomicAdd(&cfill[cls], 1)] = (u << 16) | (cls << 8) | nfull;
+        p.sched[tfull + before + atomicAdd(&cfill[cls], 1)] =
+            make_int2((u << 16) | big | (cls << 8) | nfull, (row0 + nfull * p.ntile) | (rem << 24));
     }
     if (threadIdx.x == 0) {
         int np = 0;
@@ -133,6 +144,11 @@ __global__ __launch_bounds__(1024) void k_front(Plan p) {
             for (int w = 0; w < 16; ++w) t += red[w][tt];
             c[tt] = (1.0f / sqrtf(t / (float)H + p.eps)) * (1.0f / sqrtf((float)H));
         }
+        // x16: the fp16 activation operand of the matrix-core kernels
+        // (columns with i & 2 divided by 16) and xso its per-group pair
+        // (sum of x, -1024 * sum of the stored operand).  Wave w covers
+        // group i / 64 = w + 16 j whole (H is a multiple of 64), so the
+        // bound i < H is the same for all its lanes.
         for (int i = tid; i < H; i += 1024) {
             const float rs = p.router_scale ? p.router_scale[i] : 1.0f;
 #pragma unroll
@@ -140,7 +156,11 @@ __global__ __launch_bounds__(1024) void k_front(Plan p) {
                 if (tt < nt) {
                     const float xv = bf16_to_f32(p.x[(int64_t)(t0 + tt) * p.x_stride + i]);
                     rr[tt * H + i] = xv * c[tt] * rs;
-                    p.x16[(int64_t)(t0 + tt) * H + i] = (_Float16)xv;
+                    const _Float16 xh = (_Float16)xv;
+                    const _Float16 xa = (i & 2) ? xh * (_Float16)0.0625f : xh;
+                    p.x16[(int64_t)(t0 + tt) * H + i] = xa;
+                    const float xs = wave_sum((float)xh), xn = wave_sum(-1024.0f * (float)xa);
+                    if (lane == 0) ((float2*)p.xso)[(int64_t)(t0 + tt) * p.G_H + (i >> 6)] = make_float2(xs, xn);
                 }
         }
     }
@@ -277,47 +297,108 @@ __global__ __launch_bounds__(1024) void k_front(Plan p) {
         p.perm[pos] = q;
         p.inv[q] = pos;
     }
-    build_schedule(p, cnt, scan);
+    build_schedule(p, cnt, off, scan);
 }
 
-// Eight fp16 weights s*q + b from one DEV_V1 4-bit word (column order 0..7).
-__device__ __forceinline__ half8_t dequant8(uint32_t w, half2_t s2, half2_t b2) {
+// ---------------------------------------------------------------------------
+// 4-bit codes on the matrix cores.
+//
+// codes8 turns the eight codes of a DEV_V1 word into eight fp16 operands
+// with four AND-ORs under the fp16 exponent of 1024.0 (0x6400): columns
+// c = 0, 1, 4, 5 of the eight come out as 1024 + q (the code in the low
+// mantissa bits), columns 2, 3, 6, 7 as 1024 + 16 q (the code four bits
+// higher).  Every activation operand of this path (x16, hg) holds the
+// columns with (c & 2) != 0 divided by 16, an exact power-of-two step, so
+// over one group of 64 columns, with a_c the stored activations,
+//     sum_c code_c a_c = sum_c q_c x_c + 1024 sum_c a_c.
+// The group-64 affine dequantisation w = s q + b then gives
+//     sum_c w_c x_c = s (sum_c code_c a_c - 1024 sum_c a_c) + b sum_c x_c.
+// Two ways through a work item use this:
+//  * up to 32 tokens: the codes themselves are the B operand of the MFMAs
+//    (D[token][row]); each group's accumulator starts at -1024 sum_c a_c of
+//    its tokens and the group's scale and bias are applied once per output
+//    in fp32 (one VALU operation per two weights for the codes instead of
+//    five for dequantised fp16 weights);
+//  * more tokens: the weights are dequantised to fp16 once per workgroup as
+//    s (code - 1024) + b, with 16 b for the scaled columns (16 (s q + b)
+//    rounds exactly as s q + b does), and shared by all token tiles.
+// Per token and group the front kernel stores (sum_c x_c, -1024 sum_c a_c)
+// of the layer input in xso; the gate/up kernel stores the same pair of
+// every GeGLU row and 64-column group in hso for the down projection.
+//
+// (a & m) | c in one VOP3 operation.  Left to itself the compiler uses two
+// VOP2 operations with literal constants (gfx9 VOP3 takes no literal); here
+// the mask comes from a scalar register and the exponent pattern from a
+// vector register (one scalar operand per VOP3 on gfx9).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
+    return r;
+}
+
+__device__ __forceinline__ half8_t codes8(uint32_t w) {
+    const uint32_t t = w >> 8, e = 0x64006400u;
+    u32x4_t v;
+    v[0] = and_or(w, 0x000F000Fu, e);
+    v[1] = and_or(w, 0x00F000F0u, e);
+    v[2] = and_or(t, 0x000F000Fu, e);
+    v[3] = and_or(t, 0x00F000F0u, e);
+    return __builtin_bit_cast(half8_t, v);
+}
+
+// fp16 scale and bias of a (scale | bias << 16) bf16 pair, and 16 * bias.
+struct Sb16 {
+    half2_t s, b, b16;
+};
+__device__ __forceinline__ Sb16 sb16(uint32_t pr) {
+    const _Float16 s = (_Float16)bf16_lo(pr), b = (_Float16)bf16_hi(pr);
+    const _Float16 b16 = b * (_Float16)16.0f;
+    return {(half2_t){s, s}, (half2_t){b, b}, (half2_t){b16, b16}};
+}
+
+// Dequantised fp16 weights of one word, scaled columns times 16.
+__device__ __forceinline__ half8_t dequant8s(uint32_t w, const Sb16& k) {
+    const half8_t c = codes8(w);
+    const half2_t off = {(_Float16)1024.0f, (_Float16)1024.0f};
     half8_t r;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        const uint32_t v = ((w >> (4 * m)) & 0x000F000Fu) | 0x64006400u;  // 1024 + q, two lanes
-        half2_t q = __builtin_bit_cast(half2_t, v) - (half2_t){(_Float16)1024.0f, (_Float16)1024.0f};
-        half2_t d = q * s2 + b2;
+        const half2_t q = (half2_t){c[2 * m], c[2 * m + 1]} - off;
+        const half2_t d = q * k.s + ((m & 1) ? k.b16 : k.b);
         r[2 * m] = d[0];
         r[2 * m + 1] = d[1];
     }
     return r;
 }
 
-__device__ __forceinline__ void sb_half2(uint32_t pr, half2_t* s2, half2_t* b2) {
-    const _Float16 s = (_Float16)bf16_lo(pr), b = (_Float16)bf16_hi(pr);
-    *s2 = (half2_t){s, s};
-    *b2 = (half2_t){b, b};
+// Stored activation and its group-sum pair of one GeGLU value h of column c.
+__device__ __forceinline__ _Float16 act_store(_Float16 h, int c) { return (c & 2) ? h * (_Float16)0.0625f : h; }
+
+// Sums over the 16 lanes lane / 16 * 16 + 0..15 of a wave.
+__device__ __forceinline__ float sum16(float v) {
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    v += __shfl_xor(v, 4, 64);
+    v += __shfl_xor(v, 8, 64);
+    return v;
 }
 
 // Grouped dequant-GEMM.  A work item is (64-row tile of one matrix, chunk
 // of up to p.ntile = 128 tokens of one expert); for the down projection a
 // workgroup takes kDnTiles consecutive row tiles of the item.  The shared
-// expert takes part as n_sc virtual experts of I rows each (its gate/up
+// expert takes part as n_vs virtual experts of I rows each (its gate/up
 // rows, and the matching column slices of its down projection), applied to
 // every token with weight 1, so it fills the machine together with the
 // routed work.  The schedule puts the heaviest chunks first.
 //
-// Two ways through an item, by its token count:
-//  * up to 32 tokens, the loop is bound by load latency: the four waves
-//    split the column groups (gate/up) or own 16 rows each over an operand
-//    staged once (down), keep several groups of weights in flight and take
-//    no workgroup barrier;
-//  * more tokens: the token operand is staged in LDS a batch of column
-//    groups at a time for the whole chunk, and each dequantised weight
-//    fragment feeds the MFMAs of all the chunk's 16-token tiles (wave ms
-//    owns rows 16 ms .. 16 ms + 15 of the tile).
-constexpr int kBigKB = 4;                     // most column groups per staged batch (gate/up)
+// Up to 32 tokens the loop is bound by load latency: the four waves split
+// the column groups (gate/up) or own 16 rows each over an operand staged
+// once (down), keep several groups of weights in flight and take no
+// workgroup barrier in the loop.  With more tokens the token operand is
+// staged in LDS a batch of column groups at a time for the whole chunk, and
+// each dequantised weight fragment feeds the MFMAs of all the chunk's
+// 16-token tiles (wave ms owns rows 16 ms .. 16 ms + 15 of the tile).
+constexpr int kBigKB = 2;                     // column groups per staged batch (gate/up)
 constexpr int kDnKB = 2;                      // column groups per staged batch (down)
 constexpr int kDnTiles = 4;                   // 64-row output tiles per down workgroup
 
@@ -377,8 +458,8 @@ __device__ __forceinline__ void x_store(const XLoads<NTT, KB>& X, _Float16 (*xs)
         *(u32x4_t*)&xs[threadIdx.x / (8 * KB) + (32 / KB) * i][q * 8] = X.v[i];
 }
 
-template <int NM, int NTT, int KB, int P>
-__device__ __forceinline__ void w_mma(const WLoads<NM, KB>& L, _Float16 (*xs)[P], float4_t (*acc)[8], int lane,
+template <int NM, int NTT, int KB, int P, int MT>
+__device__ __forceinline__ void w_mma(const WLoads<NM, KB>& L, _Float16 (*xs)[P], float4_t (*acc)[MT], int lane,
                                       int g0, int G) {
     const int kb = lane >> 4, n = lane & 15;
 #pragma unroll
@@ -386,10 +467,9 @@ __device__ __forceinline__ void w_mma(const WLoads<NM, KB>& L, _Float16 (*xs)[P]
         half8_t a0[NM], a1[NM];
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-            half2_t s2, b2;
-            sb_half2(g0 + u < G ? L.s[m][u] : 0u, &s2, &b2);
-            a0[m] = dequant8(L.c[m][u].x, s2, b2);
-            a1[m] = dequant8(L.c[m][u].y, s2, b2);
+            const Sb16 k = sb16(g0 + u < G ? L.s[m][u] : 0u);
+            a0[m] = dequant8s(L.c[m][u].x, k);
+            a1[m] = dequant8s(L.c[m][u].y, k);
         }
 #pragma unroll
         for (int t = 0; t < NTT; ++t) {
@@ -406,12 +486,12 @@ __device__ __forceinline__ void w_mma(const WLoads<NM, KB>& L, _Float16 (*xs)[P]
 
 // One row tile of a staged item over all G column groups: acc[m][t] holds
 // rows 16 ms + 4 (lane / 16) + i, token 16 t + lane % 16 of matrix m.
-// KBM is the widest batch the LDS rows hold; NTT > 4 halves the batch to
-// keep the prefetched token rows within the register budget.
-template <int NM, int NTT, int KBM>
+// KB column groups per batch; NTT > 4 halves the batch to keep the
+// prefetched token rows within the register budget.
+template <int NM, int NTT, int KBM, int MT>
 __device__ __forceinline__ void gg_tile_n(const uint8_t* const* tiles, int G, const _Float16* src, int64_t stride,
                                           const int* rows, int count, _Float16 (*xs)[pitch_of<KBM>()],
-                                          float4_t (*acc)[8]) {
+                                          float4_t (*acc)[MT]) {
     constexpr int KB = NTT <= 4 ? KBM : (KBM < 2 ? KBM : 2);
     const int ms = wave_id(), lane = threadIdx.x & 63;
     const uint8_t* wbase[NM];
@@ -435,7 +515,7 @@ __device__ __forceinline__ void gg_tile_n(const uint8_t* const* tiles, int G, co
         x_load(X, src, stride, rows, count, g0 + KB, G);
         w_load(B, wbase, sbase, g0 + KB, G);
         __builtin_amdgcn_sched_barrier(0);
-        w_mma<NM, NTT, KB>(A, xs, acc, lane, g0, G);
+        w_mma<NM, NTT, KB, pitch_of<KBM>(), MT>(A, xs, acc, lane, g0, G);
         __syncthreads();
         if (g0 + KB >= G) break;
         x_store(X, xs);
@@ -444,32 +524,41 @@ __device__ __forceinline__ void gg_tile_n(const uint8_t* const* tiles, int G, co
         x_load(X, src, stride, rows, count, g0 + 2 * KB, G);
         w_load(A, wbase, sbase, g0 + 2 * KB, G);
         __builtin_amdgcn_sched_barrier(0);
-        w_mma<NM, NTT, KB>(B, xs, acc, lane, g0 + KB, G);
+        w_mma<NM, NTT, KB, pitch_of<KBM>(), MT>(B, xs, acc, lane, g0 + KB, G);
         __syncthreads();
         if (g0 + 2 * KB >= G) break;
     }
 }
 
-// Dispatch on the chunk's 16-token tiles (3 .. 8) so that every MFMA
+// Dispatch on the chunk's 16-token tiles (1 .. MT) so that every MFMA
 // sequence is straight-line code.
-template <int NM, int KBM>
+template <int NM, int KBM, int MT>
 __device__ __forceinline__ void gg_tile(const uint8_t* const* tiles, int G, const _Float16* src, int64_t stride,
                                         const int* rows, int count, _Float16 (*xs)[pitch_of<KBM>()],
-                                        float4_t (*acc)[8]) {
+                                        float4_t (*acc)[MT]) {
     switch ((count + 15) / 16) {
-        case 3: gg_tile_n<NM, 3, KBM>(tiles, G, src, stride, rows, count, xs, acc); break;
-        case 4: gg_tile_n<NM, 4, KBM>(tiles, G, src, stride, rows, count, xs, acc); break;
-        case 5: gg_tile_n<NM, 5, KBM>(tiles, G, src, stride, rows, count, xs, acc); break;
-        case 6: gg_tile_n<NM, 6, KBM>(tiles, G, src, stride, rows, count, xs, acc); break;
-        case 7: gg_tile_n<NM, 7, KBM>(tiles, G, src, stride, rows, count, xs, acc); break;
-        default: gg_tile_n<NM, 8, KBM>(tiles, G, src, stride, rows, count, xs, acc); break;
+        case 1: gg_tile_n<NM, 1, KBM, MT>(tiles, G, src, stride, rows, count, xs, acc); break;
+        case 2: gg_tile_n<NM, 2, KBM, MT>(tiles, G, src, stride, rows, count, xs, acc); break;
+        case 3: gg_tile_n<NM, 3, KBM, MT>(tiles, G, src, stride, rows, count, xs, acc); break;
+        default:
+            if constexpr (MT <= 4) {
+                gg_tile_n<NM, 4, KBM, MT>(tiles, G, src, stride, rows, count, xs, acc);
+            } else {
+                switch ((count + 15) / 16) {
+                    case 4: gg_tile_n<NM, 4, KBM, MT>(tiles, G, src, stride, rows, count, xs, acc); break;
+                    case 5: gg_tile_n<NM, 5, KBM, MT>(tiles, G, src, stride, rows, count, xs, acc); break;
+                    case 6: gg_tile_n<NM, 6, KBM, MT>(tiles, G, src, stride, rows, count, xs, acc); break;
+                    case 7: gg_tile_n<NM, 7, KBM, MT>(tiles, G, src, stride, rows, count, xs, acc); break;
+                    default: gg_tile_n<NM, 8, KBM, MT>(tiles, G, src, stride, rows, count, xs, acc); break;
+                }
+            }
     }
 }
 
-// The work item of this workgroup: blockIdx.y indexes the schedule
-// (expert << 16 | tiles << 8 | chunk).  Experts E .. E+n_vs-1 are the shared expert's
-// virtual experts.
+// The work item of this workgroup: blockIdx.y indexes the schedule.
+// Experts E .. E+n_vs-1 are the shared expert's virtual experts.
 struct Item {
+    int big;            // the unit takes the dequantised-weight path
     int ntt;            // 16-token tiles of the chunk
     int count;          // tokens of the chunk
     int pos0;           // row of chunk token 0 in hg / ysort
@@ -480,17 +569,19 @@ struct Item {
     const uint8_t* w[2];
 };
 
-// The matrices of the item's row tile rt, from the schedule entry alone, so
-// that weight loads can start before the token bookkeeping arrives.
-// Returns false when the workgroup has nothing to do.
-__device__ __forceinline__ bool gg_weights(const Plan& p, bool down, int rt, Item* it) {
+// The matrices of the item's row tile rt and its tokens, from the schedule
+// entry alone.  Returns false when the workgroup has nothing to do.
+__device__ __forceinline__ bool gg_item(const Plan& p, bool down, int rt, Item* it) {
     if ((int)blockIdx.y >= *p.nsched) return false;
-    const int sc = p.sched[blockIdx.y], ex = sc >> 16, c = sc & 0xFF;
-    it->ntt = (sc >> 8) & 0xFF;
-    it->tok0 = c;   // chunk index until gg_tokens
+    const int2 sc = p.sched[blockIdx.y];
+    const int ex = sc.x >> 16, c = sc.x & 0xFF;
+    it->big = (sc.x >> 12) & 1;
+    it->ntt = (sc.x >> 8) & 0xF;
+    it->pos0 = sc.y & 0xFFFFFF;
+    it->count = (int)((uint32_t)sc.y >> 24);
+    it->tok0 = c * p.ntile;
     if (ex < p.E) {
         it->shared = 0;
-        it->pos0 = ex;   // expert until gg_tokens
         const uint8_t* base = p.pool_base + (int64_t)ex * p.expert_stride;
         if (down) {
             it->G = p.G_I;
@@ -505,7 +596,6 @@ __device__ __forceinline__ bool gg_weights(const Plan& p, bool down, int rt, Ite
     } else {
         const int j = ex - p.E;
         it->shared = 1;
-        it->pos0 = j;    // virtual expert until gg_tokens
         if (down) {
             it->G = min(p.G_I, p.G_s - j * p.G_I);
             it->rstride = (int64_t)p.G_s * kBlk4;
@@ -521,34 +611,60 @@ __device__ __forceinline__ bool gg_weights(const Plan& p, bool down, int rt, Ite
     return true;
 }
 
-// The chunk's tokens: count, first sorted position and (shared) first token.
-__device__ __forceinline__ void gg_tokens(const Plan& p, Item* it) {
-    const int c = it->tok0;
-    if (!it->shared) {
-        const int ex = it->pos0;
-        const int first = p.offsets[ex] + c * p.ntile;
-        it->count = min(p.ntile, p.offsets[ex + 1] - first);
-        it->pos0 = first;
-        it->tok0 = 0;
-    } else {
-        const int j = it->pos0;
-        it->tok0 = c * p.ntile;
-        it->count = min(p.ntile, p.T - it->tok0);
-        it->pos0 = p.T * p.k + j * p.T + it->tok0;
+// Token of chunk position n (clamped to the chunk).
+__device__ __forceinline__ int item_token(const Plan& p, const Item& it, int n) {
+    n = min(n, it.count - 1);
+    return it.shared ? it.tok0 + n : p.perm[it.pos0 + n] / p.k;
+}
+
+// LDS copies tsum[g][n], tneg[g][n] (pitch 32) of the (sum, -1024 sum)
+// pairs src[row][g] (ld pairs per row) of chunk slots n < nslot, for G
+// groups; thread tid takes slot tid % 32 and groups tid / 32 + 8 i, with
+// the loads of six groups in flight.  No barrier inside.
+__device__ __forceinline__ void stage_sums(const float2* src, int ld, int row, int G, int nslot, float* tsum,
+                                           float* tneg) {
+    const int n = threadIdx.x & 31;
+    if (n >= nslot) return;
+    constexpr int kB = 6;
+    for (int g0 = threadIdx.x >> 5; g0 < G; g0 += 8 * kB) {
+        float2 v[kB];
+#pragma unroll
+        for (int i = 0; i < kB; ++i) v[i] = src[(int64_t)row * ld + min(g0 + 8 * i, G - 1)];
+#pragma unroll
+        for (int i = 0; i < kB; ++i)
+            if (g0 + 8 * i < G) {
+                tsum[(g0 + 8 * i) * 32 + n] = v[i].x;
+                tneg[(g0 + 8 * i) * 32 + n] = v[i].y;
+            }
     }
 }
 
-// ---- gate/up, up to 32 tokens: the four waves split the column groups
-// (wave w takes groups w, w+4, ...) over all 64 rows of the tile, so each
-// wave loads only its own token fragments, straight into registers; the
-// partial sums meet in LDS at the end.
+// The (sum, -1024 sum) pair of the chunk's GeGLU rows over the tile's 64
+// columns: part[w][n] holds wave w's share for chunk token n.
+__device__ __forceinline__ void write_hso(const Plan& p, const Item& it, int rt, const float2 (*part)[128]) {
+    const int n = threadIdx.x;
+    if (n < it.count) {
+        float2 v = part[0][n];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) {
+            v.x += part[w][n].x;
+            v.y += part[w][n].y;
+        }
+        ((float2*)p.hso)[(int64_t)(it.pos0 + n) * p.G_I + rt] = v;
+    }
+}
+
+// ---- gate/up, up to 32 tokens: codes as the B operand (D[token][row]); the
+// four waves split the column groups (wave w takes groups w, w+4, ...) over
+// all 64 rows of the tile, each loading its own token fragments straight
+// into registers; the partial sums meet in LDS at the end.
 struct GuW {
     u32x4_t c[2][2];     // [matrix][row-block pair]: codes, lane's 16 bytes of each half block
     u32x4_t s[2];        // [matrix]: scale|bias of row lane % 16 in each of the four row blocks
 };
 template <int NTT>
 struct GuX {
-    half8_t x[NTT][2];   // token fragments: columns 8 (lane / 16) .. +7 and 32 + that
+    half8_t x[NTT][2];   // A operand: token 16 t + lane % 16, columns 8 (lane / 16) .. +7 and 32 + that
 };
 
 __device__ __forceinline__ void gu_wload(GuW& L, const uint8_t* w0, const uint8_t* w1, int g, int lane) {
@@ -571,49 +687,64 @@ __device__ __forceinline__ void gu_xload(GuX<NTT>& X, const _Float16* x16, const
     }
 }
 
-// One fragment is dequantised at a time (sched_barrier keeps the compiler
-// from hoisting all eight), which bounds the registers they take.
+// out[m][rb][t][i]: token 16 t + 4 (lane / 16) + i, row 16 rb + lane % 16 of
+// matrix m.  tsum / tneg: the chunk's staged group constants.  A group past
+// the wave's last (valid false) re-reads group G-1 and weighs zero, which
+// keeps the loop body free of branches: a conditional multiply splits the
+// live ranges of the prefetch buffers, and the copies the compiler then
+// makes wait for every load in flight.
 template <int NTT>
-__device__ __forceinline__ void gu_mma(const GuW& L, const GuX<NTT>& X, float4_t (*acc)[4][NTT]) {
+__device__ __forceinline__ void gu_mma(const GuW& L, const GuX<NTT>& X, const float* tsum, const float* tneg, int g,
+                                       bool valid, float4_t (*out)[4][NTT], int lane) {
+    float4_t neg[NTT], sum[NTT];
+#pragma unroll
+    for (int t = 0; t < NTT; ++t) {
+        neg[t] = *(const float4_t*)&tneg[g * 32 + 16 * t + 4 * (lane >> 4)];
+        sum[t] = *(const float4_t*)&tsum[g * 32 + 16 * t + 4 * (lane >> 4)];
+    }
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
-            __builtin_amdgcn_sched_barrier(0);
-            half2_t s2, b2;
-            sb_half2(L.s[m][rb], &s2, &b2);
-            const half8_t a0 = dequant8(L.c[m][rb >> 1][2 * (rb & 1)], s2, b2);
-            const half8_t a1 = dequant8(L.c[m][rb >> 1][2 * (rb & 1) + 1], s2, b2);
+            const uint32_t pr = valid ? L.s[m][rb] : 0u;
+            const float s = bf16_lo(pr), b = bf16_hi(pr);
+            const half8_t q0 = codes8(L.c[m][rb >> 1][2 * (rb & 1)]);
+            const half8_t q1 = codes8(L.c[m][rb >> 1][2 * (rb & 1) + 1]);
 #pragma unroll
             for (int t = 0; t < NTT; ++t) {
-                acc[m][rb][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, X.x[t][0], acc[m][rb][t], 0, 0, 0);
-                acc[m][rb][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, X.x[t][1], acc[m][rb][t], 0, 0, 0);
+                float4_t a = __builtin_amdgcn_mfma_f32_16x16x32_f16(X.x[t][0], q0, neg[t], 0, 0, 0);
+                a = __builtin_amdgcn_mfma_f32_16x16x32_f16(X.x[t][1], q1, a, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) out[m][rb][t][i] = fmaf(s, a[i], fmaf(b, sum[t][i], out[m][rb][t][i]));
             }
         }
 }
 
-typedef float4_t GuRed[4][3][2][2][64];   // [row block][other wave][matrix][tile][lane]
+typedef float4_t GuRed[4][3][2][64];   // [row block][other wave][matrix][lane], one token tile
 
 // The wave's groups are w + 4 j, j < nj; WA and WB hold the weights of
 // j = 0 and 1, loaded before the token bookkeeping.  sched_barrier pins each
 // refill right after the multiply that frees its registers, so the next
 // groups stay in flight behind the one in use: two of them for one token
 // tile, one for two (register budget).  Prefetch past the end re-reads the
-// last group; the loops have one exit, a multiply past the end is skipped.
+// last group; the loops have one exit, a multiply past the end weighs zero.
 template <int NTT>
-__device__ __forceinline__ void gu_small_n(const Plan& p, const Item& it, GuW& WA, GuW& WB, GuRed& red) {
+__device__ __forceinline__ void gu_small_n(const Plan& p, const Item& it, GuW& WA, GuW& WB, char* lds,
+                                           float2 (*hpart)[128]) {
     const int w = wave_id(), lane = threadIdx.x & 63;
     const _Float16* x16 = p.x16;
+    float* tsum = (float*)lds;            // [G][32]
+    float* tneg = tsum + it.G * 32;       // [G][32]
     int xr[NTT];
 #pragma unroll
-    for (int t = 0; t < NTT; ++t) {
-        const int n = min(16 * t + (lane & 15), it.count - 1);
-        const int tok = it.shared ? it.tok0 + n : p.perm[it.pos0 + n] / p.k;
-        xr[t] = tok * p.H + 8 * (lane >> 4);
-    }
+    for (int t = 0; t < NTT; ++t) xr[t] = item_token(p, it, 16 * t + (lane & 15)) * p.H + 8 * (lane >> 4);
     const int G = it.G, nj = (G - w + 3) / 4;
     auto grp = [&](int j) { return min(w + 4 * j, G - 1); };
     const uint8_t *w0 = it.w[0], *w1 = it.w[1];
+    GuX<NTT> XA, XB;
+    gu_xload(XA, x16, xr, grp(0));
+    gu_xload(XB, x16, xr, grp(1));
+    stage_sums((const float2*)p.xso, p.G_H, item_token(p, it, threadIdx.x & 31), G, 16 * NTT, tsum, tneg);
     float4_t acc[2][4][NTT];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
@@ -621,18 +752,16 @@ __device__ __forceinline__ void gu_small_n(const Plan& p, const Item& it, GuW& W
         for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
             for (int t = 0; t < NTT; ++t) acc[m][rb][t] = (float4_t){0.f, 0.f, 0.f, 0.f};
-    GuX<NTT> XA, XB;
-    gu_xload(XA, x16, xr, grp(0));
-    gu_xload(XB, x16, xr, grp(1));
+    __syncthreads();
     if constexpr (NTT >= 2) {
         for (int j = 0; j < nj; j += 2) {
             __builtin_amdgcn_sched_barrier(0);
-            gu_mma<NTT>(WA, XA, acc);
+            gu_mma<NTT>(WA, XA, tsum, tneg, grp(j), true, acc, lane);
             __builtin_amdgcn_sched_barrier(0);
             gu_wload(WA, w0, w1, grp(j + 2), lane);
             gu_xload(XA, x16, xr, grp(j + 2));
             __builtin_amdgcn_sched_barrier(0);
-            if (j + 1 < nj) gu_mma<NTT>(WB, XB, acc);
+            gu_mma<NTT>(WB, XB, tsum, tneg, grp(j + 1), j + 1 < nj, acc, lane);
             __builtin_amdgcn_sched_barrier(0);
             gu_wload(WB, w0, w1, grp(j + 3), lane);
             gu_xload(XB, x16, xr, grp(j + 3));
@@ -644,104 +773,130 @@ __device__ __forceinline__ void gu_small_n(const Plan& p, const Item& it, GuW& W
         gu_xload(XC, x16, xr, grp(2));
         for (int j = 0; j < nj; j += 3) {
             __builtin_amdgcn_sched_barrier(0);
-            gu_mma<NTT>(WA, XA, acc);
+            gu_mma<NTT>(WA, XA, tsum, tneg, grp(j), true, acc, lane);
             __builtin_amdgcn_sched_barrier(0);
             gu_wload(WA, w0, w1, grp(j + 3), lane);
             gu_xload(XA, x16, xr, grp(j + 3));
             __builtin_amdgcn_sched_barrier(0);
-            if (j + 1 < nj) gu_mma<NTT>(WB, XB, acc);
+            gu_mma<NTT>(WB, XB, tsum, tneg, grp(j + 1), j + 1 < nj, acc, lane);
             __builtin_amdgcn_sched_barrier(0);
             gu_wload(WB, w0, w1, grp(j + 4), lane);
             gu_xload(XB, x16, xr, grp(j + 4));
             __builtin_amdgcn_sched_barrier(0);
-            if (j + 2 < nj) gu_mma<NTT>(WC, XC, acc);
+            gu_mma<NTT>(WC, XC, tsum, tneg, grp(j + 2), j + 2 < nj, acc, lane);
             __builtin_amdgcn_sched_barrier(0);
             gu_wload(WC, w0, w1, grp(j + 5), lane);
             gu_xload(XC, x16, xr, grp(j + 5));
         }
     }
-    // wave w sums row block w over the four waves (fixed order: own, then the others by wave)
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-        if (rb != w)
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-#pragma unroll
-                for (int t = 0; t < NTT; ++t) red[rb][w < rb ? w : w - 1][m][t][lane] = acc[m][rb][t];
-    __syncthreads();
-    const int r0 = blockIdx.x * 64 + 16 * w + 4 * (lane >> 4);
+    // wave w sums row block w over the four waves (fixed order: own, then
+    // the others by wave), one token tile at a time; the buffer takes the
+    // place of the staged constants, so the first barrier also waits for
+    // every wave's last multiply
+    GuRed& red = *(GuRed*)lds;
+    const int c = blockIdx.x * 64 + 16 * w + (lane & 15);   // GeGLU column of this lane
 #pragma unroll
     for (int t = 0; t < NTT; ++t) {
+        __syncthreads();
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+            if (rb != w)
+#pragma unroll
+                for (int m = 0; m < 2; ++m) red[rb][w < rb ? w : w - 1][m][lane] = acc[m][rb][t];
+        __syncthreads();
         float4_t v[2];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             float4_t a = w == 0 ? acc[m][0][t] : w == 1 ? acc[m][1][t] : w == 2 ? acc[m][2][t] : acc[m][3][t];
 #pragma unroll
-            for (int q = 0; q < 3; ++q) a += red[w][q][m][t][lane];
+            for (int q = 0; q < 3; ++q) a += red[w][q][m][lane];
             v[m] = a;
         }
-        const int n = 16 * t + (lane & 15);
-        if (n < it.count) {
-            _Float16* dst = p.hg + (int64_t)(it.pos0 + n) * p.I + r0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[i] = (_Float16)(gelu_tanh(v[0][i]) * v[1][i]);
+        for (int i = 0; i < 4; ++i) {
+            const int n = 16 * t + 4 * (lane >> 4) + i;
+            const _Float16 h = (_Float16)(gelu_tanh(v[0][i]) * v[1][i]);
+            const _Float16 a = act_store(h, c);
+            if (n < it.count) p.hg[(int64_t)(it.pos0 + n) * p.I + c] = a;
+            const float hs = sum16((float)h), hn = sum16(-1024.0f * (float)a);
+            if ((lane & 15) == 0) hpart[w][n] = make_float2(hs, hn);
         }
     }
+    __syncthreads();
+    write_hso(p, it, blockIdx.x, hpart);
 }
 
-// ---- gate/up, more than 32 tokens: x staged in LDS for the whole chunk.
-typedef _Float16 GuXs[128][pitch_of<kBigKB>()];
+// ---- gate/up, units of more than kSmallTokens tokens: x staged in LDS for
+// the whole chunk of up to 16 MT tokens.
+template <int MT>
+using GuXs = _Float16[16 * MT][pitch_of<kBigKB>()];
 
-__device__ __forceinline__ void gu_big(const Plan& p, const Item& it, GuXs& xs, int* rows) {
+template <int MT>
+__device__ __forceinline__ void gu_big(const Plan& p, const Item& it, GuXs<MT>& xs, int* rows,
+                                       float2 (*hpart)[128]) {
     const int wave = wave_id(), lane = threadIdx.x & 63;
-    if ((int)threadIdx.x < it.count)
-        rows[threadIdx.x] = it.shared ? it.tok0 + threadIdx.x : p.perm[it.pos0 + threadIdx.x] / p.k;
+    if ((int)threadIdx.x < it.count) rows[threadIdx.x] = item_token(p, it, threadIdx.x);
     __syncthreads();
-    float4_t acc[2][8];
+    float4_t acc[2][MT];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int t = 0; t < 8; ++t) acc[m][t] = (float4_t){0.f, 0.f, 0.f, 0.f};
-    gg_tile<2, kBigKB>(it.w, it.G, p.x16, p.H, rows, it.count, xs, acc);
+        for (int t = 0; t < MT; ++t) acc[m][t] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    gg_tile<2, kBigKB, MT>(it.w, it.G, p.x16, p.H, rows, it.count, xs, acc);
+    // rows r0 + i of the GeGLU output; (r0 + i) & 2 == i & 2
     const int r0 = blockIdx.x * 64 + 16 * wave + 4 * (lane >> 4);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < MT; ++t) {
         const int n = 16 * t + (lane & 15);
+        _Float16 h[4], a[4];
+        float hs = 0.f, hn = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            h[i] = (_Float16)(gelu_tanh(acc[0][t][i]) * acc[1][t][i]);
+            a[i] = act_store(h[i], i);
+            hs += (float)h[i];
+            hn += -1024.0f * (float)a[i];
+        }
         if (n < it.count) {
             _Float16* dst = p.hg + (int64_t)(it.pos0 + n) * p.I + r0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[i] = (_Float16)(gelu_tanh(acc[0][t][i]) * acc[1][t][i]);
+            for (int i = 0; i < 4; ++i) dst[i] = a[i];
         }
+        hs = sum_kb(hs);
+        hn = sum_kb(hn);
+        if (lane < 16) hpart[wave][n] = make_float2(hs, hn);
     }
+    __syncthreads();
+    write_hso(p, it, blockIdx.x, hpart);
 }
 
-// Gate/up + GeGLU: hg[pos] = gelu(gate x) * (up x) in fp16.
-// grid (I / 64, max_tiles), block 256.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gu(Plan p) {
-    constexpr size_t kLds = sizeof(GuXs) > sizeof(GuRed) ? sizeof(GuXs) : sizeof(GuRed);
-    __shared__ __attribute__((aligned(16))) char lds[kLds];
+// Gate/up + GeGLU: hg[pos] = gelu(gate x) * (up x) in fp16 (scaled
+// columns divided by 16), hso[pos][tile] its group sums.  MT: most 16-token
+// tiles of a chunk; chunks of up to 64 tokens leave room for three waves per
+// SIMD.  grid (I / 64, max_tiles), block 256, dynamic LDS gu_lds_bytes.
+template <int MT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT <= 4 ? 3 : 2))) void k_gu(Plan p) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    __shared__ float2 hpart[4][128];
     __shared__ int rows[128];
     Item it;
-    if (!gg_weights(p, false, blockIdx.x, &it)) return;
+    if (!gg_item(p, false, blockIdx.x, &it)) return;
     const int w = wave_id(), lane = threadIdx.x & 63;
-    if (it.ntt > 2) {
-        gg_tokens(p, &it);
-        gu_big(p, it, *(GuXs*)lds, rows);
+    if (it.big) {
+        gu_big<MT>(p, it, *(GuXs<MT>*)lds, rows, hpart);
         return;
     }
     // first weights, in flight while the tokens arrive
     GuW WA, WB;
     gu_wload(WA, it.w[0], it.w[1], min(w, it.G - 1), lane);
     gu_wload(WB, it.w[0], it.w[1], min(w + 4, it.G - 1), lane);
-    gg_tokens(p, &it);
-    if (it.ntt == 1) gu_small_n<1>(p, it, WA, WB, *(GuRed*)lds);
-    else gu_small_n<2>(p, it, WA, WB, *(GuRed*)lds);
+    gu_small_n<1>(p, it, WA, WB, lds, hpart);
 }
 
-// ---- down, up to 32 tokens: the chunk's GeGLU rows are staged in LDS once;
-// the workgroup then runs over its kDnTiles output tiles with no further
-// barrier, each wave keeping three batches of four column groups of
-// weights in flight.
+// ---- down, up to 32 tokens: the chunk's GeGLU rows and group constants
+// are staged in LDS once; the workgroup then runs over its kDnTiles output
+// tiles with no further barrier, each wave keeping three batches of four
+// column groups of weights in flight.
 constexpr int kSmKB = 4;
 
 struct DnLoads {
@@ -761,24 +916,29 @@ __device__ __forceinline__ void dn_load(DnLoads& L, const uint8_t* wb, const uin
     }
 }
 
-// Batch of groups g0 .. g0+kSmKB-1; a group past the end (zero weights)
-// reads the staged columns of group G-1, which hold finite values.
+// Batch of groups g0 .. g0+kSmKB-1; a group past the end (zero scale and
+// bias) reads the staged columns and constants of group G-1, which hold
+// finite values.  acc[t][i]: token 16 t + 4 (lane / 16) + i, row lane % 16
+// of the wave's row block.
 template <int NTT>
-__device__ __forceinline__ void dn_mma(const DnLoads& L, const _Float16* hs, int pitch, int g0, int G, float4_t* acc,
-                                       int lane) {
+__device__ __forceinline__ void dn_mma(const DnLoads& L, const _Float16* hs, int pitch, const float* tsum,
+                                       const float* tneg, int g0, int G, float4_t* acc, int lane) {
     const int kb = lane >> 4, n = lane & 15;
 #pragma unroll
     for (int u = 0; u < kSmKB; ++u) {
-        const int col0 = min(g0 + u, G - 1) * 64;
-        half2_t s2, b2;
-        sb_half2(g0 + u < G ? L.s[u] : 0u, &s2, &b2);   // groups past the end weigh zero
-        const half8_t a0 = dequant8(L.c[u].x, s2, b2);
-        const half8_t a1 = dequant8(L.c[u].y, s2, b2);
+        const int g = min(g0 + u, G - 1);
+        const uint32_t pr = g0 + u < G ? L.s[u] : 0u;
+        const float s = bf16_lo(pr), b = bf16_hi(pr);
+        const half8_t q0 = codes8(L.c[u].x), q1 = codes8(L.c[u].y);
 #pragma unroll
         for (int t = 0; t < NTT; ++t) {
-            const _Float16* row = hs + (16 * t + n) * pitch + col0 + 8 * kb;
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, *(const half8_t*)row, acc[t], 0, 0, 0);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, *(const half8_t*)(row + 32), acc[t], 0, 0, 0);
+            const _Float16* row = hs + (16 * t + n) * pitch + g * 64 + 8 * kb;
+            const float4_t neg = *(const float4_t*)&tneg[g * 32 + 16 * t + 4 * kb];
+            const float4_t sum = *(const float4_t*)&tsum[g * 32 + 16 * t + 4 * kb];
+            float4_t a = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const half8_t*)row, q0, neg, 0, 0, 0);
+            a = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const half8_t*)(row + 32), q1, a, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[t][i] = fmaf(s, a[i], fmaf(b, sum[i], acc[t][i]));
         }
     }
 }
@@ -786,8 +946,9 @@ __device__ __forceinline__ void dn_mma(const DnLoads& L, const _Float16* hs, int
 // A, B, C hold batches 0, 1, 2, loaded before the chunk was staged.
 template <int NTT>
 __device__ __forceinline__ void dn_small_n(const Plan& p, const Item& it, int rt0, int nrt, const _Float16* hs,
-                                           int pitch, const float* wrow, const uint8_t* wb, const uint8_t* sb,
-                                           DnLoads& A, DnLoads& B, DnLoads& C) {
+                                           int pitch, const float* tsum, const float* tneg, const float* wrow,
+                                           const uint8_t* wb, const uint8_t* sb, DnLoads& A, DnLoads& B,
+                                           DnLoads& C) {
     const int ms = wave_id(), lane = threadIdx.x & 63;
     const int G = it.G, nb = (G + kSmKB - 1) / kSmKB, nq = nrt * nb;
     float4_t acc[NTT];
@@ -796,15 +957,13 @@ __device__ __forceinline__ void dn_small_n(const Plan& p, const Item& it, int rt
     auto finish = [&](int q) {   // after batch q: store the tile if it was its last batch
         const int r = q / nb;
         if (q - r * nb != nb - 1) return;
-        const int r0 = (rt0 + r) * 64 + 16 * ms + 4 * (lane >> 4);
+        const int row = (rt0 + r) * 64 + 16 * ms + (lane & 15);
 #pragma unroll
         for (int t = 0; t < NTT; ++t) {
-            const int n = 16 * t + (lane & 15);
-            if (n < it.count) {
-                float* dst = p.ysort + (int64_t)(it.pos0 + n) * p.H + r0;
-                const float wt = wrow[n];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dst[i] = wt * acc[t][i];
+            for (int i = 0; i < 4; ++i) {
+                const int n = 16 * t + 4 * (lane >> 4) + i;
+                if (n < it.count) p.ysort[(int64_t)(it.pos0 + n) * p.H + row] = wrow[n] * acc[t][i];
             }
             acc[t] = (float4_t){0.f, 0.f, 0.f, 0.f};
         }
@@ -813,20 +972,20 @@ __device__ __forceinline__ void dn_small_n(const Plan& p, const Item& it, int rt
     // one exit: batches past the end skip their multiply
     for (int q = 0; q < nq; q += 3) {
         __builtin_amdgcn_sched_barrier(0);
-        dn_mma<NTT>(A, hs, pitch, grp0(q), G, acc, lane);
+        dn_mma<NTT>(A, hs, pitch, tsum, tneg, grp0(q), G, acc, lane);
         finish(q);
         __builtin_amdgcn_sched_barrier(0);
         dn_load(A, wb, sb, it.rstride, q + 3, nq, nb, G);
         __builtin_amdgcn_sched_barrier(0);
         if (q + 1 < nq) {
-            dn_mma<NTT>(B, hs, pitch, grp0(q + 1), G, acc, lane);
+            dn_mma<NTT>(B, hs, pitch, tsum, tneg, grp0(q + 1), G, acc, lane);
             finish(q + 1);
         }
         __builtin_amdgcn_sched_barrier(0);
         dn_load(B, wb, sb, it.rstride, q + 4, nq, nb, G);
         __builtin_amdgcn_sched_barrier(0);
         if (q + 2 < nq) {
-            dn_mma<NTT>(C, hs, pitch, grp0(q + 2), G, acc, lane);
+            dn_mma<NTT>(C, hs, pitch, tsum, tneg, grp0(q + 2), G, acc, lane);
             finish(q + 2);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -836,19 +995,20 @@ __device__ __forceinline__ void dn_small_n(const Plan& p, const Item& it, int rt
 
 // ---- down, more than 32 tokens: h staged in LDS kDnKB groups at a time per
 // output tile, for the whole chunk.
+template <int MT>
 __device__ __forceinline__ void dn_big(const Plan& p, const Item& it, int rt0, int nrt, _Float16* lds, int* rows,
                                        const float* wrow) {
     const int wave = wave_id(), lane = threadIdx.x & 63;
     auto xs = (_Float16(*)[pitch_of<kDnKB>()])lds;
     for (int r = 0; r < nrt; ++r) {
-        float4_t acc[1][8];
+        float4_t acc[1][MT];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) acc[0][t] = (float4_t){0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < MT; ++t) acc[0][t] = (float4_t){0.f, 0.f, 0.f, 0.f};
         const uint8_t* tiles[1] = {it.w[0] + r * it.rstride};
-        gg_tile<1, kDnKB>(tiles, it.G, p.hg, p.I, rows, it.count, xs, acc);
+        gg_tile<1, kDnKB, MT>(tiles, it.G, p.hg, p.I, rows, it.count, xs, acc);
         const int r0 = (rt0 + r) * 64 + 16 * wave + 4 * (lane >> 4);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
+        for (int t = 0; t < MT; ++t) {
             const int n = 16 * t + (lane & 15);
             if (n < it.count) {
                 const float wt = wrow[n];
@@ -860,53 +1020,75 @@ __device__ __forceinline__ void dn_big(const Plan& p, const Item& it, int rt0, i
     }
 }
 
+// Dynamic LDS of k_dn: the small path's staged chunk (kSmallTokens rows of
+// I + 8 halves, then the group constants) or the big path's batch.
+__host__ __device__ constexpr size_t dn_small_hs_bytes(int I) { return (size_t)kSmallTokens * (I + 8) * 2; }
+size_t dn_lds_bytes(int I, int MT) {
+    const size_t small = dn_small_hs_bytes(I) + (size_t)2 * (I / 64) * 32 * 4;
+    const size_t big = (size_t)16 * MT * pitch_of<kDnKB>() * 2;
+    return small > big ? small : big;
+}
+
 // Down projection: ysort[pos] = w_pair * (W_down . h), weight 1 for the
 // shared expert's slices.  grid (ceil(H / 64 / kDnTiles), max_tiles), block
-// 256, dynamic LDS dn_lds_bytes(I).
-__global__ __launch_bounds__(256) void k_dn(Plan p) {
+// 256, dynamic LDS dn_lds_bytes(I, MT).
+template <int MT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT <= 4 ? 3 : 2))) void k_dn(Plan p) {
     extern __shared__ __attribute__((aligned(16))) _Float16 hs[];
     __shared__ float wrow[128];
     __shared__ int rows[128];
     const int rt0 = blockIdx.x * kDnTiles, nrt = min(kDnTiles, p.H / 64 - rt0);
     Item it;
-    if (!gg_weights(p, true, rt0, &it)) return;
+    if (!gg_item(p, true, rt0, &it)) return;
     auto token_rows = [&]() {
         if ((int)threadIdx.x < it.count) {
             wrow[threadIdx.x] = it.shared ? 1.f : p.wts[p.perm[it.pos0 + threadIdx.x]];
             rows[threadIdx.x] = it.pos0 + threadIdx.x;
         }
     };
-    if (it.ntt > 2) {
-        gg_tokens(p, &it);
+    if (it.big) {
         token_rows();
         __syncthreads();
-        dn_big(p, it, rt0, nrt, hs, rows, wrow);
+        dn_big<MT>(p, it, rt0, nrt, hs, rows, wrow);
         return;
     }
     const int ms = wave_id(), lane = threadIdx.x & 63;
     const int nb = (it.G + kSmKB - 1) / kSmKB, nq = nrt * nb;
     const uint8_t* wb = it.w[0] + ((ms >> 1) * 64 + lane) * 16 + 8 * (ms & 1);
     const uint8_t* sb = it.w[0] + kCodes4 + (lane & 15) * 16 + 4 * ms;
-    // first weights, in flight while the tokens arrive
+    // first weights, in flight while the chunk is staged
     DnLoads A, B, C;
     dn_load(A, wb, sb, it.rstride, 0, nq, nb, it.G);
     dn_load(B, wb, sb, it.rstride, 1, nq, nb, it.G);
     dn_load(C, wb, sb, it.rstride, 2, nq, nb, it.G);
-    gg_tokens(p, &it);
     token_rows();
     // stage the chunk: rows past it repeat its last row; columns past G
     // groups are never read
     const int pitch = p.I + 8;
     const int per = it.G * 8;   // 16-byte pieces per row
     const int nrow = it.ntt * 16;
-    for (int c = threadIdx.x; c < nrow * per; c += 256) {
-        const int n = c / per, q = c - n * per;
-        const int src = it.pos0 + min(n, it.count - 1);
-        *(u32x4_t*)&hs[n * pitch + q * 8] = *(const u32x4_t*)(p.hg + (int64_t)src * p.I + q * 8);
+    // (six pieces per thread in flight at a time)
+    constexpr int kSt = 6;
+    const int total = nrow * per;
+    for (int c0 = threadIdx.x; c0 < total; c0 += 256 * kSt) {
+        u32x4_t v[kSt];
+#pragma unroll
+        for (int i = 0; i < kSt; ++i) {
+            const int c = min(c0 + 256 * i, total - 1), n = c / per, q = c - n * per;
+            v[i] = *(const u32x4_t*)(p.hg + (int64_t)(it.pos0 + min(n, it.count - 1)) * p.I + q * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < kSt; ++i) {
+            const int c = c0 + 256 * i, n = c / per, q = c - n * per;
+            if (c < total) *(u32x4_t*)&hs[n * pitch + q * 8] = v[i];
+        }
     }
+    float* tsum = (float*)((char*)hs + dn_small_hs_bytes(p.I));
+    float* tneg = tsum + it.G * 32;
+    stage_sums((const float2*)p.hso, p.G_I, it.pos0 + min((int)(threadIdx.x & 31), it.count - 1), it.G, nrow, tsum,
+               tneg);
     __syncthreads();
-    if (nrow == 16) dn_small_n<1>(p, it, rt0, nrt, hs, pitch, wrow, wb, sb, A, B, C);
-    else dn_small_n<2>(p, it, rt0, nrt, hs, pitch, wrow, wb, sb, A, B, C);
+    dn_small_n<1>(p, it, rt0, nrt, hs, pitch, tsum, tneg, wrow, wb, sb, A, B, C);
 }
 
 // out[t] = sum_j ysort[inv[t][j]] (slot order) + the shared expert's
@@ -923,24 +1105,39 @@ __global__ __launch_bounds__(256) void k_gg_combine(Plan p) {
         ((uint16_t*)p.out)[(int64_t)t * p.out_stride + i] = f32_to_bf16(v);
 }
 
-// Dynamic LDS of k_dn: the larger of the small path's staged chunk and the
-// big path's batch.
-size_t dn_lds_bytes(int I) {
-    const size_t small = (size_t)32 * (I + 8) * 2, big = (size_t)128 * pitch_of<kDnKB>() * 2;
-    return small > big ? small : big;
+// Dynamic LDS of k_gu: the big path's staged batch, the small path's
+// group constants and its reduction buffer, which reuses their space.
+size_t gu_lds_bytes(int G_H, int MT) {
+    const size_t big = (size_t)16 * MT * pitch_of<kBigKB>() * 2, red = sizeof(GuRed);
+    const size_t c = (size_t)2 * G_H * 32 * 4;
+    return big > red ? (big > c ? big : c) : (red > c ? red : c);
 }
 
-// The schedule holds chunk indices below 256 (T <= 255 * 128), and the
-// LDS of the front and down kernels must fit a workgroup.
-bool grouped_ok(int H, int I, int64_t T) {
-    return T <= 255 * 128 && dn_lds_bytes(I) <= 160 * 1024 && (size_t)kFrontTokens * H * 4 + kFrontStatic <= 160 * 1024;
+// The schedule holds chunk indices below 256 (T <= 255 * 128) and sorted
+// rows below 2^24, and the LDS of the front, gate/up and down kernels must
+// fit a workgroup.
+bool grouped_ok(int H, int I, int64_t T, int rows_per_token) {
+    return T <= 255 * 128 && T * rows_per_token < (1 << 24) && dn_lds_bytes(I, 8) <= 160 * 1024 &&
+           gu_lds_bytes(H / 64, 8) + 5 * 1024 <= 160 * 1024 &&
+           (size_t)kFrontTokens * H * 4 + kFrontStatic <= 160 * 1024;
+}
+
+// The two GEMM launches for chunks of up to 16 MT tokens.
+template <int MT>
+mq_status launch_gemms(const Plan& p, hipStream_t s) {
+    const size_t gu_lds = gu_lds_bytes(p.G_H, MT), dn_lds = dn_lds_bytes(p.I, MT);
+    if (gu_lds > 64 * 1024 && hipFuncSetAttribute((const void*)k_gu<MT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                  (int)gu_lds) != hipSuccess)
+        return MQ_ERR_UNSUPPORTED;
+    if (dn_lds > 64 * 1024 && hipFuncSetAttribute((const void*)k_dn<MT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                  (int)dn_lds) != hipSuccess)
+        return MQ_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(k_gu<MT>, dim3(p.I / 64, p.max_tiles), dim3(256), gu_lds, s, p);
+    hipLaunchKernelGGL(k_dn<MT>, dim3((p.H / 64 + kDnTiles - 1) / kDnTiles, p.max_tiles), dim3(256), dn_lds, s, p);
+    return MQ_OK;
 }
 
 mq_status launch_grouped(const Plan& p, hipStream_t s) {
-    const size_t dn_lds = dn_lds_bytes(p.I);
-    if (dn_lds > 64 * 1024 &&
-        hipFuncSetAttribute((const void*)k_dn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dn_lds) != hipSuccess)
-        return MQ_ERR_UNSUPPORTED;
     // one token per front workgroup while that fills the machine, else four
     const bool tg4 = p.T > 512;
     const int tg = tg4 ? kFrontTokens : 1;
@@ -952,8 +1149,8 @@ mq_status launch_grouped(const Plan& p, hipStream_t s) {
         hipLaunchKernelGGL(k_front<kFrontTokens>, dim3((p.T + tg - 1) / tg), dim3(1024), fr_lds, s, p);
     else
         hipLaunchKernelGGL(k_front<1>, dim3(p.T), dim3(1024), fr_lds, s, p);
-    hipLaunchKernelGGL(k_gu, dim3(p.I / 64, p.max_tiles), dim3(256), 0, s, p);
-    hipLaunchKernelGGL(k_dn, dim3((p.H / 64 + kDnTiles - 1) / kDnTiles, p.max_tiles), dim3(256), dn_lds, s, p);
+    const mq_status st = p.ntile <= 64 ? launch_gemms<4>(p, s) : launch_gemms<8>(p, s);
+    if (st != MQ_OK) return st;
     hipLaunchKernelGGL(k_gg_combine, dim3(p.T, (p.H + 255) / 256), dim3(256), 0, s, p);
     return MQ_OK;
 }

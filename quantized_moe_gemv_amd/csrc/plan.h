@@ -1,6 +1,7 @@
 // One call's resolved arguments and workspace carve-up, passed by value to
 // every kernel of the call.
 #pragma once
+#include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace mq {
@@ -61,16 +62,18 @@ struct Plan {
     float* dpart;      // [T][kDownSplits][H]
 
     // workspace (grouped path)
-    _Float16* x16;     // [T][H]
+    _Float16* x16;     // [T][H]      fp16 input, columns with (c & 2) != 0 divided by 16
+    float* xso;        // [T][G_H][2] per group: sum of x, -1024 * sum of x16
     int32_t* counts;   // [E]
     int32_t* offsets;  // [E + 1]
     int32_t* perm;     // [T*k]  pair p = t*k + j, sorted by expert (any order within one)
     int32_t* inv;      // [T*k]  position of pair p in perm
-    int32_t* sched;    // [max_tiles] (expert << 16 | token chunk)
+    int2* sched;       // [max_tiles] (unit << 16 | tiles << 8 | chunk, first row | count << 24)
     int32_t* nsched;   // [1]
     // rows T*k + j*T + t of hg / ysort belong to token t and the shared
     // expert's virtual expert j (its rows j*I .. j*I + I - 1)
-    _Float16* hg;      // [T*k + n_vs*T][I]  GeGLU activations in sorted order
+    _Float16* hg;      // [T*k + n_vs*T][I]  GeGLU activations in sorted order (scaled as x16)
+    float* hso;        // [T*k + n_vs*T][G_I][2]  their per-group pairs, as xso
     float* ysort;      // [T*k + n_vs*T][H]  weighted expert outputs in sorted order
     // single-launch decode: tagged words and counters that persist across calls
     uint64_t* f_rpart;   // [copies][E/16][8][16] partial router scores, rpart_stride apart
