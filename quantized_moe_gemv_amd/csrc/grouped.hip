@@ -1056,37 +1056,51 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT <= 4 ? 3
     const int nb = (it.G + kSmKB - 1) / kSmKB, nq = nrt * nb;
     const uint8_t* wb = it.w[0] + ((ms >> 1) * 64 + lane) * 16 + 8 * (ms & 1);
     const uint8_t* sb = it.w[0] + kCodes4 + (lane & 15) * 16 + 4 * ms;
-    // first weights, in flight while the chunk is staged
-    DnLoads A, B, C;
-    dn_load(A, wb, sb, it.rstride, 0, nq, nb, it.G);
-    dn_load(B, wb, sb, it.rstride, 1, nq, nb, it.G);
-    dn_load(C, wb, sb, it.rstride, 2, nq, nb, it.G);
-    token_rows();
     // stage the chunk: rows past it repeat its last row; columns past G
-    // groups are never read
+    // groups are never read.  The group constants and the first batch of
+    // the chunk go out before the first weights, so that waiting for them
+    // does not wait for the weights too (loads complete in issue order);
+    // six pieces per thread at a time.
     const int pitch = p.I + 8;
     const int per = it.G * 8;   // 16-byte pieces per row
     const int nrow = it.ntt * 16;
-    // (six pieces per thread in flight at a time)
     constexpr int kSt = 6;
     const int total = nrow * per;
-    for (int c0 = threadIdx.x; c0 < total; c0 += 256 * kSt) {
-        u32x4_t v[kSt];
+    float* tsum = (float*)((char*)hs + dn_small_hs_bytes(p.I));
+    float* tneg = tsum + it.G * 32;
+    stage_sums((const float2*)p.hso, p.G_I, it.pos0 + min((int)(threadIdx.x & 31), it.count - 1), it.G, nrow, tsum,
+               tneg);
+    auto stage_load = [&](u32x4_t* v, int c0) {
 #pragma unroll
         for (int i = 0; i < kSt; ++i) {
             const int c = min(c0 + 256 * i, total - 1), n = c / per, q = c - n * per;
             v[i] = *(const u32x4_t*)(p.hg + (int64_t)(it.pos0 + min(n, it.count - 1)) * p.I + q * 8);
         }
+    };
+    auto stage_store = [&](const u32x4_t* v, int c0) {
 #pragma unroll
         for (int i = 0; i < kSt; ++i) {
             const int c = c0 + 256 * i, n = c / per, q = c - n * per;
             if (c < total) *(u32x4_t*)&hs[n * pitch + q * 8] = v[i];
         }
+    };
+    // the first batch (every thread loads, clamped), then the first weights
+    // (every thread), then the stores and any further batches
+    DnLoads A, B, C;
+    {
+        u32x4_t v[kSt];
+        stage_load(v, threadIdx.x);
+        dn_load(A, wb, sb, it.rstride, 0, nq, nb, it.G);
+        dn_load(B, wb, sb, it.rstride, 1, nq, nb, it.G);
+        dn_load(C, wb, sb, it.rstride, 2, nq, nb, it.G);
+        stage_store(v, threadIdx.x);
     }
-    float* tsum = (float*)((char*)hs + dn_small_hs_bytes(p.I));
-    float* tneg = tsum + it.G * 32;
-    stage_sums((const float2*)p.hso, p.G_I, it.pos0 + min((int)(threadIdx.x & 31), it.count - 1), it.G, nrow, tsum,
-               tneg);
+    for (int c0 = threadIdx.x + 256 * kSt; c0 < total; c0 += 256 * kSt) {
+        u32x4_t v[kSt];
+        stage_load(v, c0);
+        stage_store(v, c0);
+    }
+    token_rows();
     __syncthreads();
     dn_small_n<1>(p, it, rt0, nrt, hs, pitch, tsum, tneg, wrow, wb, sb, A, B, C);
 }
