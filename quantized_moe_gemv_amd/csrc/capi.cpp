@@ -337,6 +337,13 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
     if (grouped) {
         p.x16 = (_Float16*)(ws + c.x16);
         p.xso = (float*)(ws + c.xso);
+        // column splits of the router scores: about 512 workgroups over
+        // (16-token tiles) x (64-expert row tiles), at most rsplit and 16,
+        // none empty
+        const int64_t tiles = ((T + 15) / 16) * (z.E_pad / 64);
+        int ks = (int)std::min<int64_t>(std::min(z.rsplit, 16), std::max<int64_t>(1, (512 + tiles - 1) / tiles));
+        const int gpw = (z.G_H + ks - 1) / ks;
+        p.rsplit_used = (z.G_H + gpw - 1) / gpw;
     }
 
     if (grouped) {

@@ -79,6 +79,15 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// Sum over the 16 lanes lane / 16 * 16 + 0..15 of a wave.
+__device__ __forceinline__ float sum16(float v) {
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    v += __shfl_xor(v, 4, 64);
+    v += __shfl_xor(v, 8, 64);
+    return v;
+}
+
 // Sum over the four lanes lane%16 + 16*kb (kb = 0..3) of a wave.
 __device__ __forceinline__ float sum_kb(float v) {
     v += __shfl_xor(v, 16, 64);

@@ -46,16 +46,8 @@ __device__ __forceinline__ int block_scan_total(int* buf, int n, int v, int* exc
 }
 
 // ---------------------------------------------------------------------------
-// Front of the grouped path in one launch: router input, router scores,
-// top-k and softmax, and the token -> expert permutation with the work
-// schedule.  grid (ceil(T / TG)), block 1024.
-//
-// Each workgroup scores all experts for its TG tokens and ranks them; the
-// last workgroup to finish (a counter at a fixed workspace offset, returned
-// to zero for the next call) sorts every (token, slot) pair by expert and
-// writes the schedule.  Device-scope fences order the stores before the
-// counter and the loads after it.
-constexpr int kFrontStatic = 16 * 1024;   // bytes of static LDS in k_front (upper bound)
+// Front of the grouped path: router scores (k_scores), then top-k, softmax,
+// the token -> expert permutation and the work schedule (k_select).
 // Units with at most this many tokens take the code-operand path of the
 // grouped GEMMs, the others the dequantised-weight path for all their
 // chunks: the choice is per unit, so a token's arithmetic does not depend
@@ -102,182 +94,271 @@ __device__ __forceinline__ void build_schedule(const Plan& p, int cnt, int off, 
     }
 }
 
-template <int TG>
-__global__ __launch_bounds__(1024) void k_front(Plan p) {
-    extern __shared__ __attribute__((aligned(16))) float rr[];   // [TG][H] router input
-    __shared__ float red[16][TG];
-    __shared__ float part[16][TG][16];
-    __shared__ float lg[TG][kMaxExperts];
-    __shared__ float selv[TG][kMaxTopK];
-    __shared__ int seli[TG][kMaxTopK];
-    __shared__ int scan[16];
-    __shared__ int ecount[kMaxExperts], efill[kMaxExperts], eoff[kMaxExperts];
-    __shared__ int last;
-    const int H = p.H, E = p.E, tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
-    const int t0 = blockIdx.x * TG, nt = min(TG, p.T - t0);
+// ---- router scores on the matrix cores (v_mfma_f32_16x16x4_f32: fp32
+// operands, so the scores keep fp32 precision).  The RMS factor of the
+// router input is a per-token scalar, so the scores are first taken over
+// the unnormalised input a = x * router_scale and scaled afterwards:
+//     score[t][e] = c[t] * sum_g (s[e][g] sum_{k in g} q[e][k] a[t][k]
+//                                + b[e][g] sum_{k in g} a[t][k]),
+//     c[t] = 1 / sqrt(mean(x[t]^2) + eps) / sqrt(H).
+// Workgroup (token tile of 16, router row tile of 64 experts, column split
+// ks): the staged a[16][batch columns] is the A operand (D[token][expert]),
+// wave j takes experts 16 j .. 16 j + 15 of the row tile and the 8-bit codes
+// of its DEV_V1 words are the B operand (one byte conversion each); the
+// group scale and bias are applied once per output in fp32.  The partial
+// scores of each column split go to plog[ks][t][e], the partial sums of x^2
+// to the router-sum area; the workgroups of row tile 0 also write x16 and
+// xso for their columns.  grid (ceil(T / 16), E_pad / 64, splits), block 256.
+constexpr int kScBatch = 4;   // column groups per staged batch
 
-    // router input r = x / sqrt(mean(x^2) + eps) * router_scale / sqrt(H),
-    // all TG tokens at once
-    {
-        float ss[TG];
+__global__ __launch_bounds__(256) void k_scores(Plan p) {
+    __shared__ __attribute__((aligned(16))) float A[16][kScBatch * 64 + 4];
+    __shared__ __attribute__((aligned(16))) float asum[kScBatch][16];
+    const int tt = blockIdx.x, rt = blockIdx.y, ks = blockIdx.z;
+    const int tid = threadIdx.x, j = wave_id(), lane = tid & 63;
+    const int gpw = (p.G_H + gridDim.z - 1) / gridDim.z;
+    const int g_begin = ks * gpw, g_end = min(p.G_H, g_begin + gpw);
+    // staging role: token st of the tile, columns c4 .. c4 + 3 of each group
+    const int st = tid >> 4, c4 = (tid & 15) * 4;
+    const int t_st = tt * 16 + st, tok = min(t_st, p.T - 1);
+    const uint16_t* xrow = p.x + (int64_t)tok * p.x_stride;
+    const bool writer = rt == 0 && t_st < p.T;   // x16, xso and the x^2 sums
+    const uint8_t* rbase = p.router_w + (int64_t)rt * p.G_H * kBlk8;
+    float ss = 0.f;
+    float4_t out = {0.f, 0.f, 0.f, 0.f};   // token 4 (lane / 16) + i, expert 16 j + lane % 16
+    // the batch's router words (wave j's 16 experts) and activations; groups
+    // past the range re-read its last group and are not used.  The next
+    // batch's loads go out while the current batch is multiplied.
+    u32x4_t cw[kScBatch], ncw[kScBatch];
+    uint32_t pr[kScBatch], npr[kScBatch];
+    uint2 xv[kScBatch], nxv[kScBatch];
+    float4_t rs[kScBatch], nrs[kScBatch];
+    auto load_batch = [&](int g0) {
 #pragma unroll
-        for (int tt = 0; tt < TG; ++tt) ss[tt] = 0.f;
-        for (int i = tid; i < H; i += 1024)
-#pragma unroll
-            for (int tt = 0; tt < TG; ++tt)
-                if (tt < nt) {
-                    const float v = bf16_to_f32(p.x[(int64_t)(t0 + tt) * p.x_stride + i]);
-                    ss[tt] += v * v;
-                }
-#pragma unroll
-        for (int tt = 0; tt < TG; ++tt) {
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) ss[tt] += __shfl_xor(ss[tt], o, 64);
-            if (lane == 0) red[wave][tt] = ss[tt];
+        for (int gi = 0; gi < kScBatch; ++gi) {
+            const int g = min(g0 + gi, g_end - 1);
+            ncw[gi] = *(const u32x4_t*)(rbase + (int64_t)g * kBlk8 + (j * 64 + lane) * 16);
+            npr[gi] = *(const uint32_t*)(rbase + (int64_t)g * kBlk8 + kCodes8 + (lane & 15) * 16 + 4 * j);
+            nxv[gi] = *(const uint2*)(xrow + g * 64 + c4);
+            nrs[gi] = p.router_scale ? *(const float4_t*)(p.router_scale + g * 64 + c4)
+                                     : (float4_t){1.f, 1.f, 1.f, 1.f};
         }
-        __syncthreads();
-        float c[TG];
+    };
+    load_batch(g_begin);
+    for (int g0 = g_begin; g0 < g_end; g0 += kScBatch) {
+        const int nbg = min(kScBatch, g_end - g0);
 #pragma unroll
-        for (int tt = 0; tt < TG; ++tt) {
-            float t = 0.f;
-#pragma unroll
-            for (int w = 0; w < 16; ++w) t += red[w][tt];
-            c[tt] = (1.0f / sqrtf(t / (float)H + p.eps)) * (1.0f / sqrtf((float)H));
+        for (int gi = 0; gi < kScBatch; ++gi) {
+            cw[gi] = ncw[gi];
+            pr[gi] = npr[gi];
+            xv[gi] = nxv[gi];
+            rs[gi] = nrs[gi];
         }
-        // x16: the fp16 activation operand of the matrix-core kernels
-        // (columns with i & 2 divided by 16) and xso its per-group pair
-        // (sum of x, -1024 * sum of the stored operand).  Wave w covers
-        // group i / 64 = w + 16 j whole (H is a multiple of 64), so the
-        // bound i < H is the same for all its lanes.
-        for (int i = tid; i < H; i += 1024) {
-            const float rs = p.router_scale ? p.router_scale[i] : 1.0f;
+        load_batch(g0 + kScBatch);
+        __syncthreads();   // the previous batch's operands are read
 #pragma unroll
-            for (int tt = 0; tt < TG; ++tt)
-                if (tt < nt) {
-                    const float xv = bf16_to_f32(p.x[(int64_t)(t0 + tt) * p.x_stride + i]);
-                    rr[tt * H + i] = xv * c[tt] * rs;
-                    const _Float16 xh = (_Float16)xv;
-                    const _Float16 xa = (i & 2) ? xh * (_Float16)0.0625f : xh;
-                    p.x16[(int64_t)(t0 + tt) * H + i] = xa;
-                    const float xs = wave_sum((float)xh), xn = wave_sum(-1024.0f * (float)xa);
-                    if (lane == 0) ((float2*)p.xso)[(int64_t)(t0 + tt) * p.G_H + (i >> 6)] = make_float2(xs, xn);
-                }
-        }
-    }
-    __syncthreads();
-
-    // scores: slice sl of 16 experts (rows 16 sl .. of the router) per wave
-    // set, lane owns expert row 16 sl + lane % 16 and columns
-    // 16 i + 4 (lane / 16) + 0..3 of each group; the wps waves of a slice
-    // split its groups
-    const int nsl = p.E_pad / 16, wps = 16 / nsl;   // E_pad in {64, 128, 192, 256}
-    {
-        const int sl = wave % nsl, gw = wave / nsl, kb = lane >> 4, j4 = sl & 3;
-        float acc[TG];
-#pragma unroll
-        for (int tt = 0; tt < TG; ++tt) acc[tt] = 0.f;
-        if (wave < nsl * wps) {
-            const uint8_t* base = p.router_w + (int64_t)(sl >> 2) * p.G_H * kBlk8 + (j4 * 64 + lane) * 16;
-            const int sbo = kCodes8 + (lane & 15) * 16 + 4 * j4 - (j4 * 64 + lane) * 16;
-            const int ng = (p.G_H - gw + wps - 1) / wps;   // this wave's groups gw + wps j
-            // eight groups of loads in flight per batch (the last batch
-            // re-reads, clamped, and skips what lies past the end)
-            constexpr int kRB = 8;
-            for (int j0 = 0; j0 < ng; j0 += kRB) {
-                u32x4_t cw[kRB];
-                uint32_t sb[kRB];
-#pragma unroll
-                for (int u = 0; u < kRB; ++u) {
-                    const int g = gw + wps * min(j0 + u, ng - 1);
-                    cw[u] = *(const u32x4_t*)(base + (int64_t)g * kBlk8);
-                    sb[u] = *(const uint32_t*)(base + (int64_t)g * kBlk8 + sbo);
-                }
-#pragma unroll
-                for (int u = 0; u < kRB; ++u) {
-                    if (j0 + u >= ng) break;
-                    const int g = gw + wps * (j0 + u);
-#pragma unroll
-                    for (int tt = 0; tt < TG; ++tt) {
-                        float d = 0.f, rs = 0.f;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float4_t rv = *(const float4_t*)&rr[tt * H + 64 * g + 16 * i + 4 * kb];
-                            d = fmaf((float)(cw[u][i] & 0xFFu), rv[0], d);
-                            d = fmaf((float)((cw[u][i] >> 8) & 0xFFu), rv[1], d);
-                            d = fmaf((float)((cw[u][i] >> 16) & 0xFFu), rv[2], d);
-                            d = fmaf((float)(cw[u][i] >> 24), rv[3], d);
-                            rs += (rv[0] + rv[1]) + (rv[2] + rv[3]);
-                        }
-                        acc[tt] = fmaf(bf16_lo(sb[u]), d, fmaf(bf16_hi(sb[u]), rs, acc[tt]));
-                    }
+        for (int gi = 0; gi < kScBatch; ++gi) {
+            if (gi >= nbg) break;
+            const float x0 = bf16_lo(xv[gi].x), x1 = bf16_hi(xv[gi].x), x2 = bf16_lo(xv[gi].y), x3 = bf16_hi(xv[gi].y);
+            const float4_t a = {x0 * rs[gi][0], x1 * rs[gi][1], x2 * rs[gi][2], x3 * rs[gi][3]};
+            *(float4_t*)&A[st][gi * 64 + c4] = a;
+            const float as = sum16((a[0] + a[1]) + (a[2] + a[3]));
+            if ((tid & 15) == 0) asum[gi][st] = as;
+            ss += (x0 * x0 + x1 * x1) + (x2 * x2 + x3 * x3);
+            if (rt == 0) {
+                // x16 (columns with c & 2 divided by 16; c4 + 2, c4 + 3 are those) and xso
+                const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1, h2 = (_Float16)x2, h3 = (_Float16)x3;
+                const _Float16 s2 = h2 * (_Float16)0.0625f, s3 = h3 * (_Float16)0.0625f;
+                const float xs = sum16(((float)h0 + (float)h1) + ((float)h2 + (float)h3));
+                const float xn = sum16(-1024.0f * (((float)h0 + (float)h1) + ((float)s2 + (float)s3)));
+                if (t_st < p.T) {
+                    typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+                    *(half4_t*)(p.x16 + (int64_t)t_st * p.H + (g0 + gi) * 64 + c4) = (half4_t){h0, h1, s2, s3};
+                    if ((tid & 15) == 0)
+                        ((float2*)p.xso)[(int64_t)t_st * p.G_H + g0 + gi] = make_float2(xs, xn);
                 }
             }
         }
+        __syncthreads();
 #pragma unroll
-        for (int tt = 0; tt < TG; ++tt) {
-            const float v = sum_kb(acc[tt]);
-            if (kb == 0) part[wave][tt][lane] = v;
+        for (int gi = 0; gi < kScBatch; ++gi) {
+            if (gi >= nbg) break;
+            float4_t acc[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float4_t av = *(const float4_t*)&A[lane & 15][gi * 64 + 16 * i + 4 * (lane >> 4)];
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[0], (float)((cw[gi][i] >> 0) & 0xFFu),
+                                                              (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[1], (float)((cw[gi][i] >> 8) & 0xFFu), acc[i],
+                                                              0, 0, 0);
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[2], (float)((cw[gi][i] >> 16) & 0xFFu), acc[i],
+                                                              0, 0, 0);
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[3], (float)((cw[gi][i] >> 24) & 0xFFu), acc[i],
+                                                              0, 0, 0);
+            }
+            const float4_t d = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+            const float4_t sm = *(const float4_t*)&asum[gi][4 * (lane >> 4)];
+            const float sc = bf16_lo(pr[gi]), bi = bf16_hi(pr[gi]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) out[i] = fmaf(sc, d[i], fmaf(bi, sm[i], out[i]));
         }
     }
-    __syncthreads();
-    for (int q = tid; q < TG * E; q += 1024) {
-        const int tt = q / E, e = q - tt * E, sl = e >> 4;
-        if (tt < nt) {
-            float s = 0.f;
-            for (int w = 0; w < wps; ++w) s += part[sl + w * nsl][tt][e & 15];
-            if (p.logit_bias) s += p.logit_bias[e];
-            if (p.logits_out) p.logits_out[(int64_t)(t0 + tt) * E + e] = s;
-            lg[tt][e] = (s == s) ? s : -INFINITY;   // a NaN score ranks last; ids stay distinct
-        }
+    const int e = rt * 64 + 16 * j + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = tt * 16 + 4 * (lane >> 4) + i;
+        if (t < p.T) p.plog[((int64_t)ks * p.T + t) * p.E_pad + e] = out[i];
     }
-    __syncthreads();
-    // rank: four threads per expert each count a quarter of the others
-    for (int tt = 0; tt < nt; ++tt) {
-        const int e = tid >> 2, qq = tid & 3;
-        int beat = 0;
-        float v = 0.f;
-        if (e < E) {
-            v = lg[tt][e];
-            for (int o = qq; o < E; o += 4) beat += (lg[tt][o] > v) || (lg[tt][o] == v && o < e);
-        }
-        beat += __shfl_xor(beat, 1, 64);
-        beat += __shfl_xor(beat, 2, 64);
-        if (e < E && qq == 0 && beat < p.k) {
-            selv[tt][beat] = v;
-            seli[tt][beat] = e;
-        }
-    }
-    __syncthreads();
-    if (tid < nt * p.k) {
-        const int tt = tid / p.k, j = tid - tt * p.k, t = t0 + tt;
-        float den = 0.f;
-        for (int i = 0; i < p.k; ++i) den += expf(selv[tt][i] - selv[tt][0]);
-        const int e = seli[tt][j];
-        const float w = expf(selv[tt][j] - selv[tt][0]) / den * (p.pes ? p.pes[e] : 1.0f);
-        p.ids[t * p.k + j] = e;
-        p.wts[t * p.k + j] = w;
-        if (p.ids_out) p.ids_out[t * p.k + j] = e;
-        if (p.w_out) p.w_out[t * p.k + j] = w;
-    }
+    ss = sum16(ss);
+    if (writer && (tid & 15) == 0) p.rsum8[(int64_t)ks * p.T + t_st] = ss;
+}
 
-    // the last workgroup sorts every pair by expert and builds the schedule.
-    // One thread fences for the workgroup: the barrier orders the other
-    // threads' stores before its release and its acquire before their loads.
-    __syncthreads();
-    if (tid == 0) {
-        __threadfence();
-        last = atomicAdd(&p.fcnt[kFrontMaxGroups], 1u) + 1 == gridDim.x;
-        if (last) {
-            p.fcnt[kFrontMaxGroups] = 0u;
-            __threadfence();
+// ---- selection: one wave per token.  The scores are the column splits'
+// sum times the RMS factor (plus logit_bias); the k highest are taken by
+// k rounds of a wave-wide argmax (equal scores go to the lower expert, a
+// NaN score ranks last), then the softmax over them times per_expert_scale.
+// grid (ceil(T / 4)), block 256: one wave per SIMD.
+__global__ __launch_bounds__(256) void k_select(Plan p) {
+    const int lane = threadIdx.x & 63, w = wave_id();
+    const int t = blockIdx.x * 4 + w, E = p.E, k = p.k, ns = p.rsplit_used;
+    if (t < p.T) {
+        // the column splits' partials, summed in split order; the loads of a
+        // batch of sixteen splits go out together (clamped, in bounds)
+        constexpr int kB = 16, kM = kMaxExperts / 64;
+        float ss = 0.f, sum[kM], bias[kM];
+#pragma unroll
+        for (int m = 0; m < kM; ++m) bias[m] = p.logit_bias ? p.logit_bias[min(lane + 64 * m, E - 1)] : 0.f;
+#pragma unroll
+        for (int m = 0; m < kM; ++m) sum[m] = 0.f;
+        for (int q0 = 0; q0 < ns; q0 += kB) {
+            float ps[kB], pl[kM][kB];
+#pragma unroll
+            for (int i = 0; i < kB; ++i) {
+                const int q = min(q0 + i, ns - 1);
+                ps[i] = p.rsum8[(int64_t)q * p.T + t];
+#pragma unroll
+                for (int m = 0; m < kM; ++m)
+                    pl[m][i] = p.plog[((int64_t)q * p.T + t) * p.E_pad + min(lane + 64 * m, p.E_pad - 1)];
+            }
+#pragma unroll
+            for (int i = 0; i < kB; ++i)
+                if (q0 + i < ns) {
+                    ss += ps[i];
+#pragma unroll
+                    for (int m = 0; m < kM; ++m) sum[m] += pl[m][i];
+                }
+        }
+        const float c = (1.0f / sqrtf(ss / (float)p.H + p.eps)) * (1.0f / sqrtf((float)p.H));
+        float v[kM];
+#pragma unroll
+        for (int m = 0; m < kM; ++m) {
+            const int e = lane + 64 * m;
+            float a = -INFINITY;
+            if (e < E) {
+                a = sum[m] * c;
+                if (p.logit_bias) a += bias[m];
+                if (p.logits_out) p.logits_out[(int64_t)t * E + e] = a;
+                if (!(a == a)) a = -INFINITY;   // a NaN score ranks last; ids stay distinct
+            }
+            v[m] = a;
+        }
+        // top-k by keys that order like the scores (a NaN is -inf by now):
+        // a bitwise search for the k-th largest key (compare, ballot and a
+        // scalar count per bit), then the keys above it and the lowest
+        // expert indices among those equal to it; finally each chosen
+        // expert's rank among the chosen, equal scores by lower index.
+        uint32_t key[kM];
+#pragma unroll
+        for (int m = 0; m < kM; ++m) {
+            const uint32_t b = __float_as_uint(v[m] + 0.0f);   // -0 and +0 compare equal
+            key[m] = lane + 64 * m < E ? ((b & 0x80000000u) ? ~b : (b | 0x80000000u)) : 0u;   // any score > 0
+        }
+        uint32_t thr = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = thr | (1u << bit);
+            int n = 0;
+#pragma unroll
+            for (int m = 0; m < kM; ++m) n += __popcll(__ballot(key[m] >= cand));
+            if (n >= k) thr = cand;
+        }
+        int need = k;   // chosen: every key above thr, then the lowest-index keys equal to it
+#pragma unroll
+        for (int m = 0; m < kM; ++m) need -= __popcll(__ballot(key[m] > thr));
+        bool sel[kM];
+#pragma unroll
+        for (int m = 0; m < kM; ++m) {
+            const uint64_t eq = __ballot(key[m] == thr);
+            const int below = __popcll(eq & ((1ull << lane) - 1ull));
+            sel[m] = key[m] > thr || (key[m] == thr && below < need);
+            need -= min(need, __popcll(eq));
+        }
+        int rank[kM];
+#pragma unroll
+        for (int m = 0; m < kM; ++m) rank[m] = 0;
+#pragma unroll
+        for (int m2 = 0; m2 < kM; ++m2) {
+            uint64_t bits = __ballot(sel[m2]);
+            while (bits) {
+                const int l2 = __ffsll((unsigned long long)bits) - 1;
+                bits &= bits - 1;
+                const uint32_t k2 = (uint32_t)__builtin_amdgcn_readlane((int)key[m2], l2);
+                const int e2 = l2 + 64 * m2;
+#pragma unroll
+                for (int m = 0; m < kM; ++m) {
+                    const int e = lane + 64 * m;
+                    rank[m] += sel[m] && (k2 > key[m] || (k2 == key[m] && e2 < e));
+                }
+            }
+        }
+        // lane r (r < k) takes the chosen expert of rank r
+        int myid = 0;
+        float myv = 0.f, v0 = 0.f;
+#pragma unroll
+        for (int m = 0; m < kM; ++m) {
+            const uint64_t bits = __ballot(sel[m]);
+            for (uint64_t b2 = bits; b2;) {
+                const int l2 = __ffsll((unsigned long long)b2) - 1;
+                b2 &= b2 - 1;
+                const int r2 = __builtin_amdgcn_readlane(rank[m], l2);
+                const float vv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[m]), l2));
+                if (lane == r2) {
+                    myid = l2 + 64 * m;
+                    myv = vv;
+                }
+                if (r2 == 0) v0 = vv;
+            }
+        }
+        float ex = lane < k ? expf(myv - v0) : 0.f;
+        const float den = wave_sum(ex);
+        if (lane < k) {
+            const float wt = ex / den * (p.pes ? p.pes[myid] : 1.0f);
+            p.ids[t * k + lane] = myid;
+            p.wts[t * k + lane] = wt;
+            if (p.ids_out) p.ids_out[t * k + lane] = myid;
+            if (p.w_out) p.w_out[t * k + lane] = wt;
         }
     }
-    __syncthreads();
-    if (!last) return;
-    const int P = p.T * p.k;
+}
+
+// Sort every (token, slot) pair by expert and build the schedule: one
+// workgroup.  grid 1, block 1024.
+__global__ __launch_bounds__(1024) void k_sort(Plan p) {
+    __shared__ int scan[16];
+    __shared__ int ecount[kMaxExperts], efill[kMaxExperts], eoff[kMaxExperts];
+    const int tid = threadIdx.x, E = p.E, k = p.k;
+    const int P = p.T * k;
+    // count the pairs of every expert (LDS atomics: many pairs of one
+    // popular expert contend far less here than on one global address)
     for (int e = tid; e < E; e += 1024) ecount[e] = efill[e] = 0;
     __syncthreads();
-    for (int q = tid; q < P; q += 1024) atomicAdd(&ecount[p.ids[q]], 1);
+    for (int q0 = tid; q0 < P; q0 += 1024 * 8) {
+        int ex[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ex[i] = p.ids[min(q0 + 1024 * i, P - 1)];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (q0 + 1024 * i < P) atomicAdd(&ecount[ex[i]], 1);
+    }
     __syncthreads();
     const int cnt = tid < E ? ecount[tid] : 0;
     int off;
@@ -289,13 +370,23 @@ __global__ __launch_bounds__(1024) void k_front(Plan p) {
     }
     if (tid == 0) p.offsets[E] = P;
     __syncthreads();
-    // positions within an expert's segment come from LDS atomics; every item
-    // computes each token independently, so their order changes no result
-    for (int q = tid; q < P; q += 1024) {
-        const int e = p.ids[q];
-        const int pos = eoff[e] + atomicAdd(&efill[e], 1);
-        p.perm[pos] = q;
-        p.inv[q] = pos;
+    // positions within an expert's segment come from LDS atomics; the path
+    // of a unit is chosen by its pair count, and every token is computed
+    // on its own, so their order changes no result.  Eight pairs per thread
+    // in flight at a time (the ids are read again: L2-resident now).
+    for (int q0 = tid; q0 < P; q0 += 1024 * 8) {
+        int ex[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ex[i] = p.ids[min(q0 + 1024 * i, P - 1)];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int q = q0 + 1024 * i;
+            if (q < P) {
+                const int pos = eoff[ex[i]] + atomicAdd(&efill[ex[i]], 1);
+                p.perm[pos] = q;
+                p.inv[q] = pos;
+            }
+        }
     }
     build_schedule(p, cnt, off, scan);
 }
@@ -374,14 +465,6 @@ __device__ __forceinline__ half8_t dequant8s(uint32_t w, const Sb16& k) {
 // Stored activation and its group-sum pair of one GeGLU value h of column c.
 __device__ __forceinline__ _Float16 act_store(_Float16 h, int c) { return (c & 2) ? h * (_Float16)0.0625f : h; }
 
-// Sums over the 16 lanes lane / 16 * 16 + 0..15 of a wave.
-__device__ __forceinline__ float sum16(float v) {
-    v += __shfl_xor(v, 1, 64);
-    v += __shfl_xor(v, 2, 64);
-    v += __shfl_xor(v, 4, 64);
-    v += __shfl_xor(v, 8, 64);
-    return v;
-}
 
 // Grouped dequant-GEMM.  A work item is (64-row tile of one matrix, chunk
 // of up to p.ntile = 128 tokens of one expert); for the down projection a
@@ -1128,12 +1211,11 @@ size_t gu_lds_bytes(int G_H, int MT) {
 }
 
 // The schedule holds chunk indices below 256 (T <= 255 * 128) and sorted
-// rows below 2^24, and the LDS of the front, gate/up and down kernels must
-// fit a workgroup.
+// rows below 2^24, and the LDS of the gate/up and down kernels must fit a
+// workgroup.
 bool grouped_ok(int H, int I, int64_t T, int rows_per_token) {
     return T <= 255 * 128 && T * rows_per_token < (1 << 24) && dn_lds_bytes(I, 8) <= 160 * 1024 &&
-           gu_lds_bytes(H / 64, 8) + 5 * 1024 <= 160 * 1024 &&
-           (size_t)kFrontTokens * H * 4 + kFrontStatic <= 160 * 1024;
+           gu_lds_bytes(H / 64, 8) + 5 * 1024 <= 160 * 1024;
 }
 
 // The two GEMM launches for chunks of up to 16 MT tokens.
@@ -1152,17 +1234,9 @@ mq_status launch_gemms(const Plan& p, hipStream_t s) {
 }
 
 mq_status launch_grouped(const Plan& p, hipStream_t s) {
-    // one token per front workgroup while that fills the machine, else four
-    const bool tg4 = p.T > 512;
-    const int tg = tg4 ? kFrontTokens : 1;
-    const size_t fr_lds = (size_t)tg * p.H * 4;
-    const void* fr = tg4 ? (const void*)k_front<kFrontTokens> : (const void*)k_front<1>;
-    if (fr_lds > 64 * 1024 && hipFuncSetAttribute(fr, hipFuncAttributeMaxDynamicSharedMemorySize, (int)fr_lds) != hipSuccess)
-        return MQ_ERR_UNSUPPORTED;
-    if (tg4)
-        hipLaunchKernelGGL(k_front<kFrontTokens>, dim3((p.T + tg - 1) / tg), dim3(1024), fr_lds, s, p);
-    else
-        hipLaunchKernelGGL(k_front<1>, dim3(p.T), dim3(1024), fr_lds, s, p);
+    hipLaunchKernelGGL(k_scores, dim3((p.T + 15) / 16, p.E_pad / 64, p.rsplit_used), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(k_select, dim3((p.T + 3) / 4), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(k_sort, dim3(1), dim3(1024), 0, s, p);
     const mq_status st = p.ntile <= 64 ? launch_gemms<4>(p, s) : launch_gemms<8>(p, s);
     if (st != MQ_OK) return st;
     hipLaunchKernelGGL(k_gg_combine, dim3(p.T, (p.H + 255) / 256), dim3(256), 0, s, p);

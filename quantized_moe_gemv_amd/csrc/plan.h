@@ -8,9 +8,8 @@ namespace mq {
 
 constexpr int kRouterTokens = 4;    // tokens per router workgroup
 constexpr int kMaxTopK = 16;
-// Grouped-path front: most tokens per workgroup, and the offset of its
-// call counter in the front counter area.
-constexpr int kFrontTokens = 4;
+// Grouped-path front: the offset of its call counter in the front counter
+// area.
 constexpr int kFrontMaxGroups = 0;
 constexpr int kMaxExperts = 256;
 constexpr int kDownSplits = 4;      // split of the down-projection source list (GEMV path)
@@ -22,6 +21,7 @@ struct Plan {
     int T, H, E, E_pad, k, I, Is;
     int G_H, G_I, G_s;              // groups of 64 along hidden, inter, shared inter
     int rsplit, rgroups;            // router k-splits and groups per split
+    int rsplit_used;                // grouped path: column splits of the router scores (<= rsplit)
     int has_shared;
 
     // inputs
