@@ -24,6 +24,9 @@ Profiling helpers (not part of the default run):
                          back to back, for counter runs on the grouped kernels;
   --traffic-summary F W  turns the FETCH_SIZE / WRITE_SIZE counter CSVs of
                          those runs into the traffic summary under profiles/;
+  --prefill-summary F W S  turns FETCH_SIZE / WRITE_SIZE counter CSVs and the
+                         kernel statistics CSV of --profile prefill runs into
+                         the per-kernel traffic summary of the grouped path;
   --stats-summary S J    turns the kernel statistics CSV of a rocprofv3
                          --kernel-trace --stats run of the default benchmark,
                          and the JSON line that run printed, into the kernel
@@ -52,6 +55,9 @@ METRIC = "MoE-layer tokens/s + achieved HBM GB/s (% of peak), decode and 128-tok
 DECODE_KERNEL = "k_decode"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_decode_decode_h2816_e128_traffic.txt")
 STATS_FILE = os.path.join(ROOT, "profiles", "kernel_stats_bench_decode_prefill128_stack30_prefill4096.txt")
+PREFILL_FILE = os.path.join(ROOT, "profiles", "grouped_kernels_prefill128_h2816_e128_traffic.txt")
+# The copy kernel's FETCH_SIZE reads half its bytes (see the decode traffic summary).
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 COPY_BYTES = 256 << 20       # each direction of the reference copy kernel
 # Sources whose change invalidates the recorded counter traffic of the decode kernel.
 KERNEL_SOURCES = ["fused.hip", "device.h", "plan.h", "layout.h"]
@@ -269,6 +275,44 @@ def traffic_summary(fetch_csv, write_csv, out_path):
     print("\n".join(lines))
 
 
+def prefill_summary(fetch_csv, write_csv, stats_csv, out_path):
+    """Per grouped-path kernel: HBM bytes per dispatch (counters scaled as for
+    the decode kernel) and the average duration, for 128-token prefill calls."""
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: float(np.median(v)) for k, v in vals.items()}
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    with open(stats_csv) as f:
+        dur = {r["Name"]: float(r["AverageNs"]) / 1e3 for r in csv.DictReader(f)}
+    lines = [
+        "# HBM traffic and duration per kernel of the grouped path, 128-token prefill",
+        "# workload: 128 tokens per call, Zipf(1.1) logit bias, H2816 E128 top8 I704 Is2112, rotated over 6 layers",
+        "# commands (run from /tmp with TMPDIR=/tmp):",
+        "#   rocprofv3 --pmc FETCH_SIZE -d <dir> -o pfetch --output-format csv -- python3 <repo>/bench.py --profile prefill --steps 60 --layers 6",
+        "#   rocprofv3 --pmc WRITE_SIZE -d <dir> -o pwrite --output-format csv -- python3 <repo>/bench.py --profile prefill --steps 60 --layers 6",
+        "#   rocprofv3 --kernel-trace --stats -d <dir> -o pstats --output-format csv -- python3 <repo>/bench.py --profile prefill --steps 60 --layers 6",
+        "#   python3 <repo>/bench.py --prefill-summary <fetch csv> <write csv> <pstats_kernel_stats.csv>",
+        "# counter KiB scaled by %.1f (FETCH_SIZE) and %.1f (WRITE_SIZE), as in the decode traffic summary" % (FETCH_SCALE, WRITE_SCALE),
+        "# (the FETCH_SIZE scale was measured on 128-byte line requests; a kernel whose requests are",
+        "# partly 64-byte, as the down projection's 8-byte-per-lane loads may be, reads less than shown)",
+        "",
+        "%-34s %10s %10s %10s %10s" % ("kernel", "read_MB", "write_MB", "avg_us", "GB/s"),
+    ]
+    for name in sorted(fetch, key=lambda n: -fetch[n]):
+        short = name.split("(")[0].replace("void ", "")
+        rd = fetch[name] * 1024 * FETCH_SCALE / 1e6
+        wr = write.get(name, 0.0) * 1024 * WRITE_SCALE / 1e6
+        us = next((v for k, v in dur.items() if k.startswith(name.split("(")[0])), float("nan"))
+        lines.append("%-34s %10.1f %10.1f %10.2f %10.0f" % (short, rd, wr, us, (rd + wr) * 1e3 / us))
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def stats_summary(stats_csv, bench_json, out_path):
     with open(stats_csv) as f:
         rows = list(csv.DictReader(f))
@@ -324,12 +368,16 @@ def main():
     ap.add_argument("--profile", choices=["decode", "prefill"])
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--stats-summary", nargs=2, metavar=("STATS_CSV", "BENCH_JSON"))
+    ap.add_argument("--prefill-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "STATS_CSV"))
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(args.traffic_summary[0], args.traffic_summary[1], TRAFFIC_FILE)
         return
     if args.stats_summary:
         stats_summary(args.stats_summary[0], args.stats_summary[1], STATS_FILE)
+        return
+    if args.prefill_summary:
+        prefill_summary(*args.prefill_summary, PREFILL_FILE)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: the layer runs on a single MI355X and has no multi-GPU path "

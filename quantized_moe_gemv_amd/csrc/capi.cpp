@@ -40,7 +40,7 @@ struct Sizes {
 // the start of the workspace, at offsets that do not depend on the token
 // count, and no other kernel writes it.
 struct FusedCarve {
-    size_t rpart, act, piece, ctr, fcnt, total;
+    size_t rpart, act, piece, ctr, total;
     int64_t h_stride, rpart_stride;   // in 8-byte words
 };
 
@@ -55,7 +55,6 @@ FusedCarve fused_carve(const Sizes& z) {
     f.h_stride = (int64_t)up(((size_t)z.Is + (size_t)z.k * z.I) * 8 + 8) / 8;
     f.act = take((size_t)8 * f.h_stride * 8);
     f.piece = take((size_t)z.G_H * z.n_src * 64 * 8);
-    f.fcnt = take((size_t)(kFrontMaxGroups + 1) * 4);   // grouped-path front counters
     f.total = o;
     return f;
 }
@@ -311,7 +310,6 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
     p.c_done = ctr;
     p.f_epoch = ctr + kCtrStride;
     p.f_err = ctr + 2 * kCtrStride;
-    p.fcnt = (uint32_t*)(ws + f.fcnt);
     p.n_router = z.n_router;
     p.n_sd = z.n_sd;
     p.n_sc = z.n_sc;

@@ -8,9 +8,6 @@ namespace mq {
 
 constexpr int kRouterTokens = 4;    // tokens per router workgroup
 constexpr int kMaxTopK = 16;
-// Grouped-path front: the offset of its call counter in the front counter
-// area.
-constexpr int kFrontMaxGroups = 0;
 constexpr int kMaxExperts = 256;
 constexpr int kDownSplits = 4;      // split of the down-projection source list (GEMV path)
 constexpr int kRouterPieces = 8;   // single-launch decode: column pieces of a 16-expert router slice
@@ -84,7 +81,6 @@ struct Plan {
     uint32_t* c_done;    // workgroups finished (cleared at the end of every call)
     uint32_t* f_epoch;   // calls completed with this workspace
     uint32_t* f_err;     // non-zero once a bounded wait has given up
-    uint32_t* fcnt;      // [kFrontMaxGroups + 1] grouped-path front counter (zero between calls)
     int n_router, n_sd, n_sc, n_rh, n_rng, n_src;   // n_rng: tile ranges per routed down slot
     int max_tiles;     // upper bound of scheduled (expert, token chunk) pairs
     int ntile;         // tokens per grouped chunk (32 or 128)
