@@ -13,7 +13,7 @@ per call); the roofline figure divides the call's algorithmic bytes by it.
 
 Also reported (extra fields of the same JSON line): the 128-token prefill
 chunk with Zipf(1.1)-skewed routing, the 30-layer stack (one token through
-30 layers with an RMSNorm between them), the 4096-token prefill (the
+30 layers, each call normalising its input), the 4096-token prefill (the
 matrix-core regime, reported in TFLOP/s), and the fp64 CPU oracle timed on
 a bounded sample of decode tokens.  Prints one JSON line on stdout.
 
@@ -492,8 +492,10 @@ def main():
             for l, dev in enumerate(layers):
                 src = xa[t:t + 1] if l == 0 else bufs[l % 2]
                 dst = bufs[(l + 1) % 2]
-                seq.append(lambda dev=dev, src=src, dst=dst: M.moe_layer_forward(dev, src, out=dst, workspace=ws))
-                seq.append(lambda dst=dst: M.rmsnorm(dst, out=dst))
+                # layers after the first normalise their input inside the call
+                e = 0.0 if l == 0 else cfg.eps
+                seq.append(lambda dev=dev, src=src, dst=dst, e=e:
+                           M.moe_layer_forward(dev, src, out=dst, workspace=ws, input_rmsnorm_eps=e))
             return seq
         scalls = [c for t in range(ntk) for c in token_calls(t)]
         sms, _ = time_graph(torch, scalls, len(scalls), 0)

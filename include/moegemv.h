@@ -140,6 +140,13 @@ typedef struct {
     float* logits;          /* optional [T][E]: router scores (incl. logit_bias) */
     void* workspace;        /* device scratch of workspace_bytes, 256-B aligned */
     size_t workspace_bytes;
+    /* > 0: each input row is first replaced by bf16(x / sqrt(mean(x^2) + eps))
+     * with this eps (a unit-weight RMSNorm in fp32, as mq_rmsnorm computes;
+     * the norm between the layers of a stack), inside the call: the
+     * single-launch path normalises while it stages the token, the other
+     * paths normalise into the workspace first.  x itself is not written.
+     * 0: off.  Negative or not finite: MQ_ERR_UNSUPPORTED. */
+    float input_rmsnorm_eps;
 } mq_opts;
 
 /* Device scratch one call needs for up to max_tokens tokens.  The workspace

@@ -63,7 +63,8 @@ class MqAct(ctypes.Structure):
 
 class MqOpts(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("topk_ids", ctypes.c_void_p), ("topk_w", ctypes.c_void_p),
-                ("logits", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("logits", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("input_rmsnorm_eps", ctypes.c_float)]
 
 
 _P = ctypes.c_void_p
@@ -255,8 +256,9 @@ def moe_layer_forward(layer: DeviceLayer, x: torch.Tensor, out: Optional[torch.T
                       workspace: Optional[torch.Tensor] = None, path: str = "auto",
                       out_dtype=torch.bfloat16, topk_ids: Optional[torch.Tensor] = None,
                       topk_w: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
-                      stream=None) -> torch.Tensor:
-    """out = shared(x) + sum_j w_j expert_j(x) on the current (or given) stream."""
+                      stream=None, input_rmsnorm_eps: float = 0.0) -> torch.Tensor:
+    """out = shared(x) + sum_j w_j expert_j(x) on the current (or given) stream.
+    input_rmsnorm_eps > 0 applies a unit-weight RMSNorm (rounded to bf16) to x first."""
     T = x.shape[0]
     if out is None:
         out = torch.empty((T, layer.hidden), dtype=out_dtype, device=x.device)
@@ -264,7 +266,8 @@ def moe_layer_forward(layer: DeviceLayer, x: torch.Tensor, out: Optional[torch.T
         workspace = layer.new_workspace(T, x.device)
     xa, oa = _act(x), _act(out)
     ptr = lambda t: None if t is None else t.data_ptr()
-    opts = MqOpts(PATHS[path], ptr(topk_ids), ptr(topk_w), ptr(logits), workspace.data_ptr(), workspace.numel())
+    opts = MqOpts(PATHS[path], ptr(topk_ids), ptr(topk_w), ptr(logits), workspace.data_ptr(), workspace.numel(),
+                  float(input_rmsnorm_eps))
     st = _lib.moe_layer_forward(ctypes.byref(xa), ctypes.byref(layer.router), ctypes.byref(layer.pool),
                                 _ref(layer.shared), ctypes.byref(oa), ctypes.byref(opts), _stream_handle(stream))
     _check(st, "moe_layer_forward")

@@ -1,5 +1,6 @@
 // C-ABI entry points: argument checks, workspace carve-up and launches.
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <string.h>
 
 #include <algorithm>
@@ -93,7 +94,7 @@ int device_cus() {
 // Offsets of every workspace region for up to T tokens; returns the total.
 struct Carve {
     size_t r, rsum8, xsum4, plog, ids, wts, hhi, hlo, hsum, shi, slo, ssum, dpart;
-    size_t x16, xso, counts, offsets, perm, inv, sched, nsched, hg, hso, ysort;
+    size_t xn, x16, xso, counts, offsets, perm, inv, sched, nsched, hg, hso, ysort;
     size_t total;
 };
 
@@ -114,6 +115,7 @@ Carve carve(const Sizes& z, int64_t T) {
     c.slo = take(T * z.Is * 2 + 16);
     c.ssum = take(T * z.G_s * 16 + 16);
     c.dpart = take(T * kDownSplits * z.H * 4);
+    c.xn = take(T * z.H * 2);
     c.x16 = take(T * z.H * 2);
     c.xso = take(T * z.G_H * 8);
     c.counts = take((size_t)z.E * 4);
@@ -226,6 +228,8 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
     if (x->row_stride < x->hidden || out->row_stride < out->hidden) return MQ_ERR_SHAPE;
     if (opts->path < MQ_PATH_AUTO || opts->path > MQ_PATH_FUSED) return MQ_ERR_UNSUPPORTED;
     if (opts->path == MQ_PATH_FUSED && T > 1) return MQ_ERR_UNSUPPORTED;
+    const float in_eps = opts->input_rmsnorm_eps;
+    if (!(in_eps >= 0.f) || !(in_eps < INFINITY)) return MQ_ERR_UNSUPPORTED;
     if (T == 0) return MQ_OK;
     if (!x->data || !out->data || !opts->workspace) return x->data && out->data ? MQ_ERR_WORKSPACE : MQ_ERR_NULL;
     if (!aligned(x->data, 16) || x->row_stride % 8) return MQ_ERR_ALIGN;
@@ -326,6 +330,13 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
     }
     const bool fused = opts->path == MQ_PATH_FUSED || (opts->path == MQ_PATH_AUTO && T == 1 && fused_ok(z, cus));
     p.n_rng = fused ? fused_ranges(z, cus) : 0;
+    p.in_eps = fused ? in_eps : 0.f;
+    if (!fused && in_eps > 0.f) {   // normalise into the workspace, then run on that
+        uint16_t* xn = (uint16_t*)(ws + c.xn);
+        hipLaunchKernelGGL(k_rmsnorm, dim3(T), dim3(256), 0, s, p.x, p.x_stride, xn, (int64_t)z.H, z.H, in_eps);
+        p.x = xn;
+        p.x_stride = z.H;
+    }
     if (fused) {
         hipLaunchKernelGGL(k_decode, dim3(cus), dim3(1024), 0, s, p);
         return hipGetLastError() == hipSuccess ? MQ_OK : MQ_ERR_HIP;

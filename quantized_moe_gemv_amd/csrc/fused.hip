@@ -369,7 +369,28 @@ __device__ __forceinline__ void load_token(const Plan& p, TokenLoads& t) {
 __device__ __forceinline__ void stage_token(const Plan& p, Shared& sh, const TokenLoads& tl) {
     const int t = threadIdx.x;
     const int nch = p.H / 8;
-    const uint4 v = tl.x;
+    uint4 v = tl.x;
+    if (p.in_eps > 0.f) {
+        // the input row first goes through a unit-weight RMSNorm, rounded to
+        // bf16 (the norm between the layers of a stack)
+        float s0 = 0.f;
+        if (t < nch) {
+            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s0 += bf16_lo(wv[i]) * bf16_lo(wv[i]) + bf16_hi(wv[i]) * bf16_hi(wv[i]);
+        }
+        s0 = wave_sum(s0);
+        if ((t & 63) == 0) sh.red[t >> 6][1] = s0;
+        __syncthreads();
+        float tot = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) tot += sh.red[w][1];
+        const float inv = 1.0f / sqrtf(tot / (float)p.H + p.in_eps);
+        auto nrm = [&](uint32_t wd) {
+            return (uint32_t)f32_to_bf16(bf16_lo(wd) * inv) | ((uint32_t)f32_to_bf16(bf16_hi(wd) * inv) << 16);
+        };
+        v = make_uint4(nrm(v.x), nrm(v.y), nrm(v.z), nrm(v.w));
+    }
     if (t < p.E) {
         sh.pes[t] = tl.pes;
         sh.lbias[t] = tl.lb;

@@ -29,6 +29,7 @@ struct Plan {
     const float* pes;
     const float* logit_bias;
     float eps;
+    float in_eps;                   // > 0: unit-weight RMSNorm of the input row first (single-launch path)
     const uint8_t* pool_base;
     int64_t expert_stride, gate_off, up_off, down_off;
     const uint8_t* sh_gate;

@@ -40,8 +40,9 @@ def bf16_half_ulp(v: np.ndarray) -> np.ndarray:
     return 2.0 ** (e - 8)
 
 
-def run_gpu(M, dev, x_bits, path="auto", ws=None):
-    """One call with fp32 output and one with bf16 output; routing captured."""
+def run_gpu(M, dev, x_bits, path="auto", ws=None, **kw):
+    """One call with fp32 output and one with bf16 output; routing captured.
+    Extra keywords go to both calls."""
     x = bf16_tensor(x_bits)
     T = x.shape[0]
     ids = torch.empty((T, dev.top_k), dtype=torch.int32, device="cuda")
@@ -50,8 +51,8 @@ def run_gpu(M, dev, x_bits, path="auto", ws=None):
     if ws is None:
         ws = dev.new_workspace(T)
     o32 = M.moe_layer_forward(dev, x, workspace=ws, path=path, out_dtype=torch.float32, topk_ids=ids, topk_w=w,
-                              logits=lg)
-    o16 = M.moe_layer_forward(dev, x, workspace=ws, path=path, out_dtype=torch.bfloat16)
+                              logits=lg, **kw)
+    o16 = M.moe_layer_forward(dev, x, workspace=ws, path=path, out_dtype=torch.bfloat16, **kw)
     torch.cuda.synchronize()
     assert M.workspace_errors(ws) == 0, "a bounded wait of the single-launch path gave up"
     return dict(ids=ids.cpu().numpy(), w=w.cpu().numpy(), logits=lg.cpu().numpy(),

@@ -247,6 +247,32 @@ def test_rmsnorm(M):
     assert diff.max() <= 1 and np.count_nonzero(diff) <= x.size // 1000
 
 
+@pytest.mark.parametrize("path", ["gemv", "grouped", "fused"])
+def test_input_rmsnorm_in_the_call(M, tiny, path):
+    """input_rmsnorm_eps > 0: the call normalises each input row first (x is
+    not written).  Checked against the oracle on the normalised rows; the
+    multi-launch paths normalise with the same kernel as mq_rmsnorm, so there
+    the result equals normalise-then-call bit for bit."""
+    host, dev = tiny
+    T = 1 if path == "fused" else 6
+    eps = host.cfg.eps
+    log("input rmsnorm inside the call", path, "T=%d" % T)
+    # rows far from unit RMS, like the output of a previous layer
+    xg = bf16_tensor(S.make_tokens(S.SEEDS["tiny"] + 31, T, host.cfg.hidden)) * 37.0
+    x = bf16_bits(xg)
+    got = run_gpu(M, dev, x, path, input_rmsnorm_eps=eps)
+    assert np.array_equal(bf16_bits(xg), x)
+    ref = O.forward(host, O.rmsnorm_bf16(x, eps))
+    ok, _ = check_routing(ref, got, host.cfg.top_k)
+    rel = check_output(ref, got, ok)
+    log("  max err / RMS = %.3g" % rel)
+    sep = run_gpu(M, dev, bf16_bits(M.rmsnorm(xg, eps=eps)), path)
+    if path != "fused":
+        assert np.array_equal(sep["ids"], got["ids"]) and np.array_equal(sep["out32"], got["out32"])
+    with pytest.raises(M.MoeError):
+        M.moe_layer_forward(dev, xg, path=path, input_rmsnorm_eps=-1.0)
+
+
 def test_tiny_stack(M):
     log("4-layer tiny stack with RMS norm between layers")
     cfg = S.CONFIGS["tiny"]

@@ -130,13 +130,13 @@ def fake_layer(E=16, H=256, I=64, Is=128, k=2, bits=8):
 
 
 def call(router, pool, sh, T=4, H=256, ws_bytes=None, x_ptr=FAKE, out_ptr=FAKE, x_dtype=0, path=0, ws_ptr=FAKE,
-         x_stride=None):
+         x_stride=None, in_eps=0.0):
     x = M.MqAct(x_ptr, T, H, x_dtype, H if x_stride is None else x_stride)
     out = M.MqAct(out_ptr, T, H, 0, H)
     if ws_bytes is None:
         ws_bytes = M._lib.mq_workspace_bytes(ctypes.byref(router), ctypes.byref(pool),
                                              None if sh is None else ctypes.byref(sh), max(T, 1))
-    opts = M.MqOpts(path, None, None, None, ws_ptr, ws_bytes)
+    opts = M.MqOpts(path, None, None, None, ws_ptr, ws_bytes, in_eps)
     return M._lib.moe_layer_forward(ctypes.byref(x), ctypes.byref(router), ctypes.byref(pool),
                                     None if sh is None else ctypes.byref(sh), ctypes.byref(out),
                                     ctypes.byref(opts), None)
@@ -194,6 +194,9 @@ def test_invalid_calls_are_rejected():
     assert call(r, p, s, x_stride=100) == M.MQ_ERR_SHAPE
     assert call(r, p, s, ws_ptr=FAKE + 128) == M.MQ_ERR_ALIGN
     assert call(r, p, s, path=7) == M.MQ_ERR_UNSUPPORTED
+    for bad in (-1e-6, float("nan"), float("inf")):
+        assert call(r, p, s, in_eps=bad) == M.MQ_ERR_UNSUPPORTED
+        assert call(r, p, s, T=0, x_ptr=None, out_ptr=None, ws_ptr=None, in_eps=bad) == M.MQ_ERR_UNSUPPORTED
     assert M._lib.moe_layer_forward(None, None, None, None, None, None, None) == M.MQ_ERR_NULL
 
 
