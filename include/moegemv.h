@@ -161,6 +161,34 @@ size_t mq_workspace_bytes(const mq_router* router, const mq_expert_pool* pool,
 mq_status moe_layer_forward(const mq_act* x, const mq_router* router, const mq_expert_pool* pool,
                             const mq_shared* shared, mq_act* out, const mq_opts* opts, void* stream);
 
+/* Device scratch of one moe_stack_forward call over these n_layers layers
+ * (HOST arrays of n_layers descriptors; shared NULL or n_layers entries).
+ * Zero-filled once before first use, as for mq_workspace_bytes.  A stack
+ * workspace may also serve moe_layer_forward calls on one token of any of
+ * its layers.  Returns 0 for invalid arguments. */
+size_t mq_stack_workspace_bytes(const mq_router* routers, const mq_expert_pool* pools,
+                                const mq_shared* shared, int32_t n_layers);
+
+/* One decode token through a stack of n_layers layers in one launch (the
+ * runtime decodes a token through every layer in turn, 30 of them for this
+ * model: "Why the runtime has this shape"; "Decode").  Layer l computes as
+ * moe_layer_forward on its input; layer 0's input is x, normalised first
+ * when opts->input_rmsnorm_eps > 0; layer l > 0 takes the previous layer's
+ * output rounded to bf16, normalised first when between_eps > 0 (the
+ * unit-weight RMS norm of mq_rmsnorm).  out receives the last layer's output.
+ * routers, pools, shared: HOST arrays of n_layers descriptors (shared NULL
+ * when no layer has a shared expert), every layer with the sizes of the
+ * first.  x and out: one token.  opts->path AUTO or FUSED (the single-launch
+ * path must fit the device: MQ_ERR_UNSUPPORTED otherwise); opts->topk_ids,
+ * topk_w [n_layers][k] and logits [n_layers][E] are optional per-layer
+ * reports; the workspace must hold mq_stack_workspace_bytes.  The result is
+ * bit for bit that of n_layers FUSED moe_layer_forward calls chained the
+ * same way.  Errors as moe_layer_forward; n_layers < 1 or layers of
+ * different sizes: MQ_ERR_SHAPE. */
+mq_status moe_stack_forward(const mq_act* x, int32_t n_layers, const mq_router* routers,
+                            const mq_expert_pool* pools, const mq_shared* shared, float between_eps,
+                            mq_act* out, const mq_opts* opts, void* stream);
+
 /* HOST result: the sticky error bits that the single-launch path (FUSED)
  * keeps in a workspace.  Bit 0: a bounded wait for another workgroup's
  * partial result gave up, so the calls since the bits were last clear may

@@ -30,7 +30,7 @@ LAYOUT_CANONICAL, LAYOUT_DEV_V1 = 0, 1
 DTYPE_BF16, DTYPE_F32 = 0, 1
 PATHS = {"auto": 0, "gemv": 1, "grouped": 2, "fused": 3}
 GROUP = 64
-EXPORTS = ["moe_layer_forward", "mq_workspace_bytes", "mq_workspace_errors", "mq_rmsnorm", "mq_packed_bytes", "mq_pool_layout",
+EXPORTS = ["moe_layer_forward", "mq_workspace_bytes", "moe_stack_forward", "mq_stack_workspace_bytes", "mq_workspace_errors", "mq_rmsnorm", "mq_packed_bytes", "mq_pool_layout",
            "mq_pack", "mq_unpack", "mq_debug_unpack_codes", "mq_debug_dequant", "mq_status_str"]
 
 
@@ -71,6 +71,8 @@ _P = ctypes.c_void_p
 _sig = {
     "mq_workspace_bytes": (ctypes.c_size_t, [_P, _P, _P, ctypes.c_int32]),
     "moe_layer_forward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P]),
+    "mq_stack_workspace_bytes": (ctypes.c_size_t, [_P, _P, _P, ctypes.c_int32]),
+    "moe_stack_forward": (ctypes.c_int, [_P, ctypes.c_int32, _P, _P, _P, ctypes.c_float, _P, _P, _P]),
     "mq_rmsnorm": (ctypes.c_int, [_P, _P, ctypes.c_float, _P]),
     "mq_workspace_errors": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
     "mq_packed_bytes": (ctypes.c_size_t, [ctypes.c_int32] * 5),
@@ -271,6 +273,58 @@ def moe_layer_forward(layer: DeviceLayer, x: torch.Tensor, out: Optional[torch.T
     st = _lib.moe_layer_forward(ctypes.byref(xa), ctypes.byref(layer.router), ctypes.byref(layer.pool),
                                 _ref(layer.shared), ctypes.byref(oa), ctypes.byref(opts), _stream_handle(stream))
     _check(st, "moe_layer_forward")
+    return out
+
+
+class Stack:
+    """Descriptor arrays of resident layers, all of one size, for moe_stack_forward."""
+
+    def __init__(self, layers):
+        self.layers = list(layers)
+        n = len(self.layers)
+        if n < 1:
+            raise ValueError("a stack needs at least one layer")
+        self.routers = (MqRouter * n)(*[l.router for l in self.layers])
+        self.pools = (MqExpertPool * n)(*[l.pool for l in self.layers])
+        has = [l.shared is not None for l in self.layers]
+        if any(has) and not all(has):
+            raise ValueError("either every layer of a stack has a shared expert or none has")
+        self.shared = (MqShared * n)(*[l.shared for l in self.layers]) if all(has) else None
+        first = self.layers[0]
+        self.hidden, self.top_k, self.num_experts = first.hidden, first.top_k, first.num_experts
+
+    def __len__(self) -> int:
+        return len(self.layers)
+
+    def workspace_bytes(self) -> int:
+        n = _lib.mq_stack_workspace_bytes(self.routers, self.pools, self.shared, len(self))
+        if n == 0:
+            raise MoeError(MQ_ERR_SHAPE, "mq_stack_workspace_bytes")
+        return int(n)
+
+    def new_workspace(self, device="cuda") -> torch.Tensor:
+        return torch.zeros(self.workspace_bytes(), dtype=torch.uint8, device=device)
+
+
+def moe_stack_forward(stack: Stack, x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, between_eps: float = 0.0,
+                      input_rmsnorm_eps: float = 0.0, out_dtype=torch.bfloat16, path: str = "auto",
+                      topk_ids: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None,
+                      logits: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One token through every layer of `stack` in one launch; layer l > 0
+    takes bf16(out_{l-1}), RMS-normalised first when between_eps > 0.
+    topk_ids / topk_w [n_layers][k] and logits [n_layers][E] are optional."""
+    if out is None:
+        out = torch.empty((1, stack.hidden), dtype=out_dtype, device=x.device)
+    if workspace is None:
+        workspace = stack.new_workspace(x.device)
+    xa, oa = _act(x), _act(out)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    opts = MqOpts(PATHS[path], ptr(topk_ids), ptr(topk_w), ptr(logits), workspace.data_ptr(), workspace.numel(),
+                  float(input_rmsnorm_eps))
+    st = _lib.moe_stack_forward(ctypes.byref(xa), len(stack), stack.routers, stack.pools, stack.shared,
+                                float(between_eps), ctypes.byref(oa), ctypes.byref(opts), _stream_handle(stream))
+    _check(st, "moe_stack_forward")
     return out
 
 

@@ -19,6 +19,8 @@ __global__ void k_combine(Plan p);
 __global__ void k_rmsnorm(const uint16_t* x, int64_t xs, uint16_t* y, int64_t ys, int H, float eps);
 __global__ void k_debug_read(const uint8_t* data, int rows, int cols, int bits, uint8_t* codes_out, float* w_out);
 __global__ void k_decode(Plan p);
+__global__ void k_decode_stack(const Plan* plans, int n_layers);
+__global__ void k_stack_plans(Plan base, StackChunk c, Plan* dst);
 mq_status launch_grouped(const Plan& p, hipStream_t s);
 bool grouped_ok(int H, int I, int64_t T, int rows_per_token);
 }  // namespace mq
@@ -41,8 +43,8 @@ struct Sizes {
 // the start of the workspace, at offsets that do not depend on the token
 // count, and no other kernel writes it.
 struct FusedCarve {
-    size_t rpart, act, piece, ctr, total;
-    int64_t h_stride, rpart_stride;   // in 8-byte words
+    size_t rpart, act, piece, xw, ctr, total;
+    int64_t h_stride, rpart_stride, xw_stride;   // in 8-byte words
 };
 
 FusedCarve fused_carve(const Sizes& z) {
@@ -56,6 +58,9 @@ FusedCarve fused_carve(const Sizes& z) {
     f.h_stride = (int64_t)up(((size_t)z.Is + (size_t)z.k * z.I) * 8 + 8) / 8;
     f.act = take((size_t)8 * f.h_stride * 8);
     f.piece = take((size_t)z.G_H * z.n_src * 64 * 8);
+    // one copy per XCD of a stack layer's output row (bf16 pairs)
+    f.xw_stride = (int64_t)up((size_t)z.H / 2 * 8) / 8;
+    f.xw = take((size_t)8 * f.xw_stride * 8);
     f.total = o;
     return f;
 }
@@ -204,6 +209,91 @@ void set_tiles(Sizes* z, int64_t T, bool has_shared) {
     z->max_tiles = (int)((T * z->k + z->ntile - 1) / z->ntile + z->E + z->n_vs * nch);
 }
 
+// Sizes, weights and per-layer router settings of one layer.
+void fill_layer(Plan& p, const Sizes& z, const mq_router* router, const mq_expert_pool* pool,
+                const mq_shared* shared) {
+    p.H = z.H;
+    p.E = z.E;
+    p.E_pad = z.E_pad;
+    p.k = z.k;
+    p.I = z.I;
+    p.Is = z.Is;
+    p.G_H = z.G_H;
+    p.G_I = z.G_I;
+    p.G_s = z.G_s;
+    p.rsplit = z.rsplit;
+    p.rgroups = z.rgroups;
+    p.has_shared = shared != nullptr;
+    p.router_w = (const uint8_t*)router->w.codes;
+    p.router_scale = router->router_scale;
+    p.pes = router->per_expert_scale;
+    p.logit_bias = router->logit_bias;
+    p.eps = router->eps;
+    p.pool_base = (const uint8_t*)pool->base;
+    p.expert_stride = pool->expert_stride;
+    p.gate_off = pool->gate_offset;
+    p.up_off = pool->up_offset;
+    p.down_off = pool->down_offset;
+    if (shared) {
+        p.sh_gate = (const uint8_t*)shared->gate.codes;
+        p.sh_up = (const uint8_t*)shared->up.codes;
+        p.sh_down = (const uint8_t*)shared->down.codes;
+    }
+}
+
+// The single-launch decode's regions and unit counts.
+void fill_fused(Plan& p, const Sizes& z, uint8_t* ws) {
+    const FusedCarve f = fused_carve(z);
+    p.f_rpart = (uint64_t*)(ws + f.rpart);
+    p.f_hs = (uint64_t*)(ws + f.act);
+    p.f_h = p.f_hs + z.Is;
+    p.h_stride = f.h_stride;
+    p.rpart_stride = f.rpart_stride;
+    p.f_piece = (uint64_t*)(ws + f.piece);
+    p.xw_stride = f.xw_stride;
+    uint32_t* ctr = (uint32_t*)(ws + f.ctr);
+    p.c_done = ctr;
+    p.f_epoch = ctr + kCtrStride;
+    p.f_err = ctr + 2 * kCtrStride;
+    p.n_router = z.n_router;
+    p.n_sd = z.n_sd;
+    p.n_sc = z.n_sc;
+    p.n_rh = z.n_rh;
+    p.n_src = z.n_src;
+}
+
+bool same_sizes(const Sizes& a, const Sizes& b) {
+    return a.H == b.H && a.E == b.E && a.k == b.k && a.I == b.I && a.Is == b.Is;
+}
+
+// Checks every layer of a stack; all must have the sizes of the first.
+mq_status check_stack(int32_t n, const mq_router* routers, const mq_expert_pool* pools, const mq_shared* shared,
+                      Sizes* z) {
+    if (!routers || !pools) return MQ_ERR_NULL;
+    if (n < 1) return MQ_ERR_SHAPE;
+    for (int l = 0; l < n; ++l) {
+        Sizes zl;
+        const mq_status st = check_layer(routers + l, pools + l, shared ? shared + l : nullptr, &zl);
+        if (st != MQ_OK) return st;
+        if (l == 0)
+            *z = zl;
+        else if (!same_sizes(*z, zl))
+            return MQ_ERR_SHAPE;
+    }
+    return MQ_OK;
+}
+
+size_t stack_plans_offset(const Sizes& z) { return fused_carve(z).total; }
+
+static_assert(sizeof(Plan) + sizeof(StackChunk) + sizeof(Plan*) <= 4096, "k_stack_plans arguments exceed 4 KiB");
+
+// The per-layer arguments follow the decode state; the total also covers a
+// one-token moe_layer_forward on the same workspace.
+size_t stack_bytes(Sizes z, int32_t n, bool has_shared) {
+    set_tiles(&z, 1, has_shared);
+    return std::max(stack_plans_offset(z) + up((size_t)n * sizeof(Plan)), carve(z, 1).total);
+}
+
 }  // namespace
 
 extern "C" size_t mq_workspace_bytes(const mq_router* router, const mq_expert_pool* pool, const mq_shared* shared,
@@ -242,35 +332,9 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
     Plan p;
     memset(&p, 0, sizeof(p));
     p.T = T;
-    p.H = z.H;
-    p.E = z.E;
-    p.E_pad = z.E_pad;
-    p.k = z.k;
-    p.I = z.I;
-    p.Is = z.Is;
-    p.G_H = z.G_H;
-    p.G_I = z.G_I;
-    p.G_s = z.G_s;
-    p.rsplit = z.rsplit;
-    p.rgroups = z.rgroups;
-    p.has_shared = shared != nullptr;
+    fill_layer(p, z, router, pool, shared);
     p.x = (const uint16_t*)x->data;
     p.x_stride = x->row_stride;
-    p.router_w = (const uint8_t*)router->w.codes;
-    p.router_scale = router->router_scale;
-    p.pes = router->per_expert_scale;
-    p.logit_bias = router->logit_bias;
-    p.eps = router->eps;
-    p.pool_base = (const uint8_t*)pool->base;
-    p.expert_stride = pool->expert_stride;
-    p.gate_off = pool->gate_offset;
-    p.up_off = pool->up_offset;
-    p.down_off = pool->down_offset;
-    if (shared) {
-        p.sh_gate = (const uint8_t*)shared->gate.codes;
-        p.sh_up = (const uint8_t*)shared->up.codes;
-        p.sh_down = (const uint8_t*)shared->down.codes;
-    }
     p.out = out->data;
     p.out_stride = out->row_stride;
     p.out_f32 = out->dtype == MQ_DTYPE_F32;
@@ -303,22 +367,7 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
     p.ntile = z.ntile;
     p.n_vs = z.n_vs;
 
-    const FusedCarve f = fused_carve(z);
-    p.f_rpart = (uint64_t*)(ws + f.rpart);
-    p.f_hs = (uint64_t*)(ws + f.act);
-    p.f_h = p.f_hs + z.Is;
-    p.h_stride = f.h_stride;
-    p.rpart_stride = f.rpart_stride;
-    p.f_piece = (uint64_t*)(ws + f.piece);
-    uint32_t* ctr = (uint32_t*)(ws + f.ctr);
-    p.c_done = ctr;
-    p.f_epoch = ctr + kCtrStride;
-    p.f_err = ctr + 2 * kCtrStride;
-    p.n_router = z.n_router;
-    p.n_sd = z.n_sd;
-    p.n_sc = z.n_sc;
-    p.n_rh = z.n_rh;
-    p.n_src = z.n_src;
+    fill_fused(p, z, ws);
 
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
@@ -367,6 +416,87 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
         hipLaunchKernelGGL(k_down, dim3(T, z.H / 64, kDownSplits), dim3(256), 0, s, p);
         hipLaunchKernelGGL(k_combine, dim3(T, (z.H + 255) / 256), dim3(256), 0, s, p);
     }
+    return hipGetLastError() == hipSuccess ? MQ_OK : MQ_ERR_HIP;
+}
+
+extern "C" size_t mq_stack_workspace_bytes(const mq_router* routers, const mq_expert_pool* pools,
+                                           const mq_shared* shared, int32_t n_layers) {
+    Sizes z;
+    if (check_stack(n_layers, routers, pools, shared, &z) != MQ_OK) return 0;
+    return stack_bytes(z, n_layers, shared != nullptr);
+}
+
+extern "C" mq_status moe_stack_forward(const mq_act* x, int32_t n_layers, const mq_router* routers,
+                                       const mq_expert_pool* pools, const mq_shared* shared, float between_eps,
+                                       mq_act* out, const mq_opts* opts, void* stream) {
+    if (!x || !out || !opts) return MQ_ERR_NULL;
+    Sizes z;
+    mq_status st = check_stack(n_layers, routers, pools, shared, &z);
+    if (st != MQ_OK) return st;
+    if (x->tokens != 1 || out->tokens != 1 || x->hidden != z.H || out->hidden != z.H) return MQ_ERR_SHAPE;
+    if (x->dtype != MQ_DTYPE_BF16 || (out->dtype != MQ_DTYPE_BF16 && out->dtype != MQ_DTYPE_F32))
+        return MQ_ERR_UNSUPPORTED;
+    if (opts->path != MQ_PATH_AUTO && opts->path != MQ_PATH_FUSED) return MQ_ERR_UNSUPPORTED;
+    const float in_eps = opts->input_rmsnorm_eps;
+    if (!(in_eps >= 0.f) || !(in_eps < INFINITY) || !(between_eps >= 0.f) || !(between_eps < INFINITY))
+        return MQ_ERR_UNSUPPORTED;
+    if (!x->data || !out->data || !opts->workspace) return x->data && out->data ? MQ_ERR_WORKSPACE : MQ_ERR_NULL;
+    if (!aligned(x->data, 16) || !aligned(out->data, 4) || !aligned(opts->workspace, kAlign)) return MQ_ERR_ALIGN;
+    if (opts->workspace_bytes < stack_bytes(z, n_layers, shared != nullptr)) return MQ_ERR_WORKSPACE;
+    (void)hipGetLastError();
+    const int cus = device_cus();
+    if (cus <= 0) return MQ_ERR_HIP;
+    if (!fused_ok(z, cus)) return MQ_ERR_UNSUPPORTED;
+
+    uint8_t* ws = (uint8_t*)opts->workspace;
+    Plan base;
+    memset(&base, 0, sizeof(base));
+    base.T = 1;
+    fill_layer(base, z, routers, pools, shared);
+    fill_fused(base, z, ws);
+    base.n_rng = fused_ranges(z, cus);
+    base.x_stride = x->row_stride;
+    base.out_stride = out->row_stride;
+    base.out_f32 = out->dtype == MQ_DTYPE_F32;
+    uint64_t* xw = (uint64_t*)(ws + fused_carve(z).xw);
+    Plan* plans = (Plan*)(ws + stack_plans_offset(z));
+    hipStream_t s = (hipStream_t)stream;
+    for (int l0 = 0; l0 < n_layers; l0 += kStackChunk) {
+        StackChunk c;
+        memset(&c, 0, sizeof(c));
+        c.n = std::min(kStackChunk, n_layers - l0);
+        for (int i = 0; i < c.n; ++i) {
+            const int l = l0 + i;
+            StackLayer& L = c.l[i];
+            const mq_router& r = routers[l];
+            const mq_expert_pool& pl = pools[l];
+            L.x = l == 0 ? (const uint16_t*)x->data : nullptr;
+            L.x_w = l == 0 ? nullptr : xw;
+            L.out = l == n_layers - 1 ? out->data : nullptr;
+            L.out_w = l == n_layers - 1 ? nullptr : xw;
+            L.router_w = (const uint8_t*)r.w.codes;
+            L.router_scale = r.router_scale;
+            L.pes = r.per_expert_scale;
+            L.logit_bias = r.logit_bias;
+            L.eps = r.eps;
+            L.in_eps = l == 0 ? in_eps : between_eps;
+            L.pool_base = (const uint8_t*)pl.base;
+            L.expert_stride = pl.expert_stride;
+            L.gate_off = pl.gate_offset;
+            L.up_off = pl.up_offset;
+            L.down_off = pl.down_offset;
+            if (shared) {
+                L.sh_gate = (const uint8_t*)shared[l].gate.codes;
+                L.sh_up = (const uint8_t*)shared[l].up.codes;
+                L.sh_down = (const uint8_t*)shared[l].down.codes;
+            }
+            L.ids_out = opts->topk_ids ? opts->topk_ids + (int64_t)l * z.k : nullptr;
+            L.w_out = opts->topk_w ? opts->topk_w + (int64_t)l * z.k : nullptr;
+            L.logits_out = opts->logits ? opts->logits + (int64_t)l * z.E : nullptr;
+        }
+        hipLaunchKernelGGL(k_stack_plans, dim3(c.n), dim3(64), 0, s, base, c, plans + l0);
+    }
+    hipLaunchKernelGGL(k_decode_stack, dim3(cus), dim3(1024), 0, s, (const Plan*)plans, (int)n_layers);
     return hipGetLastError() == hipSuccess ? MQ_OK : MQ_ERR_HIP;
 }
 

@@ -1,0 +1,930 @@
+// Single-launch decode of one token through the whole layer.
+//
+// The layer is cut into units of weight streaming, given to one workgroup
+// per compute unit:
+//   without expert ids: router pieces    16 experts x a column range  -> partial scores
+//                       shared gate/up   32 rows x all columns         -> h (shared)
+//                       shared down      64 output rows x a chunk of Is -> partial outputs
+//   with expert ids:    routed gate/up   (slot j, 32 rows, all columns) -> h
+//                       routed down      (slot j, a range of output tiles) -> partial outputs
+//                       output sums      (64 output rows, every source) -> out
+// Full-row gate/up units hold complete sums, so only the router scores, the
+// activations and the partial outputs cross between workgroups.  A
+// workgroup puts out the loads of all its units that need no expert ids at
+// once, and those of the rest as soon as it knows the ids, so the memory
+// system has its whole remaining stream in flight; the units are computed as
+// their data lands.  Each wait is bounded.  Partial results are
+// 64-bit words carrying the call's epoch in their high half: a reader
+// issues all of its loads, then re-reads only the words whose tag is not yet
+// current.  Each sum has a fixed reducer which sums in a fixed order, so
+// results repeat bit for bit.
+//
+// Results that many workgroups read (partial router scores, GeGLU
+// activations) are written once per XCD (eight copies) and each reader takes
+// the copy of its own XCD, so the readers do not all queue on the same
+// memory channels.  Every workgroup that runs routed units sums the router
+// scores and selects the experts itself, which costs less than waiting for
+// one workgroup to publish them.
+//
+// The shared expert and the router do not depend on each other, so the
+// shared gate/up streams while the routing decision is made ("Decode",
+// phase table: the shared expert overlaps the wait for the expert ids).
+#pragma once
+#include <math.h>
+
+#include "device.h"
+#include "plan.h"
+
+namespace mq {
+// Internal linkage: each kernel file compiles its own copy, with its own
+// kOpaqueTid (defined before this file is included).
+namespace {
+
+// 1024 threads: four waves per SIMD, so the dependent chains of one wave
+// (dequantisation, dot steps, reductions) are hidden behind the others.
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+constexpr int kItems = 2;           // 16-byte code loads per lane per unit (<= 32 items)
+constexpr int kSpinLimit = 1 << 20;
+constexpr int kCopies = 8;         // replicas of broadcast results, one per XCD
+constexpr int kItemsRH = 6;        // 16-byte code loads per lane of a full-row gate/up unit (2 G_H <= 96)
+constexpr int kSlotsSD = 2;        // shared down pieces of a shared workgroup
+constexpr int kTilesD = 3;         // output tiles of a routed down unit
+constexpr int kGroupsD = 2;        // column groups per wave pair and tile of a routed down unit (G_I <= 16)
+constexpr int kItemsD = kGroupsD * kTilesD;   // 16-byte code loads per lane of a routed down unit
+constexpr int kRq = kRouterPieces;
+
+// The copy of a broadcast result that this workgroup reads: the one of the
+// XCD it runs on (XCC_ID).  Every copy holds the same words, so the choice
+// only decides which memory channels serve the read.
+__device__ __forceinline__ int xcc_copy() {
+    uint32_t v;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+    return (int)(v & (kCopies - 1));
+}
+
+// The thread's index.  With kOpaqueTid it is opaque to the optimiser at each
+// use: in the stack kernel's layer loop, index arithmetic is then recomputed
+// where it is used instead of being hoisted and held in registers across the
+// whole layer (which spills).  The single-layer kernel keeps plain indices.
+__device__ __forceinline__ unsigned tix() {
+    unsigned t = threadIdx.x;
+    if constexpr (kOpaqueTid) asm volatile("" : "+v"(t));
+    return t;
+}
+
+// ----------------------------------------------------------------- words and counters
+
+__device__ __forceinline__ uint64_t ld_word(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_word(uint64_t* p, uint32_t tag, uint32_t payload) {
+    __hip_atomic_store(p, ((uint64_t)tag << 32) | payload, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_ctr(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Re-reads the words of v (at p[m * pstride], m < 4) whose tag is not yet
+// current, all of them in each round, until every one is.  Bounded: gives
+// up after kSpinLimit rounds, or at once when any wait of the call has
+// already given up, and records that in *err.  Bit m of `want` selects the
+// words that take part.
+__device__ __forceinline__ void await_words(const uint64_t* p, int pstride, uint64_t v[4], uint32_t want,
+                                            uint32_t tag, uint32_t* err) {
+    uint32_t stale = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        if (((want >> m) & 1) && (uint32_t)(v[m] >> 32) != tag) stale |= 1u << m;
+    int spins = 0;
+    while (stale) {
+        if (++spins > kSpinLimit || ((spins & 63) == 0 && ld_ctr(err))) {
+            atomicOr(err, 1u);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            if ((stale >> m) & 1) v[m] = ld_word(p + m * pstride);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            if ((uint32_t)(v[m] >> 32) == tag) stale &= ~(1u << m);
+    }
+}
+
+// Payload of a word once its tag is current.  Bounded, and gives up at once
+// once any wait of the call has failed (recorded in *err).
+__device__ __forceinline__ uint32_t wait_word(const uint64_t* p, uint32_t tag, uint32_t* err) {
+    uint64_t v = ld_word(p);
+    int spins = 0;
+    while ((uint32_t)(v >> 32) != tag) {
+        if (++spins > kSpinLimit || ((spins & 63) == 0 && ld_ctr(err))) {
+            atomicOr(err, 1u);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+        v = ld_word(p);
+    }
+    return (uint32_t)v;
+}
+
+// Payloads of words base[0 .. n) into dst, for n <= 4 * kThreads: every
+// load is issued before any is checked, so the gather costs one round trip
+// when the words are there (a stale word is then waited for on its own).
+__device__ __forceinline__ void gather_words(const uint64_t* base, int n, uint32_t tag, uint32_t* err,
+                                             uint32_t* dst) {
+    if (n <= 0) {
+        __syncthreads();
+        return;
+    }
+    uint64_t v[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int i = tix() + kThreads * m;
+        v[m] = ld_word(base + (i < n ? i : n - 1));   // unconditional: see issue_loads
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int i = tix() + kThreads * m;
+        if (i < n) {
+            if ((uint32_t)(v[m] >> 32) != tag) v[m] = ((uint64_t)tag << 32) | wait_word(base + i, tag, err);
+            dst[i] = (uint32_t)v[m];
+        }
+    }
+    __syncthreads();
+}
+
+
+// ----------------------------------------------------------------- units
+
+enum { U_ROUTER = 0, U_SH = 1, U_SD = 2, U_RH = 3, U_NONE = 4 };
+
+struct Unit {
+    int kind;
+    int a, b;         // router: slice; SH: half tile; SD: out tile, chunk; RH: slot, half tile
+    int q;            // piece index of the column range (router, gate/up)
+    int g0, ng;       // column-group range
+};
+
+struct Shared {
+    // arrays read with 16-byte LDS accesses come first and stay 16-byte aligned
+    alignas(16) uint16_t x[4096];
+    alignas(16) uint16_t h16[16 * 64];   // one source's GeGLU activations, fp16
+    alignas(16) float lg[256];           // expert scores (padding: -inf)
+    alignas(16) uint64_t key[256];       // selection keys (padding: 0)
+    alignas(16) float xr[4096];          // router input numerator x * router_scale
+    alignas(16) float selv[kMaxTopK];    // selected scores (padding: -inf)
+    float pes[256];           // per_expert_scale (1 when absent)
+    float lbias[256];         // logit_bias (0 when absent)
+    alignas(16) uint32_t gbuf[2048];     // gathered payloads (partial results of other units)
+    float xsum[64 * 4];       // x summed over each lane's 16 columns of a group (4-bit blocks)
+    float rsum[64 * 4];       // router input summed over each lane's 16 columns (8-bit blocks)
+    float c8[512];            // per 8-column chunk: sum of x
+    float c4[1024];           // per 4-column quarter: sum of x * router_scale
+    float red[kWaves][64];
+    float red2[kWaves][kTilesD][32];   // per-wave row sums of a routed down unit
+    float hsum[16 * 4];
+    int32_t ids[kMaxTopK];
+    float wts[kMaxTopK];
+    float rc;                 // router input scale 1/sqrt(mean(x^2)+eps)/sqrt(H)
+    uint32_t flag;
+};
+
+// Column range q of nq over G groups.
+__device__ __forceinline__ void krange(int G, int nq, int q, int* g0, int* ng) {
+    const int a = q * G / nq, b = (q + 1) * G / nq;
+    *g0 = a;
+    *ng = b - a;
+}
+
+__device__ __forceinline__ Unit no_unit() {
+    Unit x;
+    x.kind = U_NONE;
+    x.a = x.b = x.q = x.g0 = x.ng = 0;
+    return x;
+}
+
+// Router piece i: 16 experts (slice i / 8) x column range i % 8.
+__device__ __forceinline__ Unit unit_router(const Plan& p, int i) {
+    Unit x = no_unit();
+    if (i < p.n_router) {
+        x.kind = U_ROUTER;
+        x.a = i / kRq;
+        x.q = i % kRq;
+        krange(p.G_H, kRq, x.q, &x.g0, &x.ng);
+    }
+    return x;
+}
+
+// Full-row shared gate/up unit i: half tile i of the shared expert, every
+// column group.
+__device__ __forceinline__ Unit unit_sh(const Plan& p, int i) {
+    Unit x = no_unit();
+    if (i >= 0 && i < 2 * p.G_s) {
+        x.kind = U_SH;
+        x.a = i;
+        x.ng = p.G_H;
+    }
+    return x;
+}
+
+// Full-row routed gate/up unit w: slot w / (2 G_I), half tile w % (2 G_I),
+// every column group.
+__device__ __forceinline__ Unit unit_rh(const Plan& p, int w) {
+    Unit x = no_unit();
+    if (w < p.n_rh) {
+        x.kind = U_RH;
+        x.a = w / (2 * p.G_I);
+        x.b = w % (2 * p.G_I);
+        x.ng = p.G_H;
+    }
+    return x;
+}
+
+// Shared down piece i: output tile i / n_sc, chunk i % n_sc of Is.
+__device__ __forceinline__ Unit unit_sd(const Plan& p, int i) {
+    Unit x = no_unit();
+    if (i >= 0 && i < p.n_sd) {
+        x.kind = U_SD;
+        x.a = i / p.n_sc;
+        x.b = i % p.n_sc;
+        x.g0 = x.b * p.G_I;
+        x.ng = min(p.G_I, p.G_s - x.g0);
+    }
+    return x;
+}
+
+// A routed down unit: one selected expert (slot b) over output tiles
+// t0 .. t0+nt-1, so its activations are staged once for all those tiles.
+struct DownUnit {
+    int b, t0, nt;
+};
+
+// Workgroup roles.  Workgroups 0 .. n_rh-1 ("routed") run one full-row
+// routed gate/up unit and shared down piece w each; the m = grid - n_rh
+// others ("shared") run the full-row shared gate/up units (one each, the
+// first 2 G_s of them) and any further shared down pieces.  Routed down
+// work: the first S = min(n_rh / G_H, k) slots one tile per routed
+// workgroup, the other slots in n_rng tile ranges each on the shared
+// workgroups.  Router piece i runs on workgroup i and the sum of output tile
+// a on workgroup a, after all its other work.
+__device__ __forceinline__ DownUnit unit_rdu(const Plan& p, int w, int nwg) {
+    DownUnit d;
+    d.b = d.t0 = d.nt = 0;
+    const int S = min(p.n_rh / p.G_H, p.k);
+    if (w < p.n_rh) {
+        if (w < S * p.G_H) {
+            d.b = w / p.G_H;
+            d.t0 = w % p.G_H;
+            d.nt = 1;
+        }
+        return d;
+    }
+    const int v = w - p.n_rh;
+    if (S < p.k && v < (p.k - S) * p.n_rng) {
+        const int r = v % p.n_rng;
+        d.b = S + v / p.n_rng;
+        d.t0 = r * p.G_H / p.n_rng;
+        d.nt = (r + 1) * p.G_H / p.n_rng - d.t0;
+    }
+    return d;
+}
+
+// Shared down piece s of workgroup w: piece w on the routed workgroups, the
+// rest (j = n_rh + v + m s for shared workgroup v) on the shared ones.
+__device__ __forceinline__ Unit sd_piece(const Plan& p, int w, int nwg, int s) {
+    if (w < p.n_rh) return s == 0 ? unit_sd(p, w) : no_unit();
+    const int m = nwg - p.n_rh, j = p.n_rh + (w - p.n_rh) + m * s;
+    return unit_sd(p, j);
+}
+
+// A unit's weight loads, issued before the unit waits or computes.
+template <int N>
+struct LoadsN {
+    uint4 c[N];
+    uint2 s[N];
+};
+typedef LoadsN<kItems> Loads;
+
+__device__ __forceinline__ const uint8_t* tile4(const uint8_t* m, int tile, int G) {
+    return m + (int64_t)tile * G * kBlk4;
+}
+
+// The loads of one unit.  Within a unit, item it of wave w (it = w + 8m)
+// reads the block base[it & 1] + (it >> 1) * step, so each wave needs two
+// uniform base pointers, fixed for the unit, and one scalar add per item:
+//   router:  it -> 8-bit block (slice rows, group g0 + it)
+//   gate/up: even it -> gate, odd it -> up, group g0 + it/2, one half tile
+//   down:    group g0 + it/2, rows of half (it & 1) of the output tile
+// Every item issues its two loads unconditionally (items past the unit's
+// end read the router's first block and are skipped when computed): a
+// register that a load may still be filling is never written on another
+// path, which would make that write wait for the load.
+template <int N>
+__device__ __forceinline__ void issue_loads(const Plan& p, const Shared& sh, const Unit& x, LoadsN<N>& L) {
+    const int wave = wave_id(), lane = tix() & 63, par = wave & 1;
+    const uint8_t* b0 = p.router_w;
+    const uint8_t* b1 = p.router_w;
+    int64_t step = 0;
+    int n = 0, oc = 0, os = kCodes4;
+    if (x.kind == U_ROUTER) {
+        const int tile = x.a >> 2, j = x.a & 3;
+        b0 = p.router_w + ((int64_t)tile * p.G_H + x.g0) * kBlk8;
+        b1 = b0 + kBlk8;
+        step = 2 * kBlk8;
+        n = x.ng;
+        oc = j * 1024;
+        os = kCodes8 + 8 * (j >> 1);   // pair j is .x (j even) or .y
+    } else if (x.kind == U_SH || x.kind == U_RH) {
+        const int ht = x.kind == U_SH ? x.a : x.b;
+        const uint8_t* g;
+        const uint8_t* u;
+        if (x.kind == U_SH) {
+            g = p.sh_gate;
+            u = p.sh_up;
+        } else {
+            const uint8_t* blob = p.pool_base + (int64_t)sh.ids[x.a] * p.expert_stride;
+            g = blob + p.gate_off;
+            u = blob + p.up_off;
+        }
+        const int64_t o = ((int64_t)(ht >> 1) * p.G_H + x.g0) * kBlk4;
+        b0 = g + o;
+        b1 = u + o;
+        step = kBlk4;
+        n = 2 * x.ng;
+        oc = (ht & 1) * 1024;
+        os = kCodes4 + 8 * (ht & 1);
+    } else if (x.kind == U_SD) {
+        b0 = b1 = p.sh_down + ((int64_t)x.a * p.G_s + x.g0) * kBlk4;
+        step = kBlk4;
+        n = 2 * x.ng;
+        oc = par * 1024;
+        os = kCodes4 + 8 * par;
+    }
+    const uint8_t* wb = (par ? b1 : b0) + (int64_t)(wave >> 1) * step;
+    const int lc = oc + lane * 16, ls = os + (lane & 15) * 16;
+#pragma unroll
+    for (int m = 0; m < N; ++m) {
+        const uint8_t* blk = wave + kWaves * m < n ? wb + (int64_t)(kWaves / 2) * m * step : p.router_w;
+        L.c[m] = ld_stream16(blk + lc);
+        L.s[m] = *(const uint2*)(blk + ls);
+    }
+}
+
+// ----------------------------------------------------------------- setup
+
+__device__ __forceinline__ float sum8_bf16(const uint4& v) {
+    return ((bf16_lo(v.x) + bf16_hi(v.x)) + (bf16_lo(v.y) + bf16_hi(v.y))) +
+           ((bf16_lo(v.z) + bf16_hi(v.z)) + (bf16_lo(v.w) + bf16_hi(v.w)));
+}
+
+// The token and the small per-expert vectors, loaded into registers before
+// any weight so that they head the memory queues.
+struct TokenLoads {
+    uint4 x;
+    uint64_t xw[4];  // the same columns as tagged bf16 pairs (input published by the previous layer)
+    float4 r0, r1;   // router_scale of the thread's 8 columns
+    float pes, lb;   // per_expert_scale and logit_bias of expert tix()
+    bool need;       // the workgroup runs a unit that reads the token
+};
+
+__device__ __forceinline__ void load_token(const Plan& p, TokenLoads& t, bool need) {
+    const int c = tix();
+    t.x = make_uint4(0, 0, 0, 0);
+    t.r0 = t.r1 = make_float4(1.f, 1.f, 1.f, 1.f);
+    t.pes = 1.f;
+    t.lb = 0.f;
+    t.need = need;
+    if (c < p.H / 8) {
+        if (!need) {
+        } else if (p.x_w) {
+            const uint64_t* xw = p.x_w + xcc_copy() * p.xw_stride + 4 * c;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) t.xw[i] = ld_word(xw + i);
+        } else {
+            t.x = *(const uint4*)(p.x + 8 * c);
+        }
+        if (p.router_scale) {
+            t.r0 = *(const float4*)(p.router_scale + 8 * c);
+            t.r1 = *(const float4*)(p.router_scale + 8 * c + 4);
+        }
+    }
+    if (c < p.E) {
+        if (p.pes) t.pes = p.pes[c];
+        if (p.logit_bias) t.lb = p.logit_bias[c];
+    }
+}
+
+// The token into LDS, the router input scale, and the column sums the block
+// dots need: thread c holds columns 8c .. 8c+7 and contributes its partial
+// sums; each lane set is then a sum of two (4-bit) or four (8-bit) of them.
+__device__ __forceinline__ void stage_token(const Plan& p, Shared& sh, const TokenLoads& tl, uint32_t tag) {
+    const int t = tix();
+    const int nch = p.H / 8;
+    uint4 v = tl.x;
+    if (p.x_w && tl.need && t < nch) {
+        // the previous layer's output row, published with that layer's tag
+        // (one below this layer's): wait for any word not yet current
+        const uint64_t* xw = p.x_w + xcc_copy() * p.xw_stride + 4 * t;
+        uint64_t w4[4] = {tl.xw[0], tl.xw[1], tl.xw[2], tl.xw[3]};
+        await_words(xw, 1, w4, 0xFu, tag - 1, p.f_err);
+        v = make_uint4((uint32_t)w4[0], (uint32_t)w4[1], (uint32_t)w4[2], (uint32_t)w4[3]);
+    }
+    if (p.in_eps > 0.f) {
+        // the input row first goes through a unit-weight RMSNorm, rounded to
+        // bf16 (the norm between the layers of a stack)
+        float s0 = 0.f;
+        if (t < nch) {
+            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s0 += bf16_lo(wv[i]) * bf16_lo(wv[i]) + bf16_hi(wv[i]) * bf16_hi(wv[i]);
+        }
+        s0 = wave_sum(s0);
+        if ((t & 63) == 0) sh.red[t >> 6][1] = s0;
+        __syncthreads();
+        float tot = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) tot += sh.red[w][1];
+        const float inv = 1.0f / sqrtf(tot / (float)p.H + p.in_eps);
+        auto nrm = [&](uint32_t wd) {
+            return (uint32_t)f32_to_bf16(bf16_lo(wd) * inv) | ((uint32_t)f32_to_bf16(bf16_hi(wd) * inv) << 16);
+        };
+        v = make_uint4(nrm(v.x), nrm(v.y), nrm(v.z), nrm(v.w));
+    }
+    if (t < p.E) {
+        sh.pes[t] = tl.pes;
+        sh.lbias[t] = tl.lb;
+    }
+    float ss = 0.f;
+    if (t < nch) {
+        *(uint4*)(sh.x + 8 * t) = v;
+        const float a[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                            bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+        const float rs[8] = {tl.r0.x, tl.r0.y, tl.r0.z, tl.r0.w, tl.r1.x, tl.r1.y, tl.r1.z, tl.r1.w};
+        float q0 = 0.f, q1 = 0.f;   // sums of columns 8t..8t+3 and 8t+4..8t+7 (times router_scale)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ss += a[2 * i] * a[2 * i] + a[2 * i + 1] * a[2 * i + 1];
+            const float r = a[2 * i] * rs[2 * i] + a[2 * i + 1] * rs[2 * i + 1];
+            if (i < 2) q0 += r; else q1 += r;
+        }
+        float4* xr = (float4*)(sh.xr + 8 * t);
+        xr[0] = make_float4(a[0] * rs[0], a[1] * rs[1], a[2] * rs[2], a[3] * rs[3]);
+        xr[1] = make_float4(a[4] * rs[4], a[5] * rs[5], a[6] * rs[6], a[7] * rs[7]);
+        sh.c8[t] = sum8_bf16(v);
+        sh.c4[2 * t] = q0;
+        sh.c4[2 * t + 1] = q1;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    if ((t & 63) == 0) sh.red[t >> 6][0] = ss;
+    __syncthreads();
+    if (t < p.G_H * 4) {
+        float tot = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) tot += sh.red[w][0];
+        const float rc = (1.0f / sqrtf(tot / (float)p.H + p.eps)) * (1.0f / sqrtf((float)p.H));
+        if (t == 0) sh.rc = rc;
+        const int g = t >> 2, kb = t & 3;
+        // 4-bit lane set: chunks 8g + kb (columns 32*0 + 8kb) and 8g + 4 + kb
+        sh.xsum[t] = sh.c8[8 * g + kb] + sh.c8[8 * g + 4 + kb];
+        // 8-bit lane set: quarters (16 ks + 4 kb) for ks = 0..3, quarter index = 16g + 4ks + kb
+        const float r = (sh.c4[16 * g + kb] + sh.c4[16 * g + 4 + kb]) + (sh.c4[16 * g + 8 + kb] + sh.c4[16 * g + 12 + kb]);
+        sh.rsum[t] = r * rc;
+    }
+    __syncthreads();
+}
+
+// Expert ids and weights, computed by every workgroup that needs them from
+// its XCD's copy of the partial scores: sum the pieces of each score in
+// order, rank every expert (the number of scores that beat it: higher, or
+// equal with a lower index), keep ranks < k in rank order, then the softmax
+// over the selected scores times per_expert_scale.  One workgroup reports
+// the scores, ids and weights to the caller's optional outputs.
+__device__ __forceinline__ void fetch_ids(const Plan& p, Shared& sh, uint32_t tag) {
+    const int nslice = (p.E + 15) / 16, epad = (p.E + 31) & ~31;
+    gather_words(p.f_rpart + xcc_copy() * p.rpart_stride, nslice * kRq * 16, tag, p.f_err, sh.gbuf);
+    // workgroup 0 runs the first routed unit, so it always fetches the ids
+    const bool reporter = blockIdx.x == 0;
+    // Selection key of expert e: the score's bits made order-preserving as an
+    // unsigned integer (NaN as -inf, -0 as +0) above 0xFFFF - e, so that keys
+    // compare as (score, then lower index); padding keys are 0, below all.
+    for (int e = tix(); e < epad; e += kThreads) {
+        float s = -INFINITY;
+        uint64_t key = 0;
+        if (e < p.E) {
+            const int slice = e >> 4, r = e & 15;
+            float a[kRq];
+#pragma unroll
+            for (int q = 0; q < kRq; ++q) a[q] = __uint_as_float(sh.gbuf[(slice * kRq + q) * 16 + r]);
+            s = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+            s += sh.lbias[e];
+            if (reporter && p.logits_out) p.logits_out[e] = s;
+            if (!(s == s)) s = -INFINITY;   // a NaN score ranks last; ids stay distinct
+            if (s == 0.f) s = 0.f;
+            uint32_t u = __float_as_uint(s);
+            u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+            key = ((uint64_t)u << 32) | (uint32_t)(0xFFFF - e);
+        }
+        sh.lg[e] = s;
+        sh.key[e] = key;
+    }
+    if (tix() < kMaxTopK) sh.selv[tix()] = -INFINITY;
+    __syncthreads();
+    // Rank of expert e = the number of keys above its key.  Each expert's
+    // comparisons are split over nparts adjacent lanes, summed by shuffles.
+    // Part q reads the key pairs q, q + nparts, ...: the parts of a wave read
+    // adjacent 16-byte pieces, on distinct LDS banks.
+    {
+        const int lg2 = epad <= 128 ? 3 : 2, nparts = 1 << lg2;   // nparts * epad <= kThreads
+        const int e = tix() >> lg2, part = tix() & (nparts - 1), len = epad >> lg2;
+        int rank = 0;
+        if (e < p.E) {
+            const uint64_t me = sh.key[e];
+            const uint64_t* kp = sh.key + 2 * part;
+#pragma unroll 8
+            for (int o = 0; o < len; o += 2) {
+                const ulonglong2 k0 = *(const ulonglong2*)(kp + o * nparts);
+                rank += (int)(k0.x > me) + (int)(k0.y > me);
+            }
+        }
+        rank += __shfl_xor(rank, 1, 64);
+        rank += __shfl_xor(rank, 2, 64);
+        if (lg2 == 3) rank += __shfl_xor(rank, 4, 64);
+        if (e < p.E && part == 0 && rank < p.k) {
+            sh.ids[rank] = e;
+            sh.selv[rank] = sh.lg[e];
+        }
+    }
+    __syncthreads();
+    // softmax over the selected scores (padding entries are -inf, so 0)
+    if (wave_id() == 0) {
+        const int j = tix() & (kMaxTopK - 1);
+        const float ej = expf(sh.selv[j] - sh.selv[0]);
+        float den = ej;
+#pragma unroll
+        for (int o = 1; o < kMaxTopK; o <<= 1) den += __shfl_xor(den, o, 64);
+        if (tix() < p.k) {
+            const float w = ej / den * sh.pes[sh.ids[j]];
+            sh.wts[j] = w;
+            if (reporter) {
+                if (p.ids_out) p.ids_out[j] = sh.ids[j];
+                if (p.w_out) p.w_out[j] = w;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// One source's activations (64 tagged words per group, from group g0, fp16
+// in the low half of the payload) into LDS, with each lane's column sums.
+__device__ __forceinline__ void stage_h(const Plan& p, Shared& sh, const uint64_t* h, int g0, int ng, uint32_t tag) {
+    gather_words(h + 64 * g0, ng * 64, tag, p.f_err, sh.gbuf);
+    for (int q = tix(); q < ng * 64; q += kThreads) sh.h16[q] = (uint16_t)sh.gbuf[q];
+    __syncthreads();
+    for (int q = tix(); q < ng * 4; q += kThreads) {
+        const int gl = q >> 2, qb = q & 3;
+        const uint4 a0 = *(const uint4*)(sh.h16 + 64 * gl + 8 * qb);
+        const uint4 a1 = *(const uint4*)(sh.h16 + 64 * gl + 32 + 8 * qb);
+        const uint32_t w[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        float v = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v += f16_lo(w[i]) + f16_hi(w[i]);
+        sh.hsum[q] = v;
+    }
+    __syncthreads();
+}
+
+// ----------------------------------------------------------------- compute
+
+// Rows 16*r + lane%16 (r = 0, 1) of one 4-bit half block against the lane's
+// 16 input values (bf16 pairs xa for columns 8*(lane/16).., xb for +32):
+// adds sum((128 + q) * x) to d[r].
+__device__ __forceinline__ void half_block_dot(const uint4& c, const uint4& xa, const uint4& xb, float d[2]) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    const uint32_t xk[2][4] = {{xa.x, xa.y, xa.z, xa.w}, {xb.x, xb.y, xb.z, xb.w}};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) d[i >> 1] = dot2_bf16(q4_pair(w[i], q), xk[i & 1][q], d[i >> 1]);
+}
+
+// The same with fp16 activations: adds sum((1024 + q) * h) to d[r].
+__device__ __forceinline__ void half_block_dot16(const uint4& c, const uint4& ha, const uint4& hb, float d[2]) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    const uint32_t hk[2][4] = {{ha.x, ha.y, ha.z, ha.w}, {hb.x, hb.y, hb.z, hb.w}};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) d[i >> 1] = dot2_f16(q4_pair16(w[i], q), hk[i & 1][q], d[i >> 1]);
+}
+
+// Row totals over the lanes and waves: v[r] holds rows 16*r + lane%16; after
+// the call sh.red[w][row] holds wave w's part of each row.
+__device__ __forceinline__ void reduce_rows(Shared& sh, const float* v, int nr) {
+    const int wave = wave_id(), lane = tix() & 63;
+    for (int r = 0; r < nr; ++r) {
+        const float s = sum_kb(v[r]);
+        if (lane < 16) sh.red[wave][16 * r + lane] = s;
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ float row_total(const Shared& sh, int row) {
+    float v = 0.f;
+    for (int w = 0; w < kWaves; ++w) v += sh.red[w][row];
+    return v;
+}
+
+// Row (0..63) of a unit whose even waves hold rows 0..31 and odd waves
+// rows 32..63 (gate/up: gate and up rows; down: the two halves of a tile).
+__device__ __forceinline__ float row_total_par(const Shared& sh, int row) {
+    const int par = row >> 5, r = row & 31;
+    float v = 0.f;
+    for (int w = par; w < kWaves; w += 2) v += sh.red[w][r];
+    return v;
+}
+
+__device__ __forceinline__ void run_router(const Plan& p, Shared& sh, const Unit& x, const Loads& L, uint32_t tag) {
+    const int wave = wave_id(), lane = tix() & 63, kb = lane >> 4;
+    float acc = 0.f;
+#pragma unroll
+    for (int m = 0; m < kItems; ++m) {
+        const int it = wave + kWaves * m;
+        if (it < x.ng) {
+            const int g = x.g0 + it;
+            const uint32_t cw[4] = {L.c[m].x, L.c[m].y, L.c[m].z, L.c[m].w};
+            float d = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float4 r = *(const float4*)(sh.xr + 64 * g + 16 * i + 4 * kb);
+                d = fmaf((float)(cw[i] & 0xFFu), r.x, d);
+                d = fmaf((float)((cw[i] >> 8) & 0xFFu), r.y, d);
+                d = fmaf((float)((cw[i] >> 16) & 0xFFu), r.z, d);
+                d = fmaf((float)(cw[i] >> 24), r.w, d);
+            }
+            const uint32_t sw = (x.a & 1) ? L.s[m].y : L.s[m].x;
+            acc = fmaf(bf16_lo(sw), d * sh.rc, fmaf(bf16_hi(sw), sh.rsum[g * 4 + kb], acc));
+        }
+    }
+    reduce_rows(sh, &acc, 1);
+    if (wave_id() < 16 * kCopies / 64) {
+        const int r = tix() & 15, c = tix() >> 4;
+        st_word(p.f_rpart + c * p.rpart_stride + (int64_t)(x.a * kRq + x.q) * 16 + r, tag,
+                __float_as_uint(row_total(sh, r)));
+    }
+    __syncthreads();
+}
+
+// Full-row gate/up unit (routed: one selected expert; shared: the shared
+// expert): 32 rows of gate and up over every column group, so the workgroup
+// holds complete sums and publishes h = gelu(g) * u for its 32 rows without
+// any partial exchange.
+__device__ __forceinline__ void run_rh(const Plan& p, Shared& sh, const Unit& x, const LoadsN<kItemsRH>& L,
+                                       uint32_t tag) {
+    const int wave = wave_id(), lane = tix() & 63, kb = lane >> 4;
+    float acc[2] = {0.f, 0.f};    // rows 16*r + lane%16 of the wave's matrix (gate: even waves, up: odd)
+#pragma unroll
+    for (int m = 0; m < kItemsRH; ++m) {
+        const int it = wave + kWaves * m;
+        if (it < 2 * x.ng) {
+            const int g = it >> 1;
+            const uint4 xa = *(const uint4*)(sh.x + 64 * g + 8 * kb);
+            const uint4 xb = *(const uint4*)(sh.x + 64 * g + 32 + 8 * kb);
+            const float xs = sh.xsum[g * 4 + kb];
+            float d[2] = {0.f, 0.f};
+            half_block_dot(L.c[m], xa, xb, d);
+            const uint32_t sw[2] = {L.s[m].x, L.s[m].y};
+#pragma unroll
+            for (int r = 0; r < 2; ++r) acc[r] += fmaf(bf16_lo(sw[r]), fmaf(-128.f, xs, d[r]), bf16_hi(sw[r]) * xs);
+        }
+    }
+    reduce_rows(sh, acc, 2);
+    if (wave_id() == 0 && tix() < 32) {
+        const int r = tix();
+        const float h = gelu_tanh(row_total_par(sh, r)) * row_total_par(sh, 32 + r);
+        const uint32_t h16 = f32_to_f16(h);
+        uint64_t* hout = x.kind == U_SH ? p.f_hs + 32 * x.a + r : p.f_h + (int64_t)x.a * p.I + 32 * x.b + r;
+#pragma unroll
+        for (int c = 0; c < kCopies; ++c) st_word(hout + c * p.h_stride, tag, h16);
+    }
+    __syncthreads();
+}
+
+// Shared down piece: one 64-row output tile from one chunk of the shared
+// activations -> partial outputs (source k + chunk).
+__device__ __forceinline__ void run_sd_piece(const Plan& p, Shared& sh, const Unit& x, const Loads& L, uint32_t tag) {
+    stage_h(p, sh, p.f_hs + xcc_copy() * p.h_stride, x.g0, x.ng, tag);
+    const int wave = wave_id(), lane = tix() & 63, kb = lane >> 4;
+    float acc[2] = {0.f, 0.f};    // rows 32*(wave & 1) + 16*r + lane%16 of the output tile
+#pragma unroll
+    for (int m = 0; m < kItems; ++m) {
+        const int it = wave + kWaves * m;
+        if (it < 2 * x.ng) {
+            const int gl = it >> 1;
+            const uint4 ha = *(const uint4*)(sh.h16 + 64 * gl + 8 * kb);
+            const uint4 hb = *(const uint4*)(sh.h16 + 64 * gl + 32 + 8 * kb);
+            const float hs = sh.hsum[gl * 4 + kb];
+            float d[2] = {0.f, 0.f};
+            half_block_dot16(L.c[m], ha, hb, d);
+            const uint32_t sw[2] = {L.s[m].x, L.s[m].y};
+#pragma unroll
+            for (int r = 0; r < 2; ++r) acc[r] += fmaf(bf16_lo(sw[r]), fmaf(-1024.f, hs, d[r]), bf16_hi(sw[r]) * hs);
+        }
+    }
+    reduce_rows(sh, acc, 2);
+    uint64_t* dst = p.f_piece + ((int64_t)x.a * p.n_src + p.k + x.b) * 64;
+    if (wave_id() == 0) st_word(dst + tix(), tag, __float_as_uint(row_total_par(sh, tix())));
+    __syncthreads();
+}
+
+// Loads of a routed down unit: for each of its tiles, wave w takes groups
+// w/2, w/2 + kWaves/2 of the expert's intermediate, half w % 2 of the tile.
+__device__ __forceinline__ void issue_rdu(const Plan& p, const Shared& sh, const DownUnit& d, LoadsN<kItemsD>& L) {
+    const int wave = wave_id(), lane = tix() & 63, par = wave & 1;
+    const uint8_t* base = p.pool_base + (int64_t)sh.ids[d.b] * p.expert_stride + p.down_off +
+                          ((int64_t)d.t0 * p.G_I + (wave >> 1)) * kBlk4;
+    const int lc = par * 1024 + lane * 16, ls = kCodes4 + 8 * par + (lane & 15) * 16;
+#pragma unroll
+    for (int t = 0; t < kTilesD; ++t)
+#pragma unroll
+        for (int j = 0; j < kGroupsD; ++j)
+            if (t < d.nt && (wave >> 1) + (kWaves / 2) * j < p.G_I) {
+                const uint8_t* blk = base + ((int64_t)t * p.G_I + (kWaves / 2) * j) * kBlk4;
+                L.c[kGroupsD * t + j] = ld_stream16(blk + lc);
+                L.s[kGroupsD * t + j] = *(const uint2*)(blk + ls);
+            }
+}
+
+// Routed down unit: the weighted partial outputs of one selected expert for
+// each of its tiles (source = slot).
+__device__ __forceinline__ void run_rdu(const Plan& p, Shared& sh, const DownUnit& d, const LoadsN<kItemsD>& L,
+                                        uint32_t tag) {
+    stage_h(p, sh, p.f_h + xcc_copy() * p.h_stride + (int64_t)d.b * p.I, 0, p.G_I, tag);
+    const int wave = wave_id(), lane = tix() & 63, kb = lane >> 4;
+    const float wf = sh.wts[d.b];
+    float acc[kTilesD][2];
+#pragma unroll
+    for (int t = 0; t < kTilesD; ++t) acc[t][0] = acc[t][1] = 0.f;
+#pragma unroll
+    for (int j = 0; j < kGroupsD; ++j) {
+        const int g = (wave >> 1) + (kWaves / 2) * j;
+        if (g < p.G_I) {
+            const uint4 ha = *(const uint4*)(sh.h16 + 64 * g + 8 * kb);
+            const uint4 hb = *(const uint4*)(sh.h16 + 64 * g + 32 + 8 * kb);
+            const float hs = sh.hsum[g * 4 + kb];
+#pragma unroll
+            for (int t = 0; t < kTilesD; ++t)
+                if (t < d.nt) {
+                    const int m = kGroupsD * t + j;
+                    float dd[2] = {0.f, 0.f};
+                    half_block_dot16(L.c[m], ha, hb, dd);
+                    const uint32_t sw[2] = {L.s[m].x, L.s[m].y};
+#pragma unroll
+                    for (int r = 0; r < 2; ++r)
+                        acc[t][r] += wf * fmaf(bf16_lo(sw[r]), fmaf(-1024.f, hs, dd[r]), bf16_hi(sw[r]) * hs);
+                }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < kTilesD; ++t)
+        if (t < d.nt)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const float v = sum_kb(acc[t][r]);
+                if (lane < 16) sh.red2[wave][t][16 * r + lane] = v;
+            }
+    __syncthreads();
+    if (wave_id() == 0) {
+        const int row = tix(), par = row >> 5;
+        for (int t = 0; t < d.nt; ++t) {
+            float v = 0.f;
+            for (int w2 = par; w2 < kWaves; w2 += 2) v += sh.red2[w2][t][row & 31];
+            st_word(p.f_piece + ((int64_t)(d.t0 + t) * p.n_src + d.b) * 64 + row, tag, __float_as_uint(v));
+        }
+    }
+    __syncthreads();
+}
+
+// Output tile a: every source's partial outputs summed in source order
+// (routed slots, then shared chunks), rounded once.
+__device__ __forceinline__ void run_reduce(const Plan& p, Shared& sh, int a, uint32_t tag) {
+    const uint64_t* tilep = p.f_piece + (int64_t)a * p.n_src * 64;
+    gather_words(tilep, p.n_src * 64, tag, p.f_err, sh.gbuf);
+    if (wave_id() == 0) {
+        float v = 0.f;
+        for (int s2 = 0; s2 < p.n_src; ++s2) v += __uint_as_float(sh.gbuf[s2 * 64 + tix()]);
+        const int row = 64 * a + tix();
+        const uint32_t b = f32_to_bf16(v);
+        if (!p.out) {
+        } else if (p.out_f32) {
+            ((float*)p.out)[row] = v;
+        } else {
+            ((uint16_t*)p.out)[row] = (uint16_t)b;
+        }
+        if (p.out_w) {
+            // the next layer's input: bf16 pairs (row 2i in the low half), one copy per XCD
+            const uint32_t b1 = __shfl_down(b, 1, 64);
+            if ((tix() & 1) == 0) {
+#pragma unroll
+                for (int c = 0; c < kCopies; ++c) st_word(p.out_w + c * p.xw_stride + (row >> 1), tag, b | (b1 << 16));
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// ----------------------------------------------------------------- the kernel
+
+// Phases of a workgroup (every branch below is taken by all of its waves):
+//   1. the token's loads, then the weight loads of its router piece and
+//      shared gate/up pieces;
+//   2. those units;
+//   3. the expert ids (waits for the router pieces), then the weight loads of
+//      its remaining units at once: a full-row routed gate/up unit (routed
+//      workgroups) or shared down pieces (shared workgroups), and a routed
+//      down unit;
+//   4. those units, then (workgroup a < G_H) the sum of output tile a.
+// Every wait is for a unit earlier in the order router < shared gate/up <
+// ids < routed gate/up < shared down < routed down < output sums, and each
+// workgroup runs its units in that order, so with all workgroups resident
+// every wait ends.
+
+// Touch every field of the argument block the kernel reads, in one batch.
+// Left alone, the compiler fetches the block field by field near each first
+// use: a chain of dependent scalar-cache misses before the first weight load.
+// Once the lines are cached, later reads of the fields hit.
+__device__ __forceinline__ void prefetch_args(const Plan& p) {
+    asm volatile("" ::"s"(p.x), "s"(p.router_w), "s"(p.router_scale), "s"(p.pes), "s"(p.logit_bias),
+                 "s"(p.f_epoch), "s"(p.pool_base), "s"(p.sh_gate), "s"(p.sh_up), "s"(p.sh_down));
+    asm volatile("" ::"s"(p.f_rpart), "s"(p.f_hs), "s"(p.f_h), "s"(p.f_piece),
+                 "s"(p.f_err), "s"(p.c_done), "s"(p.out), "s"(p.ids_out), "s"(p.w_out), "s"(p.logits_out));
+    asm volatile("" ::"s"(p.E), "s"(p.k), "s"(p.H), "s"(p.I), "s"(p.G_H), "s"(p.G_I), "s"(p.G_s), "s"(p.n_src),
+                 "s"(p.n_router), "s"(p.n_rh), "s"(p.n_sd), "s"(p.n_sc), "s"(p.n_rng), "s"(p.eps));
+    asm volatile("" ::"s"(p.x_w), "s"(p.out_w), "s"(p.xw_stride), "s"(p.in_eps));
+    asm volatile("" ::"s"(p.h_stride), "s"(p.rpart_stride), "s"(p.expert_stride), "s"(p.gate_off), "s"(p.up_off),
+                 "s"(p.down_off), "s"(p.out_f32), "s"(gridDim.x));
+}
+
+// One layer for one token: the workgroup's part of the unit order above.
+// Ends with every wave past its last use of the shared memory.
+__device__ __forceinline__ void decode_layer(const Plan& p, Shared& sh, uint32_t tag) {
+    const int nwg = gridDim.x, w = blockIdx.x;
+    const Unit ur = unit_router(p, w);
+    const Unit us = unit_sh(p, w - p.n_rh);
+    const Unit rh = unit_rh(p, w);
+    const DownUnit du = unit_rdu(p, w, nwg);
+    TokenLoads tl;
+    load_token(p, tl, ur.kind == U_ROUTER || us.kind == U_SH || rh.kind == U_RH);
+    Loads lrt;
+    LoadsN<kItemsRH> lsh;
+    issue_loads(p, sh, ur, lrt);
+    issue_loads(p, sh, us, lsh);
+    stage_token(p, sh, tl, tag);
+    if (ur.kind == U_ROUTER) run_router(p, sh, ur, lrt, tag);
+    if (us.kind == U_SH) run_rh(p, sh, us, lsh, tag);
+    if (rh.kind == U_RH || du.nt > 0) fetch_ids(p, sh, tag);
+    LoadsN<kItemsD> ld;
+    if (rh.kind == U_RH) {
+        LoadsN<kItemsRH> lr;
+        Loads lsd;
+        const Unit usd = sd_piece(p, w, nwg, 0);
+        issue_loads(p, sh, rh, lr);
+        issue_loads(p, sh, usd, lsd);
+        if (du.nt > 0) issue_rdu(p, sh, du, ld);
+        run_rh(p, sh, rh, lr, tag);
+        if (usd.kind == U_SD) run_sd_piece(p, sh, usd, lsd, tag);
+    } else {
+        Unit usd[kSlotsSD];
+        Loads lsd[kSlotsSD];
+#pragma unroll
+        for (int s = 0; s < kSlotsSD; ++s) {
+            usd[s] = sd_piece(p, w, nwg, s);
+            issue_loads(p, sh, usd[s], lsd[s]);
+        }
+        if (du.nt > 0) issue_rdu(p, sh, du, ld);
+#pragma unroll
+        for (int s = 0; s < kSlotsSD; ++s)
+            if (usd[s].kind == U_SD) run_sd_piece(p, sh, usd[s], lsd[s], tag);
+    }
+    if (du.nt > 0) run_rdu(p, sh, du, ld, tag);
+    if (w < p.G_H) run_reduce(p, sh, w, tag);
+    __syncthreads();
+}
+
+// The last workgroup to finish clears the done counter and advances the
+// epoch to the call's last tag.
+__device__ __forceinline__ void finish_call(const Plan& p, Shared& sh, uint32_t last_tag) {
+    __syncthreads();
+    if (tix() == 0) sh.flag = atomicAdd(p.c_done, 1u) + 1 == gridDim.x;
+    __syncthreads();
+    if (sh.flag) {
+        if (tix() == 0) {
+            __hip_atomic_store(p.c_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(p.f_epoch, last_tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+}  // namespace
+}  // namespace mq

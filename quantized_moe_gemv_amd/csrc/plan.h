@@ -79,6 +79,12 @@ struct Plan {
     uint64_t* f_h;       // [copies][k][I]      routed GeGLU activations, h_stride apart
     int64_t h_stride, rpart_stride;
     uint64_t* f_piece;   // [G_H][n_src][64]    partial outputs per output tile and source
+    // a stack of layers in one launch: the layer input as tagged bf16 pairs
+    // (layers after the first) and the layer output published the same way
+    // for the next layer, one copy per XCD, xw_stride apart
+    const uint64_t* x_w;   // non-null: read the input row from here instead of x
+    uint64_t* out_w;       // non-null: publish the output row here (out may then be null)
+    int64_t xw_stride;
     uint32_t* c_done;    // workgroups finished (cleared at the end of every call)
     uint32_t* f_epoch;   // calls completed with this workspace
     uint32_t* f_err;     // non-zero once a bounded wait has given up
@@ -86,6 +92,34 @@ struct Plan {
     int max_tiles;     // upper bound of scheduled (expert, token chunk) pairs
     int ntile;         // tokens per grouped chunk (32 or 128)
     int n_vs;          // virtual experts of the shared expert (0 without one)
+};
+
+// Fields of one layer of a single-launch stack (everything else is shared).
+struct StackLayer {
+    const uint16_t* x;
+    const uint64_t* x_w;
+    void* out;
+    uint64_t* out_w;
+    const uint8_t* router_w;
+    const float* router_scale;
+    const float* pes;
+    const float* logit_bias;
+    const uint8_t* pool_base;
+    const uint8_t* sh_gate;
+    const uint8_t* sh_up;
+    const uint8_t* sh_down;
+    int32_t* ids_out;
+    float* w_out;
+    float* logits_out;
+    int64_t expert_stride, gate_off, up_off, down_off;
+    float eps, in_eps;
+};
+
+constexpr int kStackChunk = 16;  // layers per argument-writing launch (kernel arguments stay under 4 KiB)
+
+struct StackChunk {
+    int n;
+    StackLayer l[kStackChunk];
 };
 
 }  // namespace mq

@@ -1,0 +1,66 @@
+// Single-launch decode of one token through a stack of layers (the units,
+// their order and the exchanges between workgroups are in decode_units.h).
+#include "plan.h"
+
+namespace mq {
+namespace {
+constexpr bool kOpaqueTid = true;
+}
+}  // namespace mq
+
+#include "decode_units.h"
+
+namespace mq {
+
+// A stack of layers for one token in one launch.  Layer l runs with tag
+// epoch + 1 + l; its output sums publish the next layer's input as tagged
+// words, so a layer's units start as soon as the words they read are there,
+// with no launch between layers.  Every read of a layer's exchange regions
+// happens before that layer's output sums complete (each reading workgroup
+// feeds them), and the next layer writes those regions only after reading
+// its input, so one set of regions serves every layer.  The order of the
+// units (layer by layer, in the order above within a layer) keeps every wait
+// finite as in the single layer.
+__global__ __launch_bounds__(kThreads) void k_decode_stack(const Plan* __restrict__ plans, int n_layers) {
+    __shared__ Shared sh;
+    const uint32_t base = ld_ctr(plans[0].f_epoch);
+    for (int l = 0; l < n_layers; ++l) {
+        const Plan& p = plans[l];
+        prefetch_args(p);
+        decode_layer(p, sh, base + 1 + (uint32_t)l);
+    }
+    finish_call(plans[0], sh, base + (uint32_t)n_layers);
+}
+
+// The per-layer arguments of a stack, written into the workspace by one
+// small launch per chunk of layers: layer i of the chunk gets the base
+// arguments with its own fields.
+__global__ void k_stack_plans(Plan base, StackChunk c, Plan* dst) {
+    if (threadIdx.x != 0 || (int)blockIdx.x >= c.n) return;
+    const StackLayer& s = c.l[blockIdx.x];
+    Plan q = base;
+    q.x = s.x;
+    q.x_w = s.x_w;
+    q.out = s.out;
+    q.out_w = s.out_w;
+    q.router_w = s.router_w;
+    q.router_scale = s.router_scale;
+    q.pes = s.pes;
+    q.logit_bias = s.logit_bias;
+    q.eps = s.eps;
+    q.in_eps = s.in_eps;
+    q.pool_base = s.pool_base;
+    q.expert_stride = s.expert_stride;
+    q.gate_off = s.gate_off;
+    q.up_off = s.up_off;
+    q.down_off = s.down_off;
+    q.sh_gate = s.sh_gate;
+    q.sh_up = s.sh_up;
+    q.sh_down = s.sh_down;
+    q.ids_out = s.ids_out;
+    q.w_out = s.w_out;
+    q.logits_out = s.logits_out;
+    dst[blockIdx.x] = q;
+}
+
+}  // namespace mq

@@ -214,3 +214,61 @@ def test_workspace_errors_rejects_bad_arguments():
     assert lib.mq_workspace_errors(256, 4096, None, None) == M.MQ_ERR_NULL
     assert lib.mq_workspace_errors(256 + 8, 4096, ctypes.byref(v), None) == M.MQ_ERR_ALIGN
     assert lib.mq_workspace_errors(256, 16, ctypes.byref(v), None) == M.MQ_ERR_WORKSPACE
+
+
+def fake_stack(n, mutate_last=None):
+    layers = [fake_layer() for _ in range(n)]
+    if mutate_last:
+        mutate_last(*layers[-1])
+    routers = (M.MqRouter * n)(*[l[0] for l in layers])
+    pools = (M.MqExpertPool * n)(*[l[1] for l in layers])
+    shared = (M.MqShared * n)(*[l[2] for l in layers])
+    return routers, pools, shared
+
+
+def stack_call(n=3, routers=None, pools=None, shared=None, T=1, H=256, x_ptr=FAKE, out_ptr=FAKE, ws_ptr=FAKE,
+               ws_bytes=None, path=0, in_eps=0.0, between_eps=0.0):
+    if routers is None:
+        routers, pools, shared = fake_stack(n)
+    if ws_bytes is None:
+        ws_bytes = M._lib.mq_stack_workspace_bytes(routers, pools, shared, n)
+    x = M.MqAct(x_ptr, T, H, 0, H)
+    out = M.MqAct(out_ptr, T, H, 0, H)
+    opts = M.MqOpts(path, None, None, None, ws_ptr, ws_bytes, in_eps)
+    return M._lib.moe_stack_forward(ctypes.byref(x), n, routers, pools, shared, between_eps, ctypes.byref(out),
+                                    ctypes.byref(opts), None)
+
+
+def test_stack_workspace_bytes():
+    f = lambda n: M._lib.mq_stack_workspace_bytes(*fake_stack(n), n)
+    assert 0 < f(1) <= f(2) < f(30)
+    r, p, s = fake_layer()
+    # a stack workspace also serves a one-token layer call
+    assert f(1) >= M._lib.mq_workspace_bytes(ctypes.byref(r), ctypes.byref(p), ctypes.byref(s), 1)
+    assert M._lib.mq_stack_workspace_bytes(*fake_stack(2), 0) == 0
+    assert M._lib.mq_stack_workspace_bytes(*fake_stack(2, lambda r, p, s: setattr(p, "inter", 128)), 2) == 0
+    r, p, s = fake_stack(2)
+    assert M._lib.mq_stack_workspace_bytes(r, p, None, 2) > 0   # no shared expert in any layer
+
+
+def test_stack_calls_are_validated_before_any_device_work():
+    """Every check of moe_stack_forward that needs no device."""
+    assert stack_call(n=0, ws_bytes=1 << 20) == M.MQ_ERR_SHAPE
+    r, p, s = fake_stack(3, lambda r, p, s: setattr(p, "inter", 128))
+    assert stack_call(3, r, p, s, ws_bytes=1 << 24) == M.MQ_ERR_SHAPE       # layers of different sizes
+    r, p, s = fake_stack(3, lambda r, p, s: setattr(r.w, "bits", 4))
+    assert stack_call(3, r, p, s, ws_bytes=1 << 24) == M.MQ_ERR_UNSUPPORTED
+    assert stack_call(T=2) == M.MQ_ERR_SHAPE                                 # one token only
+    assert stack_call(H=128) == M.MQ_ERR_SHAPE
+    assert stack_call(path=M.PATHS["gemv"]) == M.MQ_ERR_UNSUPPORTED
+    assert stack_call(path=M.PATHS["grouped"]) == M.MQ_ERR_UNSUPPORTED
+    for bad in (-1.0, float("nan"), float("inf")):
+        assert stack_call(in_eps=bad) == M.MQ_ERR_UNSUPPORTED
+        assert stack_call(between_eps=bad) == M.MQ_ERR_UNSUPPORTED
+    assert stack_call(x_ptr=None) == M.MQ_ERR_NULL
+    assert stack_call(ws_ptr=None) == M.MQ_ERR_WORKSPACE
+    assert stack_call(x_ptr=FAKE + 2) == M.MQ_ERR_ALIGN
+    assert stack_call(ws_ptr=FAKE + 128) == M.MQ_ERR_ALIGN
+    ws = M._lib.mq_stack_workspace_bytes(*fake_stack(3), 3)
+    assert stack_call(ws_bytes=ws - 1) == M.MQ_ERR_WORKSPACE
+    assert M._lib.moe_stack_forward(None, 1, None, None, None, 0.0, None, None, None) == M.MQ_ERR_NULL
