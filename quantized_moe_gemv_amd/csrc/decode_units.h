@@ -316,12 +316,16 @@ __device__ __forceinline__ const uint8_t* tile4(const uint8_t* m, int tile, int 
 //   router:  it -> 8-bit block (slice rows, group g0 + it)
 //   gate/up: even it -> gate, odd it -> up, group g0 + it/2, one half tile
 //   down:    group g0 + it/2, rows of half (it & 1) of the output tile
-// Every item issues its two loads unconditionally (items past the unit's
-// end read the router's first block and are skipped when computed): a
-// register that a load may still be filling is never written on another
-// path, which would make that write wait for the load.
+// Within a unit every item issues its two loads unconditionally (items past
+// the unit's end read the router's first block and are skipped when
+// computed): a register that a load may still be filling is never written
+// on another path, which would make that write wait for the load.  A
+// workgroup without the unit issues nothing (its registers are never read):
+// every load costs address-unit time of the compute unit, and the
+// workgroup's first barrier waits until its last wave has issued them all.
 template <int N>
 __device__ __forceinline__ void issue_loads(const Plan& p, const Shared& sh, const Unit& x, LoadsN<N>& L) {
+    if (x.kind == U_NONE) return;
     const int wave = wave_id(), lane = tix() & 63, par = wave & 1;
     const uint8_t* b0 = p.router_w;
     const uint8_t* b1 = p.router_w;
