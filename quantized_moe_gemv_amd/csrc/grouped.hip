@@ -217,14 +217,16 @@ __global__ __launch_bounds__(256) void k_scores(Plan p) {
 // sum times the RMS factor (plus logit_bias); the k highest are taken by
 // k rounds of a wave-wide argmax (equal scores go to the lower expert, a
 // NaN score ranks last), then the softmax over them times per_expert_scale.
-// grid (ceil(T / 4)), block 256: one wave per SIMD.
+// grid (ceil(T / 4)), block 256: one wave per SIMD.  KM: 64-expert slices
+// per lane (E <= 64 KM).
+template <int KM>
 __global__ __launch_bounds__(256) void k_select(Plan p) {
     const int lane = threadIdx.x & 63, w = wave_id();
     const int t = blockIdx.x * 4 + w, E = p.E, k = p.k, ns = p.rsplit_used;
     if (t < p.T) {
         // the column splits' partials, summed in split order; the loads of a
         // batch of sixteen splits go out together (clamped, in bounds)
-        constexpr int kB = 16, kM = kMaxExperts / 64;
+        constexpr int kB = 16, kM = KM;
         float ss = 0.f, sum[kM], bias[kM];
 #pragma unroll
         for (int m = 0; m < kM; ++m) bias[m] = p.logit_bias ? p.logit_bias[min(lane + 64 * m, E - 1)] : 0.f;
@@ -1235,7 +1237,10 @@ mq_status launch_gemms(const Plan& p, hipStream_t s) {
 
 mq_status launch_grouped(const Plan& p, hipStream_t s) {
     hipLaunchKernelGGL(k_scores, dim3((p.T + 15) / 16, p.E_pad / 64, p.rsplit_used), dim3(256), 0, s, p);
-    hipLaunchKernelGGL(k_select, dim3((p.T + 3) / 4), dim3(256), 0, s, p);
+    if (p.E <= 128)
+        hipLaunchKernelGGL(k_select<2>, dim3((p.T + 3) / 4), dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL(k_select<kMaxExperts / 64>, dim3((p.T + 3) / 4), dim3(256), 0, s, p);
     hipLaunchKernelGGL(k_sort, dim3(1), dim3(1024), 0, s, p);
     const mq_status st = p.ntile <= 64 ? launch_gemms<4>(p, s) : launch_gemms<8>(p, s);
     if (st != MQ_OK) return st;
