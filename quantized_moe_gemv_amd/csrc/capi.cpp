@@ -72,7 +72,7 @@ FusedCarve fused_carve(const Sizes& z) {
 // and at most kFusedSlotsSD shared down pieces each; routed down work runs
 // one tile per routed workgroup for the first S = n_rh / G_H slots and in
 // n_rng ranges of at most kFusedTilesD tiles on the shared workgroups for
-// the others; router piece i on workgroup i; output tile a's sum on
+// the others; router piece i on workgroup G_H + i; output tile a's sum on
 // workgroup a.
 constexpr int kFusedSlotsSD = 2, kFusedTilesD = 3;
 
@@ -85,7 +85,7 @@ bool fused_ok(const Sizes& z, int cus) {
     const int m = cus - z.n_rh, r = fused_ranges(z, cus);
     if (z.G_H > 48 || z.G_I > 12 || z.n_src > 32 || m < 1 || r < 1) return false;
     return (z.G_H + r - 1) / r <= kFusedTilesD && 2 * z.G_s <= m && (std::max(z.n_sd - z.n_rh, 0) + m - 1) / m <= kFusedSlotsSD &&
-           z.n_router <= cus && z.G_H <= cus;
+           z.G_H + z.n_router <= cus;
 }
 
 int device_cus() {

@@ -207,7 +207,7 @@ __device__ __forceinline__ Unit no_unit() {
 // Router piece i: 16 experts (slice i / 8) x column range i % 8.
 __device__ __forceinline__ Unit unit_router(const Plan& p, int i) {
     Unit x = no_unit();
-    if (i < p.n_router) {
+    if (i >= 0 && i < p.n_router) {
         x.kind = U_ROUTER;
         x.a = i / kRq;
         x.q = i % kRq;
@@ -266,8 +266,10 @@ struct DownUnit {
 // first 2 G_s of them) and any further shared down pieces.  Routed down
 // work: the first S = min(n_rh / G_H, k) slots one tile per routed
 // workgroup, the other slots in n_rng tile ranges each on the shared
-// workgroups.  Router piece i runs on workgroup i and the sum of output tile
-// a on workgroup a, after all its other work.
+// workgroups.  The sum of output tile a runs on workgroup a, after all its
+// other work, and router piece i on workgroup G_H + i: in a stack of layers
+// the workgroups that sum are the last to finish a layer, and the router
+// pieces of the next layer then load their weights during that tail.
 __device__ __forceinline__ DownUnit unit_rdu(const Plan& p, int w, int nwg) {
     DownUnit d;
     d.b = d.t0 = d.nt = 0;
@@ -874,7 +876,7 @@ __device__ __forceinline__ void prefetch_args(const Plan& p) {
 // Ends with every wave past its last use of the shared memory.
 __device__ __forceinline__ void decode_layer(const Plan& p, Shared& sh, uint32_t tag) {
     const int nwg = gridDim.x, w = blockIdx.x;
-    const Unit ur = unit_router(p, w);
+    const Unit ur = unit_router(p, w - p.G_H);
     const Unit us = unit_sh(p, w - p.n_rh);
     const Unit rh = unit_rh(p, w);
     const DownUnit du = unit_rdu(p, w, nwg);
