@@ -1191,17 +1191,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT <= 4 ? 3
 }
 
 // out[t] = sum_j ysort[inv[t][j]] (slot order) + the shared expert's
-// slices, rounded once.  grid (T, ceil(H/256)).
+// slices, rounded once.  grid (T, ceil(H/1024)), block 256: each thread
+// sums four adjacent columns with 16-byte loads, and the loads of a batch of
+// rows go out together before any is added (the sum keeps the row order).
 __global__ __launch_bounds__(256) void k_gg_combine(Plan p) {
-    const int t = blockIdx.x, i = blockIdx.y * 256 + threadIdx.x;
-    if (i >= p.H) return;
-    float v = 0.f;
-    for (int j = 0; j < p.k; ++j) v += p.ysort[(int64_t)p.inv[t * p.k + j] * p.H + i];
-    for (int j = 0; j < p.n_vs; ++j) v += p.ysort[((int64_t)p.T * p.k + (int64_t)j * p.T + t) * p.H + i];
-    if (p.out_f32)
-        ((float*)p.out)[(int64_t)t * p.out_stride + i] = v;
-    else
-        ((uint16_t*)p.out)[(int64_t)t * p.out_stride + i] = f32_to_bf16(v);
+    constexpr int kRb = 8;   // rows per batch of loads
+    const int t = blockIdx.x, i = (blockIdx.y * 256 + threadIdx.x) * 4;
+    if (i >= p.H) return;    // H % 64 == 0: columns i .. i + 3 all exist
+    const int nr = p.k + p.n_vs;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int j0 = 0; j0 < nr; j0 += kRb) {
+        float4 v[kRb];
+#pragma unroll
+        for (int u = 0; u < kRb; ++u) {
+            const int j = min(j0 + u, nr - 1);   // clamped: in bounds, skipped below
+            const int64_t row = j < p.k ? (int64_t)p.inv[t * p.k + j]
+                                        : (int64_t)p.T * p.k + (int64_t)(j - p.k) * p.T + t;
+            v[u] = *(const float4*)(p.ysort + row * p.H + i);
+        }
+#pragma unroll
+        for (int u = 0; u < kRb; ++u)
+            if (j0 + u < nr) {
+                a0 += v[u].x;
+                a1 += v[u].y;
+                a2 += v[u].z;
+                a3 += v[u].w;
+            }
+    }
+    const int64_t o = (int64_t)t * p.out_stride + i;
+    if (p.out_f32) {
+        float* out = (float*)p.out + o;
+        out[0] = a0;
+        out[1] = a1;
+        out[2] = a2;
+        out[3] = a3;
+    } else {
+        uint16_t* out = (uint16_t*)p.out + o;
+        out[0] = f32_to_bf16(a0);
+        out[1] = f32_to_bf16(a1);
+        out[2] = f32_to_bf16(a2);
+        out[3] = f32_to_bf16(a3);
+    }
 }
 
 // Dynamic LDS of k_gu: the big path's staged batch, the small path's
@@ -1244,7 +1274,7 @@ mq_status launch_grouped(const Plan& p, hipStream_t s) {
     hipLaunchKernelGGL(k_sort, dim3(1), dim3(1024), 0, s, p);
     const mq_status st = p.ntile <= 64 ? launch_gemms<4>(p, s) : launch_gemms<8>(p, s);
     if (st != MQ_OK) return st;
-    hipLaunchKernelGGL(k_gg_combine, dim3(p.T, (p.H + 255) / 256), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(k_gg_combine, dim3(p.T, (p.H + 1023) / 1024), dim3(256), 0, s, p);
     return MQ_OK;
 }
 
