@@ -813,23 +813,26 @@ typedef float4_t GuRed[4][3][2][64];   // [row block][other wave][matrix][lane],
 // groups stay in flight behind the one in use: two of them for one token
 // tile, one for two (register budget).  Prefetch past the end re-reads the
 // last group; the loops have one exit, a multiply past the end weighs zero.
+// tok0 = item_token(lane % 16), tok_s = item_token(threadIdx.x % 32), looked
+// up by the caller before the first weights.
 template <int NTT>
 __device__ __forceinline__ void gu_small_n(const Plan& p, const Item& it, GuW& WA, GuW& WB, char* lds,
-                                           float2 (*hpart)[128]) {
+                                           float2 (*hpart)[128], int tok0, int tok_s) {
     const int w = wave_id(), lane = threadIdx.x & 63;
     const _Float16* x16 = p.x16;
     float* tsum = (float*)lds;            // [G][32]
     float* tneg = tsum + it.G * 32;       // [G][32]
     int xr[NTT];
 #pragma unroll
-    for (int t = 0; t < NTT; ++t) xr[t] = item_token(p, it, 16 * t + (lane & 15)) * p.H + 8 * (lane >> 4);
+    for (int t = 0; t < NTT; ++t)
+        xr[t] = (t == 0 ? tok0 : item_token(p, it, 16 * t + (lane & 15))) * p.H + 8 * (lane >> 4);
     const int G = it.G, nj = (G - w + 3) / 4;
     auto grp = [&](int j) { return min(w + 4 * j, G - 1); };
     const uint8_t *w0 = it.w[0], *w1 = it.w[1];
     GuX<NTT> XA, XB;
     gu_xload(XA, x16, xr, grp(0));
     gu_xload(XB, x16, xr, grp(1));
-    stage_sums((const float2*)p.xso, p.G_H, item_token(p, it, threadIdx.x & 31), G, 16 * NTT, tsum, tneg);
+    stage_sums((const float2*)p.xso, p.G_H, tok_s, G, 16 * NTT, tsum, tneg);
     float4_t acc[2][4][NTT];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
@@ -971,11 +974,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT <= 4 ? 3
         gu_big<MT>(p, it, *(GuXs<MT>*)lds, rows, hpart);
         return;
     }
-    // first weights, in flight while the tokens arrive
+    // the chunk's token lookups first, then the first weights, in flight
+    // while the token rows arrive: loads complete in issue order, so lookups
+    // issued behind the weights would wait for them
+    const int tok0 = item_token(p, it, lane & 15), tok_s = item_token(p, it, threadIdx.x & 31);
+    __builtin_amdgcn_sched_barrier(0);
     GuW WA, WB;
     gu_wload(WA, it.w[0], it.w[1], min(w, it.G - 1), lane);
     gu_wload(WB, it.w[0], it.w[1], min(w + 4, it.G - 1), lane);
-    gu_small_n<1>(p, it, WA, WB, lds, hpart);
+    gu_small_n<1>(p, it, WA, WB, lds, hpart, tok0, tok_s);
 }
 
 // ---- down, up to 32 tokens: the chunk's GeGLU rows and group constants
