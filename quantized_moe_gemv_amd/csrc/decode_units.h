@@ -579,7 +579,11 @@ __device__ __forceinline__ void fetch_ids(const Plan& p, Shared& sh, uint32_t ta
             }
         }
     }
-    __syncthreads();
+    // No barrier: the other waves go on to issue their routed loads, which
+    // need only the ids.  sh.wts is first read by the routed down units,
+    // after the barriers of the gate/up unit or of the activation gather,
+    // and what the softmax reads (selv, ids, pes) is not written before
+    // those barriers either.
 }
 
 // One source's activations (64 tagged words per group, from group g0, fp16
