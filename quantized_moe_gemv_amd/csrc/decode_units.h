@@ -718,7 +718,9 @@ __device__ __forceinline__ void run_rh(const Plan& p, Shared& sh, const Unit& x,
 #pragma unroll
         for (int c = 0; c < kCopies; ++c) st_word(hout + c * p.h_stride, tag, h16);
     }
-    __syncthreads();
+    // no barrier: the next writer of sh.red (a later unit's row totals)
+    // comes after the barriers of that unit's activation gather or of the
+    // ids, and nothing else that wave 0 reads here is written before them
 }
 
 // Shared down piece: one 64-row output tile from one chunk of the shared
@@ -745,7 +747,7 @@ __device__ __forceinline__ void run_sd_piece(const Plan& p, Shared& sh, const Un
     reduce_rows(sh, acc, 2);
     uint64_t* dst = p.f_piece + ((int64_t)x.a * p.n_src + p.k + x.b) * 64;
     if (wave_id() == 0) st_word(dst + tix(), tag, __float_as_uint(row_total_par(sh, tix())));
-    __syncthreads();
+    // no barrier: as at the end of run_rh
 }
 
 // Loads of a routed down unit: for each of its tiles, wave w takes groups
@@ -813,7 +815,8 @@ __device__ __forceinline__ void run_rdu(const Plan& p, Shared& sh, const DownUni
             st_word(p.f_piece + ((int64_t)(d.t0 + t) * p.n_src + d.b) * 64 + row, tag, __float_as_uint(v));
         }
     }
-    __syncthreads();
+    // no barrier: sh.red2 is written again only by the next layer's routed
+    // down unit, after the barrier that ends this layer
 }
 
 // Output tile a: every source's partial outputs summed in source order
@@ -841,7 +844,7 @@ __device__ __forceinline__ void run_reduce(const Plan& p, Shared& sh, int a, uin
             }
         }
     }
-    __syncthreads();
+    // the layer's closing barrier follows
 }
 
 // ----------------------------------------------------------------- the kernel
