@@ -15,8 +15,7 @@
  *     ("Why the runtime has this shape", 3rd bullet), combined with the
  *     routed branch ("Prefill", last bullet; "Decode", phase table, cb2).
  * Readings where the pages are silent (nibble order, the affine sign,
- * epsilon, tie-breaks, precision of the top-k decision) are stated at each
- * function.
+ * epsilon, tie-breaks) are stated at each function.
  */
 #include "moe_oracle.h"
 
@@ -92,12 +91,12 @@ double oq_gelu_tanh(double z) {
     return 0.5 * z * (1.0 + tanh(k * (z + 0.044715 * z * z * z)));
 }
 
-/* Router scores ("Decode", router listing):
- *   router_input = rmsnorm_no_scale(x)  = x / sqrt(mean(x^2) + eps)
- *   scaled_input = router_input * router_scale / sqrt(H)
- *   logits       = W_router . scaled_input  (+ logit_bias, the synthetic skew)
- * Reading: eps is a parameter (1e-6 in the workloads); the norm has no
- * learned weight; logit_bias is added after the projection. */
+/* Router scores ("Decode", the router listing): the token is divided by its
+ * root mean square (no learned weight), multiplied by router_scale and by
+ * 1/sqrt(H), and projected by the 8-bit affine router matrix to one score
+ * per expert.  Readings: eps is a parameter (1e-6 in the workloads), inside
+ * the square root; logit_bias (the synthetic Zipf skew) is added after the
+ * projection. */
 void oq_router_logits(const oq_router* rt, const uint16_t* x, int32_t H, double* logits) {
     double* r = (double*)malloc(sizeof(double) * (size_t)H);
     double ss = 0.0;
@@ -118,20 +117,19 @@ void oq_router_logits(const oq_router* rt, const uint16_t* x, int32_t H, double*
 }
 
 /* top_k = the k highest logits; weights = softmax over those k logits times
- * per_expert_scale of each chosen expert ("Decode", router listing).
- * Readings: the selection compares the logits rounded to fp32 (the precision
- * the GPU path decides in) and equal values go to the lower expert index;
- * ids come out in selection order (highest first); the softmax uses the
- * fp64 logits. */
+ * per_expert_scale of each chosen expert ("Decode", the router listing).
+ * Readings: the selection compares the exact (fp64) logits and equal values
+ * go to the lower expert index; ids come out in selection order (highest
+ * first); the softmax uses the fp64 logits. */
 void oq_topk(const oq_router* rt, const double* logits, int32_t E, int32_t* ids, double* w) {
     int32_t k = rt->top_k;
     char* taken = (char*)calloc((size_t)E, 1);
     for (int32_t j = 0; j < k; ++j) {
         int32_t best = -1;
-        float bv = 0.0f;
+        double bv = 0.0;
         for (int32_t e = 0; e < E; ++e) {
             if (taken[e]) continue;
-            float v = (float)logits[e];
+            double v = logits[e];
             if (best < 0 || v > bv) { best = e; bv = v; }
         }
         taken[best] = 1;

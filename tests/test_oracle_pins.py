@@ -268,14 +268,17 @@ def test_topk_ties_and_per_expert_scale():
     assert np.allclose(w, scipy.special.softmax([4.0, 1.0, 0.5]) * np.array([3, 6, 1]), rtol=1e-14)
 
 
-def test_topk_selection_precision_is_fp32():
+def test_topk_selection_uses_exact_logits():
     layer = tiny_layer()
     layer.cfg = S.LayerConfig(hidden=256, num_experts=4, inter=64, shared_inter=0, top_k=1)
-    # two logits that differ in fp64 but round to the same fp32 value: lower index wins
+    # two logits that round to the same fp32 value: the exact (fp64) order decides
     ids, _ = O.topk(layer, np.array([0.0, 1.0, 1.0 + 1e-12, 0.5]))
-    assert list(ids) == [1]
-    ids, _ = O.topk(layer, np.array([0.0, 1.0, 1.0 + 1e-6, 0.5]))
     assert list(ids) == [2]
+    ids, _ = O.topk(layer, np.array([0.0, 1.0 + 1e-12, 1.0, 0.5]))
+    assert list(ids) == [1]
+    # an exact tie goes to the lower index
+    ids, _ = O.topk(layer, np.array([0.0, 1.0, 1.0, 0.5]))
+    assert list(ids) == [1]
 
 
 # ------------------------------------------------------------------ experts and layer
@@ -397,19 +400,42 @@ def test_rmsnorm_bf16_closed_form_and_scale_invariance():
     assert np.allclose(np.mean(yf * yf, axis=1), 1.0, atol=2e-2)
 
 
+def test_rmsnorm_bf16_epsilon_placement():
+    """Constant rows with a large epsilon: y = c / sqrt(c^2 + eps) exactly
+    (3 / sqrt(9 + 7) = 0.75; -1 / sqrt(1 + 3) = -0.5), so an epsilon outside
+    the root or a dropped epsilon changes the value."""
+    H = 128
+    for c, eps, want in ((3.0, 7.0, 0.75), (-1.0, 3.0, -0.5), (0.5, 0.0, 1.0)):
+        x = f32_to_bf16_bits(np.full((2, H), c))
+        y = O.rmsnorm_bf16(x, eps=eps)
+        assert np.all(y == f32_to_bf16_bits(np.float32(want)))
+    # a mixed row: the mean of the squares sits inside the root beside eps
+    xr = np.concatenate([np.full(H // 2, 2.0), np.full(H // 2, -4.0)])   # mean square 10
+    y = O.rmsnorm_bf16(f32_to_bf16_bits(xr[None, :]), eps=6.0)          # sqrt(16) = 4
+    assert np.array_equal(y[0], f32_to_bf16_bits(xr / 4.0))
+
+
 # ------------------------------------------------------------------ the pins catch planted mistakes
 
-PIN_TESTS = [
-    test_page_constants_match_workload_shapes, test_bf16_round_matches_torch_cast,
-    test_bf16_round_halfway_cases, test_code_order_low_bits_first, test_one_hot_input_returns_dequantised_column,
-    test_zero_codes_closed_form, test_gelu_tanh_library_and_identities, test_router_closed_form_constant_input,
-    test_router_scale_vector_closed_form, test_router_rmsnorm_epsilon_placement, test_logit_bias_is_added,
-    test_zero_input_routes_to_first_k_uniformly, test_zero_input_with_zipf_bias_is_softmax_of_bias,
-    test_topk_ties_and_per_expert_scale, test_topk_selection_precision_is_fp32, test_expert_is_geglu_on_gate,
-    test_weights_sum_to_one, test_identical_experts_reduce_to_shared_plus_one,
-    test_without_shared_expert_output_is_weighted_routed_sum, test_expert_permutation_invariance,
-    test_rmsnorm_bf16_closed_form_and_scale_invariance,
-]
+def _pin_callables():
+    """Every pin of this file as a no-argument callable, parametrised pins
+    once per parameter value (the harness below is left out)."""
+    import functools
+    import inspect
+    out = []
+    for name, f in sorted(globals().items()):
+        if not name.startswith("test_") or name == "test_planted_mistakes_are_caught" or not inspect.isfunction(f):
+            continue
+        params = [m for m in getattr(f, "pytestmark", []) if m.name == "parametrize"]
+        if not params:
+            out.append((name, f))
+            continue
+        assert len(params) == 1, name
+        argname, values = params[0].args
+        for v in values:
+            out.append(("%s[%s]" % (name, v), functools.partial(f, **{argname: v})))
+    return out
+
 
 # (description, exact text in moe_oracle.c, replacement)
 MUTATIONS = [
@@ -440,28 +466,46 @@ MUTATIONS = [
     ("bf16 ties away from zero", "(rem == 0.5 && fmod(fl, 2.0) != 0.0)", "(rem == 0.5)"),
     ("bf16 truncates", "if (rem > 0.5 || (rem == 0.5 && fmod(fl, 2.0) != 0.0)) fl += 1.0;", ""),
     ("rmsnorm without the mean", "double inv = 1.0 / sqrt(ss / (double)H + eps);", "double inv = 1.0 / sqrt(ss + eps);"),
+    ("rmsnorm epsilon outside the root", "double inv = 1.0 / sqrt(ss / (double)H + eps);",
+     "double inv = 1.0 / (sqrt(ss / (double)H) + eps);"),
+    ("rmsnorm epsilon dropped", "double inv = 1.0 / sqrt(ss / (double)H + eps);",
+     "double inv = 1.0 / sqrt(ss / (double)H);"),
+    ("selection in fp32", "double v = logits[e];", "double v = (float)logits[e];"),
 ]
 
 
 @pytest.mark.slow
 def test_planted_mistakes_are_caught(tmp_path):
+    """Rebuild the oracle with each planted mistake and run every pin on it.
+    A mistake counts as caught only when a pin fails an assertion; any other
+    exception is an error of the harness or of a pin, and fails this test.
+    Control: every pin first passes on the unmodified oracle, built the same
+    way."""
     src = open(os.path.join(ROOT, "oracle", "moe_oracle.c")).read()
     shutil.copy(os.path.join(ROOT, "oracle", "moe_oracle.h"), tmp_path / "moe_oracle.h")
+    pins = _pin_callables()
+    assert len(pins) >= 25
+
+    def first_failure():
+        for name, pin in pins:
+            try:
+                pin()
+            except AssertionError:
+                return name
+        return None
+
+    ctrl = tmp_path / "control.c"
+    ctrl.write_text(src)
+    with O.using(O.build(force=True, src=str(ctrl), out=str(tmp_path / "control.so"))):
+        assert first_failure() is None, "a pin fails on the unmodified oracle"
     missed = []
     for i, (name, old, new) in enumerate(MUTATIONS):
         assert src.count(old) >= 1, "mutation text not found: " + name
-        mutated = src.replace(old, new)
         csrc = tmp_path / ("m%d.c" % i)
-        csrc.write_text(mutated)
+        csrc.write_text(src.replace(old, new))
         lib = O.build(force=True, src=str(csrc), out=str(tmp_path / ("m%d.so" % i)))
-        caught = False
         with O.using(lib):
-            for pin in PIN_TESTS:
-                try:
-                    pin()
-                except Exception:
-                    caught = True
-                    break
-        if not caught:
+            caught_by = first_failure()
+        if caught_by is None:
             missed.append(name)
     assert not missed, "pins missed planted mistakes: %s" % missed
