@@ -39,7 +39,13 @@ def build(force: bool = False, src: str = _SRC, out: str = _LIB_PATH) -> str:
 
 class OqTensor(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
-                ("rows", ctypes.c_int32), ("cols", ctypes.c_int32), ("bits", ctypes.c_int32)]
+                ("rows", ctypes.c_int32), ("cols", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("group", ctypes.c_int32)]
+
+
+class OqTail(ctypes.Structure):
+    _fields_ = [("norm_shared", ctypes.c_void_p), ("norm_routed", ctypes.c_void_p), ("norm_out", ctypes.c_void_p),
+                ("eps", ctypes.c_double), ("layer_scalar", ctypes.c_double)]
 
 
 class OqRouter(ctypes.Structure):
@@ -96,6 +102,9 @@ def _bind(lib):
         "oq_topk": (None, [P, P, I32, P, P]),
         "oq_expert": (None, [P, P, P, P, P]),
         "oq_moe_forward": (I32, [P, I32, I32, P, P, P, P, P, P, P, P]),
+        "oq_moe_forward_ex": (I32, [P, I32, I32, P, P, P, P, P, P, P, P, P, P]),
+        "oq_layer_tail": (None, [P, P, P, I32, P, P]),
+        "oq_qgemv_head": (None, [P, P, I32, D, P, P]),
         "oq_moe_dense_masked": (I32, [P, I32, I32, P, P, P, P]),
         "oq_rmsnorm_bf16": (None, [P, I32, I32, D, P]),
     }
@@ -126,7 +135,7 @@ def _tensor(qt, keep: _Keep) -> OqTensor:
     c = keep.arr(qt.codes, np.uint32)
     s = keep.arr(qt.scales, np.uint16)
     b = keep.arr(qt.biases, np.uint16)
-    return OqTensor(c.ctypes.data, s.ctypes.data, b.ctypes.data, qt.rows, qt.cols, qt.bits)
+    return OqTensor(c.ctypes.data, s.ctypes.data, b.ctypes.data, qt.rows, qt.cols, qt.bits, getattr(qt, "group", 64))
 
 
 def _router(layer, keep: _Keep, top_k: Optional[int] = None, eps: Optional[float] = None) -> OqRouter:
@@ -148,9 +157,8 @@ def _pool(layer, keep: _Keep, experts: Optional[Sequence[int]] = None):
     sel = range(E) if experts is None else experts
     for e in range(E):
         # shape-only placeholder keeps the shape check meaningful
-        gate_arr[e] = OqTensor(None, None, None, layer.gate.rows, layer.gate.cols, layer.gate.bits)
-        up_arr[e] = OqTensor(None, None, None, layer.up.rows, layer.up.cols, layer.up.bits)
-        down_arr[e] = OqTensor(None, None, None, layer.down.rows, layer.down.cols, layer.down.bits)
+        for arr, qt in ((gate_arr, layer.gate), (up_arr, layer.up), (down_arr, layer.down)):
+            arr[e] = OqTensor(None, None, None, qt.rows, qt.cols, qt.bits, getattr(qt, "group", 64))
     for e in sel:
         gate_arr[e] = _tensor(layer.gate.select(e), keep)
         up_arr[e] = _tensor(layer.up.select(e), keep)
@@ -252,10 +260,48 @@ def rmsnorm_bf16(x_bf16: np.ndarray, eps: float = 1e-6) -> np.ndarray:
     return out
 
 
+def _tail(tail, keep: _Keep):
+    """OqTail from a dict with optional norm_shared / norm_routed / norm_out
+    (float [H]), eps and layer_scalar; None stays None."""
+    if tail is None:
+        return None
+    w = lambda k: None if tail.get(k) is None else keep.arr(tail[k], np.float32).ctypes.data
+    return OqTail(w("norm_shared"), w("norm_routed"), w("norm_out"), float(tail.get("eps", 1e-6)),
+                  float(tail.get("layer_scalar", 1.0)))
+
+
+def layer_tail(s: np.ndarray, r: np.ndarray, tail: dict, resid: Optional[np.ndarray] = None) -> np.ndarray:
+    """One row through the layer tail: s, r float64 [H], resid bf16 bits [H] or None."""
+    keep = _Keep()
+    sv, rv = keep.arr(s, np.float64), keep.arr(r, np.float64)
+    rs = None if resid is None else keep.arr(resid, np.uint16)
+    out = np.empty(sv.size, np.float64)
+    tl = _tail(tail, keep)
+    load().oq_layer_tail(sv.ctypes.data, rv.ctypes.data, _ptr(rs), sv.size, ctypes.byref(tl), out.ctypes.data)
+    return out
+
+
+def qgemv_head(qt, x_bf16: np.ndarray, softcap: float = 0.0, want_logits: bool = True):
+    """Quantized head over token rows x (bf16 bits [T][cols]): (logits [T][rows] or None, argmax [T])."""
+    keep = _Keep()
+    t = _tensor(qt, keep)
+    x = keep.arr(np.atleast_2d(x_bf16), np.uint16)
+    T = x.shape[0]
+    lg = np.empty((T, qt.rows), np.float64) if want_logits else None
+    am = np.empty(T, np.int32)
+    load().oq_qgemv_head(ctypes.byref(t), x.ctypes.data, T, float(softcap), _ptr(lg), am.ctypes.data)
+    return lg, am
+
+
 # ---------------------------------------------------------------- the layer
 
-def forward(layer, x_bf16: np.ndarray, threads: int = 1, dense_experts: bool = True) -> dict:
+def forward(layer, x_bf16: np.ndarray, threads: int = 1, dense_experts: bool = True,
+            tail: Optional[dict] = None, resid: Optional[np.ndarray] = None) -> dict:
     """Whole layer for tokens x (bf16 bits [T][H]).
+
+    ``tail`` (a dict as for ``layer_tail``) passes the two branches through
+    the layer tail, with ``resid`` (bf16 bits [T][H], or None for zero) as
+    the residual rows.
 
     Returns ids int32 [T][k], w float64 [T][k], logits float64 [T][E],
     out64 float64 [T][H] and out_bf16 uint16 [T][H].  ``threads`` > 1 splits
@@ -281,15 +327,18 @@ def forward(layer, x_bf16: np.ndarray, threads: int = 1, dense_experts: bool = T
         experts = sorted(sel)
     pool = _pool(layer, keep, experts)
     sh = _shared(layer, keep)
+    tl = _tail(tail, keep)
+    rs = None if resid is None else keep.arr(resid, np.uint16)
 
     def run(t0, t1):
         if t1 <= t0:
             return
-        rc = lib.oq_moe_forward(x[t0:].ctypes.data, t1 - t0, H, ctypes.byref(rt), ctypes.byref(pool),
-                                None if sh is None else ctypes.byref(sh),
-                                res["ids"][t0:].ctypes.data, res["w"][t0:].ctypes.data,
-                                res["logits"][t0:].ctypes.data, res["out64"][t0:].ctypes.data,
-                                res["out_bf16"][t0:].ctypes.data)
+        rc = lib.oq_moe_forward_ex(x[t0:].ctypes.data, t1 - t0, H, ctypes.byref(rt), ctypes.byref(pool),
+                                   None if sh is None else ctypes.byref(sh), None if tl is None else ctypes.byref(tl),
+                                   None if rs is None else rs[t0:].ctypes.data,
+                                   res["ids"][t0:].ctypes.data, res["w"][t0:].ctypes.data,
+                                   res["logits"][t0:].ctypes.data, res["out64"][t0:].ctypes.data,
+                                   res["out_bf16"][t0:].ctypes.data)
         if rc != 0:
             raise ValueError("oracle rejected the layer shapes")
 

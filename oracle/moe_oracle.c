@@ -64,10 +64,13 @@ int32_t oq_code(const oq_tensor* t, int32_t r, int32_t c) {
     return (int32_t)((word >> (t->bits * (c % per_word))) & mask);
 }
 
-/* Affine dequantisation: w = scale * q + bias, q unsigned (reading of "affine"). */
+/* Affine dequantisation: w = scale * q + bias, q unsigned (reading of "affine"),
+ * with one scale and bias per `group` consecutive weights of a row (64 in the
+ * checkpoint; 0 in the descriptor means 64). */
 double oq_weight(const oq_tensor* t, int32_t r, int32_t c) {
-    int32_t groups = t->cols / GROUP;
-    int64_t g = (int64_t)r * groups + c / GROUP;
+    int32_t gs = t->group > 0 ? t->group : GROUP;
+    int32_t groups = t->cols / gs;
+    int64_t g = (int64_t)r * groups + c / gs;
     return oq_bf16_to_double(t->scales[g]) * (double)oq_code(t, r, c) + oq_bf16_to_double(t->biases[g]);
 }
 
@@ -174,15 +177,54 @@ static int32_t check_shapes(int32_t H, const oq_router* rt, const oq_pool* pool,
     return 0;
 }
 
+/* Post-FFN RMS norm of one branch: v / sqrt(mean(v^2) + eps) times the
+ * learned weight w (element-wise). */
+static void tail_norm(const double* v, const float* w, int32_t H, double eps, double* out) {
+    double ss = 0.0;
+    for (int32_t i = 0; i < H; ++i) ss += v[i] * v[i];
+    const double inv = 1.0 / sqrt(ss / (double)H + eps);
+    for (int32_t i = 0; i < H; ++i) out[i] = v[i] * inv * (double)w[i];
+}
+
+/* The layer tail ("Decode", phase table, cb2: post-FFN norms, residual and
+ * layer scalar; "Why the runtime has this shape": parallel shared and routed
+ * FFNs and a learned layer scalar).  Readings: each branch may have its own
+ * post-FFN RMS norm with a learned weight (NULL: none), their sum may have
+ * one more, the residual row is added after those norms, and the layer
+ * scalar multiplies the whole result:
+ *   out = layer_scalar * (residual + N_out(N_s(s) + N_r(r))). */
+void oq_layer_tail(const double* s, const double* r, const uint16_t* resid, int32_t H, const oq_tail* tail,
+                   double* out) {
+    double* a = (double*)malloc(sizeof(double) * (size_t)H);
+    double* b = (double*)malloc(sizeof(double) * (size_t)H);
+    if (tail->norm_shared) tail_norm(s, tail->norm_shared, H, tail->eps, a);
+    else for (int32_t i = 0; i < H; ++i) a[i] = s[i];
+    if (tail->norm_routed) tail_norm(r, tail->norm_routed, H, tail->eps, b);
+    else for (int32_t i = 0; i < H; ++i) b[i] = r[i];
+    for (int32_t i = 0; i < H; ++i) a[i] += b[i];
+    if (tail->norm_out) tail_norm(a, tail->norm_out, H, tail->eps, b);
+    else for (int32_t i = 0; i < H; ++i) b[i] = a[i];
+    for (int32_t i = 0; i < H; ++i) {
+        double res = resid ? oq_bf16_to_double(resid[i]) : 0.0;
+        out[i] = tail->layer_scalar * (res + b[i]);
+    }
+    free(a);
+    free(b);
+}
+
 /* The layer, token by token: route, run the k chosen experts, weight and sum
- * them, add the shared expert, round once to bf16. */
-int32_t oq_moe_forward(const uint16_t* x, int32_t T, int32_t H, const oq_router* rt,
-                       const oq_pool* pool, const oq_shared* shared,
-                       int32_t* ids, double* w, double* logits, double* out64, uint16_t* out_bf16) {
+ * them (routed branch), run the shared expert (shared branch), add the two
+ * (or pass them through the layer tail), round once to bf16. */
+int32_t oq_moe_forward_ex(const uint16_t* x, int32_t T, int32_t H, const oq_router* rt,
+                          const oq_pool* pool, const oq_shared* shared, const oq_tail* tail,
+                          const uint16_t* resid, int32_t* ids, double* w, double* logits, double* out64,
+                          uint16_t* out_bf16) {
     if (check_shapes(H, rt, pool, shared)) return -1;
     int32_t E = pool->num_experts, k = rt->top_k;
     double* xf = (double*)malloc(sizeof(double) * (size_t)H);
     double* y = (double*)malloc(sizeof(double) * (size_t)H);
+    double* sacc = (double*)malloc(sizeof(double) * (size_t)H);
+    double* racc = (double*)malloc(sizeof(double) * (size_t)H);
     double* acc = (double*)malloc(sizeof(double) * (size_t)H);
     double* lg = (double*)malloc(sizeof(double) * (size_t)E);
     int32_t* id = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
@@ -192,16 +234,20 @@ int32_t oq_moe_forward(const uint16_t* x, int32_t T, int32_t H, const oq_router*
         for (int32_t i = 0; i < H; ++i) xf[i] = oq_bf16_to_double(xt[i]);
         oq_router_logits(rt, xt, H, lg);
         oq_topk(rt, lg, E, id, wt);
-        for (int32_t i = 0; i < H; ++i) acc[i] = 0.0;
+        for (int32_t i = 0; i < H; ++i) sacc[i] = racc[i] = 0.0;
         if (shared) {
             oq_expert(&shared->gate, &shared->up, &shared->down, xf, y);
-            for (int32_t i = 0; i < H; ++i) acc[i] += y[i];
+            for (int32_t i = 0; i < H; ++i) sacc[i] = y[i];
         }
         for (int32_t j = 0; j < k; ++j) {
             int32_t e = id[j];
             oq_expert(&pool->gate[e], &pool->up[e], &pool->down[e], xf, y);
-            for (int32_t i = 0; i < H; ++i) acc[i] += wt[j] * y[i];
+            for (int32_t i = 0; i < H; ++i) racc[i] += wt[j] * y[i];
         }
+        if (tail)
+            oq_layer_tail(sacc, racc, resid ? resid + (int64_t)t * H : NULL, H, tail, acc);
+        else
+            for (int32_t i = 0; i < H; ++i) acc[i] = sacc[i] + racc[i];
         if (ids) memcpy(ids + (int64_t)t * k, id, sizeof(int32_t) * (size_t)k);
         if (w) memcpy(w + (int64_t)t * k, wt, sizeof(double) * (size_t)k);
         if (logits) memcpy(logits + (int64_t)t * E, lg, sizeof(double) * (size_t)E);
@@ -209,8 +255,14 @@ int32_t oq_moe_forward(const uint16_t* x, int32_t T, int32_t H, const oq_router*
         if (out_bf16)
             for (int32_t i = 0; i < H; ++i) out_bf16[(int64_t)t * H + i] = oq_bf16_round(acc[i]);
     }
-    free(xf); free(y); free(acc); free(lg); free(id); free(wt);
+    free(xf); free(y); free(sacc); free(racc); free(acc); free(lg); free(id); free(wt);
     return 0;
+}
+
+int32_t oq_moe_forward(const uint16_t* x, int32_t T, int32_t H, const oq_router* rt,
+                       const oq_pool* pool, const oq_shared* shared,
+                       int32_t* ids, double* w, double* logits, double* out64, uint16_t* out_bf16) {
+    return oq_moe_forward_ex(x, T, H, rt, pool, shared, NULL, NULL, ids, w, logits, out64, out_bf16);
 }
 
 /* Brute force for small shapes: all E experts are evaluated, and the sum
@@ -258,4 +310,31 @@ void oq_rmsnorm_bf16(const uint16_t* in, int32_t T, int32_t H, double eps, uint1
         for (int32_t i = 0; i < H; ++i)
             out[(int64_t)t * H + i] = oq_bf16_round(oq_bf16_to_double(in[(int64_t)t * H + i]) * inv);
     }
+}
+
+/* The tied quantized head at the end of decode ("Why the runtime has this
+ * shape": embedding and head share quantized weights, final logit softcap
+ * 30.0; "Decode": after the last layer the head returns the argmax token
+ * directly in the greedy configuration).  For each token row x (bf16 [H]):
+ * logit_v = W_v . x, then cap * tanh(logit_v / cap) when cap > 0, and the
+ * argmax over v (the exact fp64 values; equal values to the lower index).
+ * logits [T][V] and argmax [T] may each be NULL. */
+void oq_qgemv_head(const oq_tensor* t, const uint16_t* x, int32_t T, double softcap, double* logits,
+                   int32_t* argmax) {
+    int32_t V = t->rows, H = t->cols;
+    double* xf = (double*)malloc(sizeof(double) * (size_t)H);
+    double* y = (double*)malloc(sizeof(double) * (size_t)V);
+    for (int32_t tk = 0; tk < T; ++tk) {
+        for (int32_t i = 0; i < H; ++i) xf[i] = oq_bf16_to_double(x[(int64_t)tk * H + i]);
+        oq_matvec(t, xf, y);
+        if (softcap > 0.0)
+            for (int32_t v = 0; v < V; ++v) y[v] = softcap * tanh(y[v] / softcap);
+        int32_t best = 0;
+        for (int32_t v = 1; v < V; ++v)
+            if (y[v] > y[best]) best = v;
+        if (logits) memcpy(logits + (int64_t)tk * V, y, sizeof(double) * (size_t)V);
+        if (argmax) argmax[tk] = best;
+    }
+    free(xf);
+    free(y);
 }

@@ -29,9 +29,10 @@ extern "C" {
 
 typedef struct {
     const uint32_t* codes;
-    const uint16_t* scales;
-    const uint16_t* biases;
+    const uint16_t* scales;         /* [rows][cols/group] */
+    const uint16_t* biases;         /* [rows][cols/group] */
     int32_t rows, cols, bits;
+    int32_t group;                  /* weights per scale/bias; 0 means 64 */
 } oq_tensor;
 
 typedef struct {
@@ -54,6 +55,17 @@ typedef struct {
     oq_tensor gate, up, down;       /* [Is][H], [Is][H], [H][Is] */
 } oq_shared;
 
+/* Layer tail: post-FFN RMS norms (learned weights [H], NULL: none) of the
+ * shared branch, the routed branch and their sum, then the residual and the
+ * layer scalar. */
+typedef struct {
+    const float* norm_shared;
+    const float* norm_routed;
+    const float* norm_out;
+    double eps;
+    double layer_scalar;
+} oq_tail;
+
 double   oq_bf16_to_double(uint16_t b);
 uint16_t oq_bf16_round(double v);                       /* nearest, ties to even */
 int32_t  oq_code(const oq_tensor* t, int32_t r, int32_t c);
@@ -72,6 +84,22 @@ void oq_expert(const oq_tensor* gate, const oq_tensor* up, const oq_tensor* down
 int32_t oq_moe_forward(const uint16_t* x, int32_t T, int32_t H, const oq_router* rt,
                        const oq_pool* pool, const oq_shared* shared,
                        int32_t* ids, double* w, double* logits, double* out64, uint16_t* out_bf16);
+
+/* The same with the layer tail (tail NULL: none) and an optional residual
+ * (bf16 [T][H], NULL: zero). */
+int32_t oq_moe_forward_ex(const uint16_t* x, int32_t T, int32_t H, const oq_router* rt,
+                          const oq_pool* pool, const oq_shared* shared, const oq_tail* tail,
+                          const uint16_t* resid, int32_t* ids, double* w, double* logits, double* out64,
+                          uint16_t* out_bf16);
+
+/* out = layer_scalar * (residual + N_out(N_s(s) + N_r(r))) for one row. */
+void oq_layer_tail(const double* s, const double* r, const uint16_t* resid, int32_t H, const oq_tail* tail,
+                   double* out);
+
+/* Quantized head: logits = W x per token, softcapped when softcap > 0, and
+ * the argmax (ties to the lower row).  logits [T][rows], argmax [T]; either may be NULL. */
+void oq_qgemv_head(const oq_tensor* t, const uint16_t* x, int32_t T, double softcap, double* logits,
+                   int32_t* argmax);
 
 /* Brute force: every expert evaluated densely, masked to the selected ones. */
 int32_t oq_moe_dense_masked(const uint16_t* x, int32_t T, int32_t H, const oq_router* rt,

@@ -12,6 +12,9 @@ Recipe (all draws from the counter-based SplitMix64 streams in synth.c,
 keyed by (seed, layer, expert, tensor)):
   * codes: uniform random 32-bit words, i.e. i.i.d. uniform codes;
   * scale: bf16(U[0.002, 0.01]); bias: -2^(b-1) * scale (exact in bf16);
+    or, for the general affine map, scale and bias drawn independently
+    (bf16 of uniforms over given ranges, from streams of their own);
+  * group: 64 weights per scale/bias (other sizes on request);
   * activations: bf16(N(0, 1)) by Box-Muller;
   * Zipf skew (128-token and 4096-token prefill): an additive per-expert
     logit bias 0.37 * ln p_pi(e), p_k = k^-1.1 / sum_j j^-1.1, pi a seeded
@@ -46,6 +49,8 @@ T_SUP_CODES, T_SUP_SCALES = 11, 12
 T_SDOWN_CODES, T_SDOWN_SCALES = 13, 14
 T_TOKENS = 15
 T_ZIPF_PERM = 16
+T_BIAS_FLAG = 0x100     # or-ed into a scale stream id: the independent-bias stream
+T_TAIL = 17             # layer-tail norm weights
 SHARED_SLOT = 0xFFFF
 
 
@@ -172,22 +177,27 @@ class QTensor:
     rows: int
     cols: int
     bits: int
+    group: int = GROUP
 
     def select(self, i: int) -> "QTensor":
-        return QTensor(self.codes[i], self.scales[i], self.biases[i], self.rows, self.cols, self.bits)
+        return QTensor(self.codes[i], self.scales[i], self.biases[i], self.rows, self.cols, self.bits, self.group)
 
 
 def make_qtensor(seed: int, layer: int, slot: int, t_codes: int, t_scales: int,
                  rows: int, cols: int, bits: int, batch: int = 0,
-                 scale_lo: float = 0.002, scale_hi: float = 0.01) -> QTensor:
-    """Uniform random codes, bf16 scale ~ U[scale_lo, scale_hi], bias = -2^(bits-1)*scale.
+                 scale_lo: float = 0.002, scale_hi: float = 0.01,
+                 bias_range: Optional[tuple] = None, group: int = GROUP) -> QTensor:
+    """Uniform random codes, bf16 scale ~ U[scale_lo, scale_hi], and
+    bias = -2^(bits-1)*scale, or with ``bias_range`` = (lo, hi) a bias
+    bf16(U[lo, hi]) drawn independently of the scale.  One scale and bias per
+    ``group`` weights of a row.
 
     With ``batch`` > 0 the result holds ``batch`` matrices, matrix i drawn from
     the streams of slot ``slot + i`` (one expert per slot).
     """
-    assert cols % GROUP == 0 and 32 % bits == 0
+    assert cols % group == 0 and 32 % bits == 0
     words = cols * bits // 32
-    groups = cols // GROUP
+    groups = cols // group
     nb = max(batch, 1)
     codes = np.empty((nb, rows, words), dtype=np.uint32)
     scales = np.empty((nb, rows, groups), dtype=np.uint16)
@@ -201,10 +211,14 @@ def make_qtensor(seed: int, layer: int, slot: int, t_codes: int, t_scales: int,
         list(_pool().map(one, range(nb)))
     else:
         one(0)
-    biases = neg_mul_bf16(scales, float(1 << (bits - 1)))
+    if bias_range is None:
+        biases = neg_mul_bf16(scales, float(1 << (bits - 1)))
+    else:
+        biases = np.stack([uniform_bf16(seed, stream_id(layer, slot + i, t_scales | T_BIAS_FLAG), rows * groups,
+                                        bias_range[0], bias_range[1]).reshape(rows, groups) for i in range(nb)])
     if batch == 0:
         codes, scales, biases = codes[0], scales[0], biases[0]
-    return QTensor(codes, scales, biases, rows, cols, bits)
+    return QTensor(codes, scales, biases, rows, cols, bits, group)
 
 
 def zipf_logit_bias(seed: int, layer: int, num_experts: int, s: float = 1.1,
@@ -232,6 +246,10 @@ class LayerConfig:
     zipf: bool = False
     eps: float = 1e-6
     name: str = ""
+    expert_bits: int = 4            # routed and shared expert codes (4 or 8)
+    group: int = GROUP              # weights per scale/bias of the expert matrices
+    scale_range: tuple = (0.002, 0.01)
+    bias_range: Optional[tuple] = None   # None: bias = -2^(b-1) * scale
 
 
 # The five synthetic workloads (Gemma-4-26B-A4B shapes except the first).
@@ -271,28 +289,34 @@ class Layer:
     index: int = 0
 
 
+def _qkw(cfg: LayerConfig) -> dict:
+    return dict(scale_lo=cfg.scale_range[0], scale_hi=cfg.scale_range[1], bias_range=cfg.bias_range,
+                group=cfg.group)
+
+
 def make_expert(cfg: LayerConfig, seed: int, layer: int, expert: int):
     """(gate, up, down) of one routed expert; the same values make_layer draws for it."""
-    H, I = cfg.hidden, cfg.inter
-    return (make_qtensor(seed, layer, expert, T_GATE_CODES, T_GATE_SCALES, I, H, 4),
-            make_qtensor(seed, layer, expert, T_UP_CODES, T_UP_SCALES, I, H, 4),
-            make_qtensor(seed, layer, expert, T_DOWN_CODES, T_DOWN_SCALES, H, I, 4))
+    H, I, b, kw = cfg.hidden, cfg.inter, cfg.expert_bits, _qkw(cfg)
+    return (make_qtensor(seed, layer, expert, T_GATE_CODES, T_GATE_SCALES, I, H, b, **kw),
+            make_qtensor(seed, layer, expert, T_UP_CODES, T_UP_SCALES, I, H, b, **kw),
+            make_qtensor(seed, layer, expert, T_DOWN_CODES, T_DOWN_SCALES, H, I, b, **kw))
 
 
 def make_layer(cfg: LayerConfig, seed: int, layer: int = 0, shared: bool = True, experts: bool = True) -> Layer:
     """A full layer; with experts=False the routed experts are left out (None)."""
     H, E, I, Is = cfg.hidden, cfg.num_experts, cfg.inter, cfg.shared_inter
+    b, kw = cfg.expert_bits, _qkw(cfg)
     router = make_qtensor(seed, layer, SHARED_SLOT, T_ROUTER_CODES, T_ROUTER_SCALES, E, H, 8)
     gate = up = down = None
     if experts:
-        gate = make_qtensor(seed, layer, 0, T_GATE_CODES, T_GATE_SCALES, I, H, 4, batch=E)
-        up = make_qtensor(seed, layer, 0, T_UP_CODES, T_UP_SCALES, I, H, 4, batch=E)
-        down = make_qtensor(seed, layer, 0, T_DOWN_CODES, T_DOWN_SCALES, H, I, 4, batch=E)
+        gate = make_qtensor(seed, layer, 0, T_GATE_CODES, T_GATE_SCALES, I, H, b, batch=E, **kw)
+        up = make_qtensor(seed, layer, 0, T_UP_CODES, T_UP_SCALES, I, H, b, batch=E, **kw)
+        down = make_qtensor(seed, layer, 0, T_DOWN_CODES, T_DOWN_SCALES, H, I, b, batch=E, **kw)
     sg = su = sd = None
     if shared and Is > 0:
-        sg = make_qtensor(seed, layer, SHARED_SLOT, T_SGATE_CODES, T_SGATE_SCALES, Is, H, 4)
-        su = make_qtensor(seed, layer, SHARED_SLOT, T_SUP_CODES, T_SUP_SCALES, Is, H, 4)
-        sd = make_qtensor(seed, layer, SHARED_SLOT, T_SDOWN_CODES, T_SDOWN_SCALES, H, Is, 4)
+        sg = make_qtensor(seed, layer, SHARED_SLOT, T_SGATE_CODES, T_SGATE_SCALES, Is, H, b, **kw)
+        su = make_qtensor(seed, layer, SHARED_SLOT, T_SUP_CODES, T_SUP_SCALES, Is, H, b, **kw)
+        sd = make_qtensor(seed, layer, SHARED_SLOT, T_SDOWN_CODES, T_SDOWN_SCALES, H, Is, b, **kw)
     bias = zipf_logit_bias(seed, layer, E) if cfg.zipf else None
     return Layer(cfg, router, gate, up, down, sg, su, sd, None, None, bias, seed, layer)
 
@@ -300,3 +324,28 @@ def make_layer(cfg: LayerConfig, seed: int, layer: int = 0, shared: bool = True,
 def make_tokens(seed: int, T: int, H: int, batch: int = 0, layer: int = 0) -> np.ndarray:
     """bf16 bit patterns [T][H] of N(0, 1) activations."""
     return normal_bf16(seed, stream_id(layer, batch, T_TOKENS), T * H).reshape(T, H)
+
+
+def make_tail(seed: int, layer: int, H: int, norms=("shared", "routed", "out"), layer_scalar: float = 0.75,
+              eps: float = 1e-6) -> dict:
+    """Layer-tail parameters: learned post-FFN norm weights U[0.5, 1.5] (fp32,
+    rounded through bf16 as a checkpoint stores them) for the named norms, the
+    layer scalar and epsilon."""
+    out = dict(eps=eps, layer_scalar=layer_scalar)
+    for i, n in enumerate(("shared", "routed", "out")):
+        w = None
+        if n in norms:
+            w = bf16_bits_to_f32(uniform_bf16(seed, stream_id(layer, SHARED_SLOT, T_TAIL) + (i << 20), H, 0.5, 1.5))
+        out["norm_" + n] = w
+    return out
+
+
+# Vocabulary of the synthetic tied head: the pages do not give it; 262,144
+# rows (2^18) stands in for the Gemma tokenizer's vocabulary.
+HEAD_VOCAB = 262144
+T_HEAD_CODES, T_HEAD_SCALES = 18, 19
+
+
+def make_head(seed: int, vocab: int, H: int, bits: int = 4) -> QTensor:
+    """The tied embedding/head matrix [vocab][H], drawn like the expert matrices."""
+    return make_qtensor(seed, 0, SHARED_SLOT, T_HEAD_CODES, T_HEAD_SCALES, vocab, H, bits)

@@ -415,6 +415,153 @@ def test_rmsnorm_bf16_epsilon_placement():
     assert np.array_equal(y[0], f32_to_bf16_bits(xr / 4.0))
 
 
+# ------------------------------------------------------------------ group sizes and 8-bit experts
+
+def test_group128_is_group64_with_repeated_pairs():
+    """A group-128 matrix is the group-64 matrix whose adjacent groups share
+    their scale and bias; one-hot inputs return column c with the pair of
+    group c // 128."""
+    rng = np.random.default_rng(21)
+    rows, cols = 5, 256
+    for bits in (4, 8):
+        q = rng.integers(0, 1 << bits, size=(rows, cols))
+        sc = f32_to_bf16_bits(rng.uniform(0.002, 0.01, (rows, cols // 128)))
+        bi = f32_to_bf16_bits(rng.uniform(-0.1, 0.1, (rows, cols // 128)))
+        q128 = qtensor_from_codes(q, sc, bi, bits)
+        q128.group = 128
+        q64 = qtensor_from_codes(q, np.repeat(sc, 2, axis=1), np.repeat(bi, 2, axis=1), bits)
+        x = rng.standard_normal(cols)
+        assert np.array_equal(O.matvec(q128, x), O.matvec(q64, x))
+        s64, b64 = bf16_bits_to_f64(sc), bf16_bits_to_f64(bi)
+        for c in (0, 127, 128, 200):
+            e = np.zeros(cols)
+            e[c] = 1.0
+            assert np.array_equal(O.matvec(q128, e), s64[:, c // 128] * q[:, c] + b64[:, c // 128])
+
+
+def test_dense_masked_equals_sparse_8bit_experts():
+    cfg = S.LayerConfig(hidden=256, num_experts=8, inter=64, shared_inter=128, top_k=3, expert_bits=8,
+                        bias_range=(-0.3, 0.3), scale_range=(1e-4, 0.02))
+    layer = S.make_layer(cfg, 41)
+    assert layer.gate.bits == 8 and layer.shared_down.bits == 8
+    x = S.make_tokens(41, 3, cfg.hidden)
+    r = O.forward(layer, x)
+    assert np.allclose(r["out64"], O.dense_masked(layer, x), rtol=1e-12, atol=1e-14)
+    # the expert through numpy on the dequantised matrices (independent biases)
+    xf = bf16_bits_to_f64(x[1])
+    e = int(r["ids"][1][0])
+    g, u, d = layer.gate.select(e), layer.up.select(e), layer.down.select(e)
+    h = torch.nn.functional.gelu(torch.tensor(O.dequant(g) @ xf), approximate="tanh").numpy() * (O.dequant(u) @ xf)
+    assert np.allclose(O.expert(g, u, d, xf), O.dequant(d) @ h, rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------------------------ layer tail
+
+def _const_branches(H, a, b):
+    return np.full(H, float(a)), np.full(H, float(b))
+
+
+def test_tail_closed_form_constant_branches():
+    """s = 3, r = -3 (constant rows), eps 7: each branch norm gives 3/sqrt(9 + 7)
+    = 0.75 times its weight; with w_s = 1 + d and w_r = d their sum is 0.75
+    everywhere, whose norm is 0.75/sqrt(0.5625 + 7) = 3/11 times w_out."""
+    H = 128
+    rng = np.random.default_rng(31)
+    d = rng.uniform(0.1, 0.9, H).astype(np.float32)
+    w_s = (1.0 + d).astype(np.float32)
+    w_o = rng.uniform(0.5, 1.5, H).astype(np.float32)
+    # w_s - d must be exactly 1 in fp32 for the closed form
+    d = (w_s - np.float32(1.0)).astype(np.float32)
+    s, r = _const_branches(H, 3.0, -3.0)
+    resid = f32_to_bf16_bits(rng.standard_normal(H))
+    tail = dict(norm_shared=w_s, norm_routed=d, norm_out=w_o, eps=7.0, layer_scalar=0.5)
+    got = O.layer_tail(s, r, tail, resid)
+    want = 0.5 * (bf16_bits_to_f64(resid) + (3.0 / 11.0) * w_o.astype(np.float64))
+    assert np.allclose(got, want, rtol=1e-14, atol=1e-15)
+
+
+def test_tail_without_norms_is_scaled_sum_plus_residual():
+    H = 96
+    rng = np.random.default_rng(32)
+    s, r = rng.standard_normal(H), rng.standard_normal(H)
+    resid = f32_to_bf16_bits(rng.standard_normal(H))
+    got = O.layer_tail(s, r, dict(eps=1e-6, layer_scalar=1.25), resid)
+    assert np.allclose(got, 1.25 * (bf16_bits_to_f64(resid) + s + r), rtol=1e-15, atol=1e-15)
+    assert np.allclose(O.layer_tail(s, r, dict(eps=1e-6, layer_scalar=1.0)), s + r, rtol=0, atol=0)
+
+
+def test_tail_norms_are_scale_invariant_per_branch():
+    """With eps 0 each normed branch ignores its own scale."""
+    H = 64
+    rng = np.random.default_rng(33)
+    s, r = rng.standard_normal(H), rng.standard_normal(H)
+    t = S.make_tail(5, 0, H, eps=0.0)
+    base = O.layer_tail(s, r, t)
+    assert np.allclose(O.layer_tail(4.0 * s, 0.25 * r, t), base, rtol=1e-12, atol=1e-14)
+    only_out = dict(t, norm_shared=None, norm_routed=None)
+    assert np.allclose(O.layer_tail(3.0 * s, 3.0 * r, only_out), O.layer_tail(s, r, only_out), rtol=1e-12)
+    assert not np.allclose(O.layer_tail(3.0 * s, r, only_out), O.layer_tail(s, r, only_out))
+    # rms of the output norm's input: the output divided by its weight has unit mean square
+    v = O.layer_tail(s, r, t) / t["norm_out"].astype(np.float64) / t["layer_scalar"]
+    assert abs(np.mean(v * v) - 1.0) < 1e-12
+
+
+def test_layer_with_tail_composes_branches():
+    """The layer with a tail is the tail of (shared expert, weighted routed sum)."""
+    layer = tiny_layer()
+    x = tiny_tokens(T=2)
+    t = S.make_tail(9, 0, layer.cfg.hidden)
+    resid = tiny_tokens(seed=77, T=2)
+    r = O.forward(layer, x, tail=t, resid=resid)
+    base = O.forward(layer, x)
+    assert np.array_equal(r["ids"], base["ids"])
+    for tk in range(2):
+        xf = bf16_bits_to_f64(x[tk])
+        sh = O.expert(layer.shared_gate, layer.shared_up, layer.shared_down, xf)
+        ro = sum(base["w"][tk, j] * O.expert(layer.gate.select(e), layer.up.select(e), layer.down.select(e), xf)
+                 for j, e in enumerate(base["ids"][tk]))
+        assert np.allclose(r["out64"][tk], O.layer_tail(sh, ro, t, resid[tk]), rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------------------------ quantized head
+
+def test_head_one_hot_softcap_and_argmax():
+    rng = np.random.default_rng(41)
+    V, H = 40, 128
+    q = rng.integers(0, 16, size=(V, H))
+    sc = f32_to_bf16_bits(rng.uniform(0.2, 1.0, (V, H // 64)))
+    bi = f32_to_bf16_bits(rng.uniform(-4.0, 4.0, (V, H // 64)))
+    qt = qtensor_from_codes(q, sc, bi, 4)
+    s64, b64 = bf16_bits_to_f64(sc), bf16_bits_to_f64(bi)
+    c = 70
+    x = np.zeros(H, np.uint16)
+    x[c] = 0x3F80                                      # bf16 1.0
+    raw = s64[:, c // 64] * q[:, c] + b64[:, c // 64]  # up to ~19: the cap matters
+    lg, am = O.qgemv_head(qt, x[None, :], softcap=0.0)
+    assert np.array_equal(lg[0], raw) and am[0] == int(np.argmax(raw))
+    lg, am = O.qgemv_head(qt, x[None, :], softcap=5.0)
+    assert np.allclose(lg[0], 5.0 * np.tanh(raw / 5.0), rtol=1e-15, atol=1e-15)
+    assert np.all(np.abs(lg[0]) < 5.0) and am[0] == int(np.argmax(raw))
+
+
+def test_head_argmax_ties_and_dense_rows():
+    rng = np.random.default_rng(42)
+    V, H = 24, 128
+    q = rng.integers(0, 16, size=(V, H))
+    q[17] = q[5]                                       # rows 5 and 17 identical ...
+    sc = f32_to_bf16_bits(rng.uniform(0.002, 0.01, (V, H // 64)))
+    sc[17] = sc[5]
+    bi = f32_to_bf16_bits(rng.uniform(-0.1, 0.1, (V, H // 64)))
+    bi[5] = bi[17] = f32_to_bf16_bits(np.full(H // 64, 3.0))   # ... and far above the others
+    qt = qtensor_from_codes(q, sc, bi, 4)
+    x = f32_to_bf16_bits(np.abs(rng.standard_normal((3, H))) + 0.1)
+    lg, am = O.qgemv_head(qt, x, softcap=30.0)
+    W = bf16_bits_to_f64(sc).repeat(64, axis=1) * q + bf16_bits_to_f64(bi).repeat(64, axis=1)
+    raw = bf16_bits_to_f64(x) @ W.T
+    assert np.allclose(lg, 30.0 * np.tanh(raw / 30.0), rtol=1e-13, atol=1e-13)
+    assert np.all(am == 5)
+
+
 # ------------------------------------------------------------------ the pins catch planted mistakes
 
 def _pin_callables():
@@ -445,7 +592,7 @@ MUTATIONS = [
      "(double)oq_code(t, r, c) - oq_bf16_to_double(t->biases[g])"),
     ("scale and bias swapped", "return oq_bf16_to_double(t->scales[g]) * (double)oq_code(t, r, c) + oq_bf16_to_double(t->biases[g]);",
      "return oq_bf16_to_double(t->biases[g]) * (double)oq_code(t, r, c) + oq_bf16_to_double(t->scales[g]);"),
-    ("wrong group index", "int64_t g = (int64_t)r * groups + c / GROUP;", "int64_t g = (int64_t)r * groups + c % groups;"),
+    ("wrong group index", "int64_t g = (int64_t)r * groups + c / gs;", "int64_t g = (int64_t)r * groups + c % groups;"),
     ("router 1/sqrt(H) dropped", "r[i] = oq_bf16_to_double(x[i]) * inv * rs * inv_sqrt_h;",
      "r[i] = oq_bf16_to_double(x[i]) * inv * rs;"),
     ("rms uses the sum", "sqrt(ss / (double)H + rt->eps)", "sqrt(ss + rt->eps)"),
@@ -458,9 +605,9 @@ MUTATIONS = [
     ("per-expert scale by slot", "(double)rt->per_expert_scale[ids[j]]", "(double)rt->per_expert_scale[j]"),
     ("GELU on the up branch", "g[i] = oq_gelu_tanh(g[i]) * u[i];", "g[i] = g[i] * oq_gelu_tanh(u[i]);"),
     ("GELU cubic coefficient", "0.044715 * z * z * z", "0.044715 * z * z"),
-    ("shared expert weighted", "for (int32_t i = 0; i < H; ++i) acc[i] += y[i];",
-     "for (int32_t i = 0; i < H; ++i) acc[i] += wt[0] * y[i];"),
-    ("routed output unweighted", "acc[i] += wt[j] * y[i];", "acc[i] += y[i];"),
+    ("shared expert weighted", "for (int32_t i = 0; i < H; ++i) sacc[i] = y[i];",
+     "for (int32_t i = 0; i < H; ++i) sacc[i] = wt[0] * y[i];"),
+    ("routed output unweighted", "racc[i] += wt[j] * y[i];", "racc[i] += y[i];"),
     ("wrong expert for the down projection", "oq_expert(&pool->gate[e], &pool->up[e], &pool->down[e], xf, y);",
      "oq_expert(&pool->gate[e], &pool->up[e], &pool->down[(e + 1) % pool->num_experts], xf, y);"),
     ("bf16 ties away from zero", "(rem == 0.5 && fmod(fl, 2.0) != 0.0)", "(rem == 0.5)"),
@@ -471,6 +618,22 @@ MUTATIONS = [
     ("rmsnorm epsilon dropped", "double inv = 1.0 / sqrt(ss / (double)H + eps);",
      "double inv = 1.0 / sqrt(ss / (double)H);"),
     ("selection in fp32", "double v = logits[e];", "double v = (float)logits[e];"),
+    ("group size ignored", "int32_t gs = t->group > 0 ? t->group : GROUP;", "int32_t gs = GROUP;"),
+    ("tail epsilon outside the root", "const double inv = 1.0 / sqrt(ss / (double)H + eps);",
+     "const double inv = 1.0 / (sqrt(ss / (double)H) + eps);"),
+    ("tail norm weight not applied", "out[i] = v[i] * inv * (double)w[i];", "out[i] = v[i] * inv;"),
+    ("tail routed norm takes the shared weight", "tail_norm(r, tail->norm_routed, H",
+     "tail_norm(r, tail->norm_shared ? tail->norm_shared : tail->norm_routed, H"),
+    ("tail scalar only on the FFN part", "out[i] = tail->layer_scalar * (res + b[i]);",
+     "out[i] = res + tail->layer_scalar * b[i];"),
+    ("tail residual dropped", "double res = resid ? oq_bf16_to_double(resid[i]) : 0.0;", "double res = 0.0;"),
+    ("tail output norm skipped", "if (tail->norm_out) tail_norm(a, tail->norm_out, H, tail->eps, b);",
+     "if (0) tail_norm(a, tail->norm_out, H, tail->eps, b);"),
+    ("layer branches swapped into the tail", "oq_layer_tail(sacc, racc,", "oq_layer_tail(racc, sacc,"),
+    ("head softcap without the inner division", "y[v] = softcap * tanh(y[v] / softcap);",
+     "y[v] = softcap * tanh(y[v]);"),
+    ("head argmax ties to the higher row", "if (y[v] > y[best]) best = v;", "if (y[v] >= y[best]) best = v;"),
+    ("head argmax picks the lowest", "if (y[v] > y[best]) best = v;", "if (y[v] < y[best]) best = v;"),
 ]
 
 
