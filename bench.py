@@ -5,9 +5,13 @@ routed experts, shared expert, combine) for one token of a Gemma-4-26B-A4B-
 shaped layer (hidden 2816, 128 experts, top-8, expert intermediate 704,
 shared intermediate 2112; 8-bit router, 4-bit experts, group 64).  Calls
 rotate over --layers distinct resident layers with a fresh token each, so
-the 256 MB Infinity Cache cannot hold the working set.  The timed calls are
-replayed from a HIP graph (one capture of K calls); inputs are resident in
-HBM before the timer starts.  The single-launch decode kernel's own duration
+the 256 MB Infinity Cache cannot hold the working set, and every timed
+replay follows an untimed 1 GiB streaming read that evicts it.  The timed
+calls are replayed from a HIP graph (one capture of K calls); the figure is
+the median over five replays, and the workspace's error bits are checked
+after every timed region.  Inputs are resident in HBM before the timer
+starts.  The HBM read peak is also measured (mq_stream_read over 4 GiB) and
+fractions are given against both it and the vendor figure.  The single-launch decode kernel's own duration
 is the timed region's event interval over the launches in it (one launch
 per call); the roofline figure divides the call's algorithmic bytes by it.
 
@@ -15,7 +19,8 @@ Also reported (extra fields of the same JSON line): the 128-token prefill
 chunk with Zipf(1.1)-skewed routing, the 30-layer stack (one token through
 30 layers, each call normalising its input), the 4096-token prefill (the
 matrix-core regime, reported in TFLOP/s), and the fp64 CPU oracle timed on
-a bounded sample of decode tokens.  Prints one JSON line on stdout.
+bounded samples of decode and prefill tokens, on one core and on all host
+cores.  Prints one JSON line on stdout.
 
 Profiling helpers (not part of the default run):
   --profile decode       runs decode calls back to back, then a copy kernel of
@@ -109,8 +114,11 @@ def flops_per_token(cfg):
     return 2 * E * H + k * 6 * I * H + 6 * Is * H
 
 
-def time_graph(torch, calls, steps, warmup):
-    """Capture `steps` calls in one HIP graph; warm up, then time one replay."""
+def time_graph(torch, calls, steps, warmup, flush=None, reps=5):
+    """Capture `steps` calls in one HIP graph; warm up, then time `reps`
+    replays, each preceded by the untimed `flush` (a streaming read that
+    evicts the Infinity Cache).  Returns the median ms per call, the per-replay
+    values and the graph."""
     for i in range(warmup):
         calls[i % len(calls)]()
     torch.cuda.synchronize()
@@ -124,12 +132,46 @@ def time_graph(torch, calls, steps, warmup):
     torch.cuda.synchronize()
     g.replay()                      # untimed replay
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    g.replay()
-    ev1.record()
-    torch.cuda.synchronize()
-    return ev0.elapsed_time(ev1) / steps, g
+    per = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        g.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        per.append(ev0.elapsed_time(ev1) / steps)
+    return float(np.median(per)), per, g
+
+
+class Flush:
+    """Streaming reads over a buffer larger than the Infinity Cache: run
+    before each timed replay so that no weights of the timed calls are cached
+    from earlier work, and timed on its own as the measured HBM read peak."""
+
+    def __init__(self, torch, M, nbytes=4 << 30, workgroups=4096):
+        self.torch, self.M, self.wg = torch, M, workgroups
+        self.buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+        self.small = self.buf[: (1 << 30) // 4]
+        self.sink = torch.empty(workgroups, dtype=torch.int32, device="cuda")
+
+    def __call__(self):
+        self.M.stream_read(self.small, self.sink, self.wg)
+
+    def peak_gbs(self, reps=5):
+        torch = self.torch
+        for _ in range(2):
+            self.M.stream_read(self.buf, self.sink, self.wg)
+        per = []
+        for _ in range(reps):
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record()
+            self.M.stream_read(self.buf, self.sink, self.wg)
+            ev1.record()
+            torch.cuda.synchronize()
+            per.append(self.buf.numel() * 4 / (ev0.elapsed_time(ev1) * 1e-3) / 1e9)
+        return float(np.median(per)), per
 
 
 def time_eager(torch, calls, steps):
@@ -157,16 +199,51 @@ def recorded_traffic():
     return float(kv["traffic_bytes_per_launch"]), "rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel"
 
 
-def cpu_baseline(S, cfg, seed, tokens, threads):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(S, cfg, seed, threads, reps=5):
+    """The fp64 C oracle on the host cores: decode tokens of one layer of the
+    decode workload and 128-token prefill rows of the same layer with the
+    Zipf skew, on one core and on `threads` cores (tokens split over
+    threads), median of `reps` runs each, input generation excluded."""
     import oracle as O
     host = S.make_layer(cfg, seed, layer=0)
-    x = S.make_tokens(seed, tokens, cfg.hidden, batch=7)
+    zhost = S.make_layer(cfg, seed, layer=0)
+    zhost.logit_bias = S.zipf_logit_bias(seed, 0, cfg.num_experts)
+
+    def rate(layer, x, n_thr):
+        per = []
+        for _ in range(reps):
+            t0 = time.time()
+            O.forward(layer, x, threads=n_thr, dense_experts=False)
+            per.append(x.shape[0] / (time.time() - t0))
+        return float(np.median(per))
+    xd = S.make_tokens(seed, threads, cfg.hidden, batch=7)
+    xp = S.make_tokens(seed, 128, cfg.hidden, batch=8)
     t0 = time.time()
-    O.forward(host, x, threads=threads, dense_experts=False)
-    dt = time.time() - t0
-    return dict(value=tokens / dt, unit="tokens/s", cores=threads, kind="oracle",
-                sample="%d decode tokens of one layer of the decode workload (fp64 C oracle, tokens split over "
-                       "%d threads), %.1f s wall" % (tokens, threads, dt))
+    res = {
+        "decode_1core": rate(host, xd[:1], 1),
+        "decode_all_cores": rate(host, xd, threads),
+        "prefill128_1core": rate(zhost, xp[:4], 1),
+        "prefill128_all_cores": rate(zhost, xp, threads),
+    }
+    wall = time.time() - t0
+    return dict(value=res["decode_all_cores"], unit="tokens/s", cores=threads, kind="oracle",
+                sample="decode: %d tokens of one layer of the decode workload, one per thread on %d threads "
+                       "(1 token on 1 core); prefill128: the 128 rows of one chunk with the Zipf skew on %d "
+                       "threads (4 of them on 1 core); fp64 C oracle, median of %d runs each, %.0f s wall in all"
+                       % (threads, threads, threads, reps, wall),
+                host_cpu=cpu_model(), host_nproc=os.cpu_count(),
+                **{k + "_tokens_per_s": v for k, v in res.items()})
 
 
 def host_threads():
@@ -363,7 +440,6 @@ def main():
     ap.add_argument("--no-stack", action="store_true")
     ap.add_argument("--no-large", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=640)
     ap.add_argument("--path", default="auto", choices=["auto", "fused", "gemv", "grouped"])
     ap.add_argument("--profile", choices=["decode", "prefill"])
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
@@ -403,6 +479,15 @@ def main():
     expert_b, router_b, shared_b = layer_bytes(M, cfg)
     per_call = router_b + k * expert_b + shared_b + 2 * H * 2
 
+    flush = Flush(torch, M)
+    peak, peak_all = flush.peak_gbs()
+    log("streaming read of %.1f GiB: %.0f GB/s (median of %d)" % (flush.buf.numel() * 4 / 2 ** 30, peak, len(peak_all)))
+
+    def errors_clear(ws_, what):
+        bits = M.workspace_errors(ws_)
+        if bits != 0:
+            raise SystemExit("%s: workspace error bits 0x%x after the timed calls" % (what, bits))
+
     # ---------------------------------------------------------------- decode
     n_tok = args.steps
     xs = S.make_tokens(seed, n_tok, H, batch=1)
@@ -415,8 +500,10 @@ def main():
         x = xdev[i % n_tok:i % n_tok + 1]
         return lambda: M.moe_layer_forward(dev, x, out=out, workspace=ws, path=args.path)
     calls = [decode_call(i) for i in range(args.steps)]
-    ms, _ = time_graph(torch, calls, args.steps, args.warmup)
+    ms, ms_all, _ = time_graph(torch, calls, args.steps, args.warmup, flush)
+    errors_clear(ws, "decode")
     ms_eager = time_eager(torch, calls, min(args.steps, 300))
+    errors_clear(ws, "decode (eager)")
     # one launch of the decode kernel per call: the timed region's events over its launches
     gbs = per_call / (ms * 1e-3) / 1e9
     log("decode: %.2f us/call (graph), %.2f us/call (eager), %.0f GB/s" % (ms * 1e3, ms_eager * 1e3, gbs))
@@ -439,7 +526,10 @@ def main():
             "workload": "decode, 1 token per call, Gemma-4-26B-A4B-shaped MoE layer (hidden 2816, 128 experts, "
                         "top-8, expert intermediate 704, shared intermediate 2112; 8-bit router, 4-bit experts, "
                         "group 64), rotated over %d resident layers" % len(layers),
-            "tokens_per_call": 1, "resident_layers": len(layers), "launch": "hip graph of %d calls" % args.steps,
+            "tokens_per_call": 1, "resident_layers": len(layers),
+            "distinct_layers_per_replay": min(args.steps, len(layers)),
+            "launch": "hip graph of %d calls; median of %d replays, each after a 1 GiB streaming read that "
+                      "evicts the Infinity Cache" % (args.steps, len(ms_all)),
             "weights": "int4/int8 affine group-64, bf16 scale+bias", "accumulate": "fp32", "output": "bf16",
             "path": args.path,
         },
@@ -448,6 +538,9 @@ def main():
             "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
             "traffic": traffic, "traffic_source": traffic_note,
             "algorithmic_bytes_per_launch": per_call, "launch_ms": ms,
+            "launch_ms_per_replay": ms_all,
+            "measured_peak": peak, "frac_measured_peak": gbs / peak,
+            "measured_peak_source": "mq_stream_read over 4 GiB, 16-byte streaming loads, median of 5",
         },
         "decode_eager_ms_per_call": ms_eager,
     }
@@ -467,7 +560,8 @@ def main():
             dev = zl[i % len(zl)]
             return lambda: M.moe_layer_forward(dev, xp[i % nb], out=outp, workspace=ws, topk_ids=ids[i % nb])
         pcalls = [prefill_call(i) for i in range(args.prefill_steps)]
-        pms, _ = time_graph(torch, pcalls, args.prefill_steps, max(2, args.warmup // 10))
+        pms, pms_all, _ = time_graph(torch, pcalls, args.prefill_steps, max(2, args.warmup // 10), flush)
+        errors_clear(ws, "prefill128")
         idh = ids.cpu().numpy()
         touched = np.array([len(np.unique(idh[i % nb])) for i in range(args.prefill_steps)])
         pbytes = router_b + touched.mean() * expert_b + shared_b + 2 * T * H * 2
@@ -476,7 +570,8 @@ def main():
             (pms * 1e3, T / (pms * 1e-3), pgbs, touched.mean()))
         result["prefill128"] = {
             "tokens_per_s": T / (pms * 1e-3), "ms_per_call": pms, "achieved_GBs": pgbs,
-            "frac_hbm_peak": pgbs / HBM_PEAK_GBS, "experts_touched_mean": float(touched.mean()),
+            "frac_hbm_peak": pgbs / HBM_PEAK_GBS, "frac_measured_peak": pgbs / peak,
+            "ms_per_call_per_replay": pms_all, "experts_touched_mean": float(touched.mean()),
             "bytes_per_call": float(pbytes), "calls": args.prefill_steps,
             "workload": "128-token prefill chunk, Zipf(1.1) logit bias, same layers",
         }
@@ -491,8 +586,8 @@ def main():
         sout = torch.empty((1, H), dtype=torch.bfloat16, device="cuda")
         scalls = [lambda t=t: M.moe_stack_forward(stack, xa[t:t + 1], out=sout, workspace=sws, between_eps=cfg.eps)
                   for t in range(ntk)]
-        per_tok, _ = time_graph(torch, scalls, len(scalls), 2)
-        assert M.workspace_errors(sws) == 0, "a bounded wait of the stack launch gave up"
+        per_tok, _, _ = time_graph(torch, scalls, len(scalls), 2, flush)
+        errors_clear(sws, "stack")
         # the same stack as one single-launch call per layer
         bufs = [torch.empty((1, H), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
 
@@ -507,14 +602,16 @@ def main():
                            M.moe_layer_forward(dev, src, out=dst, workspace=ws, input_rmsnorm_eps=e))
             return seq
         lcalls = [c for t in range(ntk) for c in token_calls(t)]
-        lms, _ = time_graph(torch, lcalls, len(lcalls), 0)
+        lms, _, _ = time_graph(torch, lcalls, len(lcalls), 0, flush)
+        errors_clear(ws, "stack as layer calls")
         per_tok_calls = lms * len(lcalls) / ntk
         sgbs = len(layers) * per_call / (per_tok * 1e-3) / 1e9
         log("stack%d: %.2f us/token, %.0f tokens/s, %.0f GB/s (one launch per token); %.2f us/token as %d layer calls"
             % (len(layers), per_tok * 1e3, 1.0 / (per_tok * 1e-3), sgbs, per_tok_calls * 1e3, len(layers)))
         result["stack"] = {
             "layers": len(layers), "tokens_per_s": 1.0 / (per_tok * 1e-3), "ms_per_token": per_tok,
-            "achieved_GBs": sgbs, "frac_hbm_peak": sgbs / HBM_PEAK_GBS, "tokens": ntk,
+            "achieved_GBs": sgbs, "frac_hbm_peak": sgbs / HBM_PEAK_GBS, "frac_measured_peak": sgbs / peak,
+            "tokens": ntk,
             "launch": "moe_stack_forward: one launch per token through every layer (hip graph of %d tokens)" % ntk,
             "layer_calls_ms_per_token": per_tok_calls,
             "workload": "one decode token through %d resident layers, unit-weight RMSNorm between layers" % len(layers),
@@ -529,7 +626,8 @@ def main():
         wsl = dev.new_workspace(T)
         outl = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
         lcall = [lambda: M.moe_layer_forward(dev, xl, out=outl, workspace=wsl)]
-        lms, _ = time_graph(torch, lcall, 3, 1)
+        lms, _, _ = time_graph(torch, lcall, 3, 1, flush)
+        errors_clear(wsl, "prefill4096")
         tf = T * flops_per_token(cfg) / (lms * 1e-3) / 1e12
         log("prefill4096: %.3f ms/call, %.0f tokens/s, %.1f TFLOP/s" % (lms, T / (lms * 1e-3), tf))
         result["prefill4096"] = {
@@ -541,8 +639,11 @@ def main():
 
     # ---------------------------------------------------------------- CPU oracle
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(S, cfg, seed, args.cpu_tokens, threads)
-        log("cpu oracle: %.2f tokens/s on %d threads" % (result["cpu_baseline"]["value"], threads))
+        result["cpu_baseline"] = cpu_baseline(S, cfg, seed, threads)
+        cb = result["cpu_baseline"]
+        log("cpu oracle (%s, %d threads): decode %.2f tok/s (1 core %.2f), prefill128 %.2f tok/s (1 core %.2f)" %
+            (cb["host_cpu"], threads, cb["decode_all_cores_tokens_per_s"], cb["decode_1core_tokens_per_s"],
+             cb["prefill128_all_cores_tokens_per_s"], cb["prefill128_1core_tokens_per_s"]))
 
     print(json.dumps(result), flush=True)
 

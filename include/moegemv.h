@@ -155,9 +155,29 @@ typedef struct {
 size_t mq_workspace_bytes(const mq_router* router, const mq_expert_pool* pool,
                           const mq_shared* shared, int32_t max_tokens);
 
-/* out = shared(x) + sum_j w_j * expert_{id_j}(x) for every token of x.
+/* out = shared(x) + sum_j w_j * expert_{id_j}(x) for every token of x
+ * ("Decode": router listing, phase table cb2; "Prefill": routed work grouped
+ * by expert, combined with the shared branch; "Metal execution": affine
+ * decode, GeGLU and the weighted expert reduction in the expert kernels).
  * x: bf16 [T][H].  out: bf16 (rounded once, to nearest even) or f32 (the
- * same sums before that rounding), [T][H].  T = 0 is valid and does nothing. */
+ * same sums before that rounding), [T][H].  T = 0 is valid and does nothing.
+ *
+ * Preconditions that the host cannot check (they depend on values):
+ *   - Range.  The GROUPED and FUSED paths carry x (GROUPED) and the GeGLU
+ *     activations gelu(W_gate x) * (W_up x) (both) as fp16, as the pages'
+ *     prefill stages FP16 operands ("Prefill").  Magnitudes must stay below
+ *     65504; activations below 2^-14 lose relative precision (fp16
+ *     subnormals).  Unit-RMS inputs, such as rows after an RMS norm
+ *     (input_rmsnorm_eps > 0), meet this with a wide margin for weight
+ *     scales up to 0.05.  An overflow sets bit 1 of mq_workspace_errors and
+ *     the affected outputs are not finite.  The GEMV path keeps activations
+ *     as bf16 high/low pairs (fp32 range) and has no such limit.
+ *   - Co-residency (FUSED, and moe_stack_forward).  The single launch runs
+ *     one workgroup per compute unit and its workgroups wait for each other's
+ *     partial results, so all of them must be resident at once: do not run
+ *     it beside other work that occupies whole compute units.  Every wait is
+ *     bounded; a wait that gives up sets bit 0 of mq_workspace_errors and the
+ *     output rows of that call read NaN. */
 mq_status moe_layer_forward(const mq_act* x, const mq_router* router, const mq_expert_pool* pool,
                             const mq_shared* shared, mq_act* out, const mq_opts* opts, void* stream);
 
@@ -189,13 +209,18 @@ mq_status moe_stack_forward(const mq_act* x, int32_t n_layers, const mq_router* 
                             const mq_expert_pool* pools, const mq_shared* shared, float between_eps,
                             mq_act* out, const mq_opts* opts, void* stream);
 
-/* HOST result: the sticky error bits that the single-launch path (FUSED)
- * keeps in a workspace.  Bit 0: a bounded wait for another workgroup's
- * partial result gave up, so the calls since the bits were last clear may
- * have wrong results (it happens only if the workgroups of a launch are not
- * all resident at once).  Copies the bits into *errors after the work queued
- * on `stream` has finished (the call synchronises the stream).  The bits stay
- * set until the workspace is zero-filled again.  workspace_bytes >= 1024. */
+/* HOST result: the sticky error bits that the kernels keep in a workspace
+ * ("Correctness and safety invariants": a queued consumer owns its scratch
+ * until completion, so the bits are read after the stream has finished).
+ *   Bit 0 (FUSED, stack): a bounded wait for another workgroup's partial
+ *         result gave up, so the calls since the bits were last clear may
+ *         have wrong results; their outputs read NaN (it happens only if the
+ *         workgroups of a launch are not all resident at once).
+ *   Bit 1 (FUSED, GROUPED, stack): an fp16 activation overflowed or was NaN
+ *         (see the range precondition of moe_layer_forward).
+ * Copies the bits into *errors after the work queued on `stream` has
+ * finished (the call synchronises the stream).  The bits stay set until the
+ * workspace is zero-filled again.  workspace_bytes >= 1024. */
 mq_status mq_workspace_errors(const void* workspace, size_t workspace_bytes, uint32_t* errors, void* stream);
 
 /* Unit-weight RMS norm between stacked layers: out = bf16(x / sqrt(mean(x^2) + eps)).
@@ -227,6 +252,15 @@ mq_status mq_unpack(const mq_qtensor* src, uint32_t* codes, uint16_t* scales, ui
  * synthetic bias = -2^(bits-1) * scale). */
 mq_status mq_debug_unpack_codes(const mq_qtensor* t, uint8_t* codes_out, void* stream);
 mq_status mq_debug_dequant(const mq_qtensor* t, float* w_out, void* stream);
+
+/* Measurement: reads bytes of buf once with 16-byte streaming loads, the
+ * access the expert kernels use, over `workgroups` workgroups of 256
+ * threads, and writes one fold of the words per workgroup to sink
+ * [workgroups].  It gives the HBM read rate the device reaches, which the
+ * benchmark reports beside the vendor peak ("Correctness and safety
+ * invariants": throughput evidence comes from production-mode runs, not slow
+ * profiling modes).  buf 16-byte aligned, bytes a multiple of 16. */
+mq_status mq_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t workgroups, void* stream);
 
 const char* mq_status_str(mq_status s);
 

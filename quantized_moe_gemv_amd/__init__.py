@@ -31,7 +31,8 @@ DTYPE_BF16, DTYPE_F32 = 0, 1
 PATHS = {"auto": 0, "gemv": 1, "grouped": 2, "fused": 3}
 GROUP = 64
 EXPORTS = ["moe_layer_forward", "mq_workspace_bytes", "moe_stack_forward", "mq_stack_workspace_bytes", "mq_workspace_errors", "mq_rmsnorm", "mq_packed_bytes", "mq_pool_layout",
-           "mq_pack", "mq_unpack", "mq_debug_unpack_codes", "mq_debug_dequant", "mq_status_str"]
+           "mq_pack", "mq_unpack", "mq_debug_unpack_codes", "mq_debug_dequant", "mq_stream_read",
+           "mq_status_str"]
 
 
 class MqQTensor(ctypes.Structure):
@@ -81,6 +82,7 @@ _sig = {
     "mq_unpack": (ctypes.c_int, [_P, _P, _P, _P]),
     "mq_debug_unpack_codes": (ctypes.c_int, [_P, _P, _P]),
     "mq_debug_dequant": (ctypes.c_int, [_P, _P, _P]),
+    "mq_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, _P, ctypes.c_int32, _P]),
     "mq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
 }
 for _name, (_res, _args) in _sig.items():
@@ -357,3 +359,10 @@ def debug_dequant(buf: torch.Tensor, rows: int, cols: int, bits: int, stream=Non
     d = MqQTensor(buf.data_ptr(), None, None, rows, cols, bits, GROUP, LAYOUT_DEV_V1)
     _check(_lib.mq_debug_dequant(ctypes.byref(d), out.data_ptr(), _stream_handle(stream)), "mq_debug_dequant")
     return out
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, workgroups: int, stream=None) -> None:
+    """One streaming read of every byte of buf (a measurement kernel); sink int32 [workgroups]."""
+    assert sink.numel() >= workgroups and sink.element_size() == 4
+    _check(_lib.mq_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), workgroups,
+                               _stream_handle(stream)), "mq_stream_read")

@@ -21,6 +21,7 @@ __global__ void k_debug_read(const uint8_t* data, int rows, int cols, int bits, 
 __global__ void k_decode(Plan p);
 __global__ void k_decode_stack(const Plan* plans, int n_layers);
 __global__ void k_stack_plans(Plan base, StackChunk c, Plan* dst);
+__global__ void k_stream_read(const uint4* buf, int64_t n16, uint32_t* sink);
 mq_status launch_grouped(const Plan& p, hipStream_t s);
 bool grouped_ok(int H, int I, int64_t T, int rows_per_token);
 }  // namespace mq
@@ -552,6 +553,17 @@ extern "C" mq_status mq_debug_unpack_codes(const mq_qtensor* t, uint8_t* codes_o
 extern "C" mq_status mq_debug_dequant(const mq_qtensor* t, float* w_out, void* stream) {
     if (!w_out) return MQ_ERR_NULL;
     return debug_read(t, nullptr, w_out, stream);
+}
+
+extern "C" mq_status mq_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t workgroups,
+                                    void* stream) {
+    if (!buf || !sink) return MQ_ERR_NULL;
+    if (!aligned(buf, 16) || bytes % 16) return MQ_ERR_ALIGN;
+    if (workgroups < 1 || bytes == 0) return MQ_ERR_SHAPE;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(k_stream_read, dim3(workgroups), dim3(256), 0, (hipStream_t)stream, (const uint4*)buf,
+                       (int64_t)(bytes / 16), sink);
+    return hipGetLastError() == hipSuccess ? MQ_OK : MQ_ERR_HIP;
 }
 
 extern "C" const char* mq_status_str(mq_status s) {

@@ -88,7 +88,7 @@ __device__ __forceinline__ uint32_t ld_ctr(const uint32_t* p) {
 // Re-reads the words of v (at p[m * pstride], m < 4) whose tag is not yet
 // current, all of them in each round, until every one is.  Bounded: gives
 // up after kSpinLimit rounds, or at once when any wait of the call has
-// already given up, and records that in *err.  Bit m of `want` selects the
+// already given up, and records that in *err (bit kErrWait).  Bit m of `want` selects the
 // words that take part.
 __device__ __forceinline__ void await_words(const uint64_t* p, int pstride, uint64_t v[4], uint32_t want,
                                             uint32_t tag, uint32_t* err) {
@@ -98,8 +98,8 @@ __device__ __forceinline__ void await_words(const uint64_t* p, int pstride, uint
         if (((want >> m) & 1) && (uint32_t)(v[m] >> 32) != tag) stale |= 1u << m;
     int spins = 0;
     while (stale) {
-        if (++spins > kSpinLimit || ((spins & 63) == 0 && ld_ctr(err))) {
-            atomicOr(err, 1u);
+        if (++spins > kSpinLimit || ((spins & 63) == 0 && (ld_ctr(err) & kErrWait))) {
+            atomicOr(err, kErrWait);
             break;
         }
         __builtin_amdgcn_s_sleep(2);
@@ -118,8 +118,8 @@ __device__ __forceinline__ uint32_t wait_word(const uint64_t* p, uint32_t tag, u
     uint64_t v = ld_word(p);
     int spins = 0;
     while ((uint32_t)(v >> 32) != tag) {
-        if (++spins > kSpinLimit || ((spins & 63) == 0 && ld_ctr(err))) {
-            atomicOr(err, 1u);
+        if (++spins > kSpinLimit || ((spins & 63) == 0 && (ld_ctr(err) & kErrWait))) {
+            atomicOr(err, kErrWait);
             break;
         }
         __builtin_amdgcn_s_sleep(2);
@@ -713,7 +713,9 @@ __device__ __forceinline__ void run_rh(const Plan& p, Shared& sh, const Unit& x,
     if (wave_id() == 0 && tix() < 32) {
         const int r = tix();
         const float h = gelu_tanh(row_total_par(sh, r)) * row_total_par(sh, 32 + r);
-        const uint32_t h16 = f32_to_f16(h);
+        const _Float16 hh = (_Float16)h;
+        flag_error(p.f_err, f16_bad(hh), kErrRange);
+        const uint32_t h16 = __builtin_bit_cast(uint16_t, hh);
         uint64_t* hout = x.kind == U_SH ? p.f_hs + 32 * x.a + r : p.f_h + (int64_t)x.a * p.I + 32 * x.b + r;
 #pragma unroll
         for (int c = 0; c < kCopies; ++c) st_word(hout + c * p.h_stride, tag, h16);
@@ -827,6 +829,9 @@ __device__ __forceinline__ void run_reduce(const Plan& p, Shared& sh, int a, uin
     if (wave_id() == 0) {
         float v = 0.f;
         for (int s2 = 0; s2 < p.n_src; ++s2) v += __uint_as_float(sh.gbuf[s2 * 64 + tix()]);
+        // a wait of this call that gave up may have fed stale partial results
+        // into the sums: the output then reads NaN rather than a plausible row
+        if (ld_ctr(p.f_err) & kErrWait) v = __builtin_nanf("");
         const int row = 64 * a + tix();
         const uint32_t b = f32_to_bf16(v);
         if (!p.out) {

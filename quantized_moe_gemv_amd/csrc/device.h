@@ -72,6 +72,18 @@ __device__ __forceinline__ uint16_t f32_to_f16(float f) { return __builtin_bit_c
 __device__ __forceinline__ float f16_lo(uint32_t v) { return (float)__builtin_bit_cast(f16x2_t, v)[0]; }
 __device__ __forceinline__ float f16_hi(uint32_t v) { return (float)__builtin_bit_cast(f16x2_t, v)[1]; }
 
+// True when an fp16 value is inf or NaN (all exponent bits set): the
+// conversion of an activation overflowed fp16's range (|v| >= 65520) or the
+// value was already NaN.
+__device__ __forceinline__ bool f16_bad(_Float16 h) {
+    return (__builtin_bit_cast(uint16_t, h) & 0x7C00u) == 0x7C00u;
+}
+
+// Records kErrRange-type errors in the sticky error word (rare path only).
+__device__ __forceinline__ void flag_error(uint32_t* err, bool bad, uint32_t bit) {
+    if (__builtin_expect(bad, 0)) atomicOr(err, bit);
+}
+
 // Sum over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

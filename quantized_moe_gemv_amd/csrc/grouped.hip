@@ -169,6 +169,7 @@ __global__ __launch_bounds__(256) void k_scores(Plan p) {
                 // x16 (columns with c & 2 divided by 16; c4 + 2, c4 + 3 are those) and xso
                 const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1, h2 = (_Float16)x2, h3 = (_Float16)x3;
                 const _Float16 s2 = h2 * (_Float16)0.0625f, s3 = h3 * (_Float16)0.0625f;
+                flag_error(p.f_err, t_st < p.T && (f16_bad(h0) || f16_bad(h1) || f16_bad(h2) || f16_bad(h3)), kErrRange);
                 const float xs = sum16(((float)h0 + (float)h1) + ((float)h2 + (float)h3));
                 const float xn = sum16(-1024.0f * (((float)h0 + (float)h1) + ((float)s2 + (float)s3)));
                 if (t_st < p.T) {
@@ -905,6 +906,7 @@ __device__ __forceinline__ void gu_small_n(const Plan& p, const Item& it, GuW& W
             const int n = 16 * t + 4 * (lane >> 4) + i;
             const _Float16 h = (_Float16)(gelu_tanh(v[0][i]) * v[1][i]);
             const _Float16 a = act_store(h, c);
+            flag_error(p.f_err, n < it.count && f16_bad(h), kErrRange);
             if (n < it.count) p.hg[(int64_t)(it.pos0 + n) * p.I + c] = a;
             const float hs = sum16((float)h), hn = sum16(-1024.0f * (float)a);
             if ((lane & 15) == 0) hpart[w][n] = make_float2(hs, hn);
@@ -945,6 +947,8 @@ __device__ __forceinline__ void gu_big(const Plan& p, const Item& it, GuXs<MT>& 
             hs += (float)h[i];
             hn += -1024.0f * (float)a[i];
         }
+        flag_error(p.f_err, n < it.count && (f16_bad(h[0]) || f16_bad(h[1]) || f16_bad(h[2]) || f16_bad(h[3])),
+                   kErrRange);
         if (n < it.count) {
             _Float16* dst = p.hg + (int64_t)(it.pos0 + n) * p.I + r0;
 #pragma unroll

@@ -12,6 +12,9 @@ constexpr int kMaxExperts = 256;
 constexpr int kDownSplits = 4;      // split of the down-projection source list (GEMV path)
 constexpr int kRouterPieces = 8;   // single-launch decode: column pieces of a 16-expert router slice
 constexpr int kCtrStride = 64;      // counters of the single-launch decode sit 256 bytes apart
+// Sticky error bits kept in every workspace (read by mq_workspace_errors).
+constexpr uint32_t kErrWait = 1u;   // a bounded wait for another workgroup's result gave up
+constexpr uint32_t kErrRange = 2u;  // an fp16 activation overflowed (inf) or was NaN
 
 struct Plan {
     // sizes
