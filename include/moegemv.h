@@ -133,6 +133,31 @@ typedef struct {
     int64_t row_stride;
 } mq_act;
 
+/* The layer tail ("Decode", phase table cb2: after the routed branch is
+ * reduced and combined with the shared branch, the post-FFN norms, the
+ * residual and the layer scalar are applied; "Why the runtime has this
+ * shape": parallel shared and routed FFNs, a learned layer scalar).  With s
+ * the shared branch and r the weighted routed sum of a token:
+ *   out = layer_scalar * (residual + N_out(N_s(s) + N_r(r))),
+ *   N(v) = v / sqrt(mean(v^2) + eps) * w   (element-wise learned weight w),
+ * where a NULL weight leaves that norm out (N(v) = v).  All in fp32 and
+ * rounded once at the end, like the plain layer.  Readings where the pages
+ * say only "post-FFN norms": one norm per branch and one on their sum, each
+ * optional; the weight multiplies the normalised value directly (a
+ * checkpoint that stores 1 + w passes 1 + w); the scalar multiplies the
+ * residual too. */
+typedef struct {
+    const float* norm_shared;   /* [H] or NULL */
+    const float* norm_routed;   /* [H] or NULL */
+    const float* norm_out;      /* [H] or NULL */
+    const void* residual;       /* bf16 [T][H] rows, residual_stride apart; NULL: none (zero) */
+    int64_t residual_stride;    /* elements, >= H when residual is given */
+    int32_t residual_is_input;  /* 1: the residual rows are x itself, as given (before
+                                   input_rmsnorm_eps normalises it); residual is then ignored */
+    float eps;                  /* >= 0, finite */
+    float layer_scalar;         /* finite */
+} mq_tail;
+
 typedef struct {
     int32_t path;           /* MQ_PATH_*: AUTO picks by token count */
     int32_t* topk_ids;      /* optional [T][top_k]: selected experts, highest score first */
@@ -147,6 +172,29 @@ typedef struct {
      * paths normalise into the workspace first.  x itself is not written.
      * 0: off.  Negative or not finite: MQ_ERR_UNSUPPORTED. */
     float input_rmsnorm_eps;
+    /* NULL: out = s + r.  Otherwise the layer tail above is applied to every
+     * token (H <= 16384; weights 4-byte aligned).  moe_stack_forward takes a
+     * HOST array of n_layers tails here; in a stack only layer 0 may name an
+     * explicit residual, later layers use residual_is_input (their input is
+     * the previous layer's output). */
+    const mq_tail* tail;
+    /* Given routing (GEMV path; AUTO runs it there, FUSED and GROUPED refuse
+     * it): the router does not run and the experts come from these device
+     * arrays.  route_ids int32 [T][top_k], route_w float [T][top_k]; both or
+     * neither.  route_slots (optional, int32 [T][top_k]): the blob of the
+     * pool that each (token, j) reads, for a pool of expert slots (a cache of
+     * a larger pool held elsewhere); NULL reads blob route_ids[t][j].  Values
+     * are not checked: each must name a blob of the pool.  topk_ids, topk_w
+     * and logits are not written. */
+    const int32_t* route_ids;
+    const float* route_w;
+    const int32_t* route_slots;
+    /* hipEvent_t or NULL (GEMV path): the kernels of the routed experts are
+     * enqueued after the stream waits for this event, those of the shared
+     * expert before it, so the shared expert runs while the event's work
+     * (e.g. copies that fill expert slots) is still in flight ("Decode",
+     * phase table: the shared branch overlaps the expert reads). */
+    void* experts_ready;
 } mq_opts;
 
 /* Device scratch one call needs for up to max_tokens tokens.  The workspace
@@ -252,6 +300,57 @@ mq_status mq_unpack(const mq_qtensor* src, uint32_t* codes, uint16_t* scales, ui
  * synthetic bias = -2^(bits-1) * scale). */
 mq_status mq_debug_unpack_codes(const mq_qtensor* t, uint8_t* codes_out, void* stream);
 mq_status mq_debug_dequant(const mq_qtensor* t, float* w_out, void* stream);
+
+/* Routing only: the router input, projection, top-k and softmax weights of
+ * moe_layer_forward for every token of x ("Decode": the first phase ends
+ * when the top-8 ids are ready for the CPU to read, before it plans the
+ * expert reads).  ids int32 [T][top_k] and w float [T][top_k] (device,
+ * required), logits float [T][E] (optional).  The workspace holds
+ * mq_route_workspace_bytes(router, T) bytes (256-byte aligned, no clearing).
+ * Errors as moe_layer_forward. */
+size_t mq_route_workspace_bytes(const mq_router* router, int32_t max_tokens);
+mq_status mq_route(const mq_act* x, const mq_router* router, int32_t* ids, float* w, float* logits,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* HOST: the expert slot cache of a pool kept in host memory ("Load and
+ * ownership": a fixed group of slots per layer, the cache records which
+ * expert occupies each slot, least-frequently-used eviction with recency
+ * as the tie-breaker, a hit reuses its slot, a miss takes an evictable slot
+ * and starts a read, no two reads into one slot).  The state is a caller
+ * buffer of mq_lfu_state_bytes (8-byte aligned) set up by mq_lfu_init.
+ * mq_lfu_plan takes the n expert ids one layer call will use (repeats
+ * allowed) and, for each, the slot that holds it after the plan
+ * (slot_of_id [n]); every distinct expert counts one use; missing experts
+ * get slots that no expert of this call holds, empty slots first, then the
+ * resident expert with the fewest uses, ties to the one used longest ago,
+ * then the lower slot; the misses to fill are (miss_expert, miss_slot)
+ * [*n_miss] (arrays of n entries).  More distinct experts than slots, or an
+ * id outside [0, num_experts): MQ_ERR_SHAPE with the state unchanged.  The
+ * caller keeps slot reads ordered after the device work that last used the
+ * slot ("Correctness and safety invariants": a queued consumer owns its
+ * slot until completion). */
+size_t mq_lfu_state_bytes(int32_t num_experts, int32_t num_slots);
+mq_status mq_lfu_init(void* state, size_t state_bytes, int32_t num_experts, int32_t num_slots);
+mq_status mq_lfu_plan(void* state, size_t state_bytes, const int32_t* ids, int32_t n, int32_t* slot_of_id,
+                      int32_t* miss_expert, int32_t* miss_slot, int32_t* n_miss);
+
+/* The same affine dequant-GEMV at other shapes: the tied 4-bit head at the
+ * end of decode ("Why the runtime has this shape": embedding and head share
+ * one quantized matrix, final logit softcap 30.0; "Decode": after the last
+ * layer the head returns the argmax token directly in the greedy
+ * configuration) or any other projection.
+ *   w: DEV_V1 [rows][cols], 4- or 8-bit, group 64 (16-byte aligned).
+ *   x: bf16 [T][cols] token rows, T <= 8 and T * cols * 2.25 <= 60 KiB
+ *      (the rows and their partial sums are staged on chip).
+ *   y: optional ([T][rows], bf16 or f32): y = W x in fp32, then
+ *      softcap * tanh(y / softcap) when softcap > 0 (0: none).
+ *   argmax: optional int32 [T], the row of the largest (softcapped) value,
+ *      equal values to the lower row, NaN ranking last; it needs a workspace
+ *      of mq_qgemv_workspace_bytes(rows, T) (16-byte aligned; no clearing).
+ * At least one of y and argmax.  Errors as moe_layer_forward. */
+size_t mq_qgemv_workspace_bytes(int32_t rows, int32_t tokens);
+mq_status mq_qgemv(const mq_qtensor* w, const mq_act* x, mq_act* y, float softcap, int32_t* argmax,
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* Measurement: reads bytes of buf once with 16-byte streaming loads, the
  * access the expert kernels use, over `workgroups` workgroups of 256

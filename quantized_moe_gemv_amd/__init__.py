@@ -32,6 +32,8 @@ PATHS = {"auto": 0, "gemv": 1, "grouped": 2, "fused": 3}
 GROUP = 64
 EXPORTS = ["moe_layer_forward", "mq_workspace_bytes", "moe_stack_forward", "mq_stack_workspace_bytes", "mq_workspace_errors", "mq_rmsnorm", "mq_packed_bytes", "mq_pool_layout",
            "mq_pack", "mq_unpack", "mq_debug_unpack_codes", "mq_debug_dequant", "mq_stream_read",
+           "mq_qgemv", "mq_qgemv_workspace_bytes",
+           "mq_route", "mq_route_workspace_bytes", "mq_lfu_state_bytes", "mq_lfu_init", "mq_lfu_plan",
            "mq_status_str"]
 
 
@@ -62,10 +64,39 @@ class MqAct(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("row_stride", ctypes.c_int64)]
 
 
+class MqTail(ctypes.Structure):
+    _fields_ = [("norm_shared", ctypes.c_void_p), ("norm_routed", ctypes.c_void_p), ("norm_out", ctypes.c_void_p),
+                ("residual", ctypes.c_void_p), ("residual_stride", ctypes.c_int64),
+                ("residual_is_input", ctypes.c_int32), ("eps", ctypes.c_float), ("layer_scalar", ctypes.c_float)]
+
+
 class MqOpts(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("topk_ids", ctypes.c_void_p), ("topk_w", ctypes.c_void_p),
                 ("logits", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("input_rmsnorm_eps", ctypes.c_float)]
+                ("input_rmsnorm_eps", ctypes.c_float), ("tail", ctypes.c_void_p),
+                ("route_ids", ctypes.c_void_p), ("route_w", ctypes.c_void_p), ("route_slots", ctypes.c_void_p),
+                ("experts_ready", ctypes.c_void_p)]
+
+
+class Tail:
+    """Layer-tail parameters on the device: post-FFN norm weights (fp32 [H] or
+    None), a residual (bf16 [T][H] tensor, None, or residual_is_input), the
+    epsilon and the layer scalar."""
+
+    def __init__(self, norm_shared=None, norm_routed=None, norm_out=None, residual: Optional[torch.Tensor] = None,
+                 residual_is_input: bool = False, eps: float = 1e-6, layer_scalar: float = 1.0, device="cuda"):
+        dev = lambda a: None if a is None else torch.as_tensor(np.asarray(a, np.float32)).to(device)
+        self.w = [dev(norm_shared), dev(norm_routed), dev(norm_out)]
+        self.residual = residual
+        ptr = lambda t: None if t is None else t.data_ptr()
+        self.struct = MqTail(ptr(self.w[0]), ptr(self.w[1]), ptr(self.w[2]), ptr(residual),
+                             0 if residual is None else residual.stride(0), int(bool(residual_is_input)),
+                             float(eps), float(layer_scalar))
+
+    @classmethod
+    def from_dict(cls, d: dict, **kw) -> "Tail":
+        return cls(d.get("norm_shared"), d.get("norm_routed"), d.get("norm_out"), eps=d.get("eps", 1e-6),
+                   layer_scalar=d.get("layer_scalar", 1.0), **kw)
 
 
 _P = ctypes.c_void_p
@@ -83,6 +114,13 @@ _sig = {
     "mq_debug_unpack_codes": (ctypes.c_int, [_P, _P, _P]),
     "mq_debug_dequant": (ctypes.c_int, [_P, _P, _P]),
     "mq_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, _P, ctypes.c_int32, _P]),
+    "mq_qgemv_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32]),
+    "mq_route_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int32]),
+    "mq_route": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "mq_lfu_state_bytes": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32]),
+    "mq_lfu_init": (ctypes.c_int, [_P, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32]),
+    "mq_lfu_plan": (ctypes.c_int, [_P, ctypes.c_size_t, _P, ctypes.c_int32, _P, _P, _P, _P]),
+    "mq_qgemv": (ctypes.c_int, [_P, _P, _P, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]),
     "mq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
 }
 for _name, (_res, _args) in _sig.items():
@@ -117,21 +155,26 @@ def _stream_handle(stream=None) -> int:
 
 # ------------------------------------------------------------------ host packing
 
-def packed_bytes(rows: int, cols: int, bits: int, layout: int = LAYOUT_DEV_V1) -> int:
-    return int(_lib.mq_packed_bytes(rows, cols, bits, GROUP, layout))
+def packed_bytes(rows: int, cols: int, bits: int, layout: int = LAYOUT_DEV_V1, group: int = GROUP) -> int:
+    return int(_lib.mq_packed_bytes(rows, cols, bits, group, layout))
 
 
 def _canonical_desc(qt) -> tuple:
     c = np.ascontiguousarray(qt.codes, dtype=np.uint32)
     s = np.ascontiguousarray(qt.scales, dtype=np.uint16)
     b = np.ascontiguousarray(qt.biases, dtype=np.uint16)
-    d = MqQTensor(c.ctypes.data, s.ctypes.data, b.ctypes.data, qt.rows, qt.cols, qt.bits, GROUP, LAYOUT_CANONICAL)
+    d = MqQTensor(c.ctypes.data, s.ctypes.data, b.ctypes.data, qt.rows, qt.cols, qt.bits, _group(qt),
+                  LAYOUT_CANONICAL)
     return d, (c, s, b)
+
+
+def _group(qt) -> int:
+    return int(getattr(qt, "group", GROUP))
 
 
 def pack_into(qt, dst: np.ndarray, offset: int = 0) -> int:
     """Pack a canonical host tensor into dst[offset:] (uint8); returns the byte count."""
-    n = packed_bytes(qt.rows, qt.cols, qt.bits)
+    n = packed_bytes(qt.rows, qt.cols, qt.bits, group=_group(qt))
     assert dst.dtype == np.uint8 and dst.flags.c_contiguous and offset + n <= dst.size
     d, keep = _canonical_desc(qt)
     _check(_lib.mq_pack(ctypes.byref(d), dst.ctypes.data + offset, n, None), "mq_pack")
@@ -139,25 +182,25 @@ def pack_into(qt, dst: np.ndarray, offset: int = 0) -> int:
 
 
 def pack(qt) -> np.ndarray:
-    out = np.empty(packed_bytes(qt.rows, qt.cols, qt.bits), dtype=np.uint8)
+    out = np.empty(packed_bytes(qt.rows, qt.cols, qt.bits, group=_group(qt)), dtype=np.uint8)
     pack_into(qt, out)
     return out
 
 
-def unpack(packed: np.ndarray, rows: int, cols: int, bits: int):
+def unpack(packed: np.ndarray, rows: int, cols: int, bits: int, group: int = GROUP):
     """DEV_V1 host bytes -> canonical (codes uint32, scales uint16, biases uint16)."""
     packed = np.ascontiguousarray(packed, dtype=np.uint8)
     codes = np.empty((rows, cols * bits // 32), np.uint32)
-    scales = np.empty((rows, cols // GROUP), np.uint16)
-    biases = np.empty((rows, cols // GROUP), np.uint16)
-    d = MqQTensor(packed.ctypes.data, None, None, rows, cols, bits, GROUP, LAYOUT_DEV_V1)
+    scales = np.empty((rows, cols // group), np.uint16)
+    biases = np.empty((rows, cols // group), np.uint16)
+    d = MqQTensor(packed.ctypes.data, None, None, rows, cols, bits, group, LAYOUT_DEV_V1)
     _check(_lib.mq_unpack(ctypes.byref(d), codes.ctypes.data, scales.ctypes.data, biases.ctypes.data), "mq_unpack")
     return codes, scales, biases
 
 
-def pool_layout(hidden: int, inter: int, page_bytes: int = 16384, bits: int = 4) -> MqExpertPool:
+def pool_layout(hidden: int, inter: int, page_bytes: int = 16384, bits: int = 4, group: int = GROUP) -> MqExpertPool:
     pool = MqExpertPool()
-    stride = _lib.mq_pool_layout(hidden, inter, bits, GROUP, page_bytes, ctypes.byref(pool))
+    stride = _lib.mq_pool_layout(hidden, inter, bits, group, page_bytes, ctypes.byref(pool))
     if stride <= 0:
         raise MoeError(MQ_ERR_SHAPE, "mq_pool_layout")
     return pool
@@ -182,15 +225,22 @@ class DeviceLayer:
     """
 
     def __init__(self, src, device="cuda", page_bytes: int = 16384, threads: int = 16,
-                 pool_host: Optional[np.ndarray] = None):
+                 pool_host: Optional[np.ndarray] = None, resident_experts: bool = True):
         cfg = src.cfg
         self.hidden, self.num_experts, self.inter = cfg.hidden, cfg.num_experts, cfg.inter
         self.top_k, self.eps = cfg.top_k, cfg.eps
         self.shared_inter = 0 if src.shared_gate is None else src.shared_gate.rows
         E = self.num_experts
-        self.pool = pool_layout(self.hidden, self.inter, page_bytes)
+        self.pool = pool_layout(self.hidden, self.inter, page_bytes, bits=src.gate.bits if src.gate is not None
+                                else getattr(cfg, "expert_bits", 4), group=_group(src.gate) if src.gate is not None
+                                else getattr(cfg, "group", GROUP))
         stride = self.pool.expert_stride
-        if pool_host is not None:
+        if not resident_experts:
+            # the experts live elsewhere (OffloadedLayer): no device pool here
+            self.pool_buf = None
+            self.pool.num_experts = E
+            host = None
+        elif pool_host is not None:
             # experts already packed by the caller (e.g. with pack_pool_into)
             assert pool_host.dtype == np.uint8 and pool_host.size == E * stride
             host = pool_host
@@ -201,14 +251,15 @@ class DeviceLayer:
                 pack_expert_into(self.pool, e, src.gate.select(e), src.up.select(e), src.down.select(e), host)
             with ThreadPoolExecutor(threads) as ex:
                 list(ex.map(pack_expert, range(E)))
-        self.pool_buf = torch.from_numpy(host).to(device)
-        del host
-        self.pool.base = self.pool_buf.data_ptr()
-        self.pool.num_experts = E
+        if host is not None:
+            self.pool_buf = torch.from_numpy(host).to(device)
+            del host
+            self.pool.base = self.pool_buf.data_ptr()
+            self.pool.num_experts = E
 
         def dev_tensor(qt):
             buf = torch.from_numpy(pack(qt)).to(device)
-            return buf, MqQTensor(buf.data_ptr(), None, None, qt.rows, qt.cols, qt.bits, GROUP, LAYOUT_DEV_V1)
+            return buf, MqQTensor(buf.data_ptr(), None, None, qt.rows, qt.cols, qt.bits, _group(qt), LAYOUT_DEV_V1)
 
         self.router_buf, self.router_w = dev_tensor(src.router)
         opt = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
@@ -244,7 +295,7 @@ class DeviceLayer:
         return torch.zeros(self.workspace_bytes(max_tokens), dtype=torch.uint8, device=device)
 
     def weight_bytes(self) -> int:
-        n = self.router_buf.numel() + self.pool_buf.numel()
+        n = self.router_buf.numel() + (0 if self.pool_buf is None else self.pool_buf.numel())
         if self.shared is not None:
             n += self.sg_buf.numel() + self.su_buf.numel() + self.sd_buf.numel()
         return n
@@ -260,9 +311,12 @@ def moe_layer_forward(layer: DeviceLayer, x: torch.Tensor, out: Optional[torch.T
                       workspace: Optional[torch.Tensor] = None, path: str = "auto",
                       out_dtype=torch.bfloat16, topk_ids: Optional[torch.Tensor] = None,
                       topk_w: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
-                      stream=None, input_rmsnorm_eps: float = 0.0) -> torch.Tensor:
+                      stream=None, input_rmsnorm_eps: float = 0.0, tail: Optional[Tail] = None,
+                      route_ids: Optional[torch.Tensor] = None, route_w: Optional[torch.Tensor] = None,
+                      route_slots: Optional[torch.Tensor] = None, experts_ready=None) -> torch.Tensor:
     """out = shared(x) + sum_j w_j expert_j(x) on the current (or given) stream.
-    input_rmsnorm_eps > 0 applies a unit-weight RMSNorm (rounded to bf16) to x first."""
+    input_rmsnorm_eps > 0 applies a unit-weight RMSNorm (rounded to bf16) to x first;
+    ``tail`` applies the layer tail (post-FFN norms, residual, layer scalar)."""
     T = x.shape[0]
     if out is None:
         out = torch.empty((T, layer.hidden), dtype=out_dtype, device=x.device)
@@ -271,7 +325,9 @@ def moe_layer_forward(layer: DeviceLayer, x: torch.Tensor, out: Optional[torch.T
     xa, oa = _act(x), _act(out)
     ptr = lambda t: None if t is None else t.data_ptr()
     opts = MqOpts(PATHS[path], ptr(topk_ids), ptr(topk_w), ptr(logits), workspace.data_ptr(), workspace.numel(),
-                  float(input_rmsnorm_eps))
+                  float(input_rmsnorm_eps), None if tail is None else ctypes.addressof(tail.struct),
+                  ptr(route_ids), ptr(route_w), ptr(route_slots),
+                  None if experts_ready is None else experts_ready.cuda_event)
     st = _lib.moe_layer_forward(ctypes.byref(xa), ctypes.byref(layer.router), ctypes.byref(layer.pool),
                                 _ref(layer.shared), ctypes.byref(oa), ctypes.byref(opts), _stream_handle(stream))
     _check(st, "moe_layer_forward")
@@ -312,18 +368,23 @@ def moe_stack_forward(stack: Stack, x: torch.Tensor, out: Optional[torch.Tensor]
                       workspace: Optional[torch.Tensor] = None, between_eps: float = 0.0,
                       input_rmsnorm_eps: float = 0.0, out_dtype=torch.bfloat16, path: str = "auto",
                       topk_ids: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None,
-                      logits: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                      logits: Optional[torch.Tensor] = None, stream=None, tails=None) -> torch.Tensor:
     """One token through every layer of `stack` in one launch; layer l > 0
     takes bf16(out_{l-1}), RMS-normalised first when between_eps > 0.
-    topk_ids / topk_w [n_layers][k] and logits [n_layers][E] are optional."""
+    topk_ids / topk_w [n_layers][k] and logits [n_layers][E] are optional;
+    ``tails`` is None or one Tail per layer."""
     if out is None:
         out = torch.empty((1, stack.hidden), dtype=out_dtype, device=x.device)
     if workspace is None:
         workspace = stack.new_workspace(x.device)
     xa, oa = _act(x), _act(out)
     ptr = lambda t: None if t is None else t.data_ptr()
+    tarr = None
+    if tails is not None:
+        assert len(tails) == len(stack)
+        tarr = (MqTail * len(stack))(*[t.struct for t in tails])
     opts = MqOpts(PATHS[path], ptr(topk_ids), ptr(topk_w), ptr(logits), workspace.data_ptr(), workspace.numel(),
-                  float(input_rmsnorm_eps))
+                  float(input_rmsnorm_eps), None if tarr is None else ctypes.addressof(tarr))
     st = _lib.moe_stack_forward(ctypes.byref(xa), len(stack), stack.routers, stack.pools, stack.shared,
                                 float(between_eps), ctypes.byref(oa), ctypes.byref(opts), _stream_handle(stream))
     _check(st, "moe_stack_forward")
@@ -366,3 +427,140 @@ def stream_read(buf: torch.Tensor, sink: torch.Tensor, workgroups: int, stream=N
     assert sink.numel() >= workgroups and sink.element_size() == 4
     _check(_lib.mq_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), workgroups,
                                _stream_handle(stream)), "mq_stream_read")
+
+
+def qgemv(w_buf: torch.Tensor, rows: int, cols: int, bits: int, x: torch.Tensor, softcap: float = 0.0,
+          want_y: bool = True, y_dtype=torch.float32, want_argmax: bool = True, workspace=None, stream=None):
+    """y = W x (softcapped when softcap > 0) for bf16 token rows x [T][cols],
+    with W a DEV_V1 device buffer; returns (y [T][rows] or None, argmax [T] or None)."""
+    T = x.shape[0]
+    d = MqQTensor(w_buf.data_ptr(), None, None, rows, cols, bits, GROUP, LAYOUT_DEV_V1)
+    y = torch.empty((T, rows), dtype=y_dtype, device=x.device) if want_y else None
+    am = torch.empty(T, dtype=torch.int32, device=x.device) if want_argmax else None
+    if want_argmax and workspace is None:
+        workspace = torch.empty(max(1, _lib.mq_qgemv_workspace_bytes(rows, T)), dtype=torch.uint8, device=x.device)
+    xa = _act(x)
+    ya = _act(y) if y is not None else None
+    st = _lib.mq_qgemv(ctypes.byref(d), ctypes.byref(xa), _ref(ya), float(softcap),
+                       None if am is None else am.data_ptr(), None if workspace is None else workspace.data_ptr(),
+                       0 if workspace is None else workspace.numel(), _stream_handle(stream))
+    _check(st, "mq_qgemv")
+    return y, am
+
+
+# ------------------------------------------------------------------ routing only, host-offloaded experts
+
+def route(router_layer, x: torch.Tensor, ids: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None,
+          logits: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Router, top-k and routing weights only (mq_route): (ids [T][k] int32, w [T][k] fp32)."""
+    T = x.shape[0]
+    k = router_layer.top_k
+    if ids is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    if w is None:
+        w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(256, _lib.mq_route_workspace_bytes(ctypes.byref(router_layer.router), T)),
+                                dtype=torch.uint8, device=x.device)
+    xa = _act(x)
+    _check(_lib.mq_route(ctypes.byref(xa), ctypes.byref(router_layer.router), ids.data_ptr(), w.data_ptr(),
+                         None if logits is None else logits.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                         _stream_handle(stream)), "mq_route")
+    return ids, w
+
+
+class LfuCache:
+    """The host slot cache of mq_lfu_* (state in a host buffer)."""
+
+    def __init__(self, num_experts: int, num_slots: int):
+        n = _lib.mq_lfu_state_bytes(num_experts, num_slots)
+        if n == 0:
+            raise MoeError(MQ_ERR_SHAPE, "mq_lfu_state_bytes")
+        self.state = np.zeros((n + 7) // 8, dtype=np.uint64)
+        self.nbytes = self.state.nbytes
+        self.num_experts, self.num_slots = num_experts, num_slots
+        _check(_lib.mq_lfu_init(self.state.ctypes.data, self.nbytes, num_experts, num_slots), "mq_lfu_init")
+
+    def plan(self, ids: np.ndarray):
+        """(slot of each id, [(expert, slot) to fill])."""
+        ids = np.ascontiguousarray(ids, dtype=np.int32).ravel()
+        n = ids.size
+        slots = np.empty(n, np.int32)
+        me, ms = np.empty(max(n, 1), np.int32), np.empty(max(n, 1), np.int32)
+        nm = ctypes.c_int32(0)
+        _check(_lib.mq_lfu_plan(self.state.ctypes.data, self.nbytes, ids.ctypes.data, n, slots.ctypes.data,
+                                me.ctypes.data, ms.ctypes.data, ctypes.byref(nm)), "mq_lfu_plan")
+        return slots, list(zip(me[:nm.value].tolist(), ms[:nm.value].tolist()))
+
+
+class OffloadedLayer:
+    """A layer whose routed experts stay in pinned host memory, with
+    `num_slots` device slots managed by the LFU cache.  Each call routes the
+    tokens on the GPU, reads the ids on the host, plans hits and misses,
+    copies the missing experts into their slots on a copy stream (after the
+    previous call's kernels, which own their slots until they finish), and
+    runs the layer with that routing: the shared expert's kernels start at
+    once and the routed experts' wait for the copies."""
+
+    def __init__(self, src, num_slots: int = 16, device="cuda", max_tokens: int = 4, threads: int = 16):
+        self.dev = DeviceLayer(src, device=device, resident_experts=False)
+        d = self.dev
+        E, stride = d.num_experts, d.pool.expert_stride
+        self.stride = stride
+        self.host_pool = torch.empty(E * stride, dtype=torch.uint8, pin_memory=True)
+        hp = self.host_pool.numpy()
+
+        def pack_expert(e):
+            pack_expert_into(d.pool, e, src.gate.select(e), src.up.select(e), src.down.select(e), hp)
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(pack_expert, range(E)))
+        self.slot_buf = torch.empty(num_slots * stride, dtype=torch.uint8, device=device)
+        d.pool.base = self.slot_buf.data_ptr()
+        self.cache = LfuCache(E, num_slots)
+        self.max_tokens, k = max_tokens, d.top_k
+        self.ids = torch.empty((max_tokens, k), dtype=torch.int32, device=device)
+        self.w = torch.empty((max_tokens, k), dtype=torch.float32, device=device)
+        self.slots = torch.empty((max_tokens, k), dtype=torch.int32, device=device)
+        self.ids_h = torch.empty(max_tokens * k, dtype=torch.int32, pin_memory=True)
+        self.slots_h = torch.empty(max_tokens * k, dtype=torch.int32, pin_memory=True)
+        self.route_ws = torch.empty(max(256, _lib.mq_route_workspace_bytes(ctypes.byref(d.router), max_tokens)),
+                                    dtype=torch.uint8, device=device)
+        self.workspace = d.new_workspace(max_tokens)
+        self.copy_stream = torch.cuda.Stream(device=device)
+        self.ready = torch.cuda.Event()
+        self.done = torch.cuda.Event()
+        self.done.record()
+        self.hits = self.misses = 0
+
+    def forward(self, x: torch.Tensor, out: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16,
+                tail: Optional[Tail] = None, input_rmsnorm_eps: float = 0.0) -> torch.Tensor:
+        T = x.shape[0]
+        k = self.dev.top_k
+        assert 0 < T <= self.max_tokens
+        s = torch.cuda.current_stream()
+        ids, w, slots = self.ids[:T], self.w[:T], self.slots[:T]
+        if input_rmsnorm_eps > 0:
+            # the router sees the same normalised rows as the experts
+            xr = rmsnorm(x, eps=input_rmsnorm_eps)
+        else:
+            xr = x
+        route(self.dev, xr, ids, w, workspace=self.route_ws)
+        self.ids_h[:T * k].copy_(ids.view(-1), non_blocking=True)
+        s.synchronize()                                   # the host reads the expert ids
+        slot_of, fills = self.cache.plan(self.ids_h[:T * k].numpy())
+        self.misses += len(fills)
+        self.hits += len(set(self.ids_h[:T * k].tolist())) - len(fills)
+        cs = self.copy_stream
+        cs.wait_event(self.done)                          # earlier kernels own their slots until done
+        with torch.cuda.stream(cs):
+            for e, sl in fills:
+                self.slot_buf[sl * self.stride:(sl + 1) * self.stride].copy_(
+                    self.host_pool[e * self.stride:(e + 1) * self.stride], non_blocking=True)
+            self.ready.record(cs)
+        self.slots_h[:T * k] = torch.from_numpy(slot_of)
+        slots.view(-1).copy_(self.slots_h[:T * k], non_blocking=True)
+        out = moe_layer_forward(self.dev, x, out=out, workspace=self.workspace, path="gemv", out_dtype=out_dtype,
+                                tail=tail, input_rmsnorm_eps=input_rmsnorm_eps, route_ids=ids, route_w=w,
+                                route_slots=slots, experts_ready=self.ready)
+        self.done.record(s)
+        return out

@@ -14,7 +14,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoegemv.so")
-SOURCES = ["capi.cpp", "pack.cpp", "gemv.hip", "grouped.hip", "fused.hip", "stack.hip", "stream.hip"]
+SOURCES = ["capi.cpp", "pack.cpp", "gemv.hip", "grouped.hip", "fused.hip", "stack.hip", "stream.hip", "tail.hip", "head.hip", "lfu.cpp"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -424,7 +424,10 @@ __device__ __forceinline__ void load_token(const Plan& p, TokenLoads& t, bool ne
 // The token into LDS, the router input scale, and the column sums the block
 // dots need: thread c holds columns 8c .. 8c+7 and contributes its partial
 // sums; each lane set is then a sum of two (4-bit) or four (8-bit) of them.
-__device__ __forceinline__ void stage_token(const Plan& p, Shared& sh, const TokenLoads& tl, uint32_t tag) {
+// xraw (TAIL only): LDS for the input row as given, the layer tail's residual.
+template <bool TAIL>
+__device__ __forceinline__ void stage_token(const Plan& p, Shared& sh, const TokenLoads& tl, uint32_t tag,
+                                            uint16_t* xraw) {
     const int t = tix();
     const int nch = p.H / 8;
     uint4 v = tl.x;
@@ -436,6 +439,8 @@ __device__ __forceinline__ void stage_token(const Plan& p, Shared& sh, const Tok
         await_words(xw, 1, w4, 0xFu, tag - 1, p.f_err);
         v = make_uint4((uint32_t)w4[0], (uint32_t)w4[1], (uint32_t)w4[2], (uint32_t)w4[3]);
     }
+    if constexpr (TAIL)
+        if (p.t_res_in && t < nch) *(uint4*)(xraw + 8 * t) = v;
     if (p.in_eps > 0.f) {
         // the input row first goes through a unit-weight RMSNorm, rounded to
         // bf16 (the norm between the layers of a stack)
@@ -821,35 +826,92 @@ __device__ __forceinline__ void run_rdu(const Plan& p, Shared& sh, const DownUni
     // down unit, after the barrier that ends this layer
 }
 
-// Output tile a: every source's partial outputs summed in source order
-// (routed slots, then shared chunks), rounded once.
-__device__ __forceinline__ void run_reduce(const Plan& p, Shared& sh, int a, uint32_t tag) {
-    const uint64_t* tilep = p.f_piece + (int64_t)a * p.n_src * 64;
-    gather_words(tilep, p.n_src * 64, tag, p.f_err, sh.gbuf);
-    if (wave_id() == 0) {
-        float v = 0.f;
-        for (int s2 = 0; s2 < p.n_src; ++s2) v += __uint_as_float(sh.gbuf[s2 * 64 + tix()]);
-        // a wait of this call that gave up may have fed stale partial results
-        // into the sums: the output then reads NaN rather than a plausible row
-        if (ld_ctr(p.f_err) & kErrWait) v = __builtin_nanf("");
-        const int row = 64 * a + tix();
-        const uint32_t b = f32_to_bf16(v);
-        if (!p.out) {
-        } else if (p.out_f32) {
-            ((float*)p.out)[row] = v;
-        } else {
-            ((uint16_t*)p.out)[row] = (uint16_t)b;
-        }
-        if (p.out_w) {
-            // the next layer's input: bf16 pairs (row 2i in the low half), one copy per XCD
-            const uint32_t b1 = __shfl_down(b, 1, 64);
-            if ((tix() & 1) == 0) {
+// Writes output row `row` (v: its fp32 value) to out and, in a stack, to
+// the next layer's input words.
+__device__ __forceinline__ void put_row(const Plan& p, int row, float v, uint32_t tag) {
+    // a wait of this call that gave up may have fed stale partial results
+    // into the sums: the output then reads NaN rather than a plausible row
+    if (ld_ctr(p.f_err) & kErrWait) v = __builtin_nanf("");
+    const uint32_t b = f32_to_bf16(v);
+    if (!p.out) {
+    } else if (p.out_f32) {
+        ((float*)p.out)[row] = v;
+    } else {
+        ((uint16_t*)p.out)[row] = (uint16_t)b;
+    }
+    if (p.out_w) {
+        // the next layer's input: bf16 pairs (row 2i in the low half), one copy per XCD
+        const uint32_t b1 = __shfl_down(b, 1, 64);
+        if ((tix() & 1) == 0) {
 #pragma unroll
-                for (int c = 0; c < kCopies; ++c) st_word(p.out_w + c * p.xw_stride + (row >> 1), tag, b | (b1 << 16));
-            }
+            for (int c = 0; c < kCopies; ++c) st_word(p.out_w + c * p.xw_stride + (row >> 1), tag, b | (b1 << 16));
         }
     }
+}
+
+// Output tile a: every source's partial outputs summed in source order
+// (routed slots, then shared chunks), rounded once.  With the layer tail the
+// two branches are summed apart, s (shared) and r (routed); every output
+// tile publishes five partial sums over its 64 rows,
+//     s^2, r^2, (w_s s)^2, (w_r r)^2, (w_s s)(w_r r),
+// and each one sums all tiles' in tile order: that gives the two branch
+// norms' factors a, b and, since |a w_s s + b w_r r|^2 expands into those
+// sums, the output norm's factor c without a second exchange.
+// The output sums of tile a with the layer tail (see run_reduce).
+__device__ __forceinline__ void run_reduce_tail(const Plan& p, Shared& sh, int a, uint32_t tag, const uint16_t* xraw) {
+    const int row = 64 * a + tix();
+    float sv = 0.f, rv = 0.f, ws = 1.f, wr = 1.f;
+    if (wave_id() == 0) {
+        if (p.tn_s) ws = p.tn_s[row];
+        if (p.tn_r) wr = p.tn_r[row];
+        for (int s2 = 0; s2 < p.k; ++s2) rv += __uint_as_float(sh.gbuf[s2 * 64 + tix()]);
+        for (int s2 = p.k; s2 < p.n_src; ++s2) sv += __uint_as_float(sh.gbuf[s2 * 64 + tix()]);
+        const float q[5] = {wave_sum(sv * sv), wave_sum(rv * rv), wave_sum((ws * sv) * (ws * sv)),
+                            wave_sum((wr * rv) * (wr * rv)), wave_sum((ws * sv) * (wr * rv))};
+        if (tix() < 8) {
+            float mine = 0.f;
+#pragma unroll
+            for (int i = 0; i < 5; ++i)
+                if ((int)tix() == i) mine = q[i];
+            st_word(p.f_tail + (int64_t)a * 8 + tix(), tag, __float_as_uint(mine));
+        }
+    }
+    gather_words(p.f_tail, p.G_H * 8, tag, p.f_err, sh.gbuf);
+    if (wave_id() == 0) {
+        float tot[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int t2 = 0; t2 < p.G_H; ++t2)
+#pragma unroll
+            for (int i = 0; i < 5; ++i) tot[i] += __uint_as_float(sh.gbuf[t2 * 8 + i]);
+        const float H = (float)p.H;
+        const float fa = p.tn_s ? 1.0f / sqrtf(tot[0] / H + p.t_eps) : 1.0f;
+        const float fb = p.tn_r ? 1.0f / sqrtf(tot[1] / H + p.t_eps) : 1.0f;
+        const float ff = fa * fa * tot[2] + fb * fb * tot[3] + 2.0f * fa * fb * tot[4];
+        const float fc = p.tn_o ? 1.0f / sqrtf(ff / H + p.t_eps) : 1.0f;
+        const float wo = p.tn_o ? p.tn_o[row] : 1.0f;
+        float res = 0.f;
+        if (p.t_res_in)
+            res = bf16_to_f32(xraw[row]);
+        else if (p.t_res)
+            res = bf16_to_f32(p.t_res[row]);
+        put_row(p, row, p.t_scalar * (res + fc * wo * (fa * ws * sv + fb * wr * rv)), tag);
+    }
     // the layer's closing barrier follows
+}
+
+template <bool TAIL>
+__device__ __forceinline__ void run_reduce(const Plan& p, Shared& sh, int a, uint32_t tag, const uint16_t* xraw) {
+    const uint64_t* tilep = p.f_piece + (int64_t)a * p.n_src * 64;
+    gather_words(tilep, p.n_src * 64, tag, p.f_err, sh.gbuf);
+    if constexpr (!TAIL) {
+        if (wave_id() == 0) {
+            float v = 0.f;
+            for (int s2 = 0; s2 < p.n_src; ++s2) v += __uint_as_float(sh.gbuf[s2 * 64 + tix()]);
+            put_row(p, 64 * a + tix(), v, tag);
+        }
+        // the layer's closing barrier follows
+    } else {
+        run_reduce_tail(p, sh, a, tag, xraw);
+    }
 }
 
 // ----------------------------------------------------------------- the kernel
@@ -886,7 +948,8 @@ __device__ __forceinline__ void prefetch_args(const Plan& p) {
 
 // One layer for one token: the workgroup's part of the unit order above.
 // Ends with every wave past its last use of the shared memory.
-__device__ __forceinline__ void decode_layer(const Plan& p, Shared& sh, uint32_t tag) {
+template <bool TAIL>
+__device__ __forceinline__ void decode_layer(const Plan& p, Shared& sh, uint32_t tag, uint16_t* xraw) {
     const int nwg = gridDim.x, w = blockIdx.x;
     const Unit ur = unit_router(p, w - p.G_H);
     const Unit us = unit_sh(p, w - p.n_rh);
@@ -898,7 +961,7 @@ __device__ __forceinline__ void decode_layer(const Plan& p, Shared& sh, uint32_t
     LoadsN<kItemsRH> lsh;
     issue_loads(p, sh, ur, lrt);
     issue_loads(p, sh, us, lsh);
-    stage_token(p, sh, tl, tag);
+    stage_token<TAIL>(p, sh, tl, tag, xraw);
     if (ur.kind == U_ROUTER) run_router(p, sh, ur, lrt, tag);
     if (us.kind == U_SH) run_rh(p, sh, us, lsh, tag);
     if (rh.kind == U_RH || du.nt > 0) fetch_ids(p, sh, tag);
@@ -926,7 +989,7 @@ __device__ __forceinline__ void decode_layer(const Plan& p, Shared& sh, uint32_t
             if (usd[s].kind == U_SD) run_sd_piece(p, sh, usd[s], lsd[s], tag);
     }
     if (du.nt > 0) run_rdu(p, sh, du, ld, tag);
-    if (w < p.G_H) run_reduce(p, sh, w, tag);
+    if (w < p.G_H) run_reduce<TAIL>(p, sh, w, tag, xraw);
     __syncthreads();
 }
 

@@ -12,12 +12,23 @@ constexpr bool kOpaqueTid = false;
 
 namespace mq {
 
-__global__ __launch_bounds__(kThreads) void k_decode(Plan p) {
+// TAIL: the layer tail is applied in the output sums (a separate instance,
+// so the layer without a tail carries none of its code).
+template <bool TAIL>
+__device__ __forceinline__ void decode_one(const Plan& p) {
     __shared__ Shared sh;
+    uint16_t* xraw = nullptr;
+    if constexpr (TAIL) {
+        __shared__ alignas(16) uint16_t xraw_lds[4096];   // the input row as given (the tail's residual)
+        xraw = xraw_lds;
+    }
     prefetch_args(p);
     const uint32_t tag = ld_ctr(p.f_epoch) + 1;
-    decode_layer(p, sh, tag);
+    decode_layer<TAIL>(p, sh, tag, xraw);
     finish_call(p, sh, tag);
 }
+
+__global__ __launch_bounds__(kThreads) void k_decode(Plan p) { decode_one<false>(p); }
+__global__ __launch_bounds__(kThreads) void k_decode_tail(Plan p) { decode_one<true>(p); }
 
 }  // namespace mq

@@ -47,6 +47,12 @@ __global__ __launch_bounds__(256) void k_prep(Plan p) {
             for (int e = 0; e < 8; ++e) s4 += bf16_to_f32(x[64 * g + 32 * ks + 8 * kb + e]);
         p.rsum8[((int64_t)t * p.G_H + g) * 4 + kb] = s8;
         p.xsum4[((int64_t)t * p.G_H + g) * 4 + kb] = s4;
+        if (p.ebits == 8) {   // the same sums over the 8-bit blocks' lane columns
+            float x8 = 0.f;
+            for (int ks = 0; ks < 4; ++ks)
+                for (int e = 0; e < 4; ++e) x8 += bf16_to_f32(x[64 * g + 16 * ks + 4 * kb + e]);
+            p.xsum8[((int64_t)t * p.G_H + g) * 4 + kb] = x8;
+        }
     }
 }
 
@@ -150,12 +156,33 @@ __global__ __launch_bounds__(256) void k_topk(Plan p) {
     }
 }
 
+// Partial dots of one lane over one 8-bit DEV_V1 block: rows 16*m + lane%16
+// (m = 0..3), over the lane's 16 columns 16*i + 4*(lane/16) + 0..3 (i = 0..3).
+// c[m]: the lane's code words of row block m; xv[i]: four fp32 inputs of
+// columns 16*i + 4*(lane/16)... Adds sum(q * x) of row m to d[m].
+__device__ __forceinline__ void q8_block_dot(const uint4 c[4], const float xv[4][4], float d[4]) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const uint32_t cw[4] = {c[m].x, c[m].y, c[m].z, c[m].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            d[m] = fmaf((float)(cw[i] & 0xFFu), xv[i][0], d[m]);
+            d[m] = fmaf((float)((cw[i] >> 8) & 0xFFu), xv[i][1], d[m]);
+            d[m] = fmaf((float)((cw[i] >> 16) & 0xFFu), xv[i][2], d[m]);
+            d[m] = fmaf((float)(cw[i] >> 24), xv[i][3], d[m]);
+        }
+    }
+}
+
 // Gate and up projections of one 64-row tile for one (token, expert) pair,
 // or for the shared expert, with GeGLU: h = gelu_tanh(g) * u.  h is stored
-// as a bf16 high/low pair (h ~= hi + lo to 2^-16) for the down projection.
-// grid (T, k * I/64 + Is/64).
-__global__ __launch_bounds__(256) void k_gateup(Plan p) {
-    const int t = blockIdx.x, item = blockIdx.y;
+// as a bf16 high/low pair (h ~= hi + lo to 2^-16) for the down projection,
+// with the sums of each lane set's columns of it (the lane columns of
+// BITS-bit blocks).  grid (T, k * I/64 + Is/64).
+template <int BITS>
+__device__ __forceinline__ void gateup_tile(const Plan& p) {
+    constexpr int BLK = blk_bytes(BITS);
+    const int t = blockIdx.x, item = blockIdx.y + p.gu_item0;
     const int wave = wave_id(), lane = threadIdx.x & 63, kb = lane >> 4;
     const int It = p.I / 64, routed = p.k * It;
     const uint8_t *gw, *uw;
@@ -163,42 +190,68 @@ __global__ __launch_bounds__(256) void k_gateup(Plan p) {
     float* hsum;
     if (item < routed) {
         const int j = item / It, rt = item % It;
-        const int e = p.ids[t * p.k + j];
+        const int e = p.slots ? p.slots[t * p.k + j] : p.ids[t * p.k + j];
         const uint8_t* blob = p.pool_base + (int64_t)e * p.expert_stride;
-        gw = blob + p.gate_off + (int64_t)rt * p.G_H * kBlk4;
-        uw = blob + p.up_off + (int64_t)rt * p.G_H * kBlk4;
+        gw = blob + p.gate_off + (int64_t)rt * p.G_H * BLK;
+        uw = blob + p.up_off + (int64_t)rt * p.G_H * BLK;
         const int64_t hrow = ((int64_t)t * p.k + j) * p.I + rt * 64;
         hi = p.hhi + hrow;
         lo = p.hlo + hrow;
         hsum = p.hsum + (((int64_t)t * p.k + j) * p.G_I + rt) * 4;
     } else {
         const int rt = item - routed;
-        gw = p.sh_gate + (int64_t)rt * p.G_H * kBlk4;
-        uw = p.sh_up + (int64_t)rt * p.G_H * kBlk4;
+        gw = p.sh_gate + (int64_t)rt * p.G_H * BLK;
+        uw = p.sh_up + (int64_t)rt * p.G_H * BLK;
         hi = p.shi + (int64_t)t * p.Is + rt * 64;
         lo = p.slo + (int64_t)t * p.Is + rt * 64;
         hsum = p.ssum + ((int64_t)t * p.G_s + rt) * 4;
     }
     const uint16_t* x = p.x + (int64_t)t * p.x_stride;
+    const float* xsum = BITS == 4 ? p.xsum4 : p.xsum8;
     float ag[4] = {0.f, 0.f, 0.f, 0.f}, au[4] = {0.f, 0.f, 0.f, 0.f};
     for (int g = wave; g < p.G_H; g += 4) {
-        const uint8_t* bg = gw + (int64_t)g * kBlk4;
-        const uint8_t* bu = uw + (int64_t)g * kBlk4;
-        const uint4 g0 = *(const uint4*)(bg + lane * 16), g1 = *(const uint4*)(bg + 1024 + lane * 16);
-        const uint4 u0 = *(const uint4*)(bu + lane * 16), u1 = *(const uint4*)(bu + 1024 + lane * 16);
-        const uint4 sg = *(const uint4*)(bg + kCodes4 + (lane & 15) * 16);
-        const uint4 su = *(const uint4*)(bu + kCodes4 + (lane & 15) * 16);
-        const uint4 xa = *(const uint4*)(x + 64 * g + 8 * kb);
-        const uint4 xb = *(const uint4*)(x + 64 * g + 32 + 8 * kb);
-        const float xs = p.xsum4[((int64_t)t * p.G_H + g) * 4 + kb];
+        const uint8_t* bg = gw + (int64_t)g * BLK;
+        const uint8_t* bu = uw + (int64_t)g * BLK;
+        const uint4 sg = *(const uint4*)(bg + code_bytes(BITS) + (lane & 15) * 16);
+        const uint4 su = *(const uint4*)(bu + code_bytes(BITS) + (lane & 15) * 16);
+        const float xs = xsum[((int64_t)t * p.G_H + g) * 4 + kb];
         float dg[4] = {0.f, 0.f, 0.f, 0.f}, du[4] = {0.f, 0.f, 0.f, 0.f};
-        q4_block_dot(g0, g1, xa, xb, dg);
-        q4_block_dot(u0, u1, xa, xb, du);
         const uint32_t sgw[4] = {sg.x, sg.y, sg.z, sg.w}, suw[4] = {su.x, su.y, su.z, su.w};
+        if constexpr (BITS == 4) {
+            const uint4 g0 = *(const uint4*)(bg + lane * 16), g1 = *(const uint4*)(bg + 1024 + lane * 16);
+            const uint4 u0 = *(const uint4*)(bu + lane * 16), u1 = *(const uint4*)(bu + 1024 + lane * 16);
+            const uint4 xa = *(const uint4*)(x + 64 * g + 8 * kb);
+            const uint4 xb = *(const uint4*)(x + 64 * g + 32 + 8 * kb);
+            q4_block_dot(g0, g1, xa, xb, dg);
+            q4_block_dot(u0, u1, xa, xb, du);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            ag[m] = fmaf(bf16_lo(sgw[m]), fmaf(-128.f, xs, dg[m]), fmaf(bf16_hi(sgw[m]), xs, ag[m]));
-            au[m] = fmaf(bf16_lo(suw[m]), fmaf(-128.f, xs, du[m]), fmaf(bf16_hi(suw[m]), xs, au[m]));
+            for (int m = 0; m < 4; ++m) {
+                ag[m] = fmaf(bf16_lo(sgw[m]), fmaf(-128.f, xs, dg[m]), fmaf(bf16_hi(sgw[m]), xs, ag[m]));
+                au[m] = fmaf(bf16_lo(suw[m]), fmaf(-128.f, xs, du[m]), fmaf(bf16_hi(suw[m]), xs, au[m]));
+            }
+        } else {
+            uint4 gc[4], uc[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                gc[m] = *(const uint4*)(bg + (m * 64 + lane) * 16);
+                uc[m] = *(const uint4*)(bu + (m * 64 + lane) * 16);
+            }
+            float xv[4][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint2 v = *(const uint2*)(x + 64 * g + 16 * i + 4 * kb);
+                xv[i][0] = bf16_lo(v.x);
+                xv[i][1] = bf16_hi(v.x);
+                xv[i][2] = bf16_lo(v.y);
+                xv[i][3] = bf16_hi(v.y);
+            }
+            q8_block_dot(gc, xv, dg);
+            q8_block_dot(uc, xv, du);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                ag[m] = fmaf(bf16_lo(sgw[m]), dg[m], fmaf(bf16_hi(sgw[m]), xs, ag[m]));
+                au[m] = fmaf(bf16_lo(suw[m]), du[m], fmaf(bf16_hi(suw[m]), xs, au[m]));
+            }
         }
     }
     __shared__ float red[4][2][64];
@@ -227,21 +280,43 @@ __global__ __launch_bounds__(256) void k_gateup(Plan p) {
     if (threadIdx.x < 4) {
         const int q = threadIdx.x;
         float s = 0.f;
-        for (int ks = 0; ks < 2; ++ks)
-            for (int e = 0; e < 8; ++e) s += hh[32 * ks + 8 * q + e];
+        if (BITS == 4) {
+            for (int ks = 0; ks < 2; ++ks)
+                for (int e = 0; e < 8; ++e) s += hh[32 * ks + 8 * q + e];
+        } else {
+            for (int ks = 0; ks < 4; ++ks)
+                for (int e = 0; e < 4; ++e) s += hh[16 * ks + 4 * q + e];
+        }
         hsum[q] = s;
     }
 }
 
+__global__ __launch_bounds__(256) void k_gateup(Plan p) { gateup_tile<4>(p); }
+__global__ __launch_bounds__(256) void k_gateup8(Plan p) { gateup_tile<8>(p); }
+
 // Down projections of one 64-row tile of the output for one token: the k
 // routed experts (weighted) and the shared expert, split over kDownSplits
-// workgroups whose partial sums k_combine adds in a fixed order.
-// grid (T, H/64, kDownSplits).
-__global__ __launch_bounds__(256) void k_down(Plan p) {
-    const int t = blockIdx.x, rt = blockIdx.y, split = blockIdx.z;
+// workgroups whose partial sums k_combine adds in a fixed order.  With a
+// shared expert, splits 0 .. kDownSplits-2 take the routed sources and the
+// last split the shared expert's, so the two branches stay apart for the
+// layer tail.  grid (T, H/64, kDownSplits).
+template <int BITS>
+__device__ __forceinline__ void down_tile(const Plan& p) {
+    constexpr int BLK = blk_bytes(BITS);
+    const int t = blockIdx.x, rt = blockIdx.y, split = blockIdx.z + p.dn_split0;
     const int wave = wave_id(), lane = threadIdx.x & 63, kb = lane >> 4;
-    const int nr = p.k * p.G_I, nb = nr + (p.has_shared ? p.G_s : 0);
-    const int b0 = split * nb / kDownSplits, b1 = (split + 1) * nb / kDownSplits;
+    const int nr = p.k * p.G_I;
+    int b0, b1;
+    if (!p.has_shared) {
+        b0 = split * nr / kDownSplits;
+        b1 = (split + 1) * nr / kDownSplits;
+    } else if (split < kDownSplits - 1) {
+        b0 = split * nr / (kDownSplits - 1);
+        b1 = (split + 1) * nr / (kDownSplits - 1);
+    } else {
+        b0 = nr;
+        b1 = nr + p.G_s;
+    }
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     for (int b = b0 + wave; b < b1; b += 4) {
         const uint8_t* blk;
@@ -249,8 +324,8 @@ __global__ __launch_bounds__(256) void k_down(Plan p) {
         float hs, wf;
         if (b < nr) {
             const int j = b / p.G_I, g = b % p.G_I;
-            const int e = p.ids[t * p.k + j];
-            blk = p.pool_base + (int64_t)e * p.expert_stride + p.down_off + ((int64_t)rt * p.G_I + g) * kBlk4;
+            const int e = p.slots ? p.slots[t * p.k + j] : p.ids[t * p.k + j];
+            blk = p.pool_base + (int64_t)e * p.expert_stride + p.down_off + ((int64_t)rt * p.G_I + g) * BLK;
             const int64_t hrow = ((int64_t)t * p.k + j) * p.I + 64 * g;
             hi = p.hhi + hrow;
             lo = p.hlo + hrow;
@@ -258,23 +333,42 @@ __global__ __launch_bounds__(256) void k_down(Plan p) {
             wf = p.wts[t * p.k + j];
         } else {
             const int g = b - nr;
-            blk = p.sh_down + ((int64_t)rt * p.G_s + g) * kBlk4;
+            blk = p.sh_down + ((int64_t)rt * p.G_s + g) * BLK;
             hi = p.shi + (int64_t)t * p.Is + 64 * g;
             lo = p.slo + (int64_t)t * p.Is + 64 * g;
             hs = p.ssum[((int64_t)t * p.G_s + g) * 4 + kb];
             wf = 1.0f;
         }
-        const uint4 c0 = *(const uint4*)(blk + lane * 16), c1 = *(const uint4*)(blk + 1024 + lane * 16);
-        const uint4 sb = *(const uint4*)(blk + kCodes4 + (lane & 15) * 16);
-        const uint4 ha = *(const uint4*)(hi + 8 * kb), hb = *(const uint4*)(hi + 32 + 8 * kb);
-        const uint4 la = *(const uint4*)(lo + 8 * kb), lb = *(const uint4*)(lo + 32 + 8 * kb);
-        float d[4] = {0.f, 0.f, 0.f, 0.f};
-        q4_block_dot(c0, c1, ha, hb, d);
-        q4_block_dot(c0, c1, la, lb, d);
+        const uint4 sb = *(const uint4*)(blk + code_bytes(BITS) + (lane & 15) * 16);
         const uint32_t sbw[4] = {sb.x, sb.y, sb.z, sb.w};
+        float d[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (BITS == 4) {
+            const uint4 c0 = *(const uint4*)(blk + lane * 16), c1 = *(const uint4*)(blk + 1024 + lane * 16);
+            const uint4 ha = *(const uint4*)(hi + 8 * kb), hb = *(const uint4*)(hi + 32 + 8 * kb);
+            const uint4 la = *(const uint4*)(lo + 8 * kb), lb = *(const uint4*)(lo + 32 + 8 * kb);
+            q4_block_dot(c0, c1, ha, hb, d);
+            q4_block_dot(c0, c1, la, lb, d);
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-            acc[m] = fmaf(wf, fmaf(bf16_lo(sbw[m]), fmaf(-128.f, hs, d[m]), bf16_hi(sbw[m]) * hs), acc[m]);
+            for (int m = 0; m < 4; ++m)
+                acc[m] = fmaf(wf, fmaf(bf16_lo(sbw[m]), fmaf(-128.f, hs, d[m]), bf16_hi(sbw[m]) * hs), acc[m]);
+        } else {
+            uint4 c[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) c[m] = *(const uint4*)(blk + (m * 64 + lane) * 16);
+            float hv[4][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint2 vh = *(const uint2*)(hi + 16 * i + 4 * kb), vl = *(const uint2*)(lo + 16 * i + 4 * kb);
+                hv[i][0] = bf16_lo(vh.x) + bf16_lo(vl.x);
+                hv[i][1] = bf16_hi(vh.x) + bf16_hi(vl.x);
+                hv[i][2] = bf16_lo(vh.y) + bf16_lo(vl.y);
+                hv[i][3] = bf16_hi(vh.y) + bf16_hi(vl.y);
+            }
+            q8_block_dot(c, hv, d);
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                acc[m] = fmaf(wf, fmaf(bf16_lo(sbw[m]), d[m], bf16_hi(sbw[m]) * hs), acc[m]);
+        }
     }
     __shared__ float red[4][64];
 #pragma unroll
@@ -289,6 +383,9 @@ __global__ __launch_bounds__(256) void k_down(Plan p) {
             (red[0][r] + red[1][r]) + (red[2][r] + red[3][r]);
     }
 }
+
+__global__ __launch_bounds__(256) void k_down(Plan p) { down_tile<4>(p); }
+__global__ __launch_bounds__(256) void k_down8(Plan p) { down_tile<8>(p); }
 
 // out[t][i] = sum of the kDownSplits partials, rounded once.  grid (T, ceil(H/256)).
 __global__ __launch_bounds__(256) void k_combine(Plan p) {

@@ -13,6 +13,8 @@
 
 namespace mq {
 
+__global__ void k_tail_grouped(Plan p);   // tail.hip
+
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
@@ -1285,7 +1287,10 @@ mq_status launch_grouped(const Plan& p, hipStream_t s) {
     hipLaunchKernelGGL(k_sort, dim3(1), dim3(1024), 0, s, p);
     const mq_status st = p.ntile <= 64 ? launch_gemms<4>(p, s) : launch_gemms<8>(p, s);
     if (st != MQ_OK) return st;
-    hipLaunchKernelGGL(k_gg_combine, dim3(p.T, (p.H + 1023) / 1024), dim3(256), 0, s, p);
+    if (p.tail)
+        hipLaunchKernelGGL(k_tail_grouped, dim3(p.T), dim3(1024), 0, s, p);
+    else
+        hipLaunchKernelGGL(k_gg_combine, dim3(p.T, (p.H + 1023) / 1024), dim3(256), 0, s, p);
     return MQ_OK;
 }
 

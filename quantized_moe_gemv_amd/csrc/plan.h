@@ -52,7 +52,7 @@ struct Plan {
     float* rsum8;      // [T][G_H][4] sums of r over each lane's 16 columns (8-bit blocks)
     float* xsum4;      // [T][G_H][4] sums of x over each lane's 16 columns (4-bit blocks)
     float* plog;       // [rsplit][T][E_pad] partial router scores
-    int32_t* ids;      // [T][k]
+    int32_t* ids;      // [T][k]  (given routing: the caller's ids)
     float* wts;        // [T][k]
     uint16_t* hhi;     // [T][k][I]   GeGLU activations, bf16 high part
     uint16_t* hlo;     // [T][k][I]   bf16 low part (h - hi)
@@ -95,6 +95,42 @@ struct Plan {
     int max_tiles;     // upper bound of scheduled (expert, token chunk) pairs
     int ntile;         // tokens per grouped chunk (32 or 128)
     int n_vs;          // virtual experts of the shared expert (0 without one)
+
+    // fields added after the single-launch decode's (its scalar argument
+    // loads are laid out around the fields above)
+    int ebits;                // code width of the routed and shared experts (4 or 8)
+    float* xsum8;             // [T][G_H][4] sums of x over the lane columns of 8-bit blocks (8-bit experts)
+    const int32_t* slots;     // [T][k] pool blob each (token, slot) reads; null: the expert id (GEMV path)
+    int gu_item0, dn_split0;  // GEMV path launch offsets: first gate/up item and first down split of a launch
+    // layer tail (tail != 0): out = t_scalar * (res + N_o(N_s(s) + N_r(r)))
+    int tail;
+    const float* tn_s;     // [H] or null: no norm of the shared branch
+    const float* tn_r;     // [H] or null: routed branch
+    const float* tn_o;     // [H] or null: their sum
+    const uint16_t* t_res; // residual rows or null (t_res_in: the input rows as given)
+    int64_t t_res_stride;
+    int t_res_in;          // residual = the layer's input row before the input norm
+    float t_eps, t_scalar;
+    uint64_t* f_tail;      // single-launch decode: [G_H][8] tagged partial sums of the tail norms
+};
+
+// Arguments of the quantized GEMV head (head.hip).
+constexpr int kHeadTokens = 8;          // tokens per call
+constexpr int kHeadLdsBytes = 60 << 10; // the call's token rows (bf16) and their lane sums staged in LDS
+
+// Dynamic LDS of the head kernel for T token rows of `cols` columns.
+inline size_t head_lds_bytes(int T, int cols) { return (size_t)T * cols * 2 + (size_t)T * (cols / 64) * 16; }
+
+struct HeadArgs {
+    const uint8_t* w;      // DEV_V1 [rows][cols]
+    int rows, cols, bits, T;
+    const uint16_t* x;     // bf16 [T][cols], x_stride apart
+    int64_t x_stride;
+    void* y;               // optional [T][rows] (y_stride apart), f32 or bf16
+    int64_t y_stride;
+    int y_f32;
+    float cap;             // > 0: softcap
+    float2* part;          // optional [T][workgroups] best (value, row as int bits) per workgroup
 };
 
 // Fields of one layer of a single-launch stack (everything else is shared).
@@ -116,9 +152,17 @@ struct StackLayer {
     float* logits_out;
     int64_t expert_stride, gate_off, up_off, down_off;
     float eps, in_eps;
+    // layer tail
+    int tail, t_res_in;
+    const float* tn_s;
+    const float* tn_r;
+    const float* tn_o;
+    const uint16_t* t_res;
+    int64_t t_res_stride;
+    float t_eps, t_scalar;
 };
 
-constexpr int kStackChunk = 16;  // layers per argument-writing launch (kernel arguments stay under 4 KiB)
+constexpr int kStackChunk = 12;  // layers per argument-writing launch (kernel arguments stay under 4 KiB)
 
 struct StackChunk {
     int n;

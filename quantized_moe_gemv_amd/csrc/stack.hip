@@ -27,7 +27,21 @@ __global__ __launch_bounds__(kThreads) void k_decode_stack(const Plan* __restric
     for (int l = 0; l < n_layers; ++l) {
         const Plan& p = plans[l];
         prefetch_args(p);
-        decode_layer(p, sh, base + 1 + (uint32_t)l);
+        decode_layer<false>(p, sh, base + 1 + (uint32_t)l, nullptr);
+    }
+    finish_call(plans[0], sh, base + (uint32_t)n_layers);
+}
+
+// The same with every layer's tail applied in its output sums (a separate
+// kernel, so the stack without tails carries none of the tail's code).
+__global__ __launch_bounds__(kThreads) void k_decode_stack_tail(const Plan* __restrict__ plans, int n_layers) {
+    __shared__ Shared sh;
+    __shared__ alignas(16) uint16_t xraw[4096];   // each layer's input row as given (its tail's residual)
+    const uint32_t base = ld_ctr(plans[0].f_epoch);
+    for (int l = 0; l < n_layers; ++l) {
+        const Plan& p = plans[l];
+        prefetch_args(p);
+        decode_layer<true>(p, sh, base + 1 + (uint32_t)l, xraw);
     }
     finish_call(plans[0], sh, base + (uint32_t)n_layers);
 }
@@ -60,6 +74,15 @@ __global__ void k_stack_plans(Plan base, StackChunk c, Plan* dst) {
     q.ids_out = s.ids_out;
     q.w_out = s.w_out;
     q.logits_out = s.logits_out;
+    q.tail = s.tail;
+    q.tn_s = s.tn_s;
+    q.tn_r = s.tn_r;
+    q.tn_o = s.tn_o;
+    q.t_eps = s.t_eps;
+    q.t_scalar = s.t_scalar;
+    q.t_res_in = s.t_res_in;
+    q.t_res = s.t_res;
+    q.t_res_stride = s.t_res_stride;
     dst[blockIdx.x] = q;
 }
 

@@ -468,3 +468,25 @@ def test_give_up_reads_nan(M, tiny):
     o = M.moe_layer_forward(dev, x, workspace=ws, path="fused", out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(o, good) and M.workspace_errors(ws) == 0
+
+
+def test_workspace_shared_across_layer_sizes(M, tiny, decode):
+    """One workspace serving a small layer on the multi-launch paths and then
+    the Gemma-shaped layer on the single-launch path: the small layer's
+    buffers must not land on the words the single-launch path keeps across
+    calls (regression: they did, and a stale word equal to the next tag was
+    taken as current)."""
+    th, td = tiny
+    dh, dd = decode
+    log("one workspace: tiny layer (gemv, grouped) then the decode layer (fused)")
+    ws = torch.zeros(max(td.workspace_bytes(40), dd.workspace_bytes(1)), dtype=torch.uint8, device="cuda")
+    xd = bf16_tensor(S.make_tokens(S.SEEDS["decode"] + 70, 1, dh.cfg.hidden))
+    want = M.moe_layer_forward(dd, xd, path="fused", out_dtype=torch.float32)
+    for i in range(3):
+        for path, T in (("gemv", 4), ("grouped", 40), ("fused", 1)):
+            xt = bf16_tensor(S.make_tokens(S.SEEDS["tiny"] + 70 + i, T, th.cfg.hidden))
+            M.moe_layer_forward(td, xt, workspace=ws, path=path)
+        got = M.moe_layer_forward(dd, xd, workspace=ws, path="fused", out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(got, want), "round %d" % i
+    assert M.workspace_errors(ws) == 0

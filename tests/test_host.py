@@ -159,7 +159,11 @@ def test_workspace_bytes_grows_with_tokens_and_rejects_bad_layers():
     (lambda r, p, s: setattr(r.w, "bits", 4), M.MQ_ERR_UNSUPPORTED),
     (lambda r, p, s: setattr(r.w, "group", 32), M.MQ_ERR_UNSUPPORTED),
     (lambda r, p, s: setattr(r.w, "layout", M.LAYOUT_CANONICAL), M.MQ_ERR_UNSUPPORTED),
-    (lambda r, p, s: setattr(p, "bits", 8), M.MQ_ERR_UNSUPPORTED),
+    (lambda r, p, s: setattr(p, "bits", 6), M.MQ_ERR_UNSUPPORTED),
+    (lambda r, p, s: setattr(p, "bits", 8), M.MQ_ERR_SHAPE),      # a 4-bit pool stride cannot hold 8-bit blobs
+    (lambda r, p, s: setattr(p, "group", 96), M.MQ_ERR_UNSUPPORTED),
+    (lambda r, p, s: setattr(p, "group", 192), M.MQ_ERR_SHAPE),   # does not divide the expert width 64
+    (lambda r, p, s: setattr(s.down, "bits", 8), M.MQ_ERR_UNSUPPORTED),
     (lambda r, p, s: setattr(r, "top_k", 0), M.MQ_ERR_SHAPE),
     (lambda r, p, s: setattr(r, "top_k", 17), M.MQ_ERR_SHAPE),
     (lambda r, p, s: setattr(r.w, "rows", 15), M.MQ_ERR_SHAPE),
@@ -272,3 +276,170 @@ def test_stack_calls_are_validated_before_any_device_work():
     ws = M._lib.mq_stack_workspace_bytes(*fake_stack(3), 3)
     assert stack_call(ws_bytes=ws - 1) == M.MQ_ERR_WORKSPACE
     assert M._lib.moe_stack_forward(None, 1, None, None, None, 0.0, None, None, None) == M.MQ_ERR_NULL
+
+
+# ------------------------------------------------------------------ layer tail validation (no GPU involved)
+
+def call_with_tail(tail, T=4, H=256):
+    r, p, s = fake_layer()
+    x = M.MqAct(FAKE, T, H, 0, H)
+    out = M.MqAct(FAKE, T, H, 0, H)
+    ws_bytes = M._lib.mq_workspace_bytes(ctypes.byref(r), ctypes.byref(p), ctypes.byref(s), T)
+    opts = M.MqOpts(0, None, None, None, FAKE, ws_bytes, 0.0, ctypes.addressof(tail))
+    return M._lib.moe_layer_forward(ctypes.byref(x), ctypes.byref(r), ctypes.byref(p), ctypes.byref(s),
+                                    ctypes.byref(out), ctypes.byref(opts), None)
+
+
+def ok_tail():
+    return M.MqTail(FAKE, FAKE + 1024, FAKE + 2048, FAKE + 4096, 256, 0, 1e-6, 1.0)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("eps", -1.0, M.MQ_ERR_UNSUPPORTED),
+    ("eps", float("nan"), M.MQ_ERR_UNSUPPORTED),
+    ("layer_scalar", float("inf"), M.MQ_ERR_UNSUPPORTED),
+    ("norm_shared", FAKE + 4, M.MQ_ERR_ALIGN),
+    ("norm_out", FAKE + 8, M.MQ_ERR_ALIGN),
+    ("residual", FAKE + 2, M.MQ_ERR_ALIGN),
+    ("residual_stride", 255, M.MQ_ERR_ALIGN),
+    ("residual_stride", 128, M.MQ_ERR_SHAPE),
+])
+def test_tail_validation(field, value, status):
+    t = ok_tail()
+    setattr(t, field, value)
+    assert call_with_tail(t, T=0) == status          # checked before the zero-token early return
+
+
+def test_tail_residual_is_input_ignores_residual_fields():
+    t = ok_tail()
+    t.residual_is_input = 1
+    t.residual, t.residual_stride = FAKE + 2, 3
+    assert call_with_tail(t, T=0) == M.MQ_OK
+
+
+
+# ------------------------------------------------------------------ other widths of the format
+
+@pytest.mark.parametrize("bits,group", [(4, 128), (8, 128), (4, 256), (8, 64)])
+def test_pack_unpack_round_trip_other_groups(bits, group):
+    rows, cols = 70, 512
+    qt = S.make_qtensor(12, 0, 0, S.T_GATE_CODES, S.T_GATE_SCALES, rows, cols, bits, group=group,
+                        bias_range=(-0.1, 0.1))
+    assert qt.scales.shape == (rows, cols // group)
+    packed = M.pack(qt)
+    assert packed.size == M.packed_bytes(rows, cols, bits)     # the device layout does not depend on the group
+    c, s_, b = M.unpack(packed, rows, cols, bits, group=group)
+    assert np.array_equal(c, qt.codes) and np.array_equal(s_, qt.scales) and np.array_equal(b, qt.biases)
+    # read back as group 64, each pair repeated over its group's blocks
+    c64, s64, b64 = M.unpack(packed, rows, cols, bits, group=64)
+    assert np.array_equal(s64, np.repeat(qt.scales, group // 64, axis=1))
+    assert np.array_equal(b64, np.repeat(qt.biases, group // 64, axis=1))
+
+
+def test_unpack_refuses_a_group_its_pairs_do_not_have():
+    qt = S.make_qtensor(13, 0, 0, S.T_GATE_CODES, S.T_GATE_SCALES, 64, 256, 4)   # group 64, distinct pairs
+    packed = M.pack(qt)
+    with pytest.raises(M.MoeError) as e:
+        M.unpack(packed, 64, 256, 4, group=128)
+    assert e.value.status == M.MQ_ERR_UNSUPPORTED
+
+
+def fake_layer8(E=16, H=256, I=64, Is=128, k=2):
+    pool = M.pool_layout(H, I, page_bytes=4096, bits=8)
+    pool.base = FAKE
+    pool.num_experts = E
+    router = M.MqRouter(M.MqQTensor(FAKE, None, None, E, H, 8, 64, M.LAYOUT_DEV_V1), None, None, None, k, 1e-6)
+    sh = M.MqShared(M.MqQTensor(FAKE, None, None, Is, H, 8, 64, 1), M.MqQTensor(FAKE, None, None, Is, H, 8, 64, 1),
+                    M.MqQTensor(FAKE, None, None, H, Is, 8, 64, 1))
+    return router, pool, sh
+
+
+@pytest.mark.parametrize("path,status", [(0, M.MQ_OK), (1, M.MQ_OK), (2, M.MQ_ERR_UNSUPPORTED),
+                                         (3, M.MQ_ERR_UNSUPPORTED)])
+def test_8bit_experts_run_on_the_gemv_kernels(path, status):
+    """8-bit experts are accepted; AUTO and GEMV run them, GROUPED and FUSED
+    refuse them before anything is enqueued (checked with T = 0 for the
+    paths that would run, which returns before any launch)."""
+    r, p, s = fake_layer8()
+    T = 1 if path == 3 else 8
+    got = call(r, p, s, T=T if status != M.MQ_OK else 0, path=path)
+    assert got == status
+
+
+# ------------------------------------------------------------------ LFU slot cache (host)
+
+class LfuModel:
+    """The slot cache written from its definition: one use per distinct
+    expert per call; misses take, among the slots no expert of the call
+    holds, an empty one (lowest first), else the one whose expert has the
+    fewest uses, ties to the least recently used, then the lowest slot."""
+
+    def __init__(self, E, S):
+        self.E, self.S = E, S
+        self.slot_of, self.expert_of = {}, [-1] * S
+        self.uses, self.last, self.clock = [0] * E, [0] * S, 0
+
+    def plan(self, ids):
+        distinct = list(dict.fromkeys(int(e) for e in ids))
+        if len(distinct) > self.S or any(not 0 <= e < self.E for e in distinct):
+            raise ValueError
+        self.clock += 1
+        held = {self.slot_of[e] for e in distinct if e in self.slot_of}
+        for e in distinct:
+            self.uses[e] += 1
+        fills = []
+        for e in distinct:
+            if e in self.slot_of:
+                continue
+            free = [s for s in range(self.S) if s not in held]
+            empty = [s for s in free if self.expert_of[s] < 0]
+            s = min(empty) if empty else min(free, key=lambda q: (self.uses[self.expert_of[q]], self.last[q], q))
+            if self.expert_of[s] >= 0:
+                del self.slot_of[self.expert_of[s]]
+            self.expert_of[s], self.slot_of[e] = e, s
+            held.add(s)
+            fills.append((e, s))
+        for e in distinct:
+            self.last[self.slot_of[e]] = self.clock
+        return [self.slot_of[int(e)] for e in ids], fills
+
+
+def test_lfu_matches_its_definition_over_a_long_skewed_sequence():
+    rng = np.random.default_rng(3)
+    E, S = 40, 7
+    p = np.arange(1, E + 1, dtype=float) ** -1.1
+    p /= p.sum()
+    c, m = M.LfuCache(E, S), LfuModel(E, S)
+    hits = 0
+    for call in range(600):
+        n = int(rng.integers(1, 9))
+        ids = rng.choice(E, size=n, p=p)
+        while len(set(ids.tolist())) > S:
+            ids = ids[:-1]
+        got_slots, got_fills = c.plan(ids)
+        want_slots, want_fills = m.plan(ids)
+        assert got_slots.tolist() == want_slots and got_fills == want_fills, call
+        hits += len(set(ids.tolist())) - len(got_fills)
+    assert 0 < hits < 600 * 8
+
+
+def test_lfu_never_two_fills_into_one_slot_and_keeps_the_calls_experts():
+    c = M.LfuCache(16, 4)
+    slots, fills = c.plan(np.array([3, 5, 3, 7]))
+    assert sorted(s for _, s in fills) == [0, 1, 2] and slots.tolist()[0] == slots.tolist()[2]
+    slots, fills = c.plan(np.array([9, 3, 11]))      # 3 stays; 9 and 11 need two slots, one of them empty
+    assert len({s for _, s in fills}) == 2 and slots[1] == 0 and 3 not in [e for e, _ in fills]
+
+
+def test_lfu_refuses_more_experts_than_slots_and_bad_ids_without_changing_state():
+    c2 = M.LfuCache(16, 3)
+    m2 = LfuModel(16, 3)
+    c2.plan(np.array([1, 2]))
+    m2.plan([1, 2])
+    for bad in ([1, 2, 3, 4], [0, 16], [-1]):
+        with pytest.raises(M.MoeError) as e:
+            c2.plan(np.array(bad))
+        assert e.value.status == M.MQ_ERR_SHAPE
+    s, f = c2.plan(np.array([5, 1]))
+    ws, wf = m2.plan([5, 1])
+    assert s.tolist() == ws and f == wf
