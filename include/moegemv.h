@@ -49,7 +49,8 @@ typedef enum {
     MQ_ERR_UNSUPPORTED = -4,  /* bits, group, layout, dtype, path or size not supported */
     MQ_ERR_WORKSPACE = -5,    /* workspace missing or smaller than mq_workspace_bytes */
     MQ_ERR_HIP = -6,          /* a HIP runtime call failed */
-    MQ_ERR_BUFFER = -7        /* a HOST output buffer is too small */
+    MQ_ERR_BUFFER = -7,       /* a HOST output buffer is too small */
+    MQ_ERR_TOO_LARGE = -8     /* the call needs more than the fixed static scratch (moe_layer_forward_noalloc) */
 } mq_status;
 
 enum { MQ_LAYOUT_CANONICAL = 0, MQ_LAYOUT_DEV_V1 = 1 };
@@ -228,6 +229,32 @@ size_t mq_workspace_bytes(const mq_router* router, const mq_expert_pool* pool,
  *     output rows of that call read NaN. */
 mq_status moe_layer_forward(const mq_act* x, const mq_router* router, const mq_expert_pool* pool,
                             const mq_shared* shared, mq_act* out, const mq_opts* opts, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call as moe_layer_forward, with the same kernels and results, but its
+ * scratch is a fixed array in device memory owned by the library instead of
+ * a caller workspace (opts->workspace and opts->workspace_bytes are
+ * ignored).  It allocates nothing: no hipMalloc, hipFree or allocating
+ * library call.
+ *   - Limit: the call's scratch (mq_workspace_bytes for its token count)
+ *     must fit mq_noalloc_scratch_bytes() = 40 MiB, every call of up to 128
+ *     tokens of the Gemma-shaped layer; larger calls return
+ *     MQ_ERR_TOO_LARGE before anything is enqueued.
+ *   - Each device holds its own copy of the array from the library's first
+ *     call on it until the process ends.  The first call on a device clears
+ *     it on `stream` and must not be under stream capture
+ *     (MQ_ERR_UNSUPPORTED); later calls may be captured.
+ *   - Every call on one device shares that device's array, which keeps the
+ *     last call's state: calls that may overlap on one device (other streams,
+ *     other threads) race and give wrong results; serialise them.
+ *   - Errors: as moe_layer_forward; the error bits of mq_workspace_errors
+ *     are not reachable for this scratch. */
+mq_status moe_layer_forward_noalloc(const mq_act* x, const mq_router* router, const mq_expert_pool* pool,
+                                    const mq_shared* shared, mq_act* out, const mq_opts* opts, void* stream);
+
+/* Bytes of the static scratch behind moe_layer_forward_noalloc. */
+size_t mq_noalloc_scratch_bytes(void);
 
 /* Device scratch of one moe_stack_forward call over these n_layers layers
  * (HOST arrays of n_layers descriptors; shared NULL or n_layers entries).

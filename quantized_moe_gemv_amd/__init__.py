@@ -26,13 +26,14 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 MQ_OK, MQ_ERR_NULL, MQ_ERR_SHAPE, MQ_ERR_ALIGN = 0, -1, -2, -3
 MQ_ERR_UNSUPPORTED, MQ_ERR_WORKSPACE, MQ_ERR_HIP, MQ_ERR_BUFFER = -4, -5, -6, -7
+MQ_ERR_TOO_LARGE = -8
 LAYOUT_CANONICAL, LAYOUT_DEV_V1 = 0, 1
 DTYPE_BF16, DTYPE_F32 = 0, 1
 PATHS = {"auto": 0, "gemv": 1, "grouped": 2, "fused": 3}
 GROUP = 64
 EXPORTS = ["moe_layer_forward", "mq_workspace_bytes", "moe_stack_forward", "mq_stack_workspace_bytes", "mq_workspace_errors", "mq_rmsnorm", "mq_packed_bytes", "mq_pool_layout",
            "mq_pack", "mq_unpack", "mq_debug_unpack_codes", "mq_debug_dequant", "mq_stream_read",
-           "mq_qgemv", "mq_qgemv_workspace_bytes",
+           "moe_layer_forward_noalloc", "mq_noalloc_scratch_bytes", "mq_qgemv", "mq_qgemv_workspace_bytes",
            "mq_route", "mq_route_workspace_bytes", "mq_lfu_state_bytes", "mq_lfu_init", "mq_lfu_plan",
            "mq_status_str"]
 
@@ -114,6 +115,7 @@ _sig = {
     "mq_debug_unpack_codes": (ctypes.c_int, [_P, _P, _P]),
     "mq_debug_dequant": (ctypes.c_int, [_P, _P, _P]),
     "mq_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, _P, ctypes.c_int32, _P]),
+    "moe_layer_forward_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P]),
     "mq_qgemv_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32]),
     "mq_route_workspace_bytes": (ctypes.c_size_t, [_P, ctypes.c_int32]),
     "mq_route": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -121,6 +123,7 @@ _sig = {
     "mq_lfu_init": (ctypes.c_int, [_P, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32]),
     "mq_lfu_plan": (ctypes.c_int, [_P, ctypes.c_size_t, _P, ctypes.c_int32, _P, _P, _P, _P]),
     "mq_qgemv": (ctypes.c_int, [_P, _P, _P, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]),
+    "mq_noalloc_scratch_bytes": (ctypes.c_size_t, []),
     "mq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
 }
 for _name, (_res, _args) in _sig.items():
@@ -332,6 +335,29 @@ def moe_layer_forward(layer: DeviceLayer, x: torch.Tensor, out: Optional[torch.T
                                 _ref(layer.shared), ctypes.byref(oa), ctypes.byref(opts), _stream_handle(stream))
     _check(st, "moe_layer_forward")
     return out
+
+
+def moe_layer_forward_noalloc(layer: DeviceLayer, x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                              path: str = "auto", out_dtype=torch.bfloat16, topk_ids: Optional[torch.Tensor] = None,
+                              topk_w: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
+                              stream=None, input_rmsnorm_eps: float = 0.0) -> torch.Tensor:
+    """moe_layer_forward on the library's fixed device scratch (no workspace).
+    ``out`` must be given by callers that cannot allocate."""
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty((T, layer.hidden), dtype=out_dtype, device=x.device)
+    xa, oa = _act(x), _act(out)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    opts = MqOpts(PATHS[path], ptr(topk_ids), ptr(topk_w), ptr(logits), None, 0, float(input_rmsnorm_eps), None)
+    st = _lib.moe_layer_forward_noalloc(ctypes.byref(xa), ctypes.byref(layer.router), ctypes.byref(layer.pool),
+                                        _ref(layer.shared), ctypes.byref(oa), ctypes.byref(opts),
+                                        _stream_handle(stream))
+    _check(st, "moe_layer_forward_noalloc")
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(_lib.mq_noalloc_scratch_bytes())
 
 
 class Stack:

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/moegemv.h"
 #include "layout.h"
@@ -558,6 +559,76 @@ extern "C" mq_status moe_layer_forward(const mq_act* x, const mq_router* router,
     return layer_forward(x, router, pool, shared, out, opts, opts->workspace, opts->workspace_bytes, stream);
 }
 
+// ---------------------------------------------------------------- allocation-free entry point
+//
+// moe_layer_forward_noalloc runs the same kernels on a fixed scratch array
+// in device memory instead of a caller workspace, for callers that cannot
+// allocate.  Each device that the library runs on holds its own copy of
+// `scratch` until the process ends.  In host code the array's name only
+// stands for the symbol: its device address comes from hipGetSymbolAddress,
+// taken once per device with that device current, and only that address is
+// ever passed to kernels.
+
+constexpr size_t kScratchBytes = (size_t)40 << 20;   // every call of up to 128 tokens of the Gemma-shaped layer
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];     // device address of `scratch`, per device
+bool g_scratch_clear[kMaxDevices];    // cleared once before its first use
+}  // namespace
+
+__global__ void k_zero_fill(uint4* p, int64_t n16) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = make_uint4(0, 0, 0, 0);
+}
+
+// The current device's scratch address; on the first call on a device the
+// array is zero-filled on `s` (a fill kernel, never a memset node).  That
+// first call must not be under stream capture: a captured clear would run
+// again at every replay and reset the state that later calls depend on.
+static mq_status device_scratch(hipStream_t s, void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MQ_ERR_HIP;
+    if (dev >= kMaxDevices) return MQ_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MQ_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    if (!g_scratch_clear[dev]) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(s, &cs) != hipSuccess) return MQ_ERR_HIP;
+        if (cs != hipStreamCaptureStatusNone) return MQ_ERR_UNSUPPORTED;
+        hipLaunchKernelGGL(k_zero_fill, dim3(1024), dim3(256), 0, s, (uint4*)g_scratch_ptr[dev],
+                           (int64_t)(kScratchBytes / 16));
+        if (hipGetLastError() != hipSuccess) return MQ_ERR_HIP;
+        g_scratch_clear[dev] = true;
+    }
+    *out = g_scratch_ptr[dev];
+    return MQ_OK;
+}
+
+extern "C" size_t mq_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+extern "C" mq_status moe_layer_forward_noalloc(const mq_act* x, const mq_router* router,
+                                               const mq_expert_pool* pool, const mq_shared* shared, mq_act* out,
+                                               const mq_opts* opts, void* stream) {
+    if (!x || !out || !opts) return MQ_ERR_NULL;
+    if (x->tokens == 0) return layer_forward(x, router, pool, shared, out, opts, nullptr, 0, stream);
+    const size_t need = mq_workspace_bytes(router, pool, shared, x->tokens > 0 ? x->tokens : 1);
+    if (need == 0) return layer_forward(x, router, pool, shared, out, opts, nullptr, 0, stream);
+    if (need > kScratchBytes) return MQ_ERR_TOO_LARGE;
+    (void)hipGetLastError();
+    void* ws = nullptr;
+    const mq_status st = device_scratch((hipStream_t)stream, &ws);
+    if (st != MQ_OK) return st;
+    return layer_forward(x, router, pool, shared, out, opts, ws, kScratchBytes, stream);
+}
+
 extern "C" size_t mq_stack_workspace_bytes(const mq_router* routers, const mq_expert_pool* pools,
                                            const mq_shared* shared, int32_t n_layers) {
     Sizes z;
@@ -869,6 +940,7 @@ extern "C" const char* mq_status_str(mq_status s) {
         case MQ_ERR_WORKSPACE: return "workspace missing or too small";
         case MQ_ERR_HIP: return "HIP runtime error";
         case MQ_ERR_BUFFER: return "host buffer too small";
+        case MQ_ERR_TOO_LARGE: return "the call needs more scratch than the fixed static buffer holds";
     }
     return "unknown status";
 }
