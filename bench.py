@@ -27,6 +27,8 @@ Profiling helpers (not part of the default run):
                          known size, for rocprofv3 counter runs;
   --profile prefill      runs 128-token prefill calls (Zipf-skewed routing)
                          back to back, for counter runs on the grouped kernels;
+  --profile large        runs 4096-token prefill calls (Zipf-skewed routing)
+                         back to back, for matrix-core counter runs;
   --traffic-summary F W  turns the FETCH_SIZE / WRITE_SIZE counter CSVs of
                          those runs into the traffic summary under profiles/;
   --prefill-summary F W S  turns FETCH_SIZE / WRITE_SIZE counter CSVs and the
@@ -300,6 +302,28 @@ def profile_prefill(args):
     log("profile run done: %d prefill calls of %d tokens" % (args.steps, T))
 
 
+def profile_large(args):
+    """Back-to-back 4096-token prefill calls on one layer."""
+    import torch
+    import qmoe_synth as S
+    import quantized_moe_gemv_amd as M
+    torch.cuda.set_device(0)
+    cfg, seed, T = S.CONFIGS["decode"], S.SEEDS["stack30"], 4096
+    layers = build_layers(M, S, cfg, seed, 1, host_threads())
+    dev = layers[0].with_logit_bias(torch.from_numpy(S.zipf_logit_bias(seed, 0, cfg.num_experts)).cuda())
+    xl = torch.from_numpy(S.make_tokens(seed, T, cfg.hidden, batch=4).view(np.int16)).view(torch.bfloat16).cuda()
+    ws = dev.new_workspace(T)
+    out = torch.empty((T, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+    for i in range(args.steps):
+        M.moe_layer_forward(dev, xl, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        log("large call %d done" % i)
+    errs = M.workspace_errors(ws)
+    if errs:
+        raise SystemExit("prefill4096: workspace error bits 0x%x" % errs)
+    log("profile run done: %d prefill calls of %d tokens" % (args.steps, T))
+
+
 def read_counter(path, counter):
     """Per-dispatch values of `counter` for the decode kernel and the copy kernel."""
     dec, cop = [], []
@@ -441,7 +465,7 @@ def main():
     ap.add_argument("--no-large", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", default="auto", choices=["auto", "fused", "gemv", "grouped"])
-    ap.add_argument("--profile", choices=["decode", "prefill"])
+    ap.add_argument("--profile", choices=["decode", "prefill", "large"])
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--stats-summary", nargs=2, metavar=("STATS_CSV", "BENCH_JSON"))
     ap.add_argument("--prefill-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "STATS_CSV"))
@@ -464,6 +488,9 @@ def main():
         return
     if args.profile == "prefill":
         profile_prefill(args)
+        return
+    if args.profile == "large":
+        profile_large(args)
         return
 
     import torch

@@ -32,6 +32,7 @@ int head_groups(int rows);
 mq_status launch_head(const HeadArgs& a, int32_t* argmax, hipStream_t s);
 mq_status launch_grouped(const Plan& p, hipStream_t s);
 bool grouped_ok(int H, int I, int64_t T, int rows_per_token);
+int grouped_shared_rows(int ntile, int n_vs);
 }  // namespace mq
 
 using namespace mq;
@@ -467,6 +468,7 @@ static mq_status layer_forward(const mq_act* x, const mq_router* router, const m
     p.max_tiles = z.max_tiles;
     p.ntile = z.ntile;
     p.n_vs = z.n_vs;
+    p.n_vs_dn = grouped_shared_rows(z.ntile, z.n_vs);
 
     fill_fused(p, z, ws);
 

@@ -479,173 +479,208 @@ __device__ __forceinline__ _Float16 act_store(_Float16 h, int c) { return (c & 2
 // every token with weight 1, so it fills the machine together with the
 // routed work.  The schedule puts the heaviest chunks first.
 //
-// Up to 32 tokens the loop is bound by load latency: the four waves split
-// the column groups (gate/up) or own 16 rows each over an operand staged
-// once (down), keep several groups of weights in flight and take no
-// workgroup barrier in the loop.  With more tokens the token operand is
-// staged in LDS a batch of column groups at a time for the whole chunk, and
-// each dequantised weight fragment feeds the MFMAs of all the chunk's
-// 16-token tiles (wave ms owns rows 16 ms .. 16 ms + 15 of the tile).
-constexpr int kBigKB = 2;                     // column groups per staged batch (gate/up)
-constexpr int kDnKB = 2;                      // column groups per staged batch (down)
+// Up to kSmallTokens tokens the loop is bound by load latency: the four
+// waves split the column groups (gate/up) or own 16 rows each over an
+// operand staged once (down), keep several groups of weights in flight and
+// take no workgroup barrier in the loop.  With more tokens the token operand
+// and the weights pass through a ring of LDS stages (below), and each
+// dequantised weight fragment feeds the MFMAs of all the chunk's 16-token
+// tiles (wave ms owns rows 16 ms .. 16 ms + 15 of each weight tile).
 constexpr int kDnTiles = 4;                   // 64-row output tiles per down workgroup
+// 64-row tiles of gate and of up per big gate/up workgroup: two for chunks
+// of 128 tokens (the chunk's tokens are then read once per two row tiles),
+// one for chunks of up to 64, whose calls have too few big units to fill
+// the machine with half the workgroups
+__host__ __device__ constexpr int gu_tiles(int MT) { return MT > 4 ? 2 : 1; }
 
-template <int KB>
-constexpr int pitch_of() { return KB * 64 + 8; }   // LDS row pitch in halves (rows fall on different banks)
+// ---- units of more than kSmallTokens tokens: a ring of kRing LDS stages,
+// one 64-column group each, filled by direct global -> LDS loads
+// (global_load_lds_dwordx4: lane i's 16 bytes land at the wave-uniform base
+// in M0 plus 16 i).  A stage holds 2 NTT token fragments of 1 KB (fragment
+// 2t + h: lane l's 16 bytes are token 16t + l % 16, columns 32h + 8 (l / 16)
+// .. +7 of the group, the B operand of v_mfma_f32_16x16x32_f16 read at 16 l,
+// which no two lanes of a pass share a bank for), then the NM weight tiles'
+// codes (2 KB each) and their scale|bias words (256 B each, in a 1 KB
+// slot).  The compiler does not see these loads, so their waits are
+// explicit: stage g + kRing - 1 goes out after the barrier of stage g, and
+// before that barrier each wave waits until only its loads of the later
+// stages are outstanding (a fixed count per wave and stage; wave 0 also
+// loads the scale|bias slot).  No other vector-memory operation is issued
+// inside the loop.
+constexpr int kRing = 3;
 
-template <int NM, int KB>
-struct WLoads {
-    uint2 c[NM][KB];
-    uint32_t s[NM][KB];
-};
+__host__ __device__ constexpr int ring_stage_bytes(int MT, int NM) { return (2 * MT + 2 * NM + 1) * 1024; }
 
-// Weight words of column groups g0 .. g0+KB-1.  A group past the end is
-// read from group G-1 (in bounds, no load is predicated); the multiply
-// forces its scale and bias to zero, so its fragment is exactly zero.
-template <int NM, int KB>
-__device__ __forceinline__ void w_load(WLoads<NM, KB>& L, const uint8_t* const* wbase, const uint8_t* const* sbase,
-                                       int g0, int G) {
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One direct load of 16 bytes per lane into LDS at lds_base + 16 lane; M0
+// takes the base (one wait state between the M0 write and the load).
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds_base)
+                 : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are
+// outstanding (expcnt and lgkmcnt left alone).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt has six bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait until the loads of the oldest stage in flight have landed, with
+// `ahead` (0 .. kRing - 2) later stages of N loads each still outstanding.
+template <int N>
+__device__ __forceinline__ void wait_stages(int ahead) {
+    static_assert(kRing >= 2 && kRing <= 4, "ring of 2 to 4 stages");
+    if (kRing > 3 && ahead >= 2)
+        wait_vm<(kRing > 3 ? 2 : 0) * N>();
+    else if (kRing > 2 && ahead >= 1)
+        wait_vm<(kRing > 2 ? 1 : 0) * N>();
+    else
+        wait_vm<0>();
+}
+
+// Token fragment of this wave's i-th fragment load.
+template <int NTT>
+__device__ __forceinline__ int ring_frag(int wave, int i) { return min(wave + 4 * i, 2 * NTT - 1); }
+
+// Weight tile m: row tile m % RT of matrix m / RT, at base + (m % RT)
+// rstride + (m / RT) mstride; row tiles from nrt on repeat row tile nrt - 1
+// (their results are dropped).
+template <int RT>
+__device__ __forceinline__ const uint8_t* ring_wtile(const uint8_t* base, int64_t rstride, int64_t mstride, int nrt,
+                                                     int m) {
+    return base + min(m % RT, nrt - 1) * rstride + (m / RT) * mstride;
+}
+
+// The loads of group g into the stage at LDS address st.  Wave w takes
+// token fragments w, w + 4, ... (clamped: a repeated fragment rewrites the
+// same bytes with the same values) and code kilobytes w, w + 4, ...
+// xsrc[i]: this lane's source of fragment ring_frag(wave, i) in group 0;
+// xoff: halves from there to the group's columns.
+template <int NM, int NTT, int RT>
+__device__ __forceinline__ void ring_issue(const uint8_t* base, int64_t rstride, int64_t mstride, int nrt, int g,
+                                           const _Float16* const* xsrc, int64_t xoff, uint32_t st, int wave,
+                                           int lane) {
 #pragma unroll
-    for (int u = 0; u < KB; ++u) {
-        const int g = min(g0 + u, G - 1);
+    for (int i = 0; i < (NTT + 1) / 2; ++i) lds_dma16(xsrc[i] + xoff, st + ring_frag<NTT>(wave, i) * 1024);
+    const uint32_t cw = st + 2 * NTT * 1024;
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            L.c[m][u] = *(const uint2*)(wbase[m] + (int64_t)g * kBlk4);
-            L.s[m][u] = *(const uint32_t*)(sbase[m] + (int64_t)g * kBlk4);
-        }
+    for (int i = 0; i < NM / 2; ++i) {
+        const int q = wave + 4 * i;
+        lds_dma16(ring_wtile<RT>(base, rstride, mstride, nrt, q >> 1) + (int64_t)g * kBlk4 + (q & 1) * 1024 + lane * 16,
+                  cw + q * 1024);
+    }
+    if (wave == 0) {
+        const int m = min(lane >> 4, NM - 1);
+        lds_dma16(ring_wtile<RT>(base, rstride, mstride, nrt, m) + (int64_t)g * kBlk4 + kCodes4 + (lane & 15) * 16,
+                  cw + 2 * NM * 1024);
     }
 }
 
-// Token-operand pieces (16 bytes) of one batch held by this thread: piece i
-// is row tid / (8 KB) + (32 / KB) i, columns (tid % (8 KB)) * 8 .. + 7 of the
-// batch.  Rows past the chunk repeat its last row and groups past the end
-// repeat group G-1 (their weights are zero), so every load is in bounds and
-// unmasked.
-template <int NTT, int KB>
-struct XLoads {
-    u32x4_t v[NTT * KB / 2];
-};
-
-template <int NTT, int KB>
-__device__ __forceinline__ void x_load(XLoads<NTT, KB>& X, const _Float16* src, int64_t stride, const int* rows,
-                                       int count, int g0, int G) {
-    const int q = threadIdx.x % (8 * KB), g = min(g0 + (q >> 3), G - 1);
-    const int col = g * 64 + (q & 7) * 8;
-#pragma unroll
-    for (int i = 0; i < NTT * KB / 2; ++i) {
-        const int n = min((int)threadIdx.x / (8 * KB) + (32 / KB) * i, count - 1);
-        X.v[i] = *(const u32x4_t*)(src + (int64_t)rows[n] * stride + col);
-    }
-}
-
-template <int NTT, int KB, int P>
-__device__ __forceinline__ void x_store(const XLoads<NTT, KB>& X, _Float16 (*xs)[P]) {
-    const int q = threadIdx.x % (8 * KB);
-#pragma unroll
-    for (int i = 0; i < NTT * KB / 2; ++i)
-        *(u32x4_t*)&xs[threadIdx.x / (8 * KB) + (32 / KB) * i][q * 8] = X.v[i];
-}
-
-template <int NM, int NTT, int KB, int P, int MT>
-__device__ __forceinline__ void w_mma(const WLoads<NM, KB>& L, _Float16 (*xs)[P], float4_t (*acc)[MT], int lane,
-                                      int g0, int G) {
-    const int kb = lane >> 4, n = lane & 15;
-#pragma unroll
-    for (int u = 0; u < KB; ++u) {
-        half8_t a0[NM], a1[NM];
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            const Sb16 k = sb16(g0 + u < G ? L.s[m][u] : 0u);
-            a0[m] = dequant8s(L.c[m][u].x, k);
-            a1[m] = dequant8s(L.c[m][u].y, k);
-        }
-#pragma unroll
-        for (int t = 0; t < NTT; ++t) {
-            const half8_t b0 = *(const half8_t*)&xs[16 * t + n][64 * u + 8 * kb];
-            const half8_t b1 = *(const half8_t*)&xs[16 * t + n][64 * u + 32 + 8 * kb];
-#pragma unroll
-            for (int m = 0; m < NM; ++m) {
-                acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[m], b0, acc[m][t], 0, 0, 0);
-                acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1[m], b1, acc[m][t], 0, 0, 0);
-            }
-        }
-    }
-}
-
-// One row tile of a staged item over all G column groups: acc[m][t] holds
-// rows 16 ms + 4 (lane / 16) + i, token 16 t + lane % 16 of matrix m.
-// KB column groups per batch; NTT > 4 halves the batch to keep the
-// prefetched token rows within the register budget.
-template <int NM, int NTT, int KBM, int MT>
-__device__ __forceinline__ void gg_tile_n(const uint8_t* const* tiles, int G, const _Float16* src, int64_t stride,
-                                          const int* rows, int count, _Float16 (*xs)[pitch_of<KBM>()],
-                                          float4_t (*acc)[MT]) {
-    constexpr int KB = NTT <= 4 ? KBM : (KBM < 2 ? KBM : 2);
-    const int ms = wave_id(), lane = threadIdx.x & 63;
-    const uint8_t* wbase[NM];
-    const uint8_t* sbase[NM];
+// The multiplies of one stage: wave ms's weight rows 16 ms .. +15 of every
+// tile (A operands dequantised once, fp16) times all 2 NTT token fragments.
+template <int NM, int NTT, int MT>
+__device__ __forceinline__ void ring_mma(const char* st, float4_t (*acc)[MT], int ms, int lane) {
+    const char* cw = st + 2 * NTT * 1024;
+    const char* sbw = cw + 2 * NM * 1024;
+    half8_t a0[NM], a1[NM];
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-        wbase[m] = tiles[m] + ((ms >> 1) * 64 + lane) * 16 + 8 * (ms & 1);
-        sbase[m] = tiles[m] + kCodes4 + (lane & 15) * 16 + 4 * ms;
+        const uint2 c = *(const uint2*)(cw + m * 2048 + ((ms >> 1) * 64 + lane) * 16 + 8 * (ms & 1));
+        const Sb16 k = sb16(*(const uint32_t*)(sbw + m * 256 + (lane & 15) * 16 + 4 * ms));
+        a0[m] = dequant8s(c.x, k);
+        a1[m] = dequant8s(c.y, k);
     }
-    WLoads<NM, KB> A, B;
-    XLoads<NTT, KB> X;
-    x_load(X, src, stride, rows, count, 0, G);
-    w_load(A, wbase, sbase, 0, G);
-    // The loads for the batch after the last one re-read (clamped) groups
-    // just read, which keeps every load unconditional.  sched_barrier keeps
-    // the compiler from sinking the prefetch towards its use.
-    for (int g0 = 0;; g0 += 2 * KB) {
-        x_store(X, xs);
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-        x_load(X, src, stride, rows, count, g0 + KB, G);
-        w_load(B, wbase, sbase, g0 + KB, G);
-        __builtin_amdgcn_sched_barrier(0);
-        w_mma<NM, NTT, KB, pitch_of<KBM>(), MT>(A, xs, acc, lane, g0, G);
-        __syncthreads();
-        if (g0 + KB >= G) break;
-        x_store(X, xs);
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-        x_load(X, src, stride, rows, count, g0 + 2 * KB, G);
-        w_load(A, wbase, sbase, g0 + 2 * KB, G);
-        __builtin_amdgcn_sched_barrier(0);
-        w_mma<NM, NTT, KB, pitch_of<KBM>(), MT>(B, xs, acc, lane, g0 + KB, G);
-        __syncthreads();
-        if (g0 + 2 * KB >= G) break;
+#pragma unroll
+    for (int t = 0; t < NTT; ++t) {
+        const half8_t b0 = *(const half8_t*)(st + (2 * t) * 1024 + lane * 16);
+        const half8_t b1 = *(const half8_t*)(st + (2 * t + 1) * 1024 + lane * 16);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[m], b0, acc[m][t], 0, 0, 0);
+            acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1[m], b1, acc[m][t], 0, 0, 0);
+        }
     }
 }
 
-// Dispatch on the chunk's 16-token tiles (1 .. MT) so that every MFMA
-// sequence is straight-line code.
-template <int NM, int KBM, int MT>
-__device__ __forceinline__ void gg_tile(const uint8_t* const* tiles, int G, const _Float16* src, int64_t stride,
-                                        const int* rows, int count, _Float16 (*xs)[pitch_of<KBM>()],
-                                        float4_t (*acc)[MT]) {
+// NM weight tiles (ring_wtile) times the chunk's tokens over G column
+// groups: acc[m][t] holds rows 16 ms + 4 (lane / 16) + i of tile m, token
+// 16 t + lane % 16.  rows[n]: source row of chunk token n (n < count).
+// lds: kRing stages of ring_stage_bytes(MT, NM).  Starts and ends with the
+// ring unused (the caller's LDS is free before and after).
+template <int NM, int RT, int NTT, int MT>
+__device__ __forceinline__ void ring_tile_n(const uint8_t* base, int64_t rstride, int64_t mstride, int nrt, int G,
+                                            int ksplit, int64_t kjump, const _Float16* src, int64_t stride,
+                                            const int* rows, int count, char* lds, float4_t (*acc)[MT]) {
+    constexpr int kSt = ring_stage_bytes(MT, NM);
+    constexpr int kOps = (NTT + 1) / 2 + NM / 2;   // loads per wave and stage (wave 0: one more)
+    const int ms = wave_id(), lane = threadIdx.x & 63;
+    const uint32_t l0 = lds_addr(lds);
+    const _Float16* xsrc[(NTT + 1) / 2];
+#pragma unroll
+    for (int i = 0; i < (NTT + 1) / 2; ++i) {
+        const int f = ring_frag<NTT>(ms, i), t = f >> 1, h = f & 1;
+        xsrc[i] = src + (int64_t)rows[min(16 * t + (lane & 15), count - 1)] * stride + 32 * h + 8 * (lane >> 4);
+    }
+#pragma unroll
+    for (int g = 0; g < kRing - 1; ++g)
+        if (g < G)
+            ring_issue<NM, NTT, RT>(base, rstride, mstride, nrt, g, xsrc, g * 64 + (g / ksplit) * kjump, l0 + g * kSt,
+                                    ms, lane);
+    for (int g = 0; g < G; ++g) {
+        // outstanding: stages g .. g + ahead; wait for stage g alone
+        const int ahead = min(kRing - 2, G - 1 - g);
+        if (ms == 0)
+            wait_stages<kOps + 1>(ahead);
+        else
+            wait_stages<kOps>(ahead);
+        __syncthreads();
+        if (g + kRing - 1 < G) {
+            const int gi = g + kRing - 1;
+            ring_issue<NM, NTT, RT>(base, rstride, mstride, nrt, gi, xsrc, gi * 64 + (gi / ksplit) * kjump,
+                                    l0 + (gi % kRing) * kSt, ms, lane);
+        }
+        ring_mma<NM, NTT, MT>(lds + (g % kRing) * kSt, acc, ms, lane);
+    }
+    __syncthreads();
+}
+
+template <int NM, int RT, int MT>
+__device__ __forceinline__ void ring_tile(const uint8_t* base, int64_t rstride, int64_t mstride, int nrt, int G,
+                                          int ksplit, int64_t kjump, const _Float16* src, int64_t stride,
+                                          const int* rows, int count, char* lds, float4_t (*acc)[MT]) {
+#define MQ_RING(N) \
+    ring_tile_n<NM, RT, N, MT>(base, rstride, mstride, nrt, G, ksplit, kjump, src, stride, rows, count, lds, acc)
     switch ((count + 15) / 16) {
-        case 1: gg_tile_n<NM, 1, KBM, MT>(tiles, G, src, stride, rows, count, xs, acc); break;
-        case 2: gg_tile_n<NM, 2, KBM, MT>(tiles, G, src, stride, rows, count, xs, acc); break;
-        case 3: gg_tile_n<NM, 3, KBM, MT>(tiles, G, src, stride, rows, count, xs, acc); break;
+        case 1: MQ_RING(1); break;
+        case 2: MQ_RING(2); break;
+        case 3: MQ_RING(3); break;
         default:
             if constexpr (MT <= 4) {
-                gg_tile_n<NM, 4, KBM, MT>(tiles, G, src, stride, rows, count, xs, acc);
+                MQ_RING(4);
             } else {
                 switch ((count + 15) / 16) {
-                    case 4: gg_tile_n<NM, 4, KBM, MT>(tiles, G, src, stride, rows, count, xs, acc); break;
-                    case 5: gg_tile_n<NM, 5, KBM, MT>(tiles, G, src, stride, rows, count, xs, acc); break;
-                    case 6: gg_tile_n<NM, 6, KBM, MT>(tiles, G, src, stride, rows, count, xs, acc); break;
-                    case 7: gg_tile_n<NM, 7, KBM, MT>(tiles, G, src, stride, rows, count, xs, acc); break;
-                    default: gg_tile_n<NM, 8, KBM, MT>(tiles, G, src, stride, rows, count, xs, acc); break;
+                    case 4: MQ_RING(4); break;
+                    case 5: MQ_RING(5); break;
+                    case 6: MQ_RING(6); break;
+                    case 7: MQ_RING(7); break;
+                    default: MQ_RING(8); break;
                 }
             }
     }
+#undef MQ_RING
 }
 
-// The work item of this workgroup: blockIdx.y indexes the schedule.
-// Experts E .. E+n_vs-1 are the shared expert's virtual experts.
+// The work item of this workgroup: a schedule entry (chunk) and a row tile
+// (gate/up) or a run of kDnTiles row tiles (down).  Experts E .. E+n_vs-1
+// are the shared expert's virtual experts.
 struct Item {
+    int rt;             // row tile (gate/up) or first row tile (down)
+    int ntiles;         // 64-row tiles of the item's matrices
     int big;            // the unit takes the dequantised-weight path
     int ntt;            // 16-token tiles of the chunk
     int count;          // tokens of the chunk
@@ -655,22 +690,44 @@ struct Item {
     int G;              // column groups of the operand
     int64_t rstride;    // bytes from one 64-row tile of the matrices to the next
     const uint8_t* w[2];
+    int ksplit;         // operand rows jump by kjump halves every ksplit column groups
+    int64_t kjump;      //   (the shared expert's down over all its columns), else ksplit = G
 };
 
-// The matrices of the item's row tile rt and its tokens, from the schedule
+// Grid position of this workgroup in a grid (nx, ny) with ny a multiple of
+// 8.  Workgroups go to the eight XCDs round robin by linear index, so XCD x
+// runs linear indices x, x + 8, ...; its j-th one takes chunk
+// 8 (j / nx) + x and row position j % nx.  Every row position of a chunk
+// then runs on one XCD, whose L2 serves the chunk's token rows to all of
+// them, and the chunks keep their heaviest-first order across the XCDs.
+// (A bijection whatever the dispatch order: only speed depends on it.)
+struct GridPos {
+    int rx, chunk;
+};
+__device__ __forceinline__ GridPos grid_pos() {
+    const int nx = gridDim.x, L = blockIdx.y * nx + blockIdx.x, j = L >> 3;
+    return {j % nx, (j / nx) * 8 + (L & 7)};
+}
+
+// The matrices of the item's row tile and its tokens, from the schedule
 // entry alone.  Returns false when the workgroup has nothing to do.
-__device__ __forceinline__ bool gg_item(const Plan& p, bool down, int rt, Item* it) {
-    if ((int)blockIdx.y >= *p.nsched) return false;
-    const int2 sc = p.sched[blockIdx.y];
+__device__ __forceinline__ bool gg_item(const Plan& p, bool down, Item* it) {
+    const GridPos gp = grid_pos();
+    if (gp.chunk >= *p.nsched) return false;
+    const int rt = down ? gp.rx * kDnTiles : gp.rx;
+    it->rt = rt;
+    const int2 sc = p.sched[gp.chunk];
     const int ex = sc.x >> 16, c = sc.x & 0xFF;
     it->big = (sc.x >> 12) & 1;
     it->ntt = (sc.x >> 8) & 0xF;
     it->pos0 = sc.y & 0xFFFFFF;
     it->count = (int)((uint32_t)sc.y >> 24);
     it->tok0 = c * p.ntile;
+    it->kjump = 0;
     if (ex < p.E) {
         it->shared = 0;
         const uint8_t* base = p.pool_base + (int64_t)ex * p.expert_stride;
+        it->ntiles = down ? p.H / 64 : p.I / 64;
         if (down) {
             it->G = p.G_I;
             it->rstride = (int64_t)p.G_I * kBlk4;
@@ -684,7 +741,18 @@ __device__ __forceinline__ bool gg_item(const Plan& p, bool down, int rt, Item* 
     } else {
         const int j = ex - p.E;
         it->shared = 1;
-        if (down) {
+        it->ntiles = down ? p.H / 64 : min(p.I, p.Is - j * p.I) / 64;
+        if (down && p.n_vs_dn == 1 && p.n_vs > 1) {
+            // the first virtual expert's item takes all G_s groups: its
+            // operand rows continue T rows further on every G_I groups
+            if (j > 0) return false;
+            it->G = p.G_s;
+            it->rstride = (int64_t)p.G_s * kBlk4;
+            it->w[0] = it->w[1] = p.sh_down + (int64_t)rt * p.G_s * kBlk4;
+            it->ksplit = p.G_I;
+            it->kjump = (int64_t)p.T * p.I - p.I;
+            return true;
+        } else if (down) {
             it->G = min(p.G_I, p.G_s - j * p.G_I);
             it->rstride = (int64_t)p.G_s * kBlk4;
             it->w[0] = it->w[1] = p.sh_down + ((int64_t)rt * p.G_s + (int64_t)j * p.G_I) * kBlk4;
@@ -696,6 +764,7 @@ __device__ __forceinline__ bool gg_item(const Plan& p, bool down, int rt, Item* 
             it->w[1] = p.sh_up + (int64_t)(j * p.G_I + rt) * p.G_H * kBlk4;
         }
     }
+    it->ksplit = it->G;
     return true;
 }
 
@@ -885,7 +954,7 @@ __device__ __forceinline__ void gu_small_n(const Plan& p, const Item& it, GuW& W
     // place of the staged constants, so the first barrier also waits for
     // every wave's last multiply
     GuRed& red = *(GuRed*)lds;
-    const int c = blockIdx.x * 64 + 16 * w + (lane & 15);   // GeGLU column of this lane
+    const int c = it.rt * 64 + 16 * w + (lane & 15);   // GeGLU column of this lane
 #pragma unroll
     for (int t = 0; t < NTT; ++t) {
         __syncthreads();
@@ -915,53 +984,58 @@ __device__ __forceinline__ void gu_small_n(const Plan& p, const Item& it, GuW& W
         }
     }
     __syncthreads();
-    write_hso(p, it, blockIdx.x, hpart);
+    write_hso(p, it, it.rt, hpart);
 }
 
-// ---- gate/up, units of more than kSmallTokens tokens: x staged in LDS for
-// the whole chunk of up to 16 MT tokens.
+// ---- gate/up, units of more than kSmallTokens tokens: gu_tiles row tiles of
+// gate and of up over the ring, so each staged token fragment feeds
+// 4 gu_tiles multiplies.
 template <int MT>
-using GuXs = _Float16[16 * MT][pitch_of<kBigKB>()];
-
-template <int MT>
-__device__ __forceinline__ void gu_big(const Plan& p, const Item& it, GuXs<MT>& xs, int* rows,
-                                       float2 (*hpart)[128]) {
+__device__ __forceinline__ void gu_big(const Plan& p, const Item& it, char* lds, int* rows, float2 (*hpart)[128]) {
+    constexpr int kGuTiles = gu_tiles(MT);
     const int wave = wave_id(), lane = threadIdx.x & 63;
     if ((int)threadIdx.x < it.count) rows[threadIdx.x] = item_token(p, it, threadIdx.x);
     __syncthreads();
-    float4_t acc[2][MT];
+    const int nrt = min(kGuTiles, it.ntiles - it.rt);
+    float4_t acc[2 * kGuTiles][MT];
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < 2 * kGuTiles; ++m)
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[m][t] = (float4_t){0.f, 0.f, 0.f, 0.f};
-    gg_tile<2, kBigKB, MT>(it.w, it.G, p.x16, p.H, rows, it.count, xs, acc);
-    // rows r0 + i of the GeGLU output; (r0 + i) & 2 == i & 2
-    const int r0 = blockIdx.x * 64 + 16 * wave + 4 * (lane >> 4);
+    ring_tile<2 * kGuTiles, kGuTiles, MT>(it.w[0], it.rstride, it.w[1] - it.w[0], nrt, it.G, it.ksplit, it.kjump,
+                                          p.x16, p.H, rows, it.count, lds, acc);
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-        const int n = 16 * t + (lane & 15);
-        _Float16 h[4], a[4];
-        float hs = 0.f, hn = 0.f;
+    for (int u = 0; u < kGuTiles; ++u) {
+        if (u >= nrt) break;
+        // rows r0 + i of the GeGLU output; (r0 + i) & 2 == i & 2
+        const int r0 = (it.rt + u) * 64 + 16 * wave + 4 * (lane >> 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            h[i] = (_Float16)(gelu_tanh(acc[0][t][i]) * acc[1][t][i]);
-            a[i] = act_store(h[i], i);
-            hs += (float)h[i];
-            hn += -1024.0f * (float)a[i];
+        for (int t = 0; t < MT; ++t) {
+            const int n = 16 * t + (lane & 15);
+            _Float16 h[4], a[4];
+            float hs = 0.f, hn = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                h[i] = (_Float16)(gelu_tanh(acc[u][t][i]) * acc[kGuTiles + u][t][i]);
+                a[i] = act_store(h[i], i);
+                hs += (float)h[i];
+                hn += -1024.0f * (float)a[i];
+            }
+            flag_error(p.f_err, n < it.count && (f16_bad(h[0]) || f16_bad(h[1]) || f16_bad(h[2]) || f16_bad(h[3])),
+                       kErrRange);
+            if (n < it.count) {
+                _Float16* dst = p.hg + (int64_t)(it.pos0 + n) * p.I + r0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[i] = a[i];
+            }
+            hs = sum_kb(hs);
+            hn = sum_kb(hn);
+            if (lane < 16) hpart[wave][n] = make_float2(hs, hn);
         }
-        flag_error(p.f_err, n < it.count && (f16_bad(h[0]) || f16_bad(h[1]) || f16_bad(h[2]) || f16_bad(h[3])),
-                   kErrRange);
-        if (n < it.count) {
-            _Float16* dst = p.hg + (int64_t)(it.pos0 + n) * p.I + r0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dst[i] = a[i];
-        }
-        hs = sum_kb(hs);
-        hn = sum_kb(hn);
-        if (lane < 16) hpart[wave][n] = make_float2(hs, hn);
+        __syncthreads();
+        write_hso(p, it, it.rt + u, hpart);
+        __syncthreads();
     }
-    __syncthreads();
-    write_hso(p, it, blockIdx.x, hpart);
 }
 
 // Gate/up + GeGLU: hg[pos] = gelu(gate x) * (up x) in fp16 (scaled
@@ -974,10 +1048,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT <= 4 ? 3
     __shared__ float2 hpart[4][128];
     __shared__ int rows[128];
     Item it;
-    if (!gg_item(p, false, blockIdx.x, &it)) return;
+    if (!gg_item(p, false, &it)) return;
     const int w = wave_id(), lane = threadIdx.x & 63;
     if (it.big) {
-        gu_big<MT>(p, it, *(GuXs<MT>*)lds, rows, hpart);
+        // gu_tiles row tiles per workgroup: the others of the run have none
+        if (it.rt % gu_tiles(MT) == 0) gu_big<MT>(p, it, lds, rows, hpart);
         return;
     }
     // the chunk's token lookups first, then the first weights, in flight
@@ -1091,20 +1166,24 @@ __device__ __forceinline__ void dn_small_n(const Plan& p, const Item& it, int rt
     }
 }
 
-// ---- down, more than 32 tokens: h staged in LDS kDnKB groups at a time per
-// output tile, for the whole chunk.
+// ---- down, more than kSmallTokens tokens: the kDnTiles output tiles of the
+// workgroup at once over the ring, so each staged token fragment feeds
+// 2 kDnTiles multiplies.
 template <int MT>
-__device__ __forceinline__ void dn_big(const Plan& p, const Item& it, int rt0, int nrt, _Float16* lds, int* rows,
+__device__ __forceinline__ void dn_big(const Plan& p, const Item& it, int rt0, int nrt, char* lds, int* rows,
                                        const float* wrow) {
     const int wave = wave_id(), lane = threadIdx.x & 63;
-    auto xs = (_Float16(*)[pitch_of<kDnKB>()])lds;
-    for (int r = 0; r < nrt; ++r) {
-        float4_t acc[1][MT];
+    float4_t acc[kDnTiles][MT];
 #pragma unroll
-        for (int t = 0; t < MT; ++t) acc[0][t] = (float4_t){0.f, 0.f, 0.f, 0.f};
-        const uint8_t* tiles[1] = {it.w[0] + r * it.rstride};
-        gg_tile<1, kDnKB, MT>(tiles, it.G, p.hg, p.I, rows, it.count, xs, acc);
-        const int r0 = (rt0 + r) * 64 + 16 * wave + 4 * (lane >> 4);
+    for (int m = 0; m < kDnTiles; ++m)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[m][t] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    ring_tile<kDnTiles, kDnTiles, MT>(it.w[0], it.rstride, 0, nrt, it.G, it.ksplit, it.kjump, p.hg, p.I, rows,
+                                      it.count, lds, acc);
+#pragma unroll
+    for (int m = 0; m < kDnTiles; ++m) {
+        if (m >= nrt) break;
+        const int r0 = (rt0 + m) * 64 + 16 * wave + 4 * (lane >> 4);
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
             const int n = 16 * t + (lane & 15);
@@ -1112,7 +1191,7 @@ __device__ __forceinline__ void dn_big(const Plan& p, const Item& it, int rt0, i
                 const float wt = wrow[n];
                 float* dst = p.ysort + (int64_t)(it.pos0 + n) * p.H + r0;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dst[i] = wt * acc[0][t][i];
+                for (int i = 0; i < 4; ++i) dst[i] = wt * acc[m][t][i];
             }
         }
     }
@@ -1123,7 +1202,7 @@ __device__ __forceinline__ void dn_big(const Plan& p, const Item& it, int rt0, i
 __host__ __device__ constexpr size_t dn_small_hs_bytes(int I) { return (size_t)kSmallTokens * (I + 8) * 2; }
 size_t dn_lds_bytes(int I, int MT) {
     const size_t small = dn_small_hs_bytes(I) + (size_t)2 * (I / 64) * 32 * 4;
-    const size_t big = (size_t)16 * MT * pitch_of<kDnKB>() * 2;
+    const size_t big = (size_t)kRing * ring_stage_bytes(MT, kDnTiles);
     return small > big ? small : big;
 }
 
@@ -1135,9 +1214,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT <= 4 ? 3
     extern __shared__ __attribute__((aligned(16))) _Float16 hs[];
     __shared__ float wrow[128];
     __shared__ int rows[128];
-    const int rt0 = blockIdx.x * kDnTiles, nrt = min(kDnTiles, p.H / 64 - rt0);
     Item it;
-    if (!gg_item(p, true, rt0, &it)) return;
+    if (!gg_item(p, true, &it)) return;
+    const int rt0 = it.rt, nrt = min(kDnTiles, p.H / 64 - rt0);
     auto token_rows = [&]() {
         if ((int)threadIdx.x < it.count) {
             wrow[threadIdx.x] = it.shared ? 1.f : p.wts[p.perm[it.pos0 + threadIdx.x]];
@@ -1147,7 +1226,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT <= 4 ? 3
     if (it.big) {
         token_rows();
         __syncthreads();
-        dn_big<MT>(p, it, rt0, nrt, hs, rows, wrow);
+        dn_big<MT>(p, it, rt0, nrt, (char*)hs, rows, wrow);
         return;
     }
     const int ms = wave_id(), lane = threadIdx.x & 63;
@@ -1211,7 +1290,7 @@ __global__ __launch_bounds__(256) void k_gg_combine(Plan p) {
     constexpr int kRb = 8;   // rows per batch of loads
     const int t = blockIdx.x, i = (blockIdx.y * 256 + threadIdx.x) * 4;
     if (i >= p.H) return;    // H % 64 == 0: columns i .. i + 3 all exist
-    const int nr = p.k + p.n_vs;
+    const int nr = p.k + p.n_vs_dn;
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
     for (int j0 = 0; j0 < nr; j0 += kRb) {
         float4 v[kRb];
@@ -1250,7 +1329,7 @@ __global__ __launch_bounds__(256) void k_gg_combine(Plan p) {
 // Dynamic LDS of k_gu: the big path's staged batch, the small path's
 // group constants and its reduction buffer, which reuses their space.
 size_t gu_lds_bytes(int G_H, int MT) {
-    const size_t big = (size_t)16 * MT * pitch_of<kBigKB>() * 2, red = sizeof(GuRed);
+    const size_t big = (size_t)kRing * ring_stage_bytes(MT, 2 * gu_tiles(MT)), red = sizeof(GuRed);
     const size_t c = (size_t)2 * G_H * 32 * 4;
     return big > red ? (big > c ? big : c) : (red > c ? red : c);
 }
@@ -1258,6 +1337,13 @@ size_t gu_lds_bytes(int G_H, int MT) {
 // The schedule holds chunk indices below 256 (T <= 255 * 128) and sorted
 // rows below 2^24, and the LDS of the gate/up and down kernels must fit a
 // workgroup.
+// Shared rows per token of ysort after the down projection.  With chunks of
+// 128 tokens (many chunks per call) one item of each shared chunk runs the
+// down projection over all the shared columns, which saves the other
+// virtual experts' rows of ysort and their reads in the combine; smaller
+// calls keep one item per virtual expert, which shortens their longest item.
+int grouped_shared_rows(int ntile, int n_vs) { return ntile > 64 && n_vs > 1 ? 1 : n_vs; }
+
 bool grouped_ok(int H, int I, int64_t T, int rows_per_token) {
     return T <= 255 * 128 && T * rows_per_token < (1 << 24) && dn_lds_bytes(I, 8) <= 160 * 1024 &&
            gu_lds_bytes(H / 64, 8) + 5 * 1024 <= 160 * 1024;
@@ -1273,8 +1359,9 @@ mq_status launch_gemms(const Plan& p, hipStream_t s) {
     if (dn_lds > 64 * 1024 && hipFuncSetAttribute((const void*)k_dn<MT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                                   (int)dn_lds) != hipSuccess)
         return MQ_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(k_gu<MT>, dim3(p.I / 64, p.max_tiles), dim3(256), gu_lds, s, p);
-    hipLaunchKernelGGL(k_dn<MT>, dim3((p.H / 64 + kDnTiles - 1) / kDnTiles, p.max_tiles), dim3(256), dn_lds, s, p);
+    const int ny = (p.max_tiles + 7) / 8 * 8;   // grid_pos needs a multiple of 8
+    hipLaunchKernelGGL(k_gu<MT>, dim3(p.I / 64, ny), dim3(256), gu_lds, s, p);
+    hipLaunchKernelGGL(k_dn<MT>, dim3((p.H / 64 + kDnTiles - 1) / kDnTiles, ny), dim3(256), dn_lds, s, p);
     return MQ_OK;
 }
 

@@ -112,6 +112,8 @@ struct Plan {
     int t_res_in;          // residual = the layer's input row before the input norm
     float t_eps, t_scalar;
     uint64_t* f_tail;      // single-launch decode: [G_H][8] tagged partial sums of the tail norms
+    int n_vs_dn;           // grouped path: shared rows per token of ysort after the down projection (1 when
+                           // one item of each chunk covers all of the shared expert's columns, else n_vs)
 };
 
 // Arguments of the quantized GEMV head (head.hip).

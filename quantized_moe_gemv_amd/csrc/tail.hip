@@ -61,7 +61,7 @@ __device__ __forceinline__ void tail_rows(const Plan& p) {
             if (p.has_shared) s[m] = ld4(d + (int64_t)(kDownSplits - 1) * p.H);
         } else {
             for (int j = 0; j < p.k; ++j) add4(r[m], ld4(p.ysort + (int64_t)p.inv[t * p.k + j] * p.H + i));
-            for (int j = 0; j < p.n_vs; ++j)
+            for (int j = 0; j < p.n_vs_dn; ++j)
                 add4(s[m], ld4(p.ysort + ((int64_t)p.T * p.k + (int64_t)j * p.T + t) * p.H + i));
         }
         ss += (s[m].x * s[m].x + s[m].y * s[m].y) + (s[m].z * s[m].z + s[m].w * s[m].w);
