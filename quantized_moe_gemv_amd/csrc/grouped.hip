@@ -493,7 +493,7 @@ constexpr int kDnTiles = 4;                   // 64-row output tiles per down wo
 // the machine with half the workgroups
 __host__ __device__ constexpr int gu_tiles(int MT) { return MT > 4 ? 2 : 1; }
 
-// ---- units of more than kSmallTokens tokens: a ring of kRing LDS stages,
+// ---- units of more than kSmallTokens tokens: a ring of LDS stages (kRing),
 // one 64-column group each, filled by direct global -> LDS loads
 // (global_load_lds_dwordx4: lane i's 16 bytes land at the wave-uniform base
 // in M0 plus 16 i).  A stage holds 2 NTT token fragments of 1 KB (fragment
@@ -507,7 +507,9 @@ __host__ __device__ constexpr int gu_tiles(int MT) { return MT > 4 ? 2 : 1; }
 // stages are outstanding (a fixed count per wave and stage; wave 0 also
 // loads the scale|bias slot).  No other vector-memory operation is issued
 // inside the loop.
-constexpr int kRing = 3;
+// Stages: three for 128-token chunks; two for smaller ones, whose smaller
+// ring leaves room for a fourth workgroup per CU.
+__host__ __device__ constexpr int ring_depth(int MT) { return MT > 4 ? 3 : 2; }
 
 __host__ __device__ constexpr int ring_stage_bytes(int MT, int NM) { return (2 * MT + 2 * NM + 1) * 1024; }
 
@@ -515,11 +517,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// One direct load of 16 bytes per lane into LDS at lds_base + 16 lane; M0
-// takes the base (one wait state between the M0 write and the load).
+// One direct load of 16 bytes per lane into LDS at lds_base + 16 lane.  The
+// base goes in M0 as an input operand, so the compiler writes M0 itself;
+// the load needs one wait state after that write.
 __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds_base)
-                 : "memory", "m0");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
 }
 
 // Wait until at most N vector-memory operations of this wave are
@@ -532,7 +535,7 @@ __device__ __forceinline__ void wait_vm() {
 
 // Wait until the loads of the oldest stage in flight have landed, with
 // `ahead` (0 .. kRing - 2) later stages of N loads each still outstanding.
-template <int N>
+template <int N, int kRing>
 __device__ __forceinline__ void wait_stages(int ahead) {
     static_assert(kRing >= 2 && kRing <= 4, "ring of 2 to 4 stages");
     if (kRing > 3 && ahead >= 2)
@@ -610,13 +613,13 @@ __device__ __forceinline__ void ring_mma(const char* st, float4_t (*acc)[MT], in
 // NM weight tiles (ring_wtile) times the chunk's tokens over G column
 // groups: acc[m][t] holds rows 16 ms + 4 (lane / 16) + i of tile m, token
 // 16 t + lane % 16.  rows[n]: source row of chunk token n (n < count).
-// lds: kRing stages of ring_stage_bytes(MT, NM).  Starts and ends with the
+// lds: ring_depth(MT) stages of ring_stage_bytes(MT, NM).  Starts and ends with the
 // ring unused (the caller's LDS is free before and after).
 template <int NM, int RT, int NTT, int MT>
 __device__ __forceinline__ void ring_tile_n(const uint8_t* base, int64_t rstride, int64_t mstride, int nrt, int G,
                                             int ksplit, int64_t kjump, const _Float16* src, int64_t stride,
                                             const int* rows, int count, char* lds, float4_t (*acc)[MT]) {
-    constexpr int kSt = ring_stage_bytes(MT, NM);
+    constexpr int kSt = ring_stage_bytes(MT, NM), kRing = ring_depth(MT);
     constexpr int kOps = (NTT + 1) / 2 + NM / 2;   // loads per wave and stage (wave 0: one more)
     const int ms = wave_id(), lane = threadIdx.x & 63;
     const uint32_t l0 = lds_addr(lds);
@@ -635,9 +638,9 @@ __device__ __forceinline__ void ring_tile_n(const uint8_t* base, int64_t rstride
         // outstanding: stages g .. g + ahead; wait for stage g alone
         const int ahead = min(kRing - 2, G - 1 - g);
         if (ms == 0)
-            wait_stages<kOps + 1>(ahead);
+            wait_stages<kOps + 1, kRing>(ahead);
         else
-            wait_stages<kOps>(ahead);
+            wait_stages<kOps, kRing>(ahead);
         __syncthreads();
         if (g + kRing - 1 < G) {
             const int gi = g + kRing - 1;
@@ -1202,7 +1205,7 @@ __device__ __forceinline__ void dn_big(const Plan& p, const Item& it, int rt0, i
 __host__ __device__ constexpr size_t dn_small_hs_bytes(int I) { return (size_t)kSmallTokens * (I + 8) * 2; }
 size_t dn_lds_bytes(int I, int MT) {
     const size_t small = dn_small_hs_bytes(I) + (size_t)2 * (I / 64) * 32 * 4;
-    const size_t big = (size_t)kRing * ring_stage_bytes(MT, kDnTiles);
+    const size_t big = (size_t)ring_depth(MT) * ring_stage_bytes(MT, kDnTiles);
     return small > big ? small : big;
 }
 
@@ -1329,7 +1332,7 @@ __global__ __launch_bounds__(256) void k_gg_combine(Plan p) {
 // Dynamic LDS of k_gu: the big path's staged batch, the small path's
 // group constants and its reduction buffer, which reuses their space.
 size_t gu_lds_bytes(int G_H, int MT) {
-    const size_t big = (size_t)kRing * ring_stage_bytes(MT, 2 * gu_tiles(MT)), red = sizeof(GuRed);
+    const size_t big = (size_t)ring_depth(MT) * ring_stage_bytes(MT, 2 * gu_tiles(MT)), red = sizeof(GuRed);
     const size_t c = (size_t)2 * G_H * 32 * 4;
     return big > red ? (big > c ? big : c) : (red > c ? red : c);
 }

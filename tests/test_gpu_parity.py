@@ -233,6 +233,30 @@ def test_prefill4096_layer(M, large):
     assert same.sum() >= T - 4 and err <= 1e-2 * rms
 
 
+def test_midsize_128_token_chunks(M):
+    """A mid-size layer past 1024 tokens, so the grouped path runs 128-token
+    chunks: full and partial chunks of routed and shared units, an odd
+    number of 64-row tiles (the last two-tile gate/up workgroup has one), the
+    down projection's four-tile workgroups, and the shared expert's down
+    projection as one item over all its columns (a partial shared chunk
+    too); every routing decision and every output row against the oracle."""
+    cfg = S.LayerConfig(hidden=512, num_experts=16, inter=192, shared_inter=576, top_k=4, tokens=1300, zipf=True,
+                        name="mid-size layer (H512 E16 I192 Is576 k4), 1300 tokens, Zipf routing")
+    host = S.make_layer(cfg, 977)
+    dev = M.DeviceLayer(host)
+    T = cfg.tokens
+    log("mid-size layer T=%d on the grouped path (128-token chunks)" % T)
+    x = S.make_tokens(978, T, cfg.hidden)
+    got = run_gpu(M, dev, x, "grouped")
+    ref = O.forward(host, x, threads=16, dense_experts=False)
+    ok, excused = check_routing(ref, got, cfg.top_k)
+    counts = np.bincount(got["ids"].ravel(), minlength=cfg.num_experts)
+    log("  tokens per expert %d .. %d, near-ties %d" % (counts.min(), counts.max(), excused))
+    assert (counts % 128 != 0).any() and counts.max() > 128   # full and partial chunks
+    rel = check_output(ref, got, ok)
+    log("  max err / RMS = %.3g over %d rows" % (rel, ok.sum()))
+
+
 def test_grouped_matches_gemv_on_prefill(M, prefill):
     host, dev = prefill
     log("prefill layer T=8: grouped vs GEMV path")
