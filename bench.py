@@ -34,6 +34,10 @@ Profiling helpers (not part of the default run):
   --prefill-summary F W S  turns FETCH_SIZE / WRITE_SIZE counter CSVs and the
                          kernel statistics CSV of --profile prefill runs into
                          the per-kernel traffic summary of the grouped path;
+  --counters-summary A B S  turns the two SQ counter passes (COUNTERS_A,
+                         COUNTERS_B) and the kernel statistics of --profile
+                         large runs into the matrix-core/LDS utilisation
+                         table under profiles/;
   --stats-summary S J    turns the kernel statistics CSV of a rocprofv3
                          --kernel-trace --stats run of the default benchmark,
                          and the JSON line that run printed, into the kernel
@@ -63,6 +67,7 @@ DECODE_KERNEL = "k_decode"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_decode_decode_h2816_e128_traffic.txt")
 STATS_FILE = os.path.join(ROOT, "profiles", "kernel_stats_bench_decode_prefill128_stack30_prefill4096.txt")
 PREFILL_FILE = os.path.join(ROOT, "profiles", "grouped_kernels_prefill128_h2816_e128_traffic.txt")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "grouped_kernels_prefill4096_h2816_e128_counters.txt")
 # The copy kernel's FETCH_SIZE reads half its bytes (see the decode traffic summary).
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 COPY_BYTES = 256 << 20       # each direction of the reference copy kernel
@@ -414,6 +419,58 @@ def prefill_summary(fetch_csv, write_csv, stats_csv, out_path):
     print("\n".join(lines))
 
 
+COUNTERS_A = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_LDS_IDX_ACTIVE "
+              "SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_LDS SQ_WAVE_CYCLES GRBM_GUI_ACTIVE")
+COUNTERS_B = ("SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_LDS "
+              "SQ_ACTIVE_INST_VMEM SQ_WAVES GRBM_GUI_ACTIVE")
+
+
+def counters_summary(a_csv, b_csv, stats_csv, out_path):
+    """Matrix-core, VALU and LDS utilisation per grouped-path kernel of the
+    4096-token prefill, from two SQ counter passes (the rocprof derived
+    metrics' formulas, written out)."""
+    vals = {}
+    for path in (a_csv, b_csv):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                vals.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    with open(stats_csv) as f:
+        dur = {r["Name"]: float(r["AverageNs"]) / 1e3 for r in csv.DictReader(f)}
+    simds, cus, xcds = 1024, 256, 8
+    lines = [
+        "# Matrix-core, VALU and LDS utilisation per kernel of the grouped path, 4096-token prefill",
+        "# workload: 4096 tokens, Zipf(1.1) logit bias, H2816 E128 top8 I704 Is2112, one layer",
+        "# commands (run from /tmp with TMPDIR=/tmp; each counter pass in a run of its own):",
+        "#   rocprofv3 --kernel-trace --stats -d <dir> -o st --output-format csv -- python3 <repo>/bench.py --profile large --steps 4",
+        "#   rocprofv3 --pmc %s -d <dir> -o pa --output-format csv -- python3 <repo>/bench.py --profile large --steps 2" % COUNTERS_A,
+        "#   rocprofv3 --pmc %s -d <dir> -o pb --output-format csv -- python3 <repo>/bench.py --profile large --steps 2" % COUNTERS_B,
+        "#   python3 <repo>/bench.py --counters-summary <pa csv> <pb csv> <st_kernel_stats.csv>",
+        "# GRBM_GUI_ACTIVE comes summed over the %d XCDs; one XCD's busy cycles G = value / %d." % (xcds, xcds),
+        "# mfma% = SQ_VALU_MFMA_BUSY_CYCLES / (G * 1024 SIMDs) (a 16x16x32 fp16 MFMA counts 16 cycles: the",
+        "#   2.5 PFLOP/s peak at 2.4 GHz); valu% = SQ_ACTIVE_INST_VALU / (G * 256 CUs); lds% = SQ_LDS_IDX_ACTIVE /",
+        "#   (G * 256); conflict% = SQ_LDS_BANK_CONFLICT / (G * 256); wait% = SQ_WAIT_ANY / SQ_WAVE_CYCLES (wave",
+        "#   time waiting on a counter: memory, LDS or a barrier); issue% = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES.",
+        "",
+        "%-22s %8s %6s %6s %6s %9s %6s %6s %9s %9s %8s" % ("kernel", "avg_us", "mfma%", "valu%", "lds%", "conflict%",
+                                                          "wait%", "issue%", "mfma_M", "valu_M", "lds_M"),
+    ]
+    for name in sorted(vals, key=lambda n: -dur.get(n, next((v for k, v in dur.items() if k.startswith(n.split("(")[0])), 0))):
+        if "mq::" not in name:
+            continue
+        v = {c: float(np.median(x)) for c, x in vals[name].items()}
+        g = v["GRBM_GUI_ACTIVE"] / xcds
+        us = next((d for k, d in dur.items() if k.startswith(name.split("(")[0])), float("nan"))
+        lines.append("%-22s %8.1f %6.1f %6.1f %6.1f %9.1f %6.1f %6.1f %9.2f %9.2f %8.2f" % (
+            name.split("(")[0].replace("void ", "").replace("mq::", ""), us,
+            100 * v["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * simds), 100 * v["SQ_ACTIVE_INST_VALU"] / (g * cus),
+            100 * v["SQ_LDS_IDX_ACTIVE"] / (g * cus), 100 * v["SQ_LDS_BANK_CONFLICT"] / (g * cus),
+            100 * v["SQ_WAIT_ANY"] / v["SQ_WAVE_CYCLES"], 100 * v["SQ_WAIT_INST_ANY"] / v["SQ_WAVE_CYCLES"],
+            v["SQ_INSTS_MFMA"] / 1e6, v["SQ_INSTS_VALU"] / 1e6, v["SQ_INSTS_LDS"] / 1e6))
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def stats_summary(stats_csv, bench_json, out_path):
     with open(stats_csv) as f:
         rows = list(csv.DictReader(f))
@@ -469,6 +526,7 @@ def main():
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--stats-summary", nargs=2, metavar=("STATS_CSV", "BENCH_JSON"))
     ap.add_argument("--prefill-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "STATS_CSV"))
+    ap.add_argument("--counters-summary", nargs=3, metavar=("PASS_A_CSV", "PASS_B_CSV", "STATS_CSV"))
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(args.traffic_summary[0], args.traffic_summary[1], TRAFFIC_FILE)
@@ -478,6 +536,9 @@ def main():
         return
     if args.prefill_summary:
         prefill_summary(*args.prefill_summary, PREFILL_FILE)
+        return
+    if args.counters_summary:
+        counters_summary(*args.counters_summary, COUNTERS_FILE)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: the layer runs on a single MI355X and has no multi-GPU path "
