@@ -963,6 +963,13 @@ __device__ __forceinline__ void decode_layer(const Plan& p, Shared& sh, uint32_t
     issue_loads(p, sh, us, lsh);
     stage_token<TAIL>(p, sh, tl, tag, xraw);
     if (ur.kind == U_ROUTER) run_router(p, sh, ur, lrt, tag);
+    // Units end without a barrier after wave 0 reads their row totals in
+    // sh.red (see run_rh); the next writer of sh.red must follow a barrier.
+    // Every later unit starts with a gather or the ids, which have one, and
+    // the layer ends with one; only a router piece followed by a shared
+    // gate/up unit on one workgroup would not (not so in the present layout,
+    // where router and shared workgroups are disjoint), so take one then.
+    if (ur.kind == U_ROUTER && us.kind == U_SH) __syncthreads();
     if (us.kind == U_SH) run_rh(p, sh, us, lsh, tag);
     if (rh.kind == U_RH || du.nt > 0) fetch_ids(p, sh, tag);
     LoadsN<kItemsD> ld;
