@@ -170,7 +170,7 @@ Carve carve(const Sizes& z, int64_t T) {
     // sized for the smallest chunk so that the carve grows with T whatever
     // chunk size set_tiles picks
     c.sched = take(((size_t)(T * z.k + 31) / 32 + z.E + (size_t)z.n_vs * ((T + 31) / 32)) * 8 + 8);
-    c.nsched = take(4);
+    c.nsched = take(8);
     const size_t rows = T * (z.k + z.n_vs);
     c.hg = take(rows * z.I * 2);
     c.hso = take(rows * z.G_I * 8);

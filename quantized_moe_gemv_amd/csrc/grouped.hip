@@ -56,43 +56,51 @@ __device__ __forceinline__ int block_scan_total(int* buf, int n, int v, int* exc
 // on which chunk of its expert it lands in.
 constexpr int kSmallTokens = 16;
 
-// Schedule entries, heaviest chunks first: the full chunks of every unit
-// (the experts, then the shared expert's virtual experts E .. E+n_vs-1 over
-// all T tokens), then the partial last chunks by decreasing number of
-// 16-token tiles.  Entry .x = unit << 16 | big << 12 | tiles << 8 | chunk
+// Schedule entries: the full chunks of every unit (the experts, then the
+// shared expert's virtual experts E .. E+n_vs-1 over all T tokens), then
+// the partial last chunks by decreasing number of 16-token tiles.  With
+// 128-token chunks the partial chunks of units on the dequantised-weight
+// path come first, then those on the code-operand path: a dequantised-weight
+// chunk streams its whole weight tiles whatever its token count, so even a
+// short one takes as long as a full one.  nsched[0] = entries, nsched[1] =
+// entries before the code-operand ones (nsched[0] with 64-token chunks, where
+// the order by size alone measured best).  Entry .x = unit << 16 | big << 12 | tiles << 8 | chunk
 // (big: the unit has more than kSmallTokens tokens), .y = first sorted row
 // of the chunk (in hg / ysort) | its token count << 24.  Items are
 // independent, so the order within a class does not matter.
 // cnt, off: this thread's expert count and first sorted row (thread u < E);
 // every thread calls it.
 __device__ __forceinline__ void build_schedule(const Plan& p, int cnt, int off, int* scan) {
-    __shared__ int ccount[17], cfill[17];
+    __shared__ int ccount[33], cfill[33];   // by class: 16-token tiles, + 16 on the dequantised-weight path
     const int T = p.T, E = p.E, nu = E + p.n_vs;   // nu <= kMaxExperts + a few <= 1024
     const int u = threadIdx.x;
     const int ucnt = u < E ? cnt : (u < nu ? T : 0);
     const int row0 = u < E ? off : T * p.k + (u - E) * T;
     const int nfull = ucnt / p.ntile, rem = ucnt - nfull * p.ntile;
-    const int cls = rem > 0 ? (rem + 15) / 16 : 0;   // 1 .. ntile / 16
+    const int tiles = rem > 0 ? (rem + 15) / 16 : 0;   // 1 .. ntile / 16
     const int big = (ucnt > kSmallTokens) << 12;
+    const int cls = tiles > 0 ? tiles + (big && p.ntile > 64 ? 16 : 0) : 0;
     int foff;
     const int tfull = block_scan_total(scan, nu, nfull, &foff);
     for (int c = 0; c < nfull; ++c)
         p.sched[foff + c] =
             make_int2((u << 16) | big | ((p.ntile / 16) << 8) | c, (row0 + c * p.ntile) | (p.ntile << 24));
-    if (threadIdx.x < 17) ccount[threadIdx.x] = cfill[threadIdx.x] = 0;
+    if (threadIdx.x < 33) ccount[threadIdx.x] = cfill[threadIdx.x] = 0;
     __syncthreads();
     if (cls > 0) atomicAdd(&ccount[cls], 1);
     __syncthreads();
     if (cls > 0) {
         int before = 0;   // partial chunks of heavier classes
-        for (int q = cls + 1; q <= 16; ++q) before += ccount[q];
+        for (int q = cls + 1; q <= 32; ++q) before += ccount[q];
         p.sched[tfull + before + atomicAdd(&cfill[cls], 1)] =
-            make_int2((u << 16) | big | (cls << 8) | nfull, (row0 + nfull * p.ntile) | (rem << 24));
+            make_int2((u << 16) | big | (tiles << 8) | nfull, (row0 + nfull * p.ntile) | (rem << 24));
     }
     if (threadIdx.x == 0) {
-        int np = 0;
-        for (int q = 1; q <= 16; ++q) np += ccount[q];
-        *p.nsched = tfull + np;
+        int nbig = 0, nsmall = 0;
+        for (int q = 17; q <= 32; ++q) nbig += ccount[q];
+        for (int q = 1; q <= 16; ++q) nsmall += ccount[q];
+        p.nsched[0] = tfull + nbig + nsmall;
+        p.nsched[1] = p.ntile > 64 ? tfull + nbig : tfull + nbig + nsmall;
     }
 }
 
@@ -507,9 +515,9 @@ __host__ __device__ constexpr int gu_tiles(int MT) { return MT > 4 ? 2 : 1; }
 // stages are outstanding (a fixed count per wave and stage; wave 0 also
 // loads the scale|bias slot).  No other vector-memory operation is issued
 // inside the loop.
-// Stages: three for 128-token chunks; two for smaller ones, whose smaller
-// ring leaves room for a fourth workgroup per CU.
-__host__ __device__ constexpr int ring_depth(int MT) { return MT > 4 ? 3 : 2; }
+// Stages of the ring: three for 128-token chunks; two for smaller ones,
+// whose smaller ring leaves room for a fourth down workgroup per CU.
+__host__ __device__ constexpr int ring_depth(int MT, int) { return MT > 4 ? 3 : 2; }
 
 __host__ __device__ constexpr int ring_stage_bytes(int MT, int NM) { return (2 * MT + 2 * NM + 1) * 1024; }
 
@@ -613,13 +621,13 @@ __device__ __forceinline__ void ring_mma(const char* st, float4_t (*acc)[MT], in
 // NM weight tiles (ring_wtile) times the chunk's tokens over G column
 // groups: acc[m][t] holds rows 16 ms + 4 (lane / 16) + i of tile m, token
 // 16 t + lane % 16.  rows[n]: source row of chunk token n (n < count).
-// lds: ring_depth(MT) stages of ring_stage_bytes(MT, NM).  Starts and ends with the
+// lds: ring_depth(MT, NM) stages of ring_stage_bytes(MT, NM).  Starts and ends with the
 // ring unused (the caller's LDS is free before and after).
 template <int NM, int RT, int NTT, int MT>
 __device__ __forceinline__ void ring_tile_n(const uint8_t* base, int64_t rstride, int64_t mstride, int nrt, int G,
                                             int ksplit, int64_t kjump, const _Float16* src, int64_t stride,
                                             const int* rows, int count, char* lds, float4_t (*acc)[MT]) {
-    constexpr int kSt = ring_stage_bytes(MT, NM), kRing = ring_depth(MT);
+    constexpr int kSt = ring_stage_bytes(MT, NM), kRing = ring_depth(MT, NM);
     constexpr int kOps = (NTT + 1) / 2 + NM / 2;   // loads per wave and stage (wave 0: one more)
     const int ms = wave_id(), lane = threadIdx.x & 63;
     const uint32_t l0 = lds_addr(lds);
@@ -716,10 +724,16 @@ __device__ __forceinline__ GridPos grid_pos() {
 // entry alone.  Returns false when the workgroup has nothing to do.
 __device__ __forceinline__ bool gg_item(const Plan& p, bool down, Item* it) {
     const GridPos gp = grid_pos();
-    if (gp.chunk >= *p.nsched) return false;
+    const int ns = p.nsched[0];
+    if (gp.chunk >= ns) return false;
+    // gate/up takes the entries in order; down takes the code-operand ones
+    // first (128-token chunks), whose workgroups stage the chunk and take
+    // longer there
+    const int nb = p.nsched[1];
+    const int e = !down ? gp.chunk : (gp.chunk < ns - nb ? nb + gp.chunk : gp.chunk - (ns - nb));
     const int rt = down ? gp.rx * kDnTiles : gp.rx;
     it->rt = rt;
-    const int2 sc = p.sched[gp.chunk];
+    const int2 sc = p.sched[e];
     const int ex = sc.x >> 16, c = sc.x & 0xFF;
     it->big = (sc.x >> 12) & 1;
     it->ntt = (sc.x >> 8) & 0xF;
@@ -1205,7 +1219,7 @@ __device__ __forceinline__ void dn_big(const Plan& p, const Item& it, int rt0, i
 __host__ __device__ constexpr size_t dn_small_hs_bytes(int I) { return (size_t)kSmallTokens * (I + 8) * 2; }
 size_t dn_lds_bytes(int I, int MT) {
     const size_t small = dn_small_hs_bytes(I) + (size_t)2 * (I / 64) * 32 * 4;
-    const size_t big = (size_t)ring_depth(MT) * ring_stage_bytes(MT, kDnTiles);
+    const size_t big = (size_t)ring_depth(MT, kDnTiles) * ring_stage_bytes(MT, kDnTiles);
     return small > big ? small : big;
 }
 
@@ -1332,7 +1346,8 @@ __global__ __launch_bounds__(256) void k_gg_combine(Plan p) {
 // Dynamic LDS of k_gu: the big path's staged batch, the small path's
 // group constants and its reduction buffer, which reuses their space.
 size_t gu_lds_bytes(int G_H, int MT) {
-    const size_t big = (size_t)ring_depth(MT) * ring_stage_bytes(MT, 2 * gu_tiles(MT)), red = sizeof(GuRed);
+    const size_t big = (size_t)ring_depth(MT, 2 * gu_tiles(MT)) * ring_stage_bytes(MT, 2 * gu_tiles(MT)),
+                 red = sizeof(GuRed);
     const size_t c = (size_t)2 * G_H * 32 * 4;
     return big > red ? (big > c ? big : c) : (red > c ? red : c);
 }

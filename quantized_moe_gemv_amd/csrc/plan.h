@@ -70,7 +70,7 @@ struct Plan {
     int32_t* perm;     // [T*k]  pair p = t*k + j, sorted by expert (any order within one)
     int32_t* inv;      // [T*k]  position of pair p in perm
     int2* sched;       // [max_tiles] (unit << 16 | tiles << 8 | chunk, first row | count << 24)
-    int32_t* nsched;   // [1]
+    int32_t* nsched;   // [2]: schedule entries, and those on the dequantised-weight path (first)
     // rows T*k + j*T + t of hg / ysort belong to token t and the shared
     // expert's virtual expert j (its rows j*I .. j*I + I - 1)
     _Float16* hg;      // [T*k + n_vs*T][I]  GeGLU activations in sorted order (scaled as x16)
