@@ -37,7 +37,7 @@
 
 namespace mq {
 // Internal linkage: each kernel file compiles its own copy, with its own
-// kOpaqueTid (defined before this file is included).
+// kOpaqueTid and kEarlySharedDown (defined before this file is included).
 namespace {
 
 // 1024 threads: four waves per SIMD, so the dependent chains of one wave
@@ -961,7 +961,16 @@ __device__ __forceinline__ void decode_layer(const Plan& p, Shared& sh, uint32_t
     LoadsN<kItemsRH> lsh;
     issue_loads(p, sh, ur, lrt);
     issue_loads(p, sh, us, lsh);
+    // A routed workgroup's shared down piece needs no ids: its weights load
+    // while the router runs, when the memory is far from busy.  In a stack
+    // they go out before the token (the previous layer's output sums are
+    // still running, so the wait for the token hides them); in a lone call
+    // the token comes first, since the staging barrier may then wait for them.
+    const Unit usd0 = rh.kind == U_RH ? sd_piece(p, w, nwg, 0) : no_unit();
+    Loads lsd0;
+    if constexpr (kEarlySharedDown) issue_loads(p, sh, usd0, lsd0);
     stage_token<TAIL>(p, sh, tl, tag, xraw);
+    if constexpr (!kEarlySharedDown) issue_loads(p, sh, usd0, lsd0);
     if (ur.kind == U_ROUTER) run_router(p, sh, ur, lrt, tag);
     // Units end without a barrier after wave 0 reads their row totals in
     // sh.red (see run_rh); the next writer of sh.red must follow a barrier.
@@ -975,13 +984,10 @@ __device__ __forceinline__ void decode_layer(const Plan& p, Shared& sh, uint32_t
     LoadsN<kItemsD> ld;
     if (rh.kind == U_RH) {
         LoadsN<kItemsRH> lr;
-        Loads lsd;
-        const Unit usd = sd_piece(p, w, nwg, 0);
         issue_loads(p, sh, rh, lr);
-        issue_loads(p, sh, usd, lsd);
         if (du.nt > 0) issue_rdu(p, sh, du, ld);
         run_rh(p, sh, rh, lr, tag);
-        if (usd.kind == U_SD) run_sd_piece(p, sh, usd, lsd, tag);
+        if (usd0.kind == U_SD) run_sd_piece(p, sh, usd0, lsd0, tag);
     } else {
         Unit usd[kSlotsSD];
         Loads lsd[kSlotsSD];

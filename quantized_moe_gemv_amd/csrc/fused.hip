@@ -5,6 +5,7 @@
 namespace mq {
 namespace {
 constexpr bool kOpaqueTid = false;
+constexpr bool kEarlySharedDown = false;
 }
 }  // namespace mq
 

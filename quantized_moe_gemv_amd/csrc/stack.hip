@@ -5,6 +5,7 @@
 namespace mq {
 namespace {
 constexpr bool kOpaqueTid = true;
+constexpr bool kEarlySharedDown = true;
 }
 }  // namespace mq
 
