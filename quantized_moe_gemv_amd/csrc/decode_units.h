@@ -128,27 +128,33 @@ __device__ __forceinline__ uint32_t wait_word(const uint64_t* p, uint32_t tag, u
     return (uint32_t)v;
 }
 
-// Payloads of words base[0 .. n) into dst, for n <= 4 * kThreads: every
-// load is issued before any is checked, so the gather costs one round trip
-// when the words are there (a stale word is then waited for on its own).
+// Payloads of words base[0 .. n) into dst: every load is issued before any
+// is checked, so the gather costs one round trip when the words are there (a
+// stale word is then waited for on its own).  Threads t0.. load, for
+// n <= 4 (kThreads - t0): t0 > 0 keeps waves that have just published a
+// unit's results out of it, since a wave's loads wait for its earlier stores,
+// which are written through to memory.
 __device__ __forceinline__ void gather_words(const uint64_t* base, int n, uint32_t tag, uint32_t* err,
-                                             uint32_t* dst) {
+                                             uint32_t* dst, int t0) {
     if (n <= 0) {
         __syncthreads();
         return;
     }
-    uint64_t v[4];
+    const int me = (int)tix() - t0, nthr = kThreads - t0;
+    if (me >= 0) {
+        uint64_t v[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int i = tix() + kThreads * m;
-        v[m] = ld_word(base + (i < n ? i : n - 1));   // unconditional: see issue_loads
-    }
+        for (int m = 0; m < 4; ++m) {
+            const int i = me + nthr * m;
+            v[m] = ld_word(base + (i < n ? i : n - 1));   // unconditional: see issue_loads
+        }
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int i = tix() + kThreads * m;
-        if (i < n) {
-            if ((uint32_t)(v[m] >> 32) != tag) v[m] = ((uint64_t)tag << 32) | wait_word(base + i, tag, err);
-            dst[i] = (uint32_t)v[m];
+        for (int m = 0; m < 4; ++m) {
+            const int i = me + nthr * m;
+            if (i < n) {
+                if ((uint32_t)(v[m] >> 32) != tag) v[m] = ((uint64_t)tag << 32) | wait_word(base + i, tag, err);
+                dst[i] = (uint32_t)v[m];
+            }
         }
     }
     __syncthreads();
@@ -189,6 +195,11 @@ struct Shared {
     float rc;                 // router input scale 1/sqrt(mean(x^2)+eps)/sqrt(H)
     uint32_t flag;
 };
+// First loading thread of the activation and output-sum gathers: waves 0
+// and 1 publish the units' results (the ids gather, after the router pieces
+// publish, measured no faster without them and keeps every thread).
+constexpr int kGatherT0 = 128;
+static_assert(sizeof(Shared::gbuf) / 4 <= 4 * (kThreads - kGatherT0), "a gather fills gbuf in one round");
 
 // Column range q of nq over G groups.
 __device__ __forceinline__ void krange(int G, int nq, int q, int* g0, int* ng) {
@@ -514,7 +525,7 @@ __device__ __forceinline__ void stage_token(const Plan& p, Shared& sh, const Tok
 // the scores, ids and weights to the caller's optional outputs.
 __device__ __forceinline__ void fetch_ids(const Plan& p, Shared& sh, uint32_t tag) {
     const int nslice = (p.E + 15) / 16, epad = (p.E + 31) & ~31;
-    gather_words(p.f_rpart + xcc_copy() * p.rpart_stride, nslice * kRq * 16, tag, p.f_err, sh.gbuf);
+    gather_words(p.f_rpart + xcc_copy() * p.rpart_stride, nslice * kRq * 16, tag, p.f_err, sh.gbuf, 0);
     // workgroup 0 runs the first routed unit, so it always fetches the ids
     const bool reporter = blockIdx.x == 0;
     // Selection key of expert e: the score's bits made order-preserving as an
@@ -594,7 +605,7 @@ __device__ __forceinline__ void fetch_ids(const Plan& p, Shared& sh, uint32_t ta
 // One source's activations (64 tagged words per group, from group g0, fp16
 // in the low half of the payload) into LDS, with each lane's column sums.
 __device__ __forceinline__ void stage_h(const Plan& p, Shared& sh, const uint64_t* h, int g0, int ng, uint32_t tag) {
-    gather_words(h + 64 * g0, ng * 64, tag, p.f_err, sh.gbuf);
+    gather_words(h + 64 * g0, ng * 64, tag, p.f_err, sh.gbuf, kGatherT0);
     for (int q = tix(); q < ng * 64; q += kThreads) sh.h16[q] = (uint16_t)sh.gbuf[q];
     __syncthreads();
     for (int q = tix(); q < ng * 4; q += kThreads) {
@@ -876,7 +887,7 @@ __device__ __forceinline__ void run_reduce_tail(const Plan& p, Shared& sh, int a
             st_word(p.f_tail + (int64_t)a * 8 + tix(), tag, __float_as_uint(mine));
         }
     }
-    gather_words(p.f_tail, p.G_H * 8, tag, p.f_err, sh.gbuf);
+    gather_words(p.f_tail, p.G_H * 8, tag, p.f_err, sh.gbuf, kGatherT0);
     if (wave_id() == 0) {
         float tot[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
         for (int t2 = 0; t2 < p.G_H; ++t2)
@@ -901,7 +912,7 @@ __device__ __forceinline__ void run_reduce_tail(const Plan& p, Shared& sh, int a
 template <bool TAIL>
 __device__ __forceinline__ void run_reduce(const Plan& p, Shared& sh, int a, uint32_t tag, const uint16_t* xraw) {
     const uint64_t* tilep = p.f_piece + (int64_t)a * p.n_src * 64;
-    gather_words(tilep, p.n_src * 64, tag, p.f_err, sh.gbuf);
+    gather_words(tilep, p.n_src * 64, tag, p.f_err, sh.gbuf, kGatherT0);
     if constexpr (!TAIL) {
         if (wave_id() == 0) {
             float v = 0.f;
