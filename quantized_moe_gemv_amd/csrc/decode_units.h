@@ -37,7 +37,8 @@
 
 namespace mq {
 // Internal linkage: each kernel file compiles its own copy, with its own
-// kOpaqueTid and kEarlySharedDown (defined before this file is included).
+// kOpaqueTid, kEarlySharedDown and kLateRoutedDown (defined before this file
+// is included).
 namespace {
 
 // 1024 threads: four waves per SIMD, so the dependent chains of one wave
@@ -743,8 +744,12 @@ __device__ __forceinline__ void run_rh(const Plan& p, Shared& sh, const Unit& x,
 
 // Shared down piece: one 64-row output tile from one chunk of the shared
 // activations -> partial outputs (source k + chunk).
-__device__ __forceinline__ void run_sd_piece(const Plan& p, Shared& sh, const Unit& x, const Loads& L, uint32_t tag) {
+__device__ __forceinline__ void stage_sd(const Plan& p, Shared& sh, const Unit& x, uint32_t tag) {
     stage_h(p, sh, p.f_hs + xcc_copy() * p.h_stride, x.g0, x.ng, tag);
+}
+
+// The piece from its activations staged in LDS.
+__device__ __forceinline__ void sd_compute(const Plan& p, Shared& sh, const Unit& x, const Loads& L, uint32_t tag) {
     const int wave = wave_id(), lane = tix() & 63, kb = lane >> 4;
     float acc[2] = {0.f, 0.f};    // rows 32*(wave & 1) + 16*r + lane%16 of the output tile
 #pragma unroll
@@ -766,6 +771,11 @@ __device__ __forceinline__ void run_sd_piece(const Plan& p, Shared& sh, const Un
     uint64_t* dst = p.f_piece + ((int64_t)x.a * p.n_src + p.k + x.b) * 64;
     if (wave_id() == 0) st_word(dst + tix(), tag, __float_as_uint(row_total_par(sh, tix())));
     // no barrier: as at the end of run_rh
+}
+
+__device__ __forceinline__ void run_sd_piece(const Plan& p, Shared& sh, const Unit& x, const Loads& L, uint32_t tag) {
+    stage_sd(p, sh, x, tag);
+    sd_compute(p, sh, x, L, tag);
 }
 
 // Loads of a routed down unit: for each of its tiles, wave w takes groups
@@ -993,7 +1003,20 @@ __device__ __forceinline__ void decode_layer(const Plan& p, Shared& sh, uint32_t
     if (us.kind == U_SH) run_rh(p, sh, us, lsh, tag);
     if (rh.kind == U_RH || du.nt > 0) fetch_ids(p, sh, tag);
     LoadsN<kItemsD> ld;
-    if (rh.kind == U_RH) {
+    if (rh.kind == U_RH && kLateRoutedDown) {
+        // The down unit's loads go out once the gate/up weights have landed
+        // (they would share the memory's rate with them) and after the shared
+        // piece's activation gather (loads complete in issue order, so the
+        // gather would wait for them).  In a lone call the piece's compute
+        // then waits for those loads (the compiler waits for every load in
+        // flight before it), which costs more than it saves.
+        LoadsN<kItemsRH> lr;
+        issue_loads(p, sh, rh, lr);
+        run_rh(p, sh, rh, lr, tag);
+        if (usd0.kind == U_SD) stage_sd(p, sh, usd0, tag);
+        if (du.nt > 0) issue_rdu(p, sh, du, ld);
+        if (usd0.kind == U_SD) sd_compute(p, sh, usd0, lsd0, tag);
+    } else if (rh.kind == U_RH) {
         LoadsN<kItemsRH> lr;
         issue_loads(p, sh, rh, lr);
         if (du.nt > 0) issue_rdu(p, sh, du, ld);

@@ -6,6 +6,7 @@ namespace mq {
 namespace {
 constexpr bool kOpaqueTid = false;
 constexpr bool kEarlySharedDown = false;
+constexpr bool kLateRoutedDown = false;
 }
 }  // namespace mq
 

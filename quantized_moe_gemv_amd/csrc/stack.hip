@@ -6,6 +6,7 @@ namespace mq {
 namespace {
 constexpr bool kOpaqueTid = true;
 constexpr bool kEarlySharedDown = true;
+constexpr bool kLateRoutedDown = true;
 }
 }  // namespace mq
 
