@@ -226,7 +226,13 @@ size_t mq_workspace_bytes(const mq_router* router, const mq_expert_pool* pool,
  *     partial results, so all of them must be resident at once: do not run
  *     it beside other work that occupies whole compute units.  Every wait is
  *     bounded; a wait that gives up sets bit 0 of mq_workspace_errors and the
- *     output rows of that call read NaN. */
+ *     output rows of that call read NaN.
+ *   - Start order (GROUPED with chunks of up to 64 tokens, T <= 1024).  The
+ *     gate/up and down projections run in one launch whose down workgroups
+ *     wait for gate/up workgroups of lower index; that every wait ends rests
+ *     on each XCD starting the workgroups it is given in index order, as the
+ *     hardware dispatcher does.  The waits are bounded all the same; a give-up
+ *     sets bit 0 and the output rows read NaN. */
 mq_status moe_layer_forward(const mq_act* x, const mq_router* router, const mq_expert_pool* pool,
                             const mq_shared* shared, mq_act* out, const mq_opts* opts, void* stream);
 
@@ -287,10 +293,11 @@ mq_status moe_stack_forward(const mq_act* x, int32_t n_layers, const mq_router* 
 /* HOST result: the sticky error bits that the kernels keep in a workspace
  * ("Correctness and safety invariants": a queued consumer owns its scratch
  * until completion, so the bits are read after the stream has finished).
- *   Bit 0 (FUSED, stack): a bounded wait for another workgroup's partial
+ *   Bit 0 (FUSED, GROUPED, stack): a bounded wait for another workgroup's
  *         result gave up, so the calls since the bits were last clear may
  *         have wrong results; their outputs read NaN (it happens only if the
- *         workgroups of a launch are not all resident at once).
+ *         workgroups of a launch are not all resident at once, or, GROUPED,
+ *         not started in index order).
  *   Bit 1 (FUSED, GROUPED, stack): an fp16 activation overflowed or was NaN
  *         (see the range precondition of moe_layer_forward).
  * Copies the bits into *errors after the work queued on `stream` has

@@ -138,7 +138,7 @@ int device_cus() {
 // Offsets of every workspace region for up to T tokens; returns the total.
 struct Carve {
     size_t r, rsum8, xsum4, xsum8, plog, ids, wts, hhi, hlo, hsum, shi, slo, ssum, dpart;
-    size_t xn, x16, xso, counts, offsets, perm, inv, sched, nsched, hg, hso, ysort;
+    size_t xn, x16, xso, counts, offsets, perm, inv, sched, nsched, gdone, gqueue, hg, hso, ysort;
     size_t total;
 };
 
@@ -169,8 +169,11 @@ Carve carve(const Sizes& z, int64_t T) {
     c.inv = take(T * z.k * 4);
     // sized for the smallest chunk so that the carve grows with T whatever
     // chunk size set_tiles picks
-    c.sched = take(((size_t)(T * z.k + 31) / 32 + z.E + (size_t)z.n_vs * ((T + 31) / 32)) * 8 + 8);
+    const size_t nentries = (size_t)(T * z.k + 31) / 32 + z.E + (size_t)z.n_vs * ((T + 31) / 32) + 1;
+    c.sched = take(nentries * 8);
     c.nsched = take(8);
+    c.gdone = take(nentries * 4);
+    c.gqueue = take(nentries * 4);
     const size_t rows = T * (z.k + z.n_vs);
     c.hg = take(rows * z.I * 2);
     c.hso = take(rows * z.G_I * 8);
@@ -462,6 +465,8 @@ static mq_status layer_forward(const mq_act* x, const mq_router* router, const m
     p.inv = (int32_t*)(ws + c.inv);
     p.sched = (int2*)(ws + c.sched);
     p.nsched = (int32_t*)(ws + c.nsched);
+    p.gdone = (int32_t*)(ws + c.gdone);
+    p.gqueue = (int32_t*)(ws + c.gqueue);
     p.hg = (_Float16*)(ws + c.hg);
     p.hso = (float*)(ws + c.hso);
     p.ysort = (float*)(ws + c.ysort);

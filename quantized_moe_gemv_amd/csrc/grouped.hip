@@ -382,6 +382,13 @@ __global__ __launch_bounds__(1024) void k_sort(Plan p) {
         p.counts[tid] = cnt;
     }
     if (tid == 0) p.offsets[E] = P;
+    // the single GEMM launch's per-entry counts of finished gate/up items
+    // and its queue of finished entries
+    for (int e = tid; e < p.max_tiles; e += 1024) {
+        p.gdone[e] = 0;
+        p.gqueue[1 + e] = -1;
+    }
+    if (tid == 0) p.gqueue[0] = 0;
     __syncthreads();
     // positions within an expert's segment come from LDS atomics; the path
     // of a unit is chosen by its pair count, and every token is computed
@@ -703,6 +710,8 @@ struct Item {
     const uint8_t* w[2];
     int ksplit;         // operand rows jump by kjump halves every ksplit column groups
     int64_t kjump;      //   (the shared expert's down over all its columns), else ksplit = G
+    int e;              // schedule entry
+    int ngu;            // gate/up workgroups of the entry (row tiles of its gate and up)
 };
 
 // Grid position of this workgroup in a grid (nx, ny) with ny a multiple of
@@ -715,24 +724,23 @@ struct Item {
 struct GridPos {
     int rx, chunk;
 };
-__device__ __forceinline__ GridPos grid_pos() {
-    const int nx = gridDim.x, L = blockIdx.y * nx + blockIdx.x, j = L >> 3;
+__device__ __forceinline__ GridPos grid_pos_at(int L, int nx) {
+    const int j = L >> 3;
     return {j % nx, (j / nx) * 8 + (L & 7)};
 }
 
-// The matrices of the item's row tile and its tokens, from the schedule
-// entry alone.  Returns false when the workgroup has nothing to do.
-__device__ __forceinline__ bool gg_item(const Plan& p, bool down, Item* it) {
-    const GridPos gp = grid_pos();
-    const int ns = p.nsched[0];
-    if (gp.chunk >= ns) return false;
-    // gate/up takes the entries in order; down takes the code-operand ones
-    // first (128-token chunks), whose workgroups stage the chunk and take
-    // longer there
-    const int nb = p.nsched[1];
-    const int e = !down ? gp.chunk : (gp.chunk < ns - nb ? nb + gp.chunk : gp.chunk - (ns - nb));
-    const int rt = down ? gp.rx * kDnTiles : gp.rx;
+// Position in a launch of one kind of item: L (linear index) < 0 takes the
+// two-dimensional grid of the launch.
+__device__ __forceinline__ GridPos grid_pos(int L, int nx) {
+    return L < 0 ? grid_pos_at(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x) : grid_pos_at(L, nx);
+}
+
+// The matrices of row position rx of schedule entry e and its tokens, from
+// the entry alone.  Returns false when the workgroup has nothing to do.
+__device__ __forceinline__ bool gg_item_at(const Plan& p, bool down, Item* it, int e, int rx) {
+    const int rt = down ? rx * kDnTiles : rx;
     it->rt = rt;
+    it->e = e;
     const int2 sc = p.sched[e];
     const int ex = sc.x >> 16, c = sc.x & 0xFF;
     it->big = (sc.x >> 12) & 1;
@@ -743,6 +751,7 @@ __device__ __forceinline__ bool gg_item(const Plan& p, bool down, Item* it) {
     it->kjump = 0;
     if (ex < p.E) {
         it->shared = 0;
+        it->ngu = p.I / 64;
         const uint8_t* base = p.pool_base + (int64_t)ex * p.expert_stride;
         it->ntiles = down ? p.H / 64 : p.I / 64;
         if (down) {
@@ -758,6 +767,7 @@ __device__ __forceinline__ bool gg_item(const Plan& p, bool down, Item* it) {
     } else {
         const int j = ex - p.E;
         it->shared = 1;
+        it->ngu = min(p.I, p.Is - j * p.I) / 64;
         it->ntiles = down ? p.H / 64 : min(p.I, p.Is - j * p.I) / 64;
         if (down && p.n_vs_dn == 1 && p.n_vs > 1) {
             // the first virtual expert's item takes all G_s groups: its
@@ -785,6 +795,19 @@ __device__ __forceinline__ bool gg_item(const Plan& p, bool down, Item* it) {
     return true;
 }
 
+// The item of this workgroup's grid position (L, nx: see grid_pos).
+__device__ __forceinline__ bool gg_item(const Plan& p, bool down, Item* it, int L = -1, int nx = 0) {
+    const GridPos gp = grid_pos(L, nx);
+    const int ns = p.nsched[0];
+    if (gp.chunk >= ns) return false;
+    // gate/up takes the entries in order; down takes the code-operand ones
+    // first (128-token chunks), whose workgroups stage the chunk and take
+    // longer there
+    const int nb = p.nsched[1];
+    const int e = !down ? gp.chunk : (gp.chunk < ns - nb ? nb + gp.chunk : gp.chunk - (ns - nb));
+    return gg_item_at(p, down, it, e, gp.rx);
+}
+
 // Token of chunk position n (clamped to the chunk).
 __device__ __forceinline__ int item_token(const Plan& p, const Item& it, int n) {
     n = min(n, it.count - 1);
@@ -795,6 +818,7 @@ __device__ __forceinline__ int item_token(const Plan& p, const Item& it, int n) 
 // pairs src[row][g] (ld pairs per row) of chunk slots n < nslot, for G
 // groups; thread tid takes slot tid % 32 and groups tid / 32 + 8 i, with
 // the loads of six groups in flight.  No barrier inside.
+template <bool AGENT = false>
 __device__ __forceinline__ void stage_sums(const float2* src, int ld, int row, int G, int nslot, float* tsum,
                                            float* tneg) {
     const int n = threadIdx.x & 31;
@@ -803,7 +827,14 @@ __device__ __forceinline__ void stage_sums(const float2* src, int ld, int row, i
     for (int g0 = threadIdx.x >> 5; g0 < G; g0 += 8 * kB) {
         float2 v[kB];
 #pragma unroll
-        for (int i = 0; i < kB; ++i) v[i] = src[(int64_t)row * ld + min(g0 + 8 * i, G - 1)];
+        for (int i = 0; i < kB; ++i) {
+            const float2* a = src + (int64_t)row * ld + min(g0 + 8 * i, G - 1);
+            if constexpr (AGENT)
+                v[i] = __builtin_bit_cast(float2, __hip_atomic_load((const uint64_t*)a, __ATOMIC_RELAXED,
+                                                                    __HIP_MEMORY_SCOPE_AGENT));
+            else
+                v[i] = *a;
+        }
 #pragma unroll
         for (int i = 0; i < kB; ++i)
             if (g0 + 8 * i < G) {
@@ -813,8 +844,35 @@ __device__ __forceinline__ void stage_sums(const float2* src, int ld, int row, i
     }
 }
 
+// GeGLU rows and their group sums.  With ONE (the down items run in the same
+// launch, on any XCD) they are stored at agent scope: such a store has
+// passed this XCD's L2 once it has completed, and gu_done waits for that.
+template <bool ONE>
+__device__ __forceinline__ void put_h(_Float16* dst, _Float16 v) {
+    if constexpr (ONE)
+        __hip_atomic_store((uint16_t*)dst, __builtin_bit_cast(uint16_t, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        *dst = v;
+}
+
+// Four adjacent GeGLU values (dst 8-byte aligned).
+template <bool ONE>
+__device__ __forceinline__ void put_h4(_Float16* dst, const _Float16* v) {
+    if constexpr (ONE) {
+        const uint64_t w = (uint64_t)__builtin_bit_cast(uint16_t, v[0]) |
+                           ((uint64_t)__builtin_bit_cast(uint16_t, v[1]) << 16) |
+                           ((uint64_t)__builtin_bit_cast(uint16_t, v[2]) << 32) |
+                           ((uint64_t)__builtin_bit_cast(uint16_t, v[3]) << 48);
+        __hip_atomic_store((uint64_t*)dst, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = v[i];
+    }
+}
+
 // The (sum, -1024 sum) pair of the chunk's GeGLU rows over the tile's 64
 // columns: part[w][n] holds wave w's share for chunk token n.
+template <bool ONE>
 __device__ __forceinline__ void write_hso(const Plan& p, const Item& it, int rt, const float2 (*part)[128]) {
     const int n = threadIdx.x;
     if (n < it.count) {
@@ -824,8 +882,56 @@ __device__ __forceinline__ void write_hso(const Plan& p, const Item& it, int rt,
             v.x += part[w][n].x;
             v.y += part[w][n].y;
         }
-        ((float2*)p.hso)[(int64_t)(it.pos0 + n) * p.G_I + rt] = v;
+        float2* dst = (float2*)p.hso + (int64_t)(it.pos0 + n) * p.G_I + rt;
+        if constexpr (ONE)
+            __hip_atomic_store((uint64_t*)dst, __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        else
+            *dst = v;
     }
+}
+
+// One launch: the item's GeGLU rows are written; count it for its entry,
+// and the last of the entry's gate/up workgroups appends the entry to the
+// queue of finished entries.  Each wave first waits for its own stores
+// (they complete in order with its loads), so the count follows every store
+// of the workgroup, and the append every store of the entry.
+template <bool ONE>
+__device__ __forceinline__ void gu_done(const Plan& p, const Item& it) {
+    if constexpr (ONE) {
+        wait_vm<0>();
+        __syncthreads();
+        if (threadIdx.x == 0 &&
+            __hip_atomic_fetch_add(p.gdone + it.e, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == it.ngu - 1) {
+            const int slot = __hip_atomic_fetch_add(p.gqueue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(p.gqueue + 1 + slot, it.e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// One launch: the down items take the entries in the order their gate/up
+// items finish.  Slot q of the queue (grid position q, see grid_pos) waits
+// for the q-th finished entry (bounded: a give-up sets kErrWait and the
+// workgroup does nothing).
+constexpr int kGuSpins = 1 << 16;
+__device__ __forceinline__ bool gg_item_ready(const Plan& p, Item* it, int L, int nx) {
+    __shared__ int s_entry;
+    const GridPos gp = grid_pos_at(L, nx);
+    if (gp.chunk >= p.nsched[0]) return false;
+    if (threadIdx.x == 0) {
+        int e, n = 0;
+        while ((e = __hip_atomic_load(p.gqueue + 1 + gp.chunk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < 0) {
+            if (++n > kGuSpins) {
+                atomicOr(p.f_err, kErrWait);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(8);
+        }
+        s_entry = e;
+    }
+    __syncthreads();
+    const int e = s_entry;
+    return e >= 0 && gg_item_at(p, true, it, e, gp.rx);
 }
 
 // ---- gate/up, up to 32 tokens: codes as the B operand (D[token][row]); the
@@ -904,7 +1010,7 @@ typedef float4_t GuRed[4][3][2][64];   // [row block][other wave][matrix][lane],
 // last group; the loops have one exit, a multiply past the end weighs zero.
 // tok0 = item_token(lane % 16), tok_s = item_token(threadIdx.x % 32), looked
 // up by the caller before the first weights.
-template <int NTT>
+template <int NTT, bool ONE>
 __device__ __forceinline__ void gu_small_n(const Plan& p, const Item& it, GuW& WA, GuW& WB, char* lds,
                                            float2 (*hpart)[128], int tok0, int tok_s) {
     const int w = wave_id(), lane = threadIdx.x & 63;
@@ -995,19 +1101,20 @@ __device__ __forceinline__ void gu_small_n(const Plan& p, const Item& it, GuW& W
             const _Float16 h = (_Float16)(gelu_tanh(v[0][i]) * v[1][i]);
             const _Float16 a = act_store(h, c);
             flag_error(p.f_err, n < it.count && f16_bad(h), kErrRange);
-            if (n < it.count) p.hg[(int64_t)(it.pos0 + n) * p.I + c] = a;
+            if (n < it.count) put_h<ONE>(p.hg + (int64_t)(it.pos0 + n) * p.I + c, a);
             const float hs = sum16((float)h), hn = sum16(-1024.0f * (float)a);
             if ((lane & 15) == 0) hpart[w][n] = make_float2(hs, hn);
         }
     }
     __syncthreads();
-    write_hso(p, it, it.rt, hpart);
+    write_hso<ONE>(p, it, it.rt, hpart);
+    gu_done<ONE>(p, it);
 }
 
 // ---- gate/up, units of more than kSmallTokens tokens: gu_tiles row tiles of
 // gate and of up over the ring, so each staged token fragment feeds
 // 4 gu_tiles multiplies.
-template <int MT>
+template <int MT, bool ONE>
 __device__ __forceinline__ void gu_big(const Plan& p, const Item& it, char* lds, int* rows, float2 (*hpart)[128]) {
     constexpr int kGuTiles = gu_tiles(MT);
     const int wave = wave_id(), lane = threadIdx.x & 63;
@@ -1040,36 +1147,32 @@ __device__ __forceinline__ void gu_big(const Plan& p, const Item& it, char* lds,
             }
             flag_error(p.f_err, n < it.count && (f16_bad(h[0]) || f16_bad(h[1]) || f16_bad(h[2]) || f16_bad(h[3])),
                        kErrRange);
-            if (n < it.count) {
-                _Float16* dst = p.hg + (int64_t)(it.pos0 + n) * p.I + r0;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dst[i] = a[i];
-            }
+            if (n < it.count) put_h4<ONE>(p.hg + (int64_t)(it.pos0 + n) * p.I + r0, a);
             hs = sum_kb(hs);
             hn = sum_kb(hn);
             if (lane < 16) hpart[wave][n] = make_float2(hs, hn);
         }
         __syncthreads();
-        write_hso(p, it, it.rt + u, hpart);
+        write_hso<ONE>(p, it, it.rt + u, hpart);
         __syncthreads();
     }
+    gu_done<ONE>(p, it);
 }
 
 // Gate/up + GeGLU: hg[pos] = gelu(gate x) * (up x) in fp16 (scaled
 // columns divided by 16), hso[pos][tile] its group sums.  MT: most 16-token
 // tiles of a chunk; chunks of up to 64 tokens leave room for three waves per
 // SIMD.  grid (I / 64, max_tiles), block 256, dynamic LDS gu_lds_bytes.
-template <int MT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT <= 4 ? 3 : 2))) void k_gu(Plan p) {
-    extern __shared__ __attribute__((aligned(16))) char lds[];
-    __shared__ float2 hpart[4][128];
-    __shared__ int rows[128];
+// (L, nx: see grid_pos; ONE: see put_h.)
+template <int MT, bool ONE>
+__device__ __forceinline__ void gu_item(const Plan& p, char* lds, float2 (*hpart)[128], int* rows, int L, int nx) {
+    static_assert(!ONE || gu_tiles(MT) == 1, "one launch: every row tile of an entry is a workgroup that counts");
     Item it;
-    if (!gg_item(p, false, &it)) return;
+    if (!gg_item(p, false, &it, L, nx)) return;
     const int w = wave_id(), lane = threadIdx.x & 63;
     if (it.big) {
         // gu_tiles row tiles per workgroup: the others of the run have none
-        if (it.rt % gu_tiles(MT) == 0) gu_big<MT>(p, it, lds, rows, hpart);
+        if (it.rt % gu_tiles(MT) == 0) gu_big<MT, ONE>(p, it, lds, rows, hpart);
         return;
     }
     // the chunk's token lookups first, then the first weights, in flight
@@ -1080,7 +1183,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT <= 4 ? 3
     GuW WA, WB;
     gu_wload(WA, it.w[0], it.w[1], min(w, it.G - 1), lane);
     gu_wload(WB, it.w[0], it.w[1], min(w + 4, it.G - 1), lane);
-    gu_small_n<1>(p, it, WA, WB, lds, hpart, tok0, tok_s);
+    gu_small_n<1, ONE>(p, it, WA, WB, lds, hpart, tok0, tok_s);
+}
+
+template <int MT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT <= 4 ? 3 : 2))) void k_gu(Plan p) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    __shared__ float2 hpart[4][128];
+    __shared__ int rows[128];
+    gu_item<MT, false>(p, lds, hpart, rows, -1, 0);
 }
 
 // ---- down, up to 32 tokens: the chunk's GeGLU rows and group constants
@@ -1226,13 +1337,14 @@ size_t dn_lds_bytes(int I, int MT) {
 // Down projection: ysort[pos] = w_pair * (W_down . h), weight 1 for the
 // shared expert's slices.  grid (ceil(H / 64 / kDnTiles), max_tiles), block
 // 256, dynamic LDS dn_lds_bytes(I, MT).
-template <int MT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT <= 4 ? 3 : 2))) void k_dn(Plan p) {
-    extern __shared__ __attribute__((aligned(16))) _Float16 hs[];
-    __shared__ float wrow[128];
-    __shared__ int rows[128];
+template <int MT, bool ONE>
+__device__ __forceinline__ void dn_item(const Plan& p, _Float16* hs, float* wrow, int* rows, int L, int nx) {
     Item it;
-    if (!gg_item(p, true, &it)) return;
+    if constexpr (ONE) {
+        if (!gg_item_ready(p, &it, L, nx)) return;
+    } else if (!gg_item(p, true, &it, L, nx)) {
+        return;
+    }
     const int rt0 = it.rt, nrt = min(kDnTiles, p.H / 64 - rt0);
     auto token_rows = [&]() {
         if ((int)threadIdx.x < it.count) {
@@ -1262,8 +1374,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT <= 4 ? 3
     const int total = nrow * per;
     float* tsum = (float*)((char*)hs + dn_small_hs_bytes(p.I));
     float* tneg = tsum + it.G * 32;
-    stage_sums((const float2*)p.hso, p.G_I, it.pos0 + min((int)(threadIdx.x & 31), it.count - 1), it.G, nrow, tsum,
-               tneg);
+    stage_sums<ONE>((const float2*)p.hso, p.G_I, it.pos0 + min((int)(threadIdx.x & 31), it.count - 1), it.G, nrow,
+                    tsum, tneg);
     auto stage_load = [&](u32x4_t* v, int c0) {
 #pragma unroll
         for (int i = 0; i < kSt; ++i) {
@@ -1299,6 +1411,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT <= 4 ? 3
     dn_small_n<1>(p, it, rt0, nrt, hs, pitch, tsum, tneg, wrow, wb, sb, A, B, C);
 }
 
+template <int MT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT <= 4 ? 3 : 2))) void k_dn(Plan p) {
+    extern __shared__ __attribute__((aligned(16))) _Float16 hs[];
+    __shared__ float wrow[128];
+    __shared__ int rows[128];
+    dn_item<MT, false>(p, hs, wrow, rows, -1, 0);
+}
+
+// Gate/up and down items in one launch (chunks of up to 64 tokens): linear
+// indices below ngu run the gate/up items (grid position over nxg row
+// positions), the others the down items (nxd), which take the entries in
+// the order their gate/up items finish (gu_done, gg_item_ready).
+// Workgroups go to the XCDs round robin by index and each XCD starts its
+// own in index order, so once a down workgroup runs, every gate/up
+// workgroup on its XCD has started, and on any other XCD either all have
+// started or only gate/up workgroups, which wait for nothing, hold its
+// slots: every entry finishes and every wait ends (the wait is bounded
+// besides).  The down items thus fill the compute units that the last
+// gate/up items leave idle.  grid ngu + nxd * ny, block 256.
+template <int MT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_gd(Plan p, int ngu, int nxg, int nxd) {
+    static_assert(MT <= 4, "one launch for chunks of up to 64 tokens");
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    __shared__ float2 hpart[4][128];
+    __shared__ int rows[128];
+    __shared__ float wrow[128];
+    const int L = blockIdx.x;
+    if (L < ngu)
+        gu_item<MT, true>(p, lds, hpart, rows, L, nxg);
+    else
+        dn_item<MT, true>(p, (_Float16*)lds, wrow, rows, L - ngu, nxd);
+}
+
 // out[t] = sum_j ysort[inv[t][j]] (slot order) + the shared expert's
 // slices, rounded once.  grid (T, ceil(H/1024)), block 256: each thread
 // sums four adjacent columns with 16-byte loads, and the loads of a batch of
@@ -1326,6 +1471,11 @@ __global__ __launch_bounds__(256) void k_gg_combine(Plan p) {
                 a2 += v[u].z;
                 a3 += v[u].w;
             }
+    }
+    if (*p.f_err & kErrWait) {
+        // a down item of the single GEMM launch gave up waiting: its rows may
+        // be stale, so the output reads NaN rather than a plausible row
+        a0 = a1 = a2 = a3 = __builtin_nanf("");
     }
     const int64_t o = (int64_t)t * p.out_stride + i;
     if (p.out_f32) {
@@ -1371,15 +1521,30 @@ bool grouped_ok(int H, int I, int64_t T, int rows_per_token) {
 template <int MT>
 mq_status launch_gemms(const Plan& p, hipStream_t s) {
     const size_t gu_lds = gu_lds_bytes(p.G_H, MT), dn_lds = dn_lds_bytes(p.I, MT);
-    if (gu_lds > 64 * 1024 && hipFuncSetAttribute((const void*)k_gu<MT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                  (int)gu_lds) != hipSuccess)
-        return MQ_ERR_UNSUPPORTED;
-    if (dn_lds > 64 * 1024 && hipFuncSetAttribute((const void*)k_dn<MT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                  (int)dn_lds) != hipSuccess)
-        return MQ_ERR_UNSUPPORTED;
     const int ny = (p.max_tiles + 7) / 8 * 8;   // grid_pos needs a multiple of 8
-    hipLaunchKernelGGL(k_gu<MT>, dim3(p.I / 64, ny), dim3(256), gu_lds, s, p);
-    hipLaunchKernelGGL(k_dn<MT>, dim3((p.H / 64 + kDnTiles - 1) / kDnTiles, ny), dim3(256), dn_lds, s, p);
+    const int nxg = p.I / 64, nxd = (p.H / 64 + kDnTiles - 1) / kDnTiles;
+    if constexpr (MT <= 4) {
+        // a down item waits for its own entry only: no item may span the
+        // shared expert's virtual experts (merged only at 128-token chunks)
+        if (p.n_vs_dn != p.n_vs) return MQ_ERR_UNSUPPORTED;
+        const size_t lds = gu_lds > dn_lds ? gu_lds : dn_lds;
+        if (lds > 64 * 1024 &&
+            hipFuncSetAttribute((const void*)k_gd<MT>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
+                hipSuccess)
+            return MQ_ERR_UNSUPPORTED;
+        hipLaunchKernelGGL(k_gd<MT>, dim3((nxg + nxd) * ny), dim3(256), lds, s, p, nxg * ny, nxg, nxd);
+    } else {
+        if (gu_lds > 64 * 1024 && hipFuncSetAttribute((const void*)k_gu<MT>,
+                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                      (int)gu_lds) != hipSuccess)
+            return MQ_ERR_UNSUPPORTED;
+        if (dn_lds > 64 * 1024 && hipFuncSetAttribute((const void*)k_dn<MT>,
+                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                      (int)dn_lds) != hipSuccess)
+            return MQ_ERR_UNSUPPORTED;
+        hipLaunchKernelGGL(k_gu<MT>, dim3(nxg, ny), dim3(256), gu_lds, s, p);
+        hipLaunchKernelGGL(k_dn<MT>, dim3(nxd, ny), dim3(256), dn_lds, s, p);
+    }
     return MQ_OK;
 }
 

@@ -114,6 +114,8 @@ struct Plan {
     uint64_t* f_tail;      // single-launch decode: [G_H][8] tagged partial sums of the tail norms
     int n_vs_dn;           // grouped path: shared rows per token of ysort after the down projection (1 when
                            // one item of each chunk covers all of the shared expert's columns, else n_vs)
+    int32_t* gdone;        // grouped path, one GEMM launch: gate/up workgroups finished per schedule entry
+    int32_t* gqueue;       //   [0] entries finished, [1 + i] the i-th to finish (-1 until then)
 };
 
 // Arguments of the quantized GEMV head (head.hip).

@@ -85,7 +85,10 @@ __device__ __forceinline__ void tail_rows(const Plan& p) {
         f[m].w = a * ws.w * s[m].w + b * wr.w * r[m].w;
         ff += (f[m].x * f[m].x + f[m].y * f[m].y) + (f[m].z * f[m].z + f[m].w * f[m].w);
     }
-    const float c = p.tn_o ? 1.0f / sqrtf(block_sum2(ff, 0.f, buf).x / (float)p.H + p.t_eps) : 1.0f;
+    float c = p.tn_o ? 1.0f / sqrtf(block_sum2(ff, 0.f, buf).x / (float)p.H + p.t_eps) : 1.0f;
+    // the grouped path's single GEMM launch gave up a wait: NaN rows rather
+    // than plausible ones
+    if (SRC == 1 && (*p.f_err & kErrWait)) c = __builtin_nanf("");
 #pragma unroll
     for (int m = 0; m < kTailIters; ++m) {
         const int i = 4 * (threadIdx.x + kTailThreads * m);

@@ -492,6 +492,28 @@ def test_give_up_reads_nan(M, tiny):
     o = M.moe_layer_forward(dev, x, workspace=ws, path="fused", out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(o, good) and M.workspace_errors(ws) == 0
+    # the grouped path's single GEMM launch (down items waiting for gate/up
+    # items): the same contract, with and without the layer tail
+    log("grouped output after a forced give-up")
+    xs = bf16_tensor(S.make_tokens(S.SEEDS["tiny"] + 53, 5, host.cfg.hidden))
+    ws = dev.new_workspace(5)
+    good = M.moe_layer_forward(dev, xs, workspace=ws, path="grouped", out_dtype=torch.float32).clone()
+    ws.view(torch.int32)[128] = 1
+    torch.cuda.synchronize()
+    o = M.moe_layer_forward(dev, xs, workspace=ws, path="grouped", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.isnan(o).all() and M.workspace_errors(ws) & 1
+    ws.zero_()
+    o = M.moe_layer_forward(dev, xs, workspace=ws, path="grouped", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o, good) and M.workspace_errors(ws) == 0
+    tail = M.Tail.from_dict(S.make_tail(S.SEEDS["tiny"] + 3, 0, host.cfg.hidden, norms=("shared", "routed", "out"),
+                                        layer_scalar=0.75), residual_is_input=True)
+    ws.view(torch.int32)[128] = 1
+    torch.cuda.synchronize()
+    o = M.moe_layer_forward(dev, xs, workspace=ws, path="grouped", out_dtype=torch.float32, tail=tail)
+    torch.cuda.synchronize()
+    assert torch.isnan(o).all() and M.workspace_errors(ws) & 1
 
 
 def test_workspace_shared_across_layer_sizes(M, tiny, decode):
