@@ -522,9 +522,10 @@ __host__ __device__ constexpr int gu_tiles(int MT) { return MT > 4 ? 2 : 1; }
 // stages are outstanding (a fixed count per wave and stage; wave 0 also
 // loads the scale|bias slot).  No other vector-memory operation is issued
 // inside the loop.
-// Stages of the ring: three for 128-token chunks; two for smaller ones,
-// whose smaller ring leaves room for a fourth down workgroup per CU.
-__host__ __device__ constexpr int ring_depth(int MT, int) { return MT > 4 ? 3 : 2; }
+// Stages of the ring: three, except for the down items of chunks of up to
+// 64 tokens (four output tiles: 17 KB a stage), where two keep the single
+// GEMM launch's LDS within three workgroups per CU.
+__host__ __device__ constexpr int ring_depth(int MT, int NM) { return MT > 4 || NM <= 2 ? 3 : 2; }
 
 __host__ __device__ constexpr int ring_stage_bytes(int MT, int NM) { return (2 * MT + 2 * NM + 1) * 1024; }
 
@@ -1419,10 +1420,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT <= 4 ? 3
     dn_item<MT, false>(p, hs, wrow, rows, -1, 0);
 }
 
-// Gate/up and down items in one launch (chunks of up to 64 tokens): linear
-// indices below ngu run the gate/up items (grid position over nxg row
-// positions), the others the down items (nxd), which take the entries in
-// the order their gate/up items finish (gu_done, gg_item_ready).
+// Gate/up and down items in one launch (chunks of up to 64 tokens): the
+// first nxg ns8 linear indices run the gate/up items of the ns schedule
+// entries (ns8: ns rounded up to 8; grid position over nxg row positions),
+// the next nxd ny the down items (nxd), which take the entries in the order
+// their gate/up items finish (gu_done, gg_item_ready), and the rest (the
+// gate/up positions of entries the schedule did not fill) have nothing to
+// do: they come last, so that workgroups with work start first.
 // Workgroups go to the XCDs round robin by index and each XCD starts its
 // own in index order, so once a down workgroup runs, every gate/up
 // workgroup on its XCD has started, and on any other XCD either all have
@@ -1431,16 +1435,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT <= 4 ? 3
 // besides).  The down items thus fill the compute units that the last
 // gate/up items leave idle.  grid ngu + nxd * ny, block 256.
 template <int MT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_gd(Plan p, int ngu, int nxg, int nxd) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_gd(Plan p, int ny, int nxg, int nxd) {
     static_assert(MT <= 4, "one launch for chunks of up to 64 tokens");
     extern __shared__ __attribute__((aligned(16))) char lds[];
     __shared__ float2 hpart[4][128];
     __shared__ int rows[128];
     __shared__ float wrow[128];
-    const int L = blockIdx.x;
+    const int L = blockIdx.x, ngu = nxg * ((p.nsched[0] + 7) & ~7);
     if (L < ngu)
         gu_item<MT, true>(p, lds, hpart, rows, L, nxg);
-    else
+    else if (L < ngu + nxd * ny)
         dn_item<MT, true>(p, (_Float16*)lds, wrow, rows, L - ngu, nxd);
 }
 
@@ -1532,7 +1536,7 @@ mq_status launch_gemms(const Plan& p, hipStream_t s) {
             hipFuncSetAttribute((const void*)k_gd<MT>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
                 hipSuccess)
             return MQ_ERR_UNSUPPORTED;
-        hipLaunchKernelGGL(k_gd<MT>, dim3((nxg + nxd) * ny), dim3(256), lds, s, p, nxg * ny, nxg, nxd);
+        hipLaunchKernelGGL(k_gd<MT>, dim3((nxg + nxd) * ny), dim3(256), lds, s, p, ny, nxg, nxd);
     } else {
         if (gu_lds > 64 * 1024 && hipFuncSetAttribute((const void*)k_gu<MT>,
                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
