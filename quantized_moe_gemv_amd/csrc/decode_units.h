@@ -673,9 +673,16 @@ __device__ __forceinline__ void reduce_rows(Shared& sh, const float* v, int nr) 
     __syncthreads();
 }
 
+// Sums in wave order.  The reads all go out before the first add (a loop
+// whose reads each waited for the previous one took about 0.4 us, on the
+// path of every publish step).
 __device__ __forceinline__ float row_total(const Shared& sh, int row) {
+    float t[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) t[w] = sh.red[w][row];
     float v = 0.f;
-    for (int w = 0; w < kWaves; ++w) v += sh.red[w][row];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) v += t[w];
     return v;
 }
 
@@ -683,8 +690,12 @@ __device__ __forceinline__ float row_total(const Shared& sh, int row) {
 // rows 32..63 (gate/up: gate and up rows; down: the two halves of a tile).
 __device__ __forceinline__ float row_total_par(const Shared& sh, int row) {
     const int par = row >> 5, r = row & 31;
+    float t[kWaves / 2];
+#pragma unroll
+    for (int i = 0; i < kWaves / 2; ++i) t[i] = sh.red[2 * i + par][r];
     float v = 0.f;
-    for (int w = par; w < kWaves; w += 2) v += sh.red[w][r];
+#pragma unroll
+    for (int i = 0; i < kWaves / 2; ++i) v += t[i];
     return v;
 }
 
@@ -858,11 +869,17 @@ __device__ __forceinline__ void run_rdu(const Plan& p, Shared& sh, const DownUni
     __syncthreads();
     if (wave_id() == 0) {
         const int row = tix(), par = row >> 5;
-        for (int t = 0; t < d.nt; ++t) {
-            float v = 0.f;
-            for (int w2 = par; w2 < kWaves; w2 += 2) v += sh.red2[w2][t][row & 31];
-            st_word(p.f_piece + ((int64_t)(d.t0 + t) * p.n_src + d.b) * 64 + row, tag, __float_as_uint(v));
-        }
+#pragma unroll
+        for (int t = 0; t < kTilesD; ++t)
+            if (t < d.nt) {
+                float u[kWaves / 2];
+#pragma unroll
+                for (int i = 0; i < kWaves / 2; ++i) u[i] = sh.red2[2 * i + par][t][row & 31];
+                float v = 0.f;
+#pragma unroll
+                for (int i = 0; i < kWaves / 2; ++i) v += u[i];
+                st_word(p.f_piece + ((int64_t)(d.t0 + t) * p.n_src + d.b) * 64 + row, tag, __float_as_uint(v));
+            }
     }
     // no barrier: sh.red2 is written again only by the next layer's routed
     // down unit, after the barrier that ends this layer
@@ -900,14 +917,29 @@ __device__ __forceinline__ void put_row(const Plan& p, int row, float v, uint32_
 // norms' factors a, b and, since |a w_s s + b w_r r|^2 expands into those
 // sums, the output norm's factor c without a second exchange.
 // The output sums of tile a with the layer tail (see run_reduce).
+// Sum of the gathered sources s0 .. s1-1 (< 32) of row r, in source order,
+// eight reads at a time.
+__device__ __forceinline__ float sum_sources(const Shared& sh, int s0, int s1, int r) {
+    float v = 0.f;
+    for (int b = s0; b < s1; b += 8) {
+        float t[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t[i] = __uint_as_float(sh.gbuf[min(b + i, 31) * 64 + r]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (b + i < s1) v += t[i];
+    }
+    return v;
+}
+
 __device__ __forceinline__ void run_reduce_tail(const Plan& p, Shared& sh, int a, uint32_t tag, const uint16_t* xraw) {
     const int row = 64 * a + tix();
     float sv = 0.f, rv = 0.f, ws = 1.f, wr = 1.f;
     if (wave_id() == 0) {
         if (p.tn_s) ws = p.tn_s[row];
         if (p.tn_r) wr = p.tn_r[row];
-        for (int s2 = 0; s2 < p.k; ++s2) rv += __uint_as_float(sh.gbuf[s2 * 64 + tix()]);
-        for (int s2 = p.k; s2 < p.n_src; ++s2) sv += __uint_as_float(sh.gbuf[s2 * 64 + tix()]);
+        rv = sum_sources(sh, 0, p.k, tix());
+        sv = sum_sources(sh, p.k, p.n_src, tix());
         const float q[5] = {wave_sum(sv * sv), wave_sum(rv * rv), wave_sum((ws * sv) * (ws * sv)),
                             wave_sum((wr * rv) * (wr * rv)), wave_sum((ws * sv) * (wr * rv))};
         if (tix() < 8) {
@@ -947,9 +979,7 @@ __device__ __forceinline__ void run_reduce(const Plan& p, Shared& sh, int a, uin
     if constexpr (!TAIL) {
         if (wave_id() == kSumWave) {
             const int r = (int)tix() - 64 * kSumWave;
-            float v = 0.f;
-            for (int s2 = 0; s2 < p.n_src; ++s2) v += __uint_as_float(sh.gbuf[s2 * 64 + r]);
-            put_row(p, 64 * a + r, v, tag);
+            put_row(p, 64 * a + r, sum_sources(sh, 0, p.n_src, r), tag);
         }
         // the layer's closing barrier follows
     } else {
