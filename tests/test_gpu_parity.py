@@ -233,28 +233,59 @@ def test_prefill4096_layer(M, large):
     assert same.sum() >= T - 4 and err <= 1e-2 * rms
 
 
-def test_midsize_128_token_chunks(M):
-    """A mid-size layer past 1024 tokens, so the grouped path runs 128-token
-    chunks: full and partial chunks of routed and shared units, an odd
-    number of 64-row tiles (the last two-tile gate/up workgroup has one), the
-    down projection's four-tile workgroups, and the shared expert's down
-    projection as one item over all its columns (a partial shared chunk
-    too); every routing decision and every output row against the oracle."""
-    cfg = S.LayerConfig(hidden=512, num_experts=16, inter=192, shared_inter=576, top_k=4, tokens=1300, zipf=True,
-                        name="mid-size layer (H512 E16 I192 Is576 k4), 1300 tokens, Zipf routing")
+@pytest.mark.parametrize("T,chunk", [(1300, 128), (1000, 64)])
+def test_midsize_layer(M, T, chunk):
+    """A mid-size layer with many chunks per unit, every routing decision and
+    every output row against the oracle.  Past 1024 tokens the grouped path
+    runs 128-token chunks: full and partial chunks of routed and shared
+    units, an odd number of 64-row tiles (the last two-tile gate/up
+    workgroup has one), the down projection's four-tile workgroups, and the
+    shared expert's down projection as one item over all its columns (a
+    partial shared chunk too).  Up to 1024 tokens it runs 64-token chunks in
+    the single GEMM launch, whose down items take the entries in the order
+    their gate/up items finish (here some 60 entries, several per unit)."""
+    cfg = S.LayerConfig(hidden=512, num_experts=16, inter=192, shared_inter=576, top_k=4, tokens=T, zipf=True,
+                        name="mid-size layer (H512 E16 I192 Is576 k4), %d tokens, Zipf routing" % T)
     host = S.make_layer(cfg, 977)
     dev = M.DeviceLayer(host)
-    T = cfg.tokens
-    log("mid-size layer T=%d on the grouped path (128-token chunks)" % T)
+    log("mid-size layer T=%d on the grouped path (%d-token chunks)" % (T, chunk))
     x = S.make_tokens(978, T, cfg.hidden)
     got = run_gpu(M, dev, x, "grouped")
     ref = O.forward(host, x, threads=16, dense_experts=False)
     ok, excused = check_routing(ref, got, cfg.top_k)
     counts = np.bincount(got["ids"].ravel(), minlength=cfg.num_experts)
     log("  tokens per expert %d .. %d, near-ties %d" % (counts.min(), counts.max(), excused))
-    assert (counts % 128 != 0).any() and counts.max() > 128   # full and partial chunks
+    assert (counts % chunk != 0).any() and counts.max() > chunk   # full and partial chunks
     rel = check_output(ref, got, ok)
     log("  max err / RMS = %.3g over %d rows" % (rel, ok.sum()))
+
+
+def test_prefill1024_layer(M, large):
+    """The Gemma-shaped layer at 1024 tokens, the largest call of the single
+    GEMM launch (64-token chunks; about 250 schedule entries): every routing
+    decision against the oracle's router, 128 seeded tokens against the full
+    oracle, and every output row against the GEMV kernels."""
+    host, dev = large
+    T = 1024
+    log("prefill layer T=1024 with Zipf routing (single GEMM launch)")
+    x = S.make_tokens(S.SEEDS["prefill4096"] + 1, T, host.cfg.hidden)
+    got = run_gpu(M, dev, x, "grouped")
+    ref_r = oracle_routing(host, x)
+    ok, excused = check_routing(ref_r, got, host.cfg.top_k)
+    sample = np.union1d(np.random.default_rng(3).choice(T, 128, replace=False), [0, T - 1])
+    ref = O.forward(host, x[sample], threads=16, dense_experts=False)
+    sub = {key: got[key][sample] for key in ("ids", "w", "logits", "out32", "out16")}
+    rel = check_output(ref, sub, ok[sample])
+    log("  near-ties %d; max err / RMS = %.3g (oracle on %d tokens)" % (excused, rel, sample.size))
+    gv = run_gpu(M, dev, x, "gemv")
+    same = np.all(gv["ids"] == got["ids"], axis=1)
+    for t in np.nonzero(~same)[0]:            # a flip between the two kernels must be an exact near-tie
+        srt = np.sort(ref_r["logits"][t])[::-1]
+        assert srt[host.cfg.top_k - 1] - srt[host.cfg.top_k] < 1e-5, t
+    rms = np.sqrt(np.mean(gv["out32"][same] ** 2))
+    err = np.max(np.abs(gv["out32"][same] - got["out32"][same]))
+    log("  grouped vs GEMV kernels on %d of %d rows: max err / RMS = %.3g" % (same.sum(), T, err / rms))
+    assert same.sum() >= T - 2 and err <= 1e-2 * rms
 
 
 def test_grouped_matches_gemv_on_prefill(M, prefill):
