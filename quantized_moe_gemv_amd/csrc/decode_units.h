@@ -596,14 +596,16 @@ __device__ __forceinline__ void fetch_ids(const Plan& p, Shared& sh, uint32_t ta
         }
     }
     __syncthreads();
-    // softmax over the selected scores (padding entries are -inf, so 0)
-    if (wave_id() == 0) {
+    // softmax over the selected scores (padding entries are -inf, so 0), on
+    // the last wave: it has one gate/up item fewer than wave 0 and publishes
+    // nothing (stack 585 -> 576 us/token, the lone call unchanged)
+    if (wave_id() == kWaves - 1) {
         const int j = tix() & (kMaxTopK - 1);
         const float ej = expf(sh.selv[j] - sh.selv[0]);
         float den = ej;
 #pragma unroll
         for (int o = 1; o < kMaxTopK; o <<= 1) den += __shfl_xor(den, o, 64);
-        if (tix() < p.k) {
+        if ((tix() & 63) < p.k) {
             const float w = ej / den * sh.pes[sh.ids[j]];
             sh.wts[j] = w;
             if (reporter) {
