@@ -37,8 +37,9 @@
 
 namespace mq {
 // Internal linkage: each kernel file compiles its own copy, with its own
-// kOpaqueTid, kEarlySharedDown and kLateRoutedDown (defined before this file
-// is included; they change speed only, never the arithmetic).
+// kOpaqueTid, kEarlySharedDown, kLateRoutedDown and kLateSharedGateUp
+// (defined before this file is included; they change speed only, never the
+// arithmetic).
 namespace {
 
 // 1024 threads: four waves per SIMD, so the dependent chains of one wave
@@ -1035,7 +1036,10 @@ __device__ __forceinline__ void decode_layer(const Plan& p, Shared& sh, uint32_t
     Loads lrt;
     LoadsN<kItemsRH> lsh;
     issue_loads(p, sh, ur, lrt);
-    issue_loads(p, sh, us, lsh);
+    // In a stack the shared gate/up loads (6.7 MB in all) wait for the token:
+    // issued at the layer's start they would compete with the previous
+    // layer's routed down units and output sums, which are still running.
+    if constexpr (!kLateSharedGateUp) issue_loads(p, sh, us, lsh);
     // A routed workgroup's shared down piece needs no ids: its weights load
     // while the router runs, when the memory is far from busy.  In a stack
     // they go out before the token (the previous layer's output sums are
@@ -1046,6 +1050,7 @@ __device__ __forceinline__ void decode_layer(const Plan& p, Shared& sh, uint32_t
     if constexpr (kEarlySharedDown) issue_loads(p, sh, usd0, lsd0);
     stage_token<TAIL>(p, sh, tl, tag, xraw);
     if constexpr (!kEarlySharedDown) issue_loads(p, sh, usd0, lsd0);
+    if constexpr (kLateSharedGateUp) issue_loads(p, sh, us, lsh);
     if (ur.kind == U_ROUTER) run_router(p, sh, ur, lrt, tag);
     // Units end without a barrier after wave 0 reads their row totals in
     // sh.red (see run_rh); the next writer of sh.red must follow a barrier.

@@ -7,6 +7,7 @@ namespace {
 constexpr bool kOpaqueTid = false;
 constexpr bool kEarlySharedDown = false;
 constexpr bool kLateRoutedDown = false;
+constexpr bool kLateSharedGateUp = false;
 }
 }  // namespace mq
 

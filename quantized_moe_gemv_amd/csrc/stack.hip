@@ -7,6 +7,7 @@ namespace {
 constexpr bool kOpaqueTid = true;
 constexpr bool kEarlySharedDown = true;
 constexpr bool kLateRoutedDown = true;
+constexpr bool kLateSharedGateUp = true;
 }
 }  // namespace mq
 
