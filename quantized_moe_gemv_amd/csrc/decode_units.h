@@ -37,10 +37,17 @@
 
 namespace mq {
 // Internal linkage: each kernel file compiles its own copy, with its own
-// kOpaqueTid, kEarlySharedDown, kLateRoutedDown and kLateSharedGateUp
-// (defined before this file is included; they change speed only, never the
-// arithmetic).
+// kOpaqueTid, kEarlySharedDown, kLateRoutedDown, kLateSharedGateUp and
+// kSwapKb (defined before this file is included; they change speed only,
+// never the arithmetic).
 namespace {
+
+// Sum over the four lanes of a row's column blocks (lane%16 + 16 kb): by
+// permlane swaps or through the LDS crossbar, which give the same bits.
+__device__ __forceinline__ float row_sum_kb(float v) {
+    if constexpr (kSwapKb) return sum_kb(v);
+    else return sum_kb_bpermute(v);
+}
 
 // 1024 threads: four waves per SIMD, so the dependent chains of one wave
 // (dequantisation, dot steps, reductions) are hidden behind the others.
@@ -515,8 +522,7 @@ __device__ __forceinline__ void stage_token(const Plan& p, Shared& sh, const Tok
         sh.c4[2 * t] = q0;
         sh.c4[2 * t + 1] = q1;
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    ss = wave_sum(ss);
     if ((t & 63) == 0) sh.red[t >> 6][0] = ss;
     __syncthreads();
     if (t < p.G_H * 4) {
@@ -588,9 +594,7 @@ __device__ __forceinline__ void fetch_ids(const Plan& p, Shared& sh, uint32_t ta
                 rank += (int)(k0.x > me) + (int)(k0.y > me);
             }
         }
-        rank += __shfl_xor(rank, 1, 64);
-        rank += __shfl_xor(rank, 2, 64);
-        if (lg2 == 3) rank += __shfl_xor(rank, 4, 64);
+        rank = lg2 == 3 ? group_sum_i<true>(rank) : group_sum_i<false>(rank);
         if (e < p.E && part == 0 && rank < p.k) {
             sh.ids[rank] = e;
             sh.selv[rank] = sh.lg[e];
@@ -603,9 +607,8 @@ __device__ __forceinline__ void fetch_ids(const Plan& p, Shared& sh, uint32_t ta
     if (wave_id() == kWaves - 1) {
         const int j = tix() & (kMaxTopK - 1);
         const float ej = expf(sh.selv[j] - sh.selv[0]);
-        float den = ej;
-#pragma unroll
-        for (int o = 1; o < kMaxTopK; o <<= 1) den += __shfl_xor(den, o, 64);
+        static_assert(kMaxTopK == 16, "the softmax sums one 16-lane row");
+        const float den = sum16(ej);
         if ((tix() & 63) < p.k) {
             const float w = ej / den * sh.pes[sh.ids[j]];
             sh.wts[j] = w;
@@ -670,7 +673,7 @@ __device__ __forceinline__ void half_block_dot16(const uint4& c, const uint4& ha
 __device__ __forceinline__ void reduce_rows(Shared& sh, const float* v, int nr) {
     const int wave = wave_id(), lane = tix() & 63;
     for (int r = 0; r < nr; ++r) {
-        const float s = sum_kb(v[r]);
+        const float s = row_sum_kb(v[r]);
         if (lane < 16) sh.red[wave][16 * r + lane] = s;
     }
     __syncthreads();
@@ -866,7 +869,7 @@ __device__ __forceinline__ void run_rdu(const Plan& p, Shared& sh, const DownUni
         if (t < d.nt)
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
-                const float v = sum_kb(acc[t][r]);
+                const float v = row_sum_kb(acc[t][r]);
                 if (lane < 16) sh.red2[wave][t][16 * r + lane] = v;
             }
     __syncthreads();
@@ -903,7 +906,7 @@ __device__ __forceinline__ void put_row(const Plan& p, int row, float v, uint32_
     }
     if (p.out_w) {
         // the next layer's input: bf16 pairs (row 2i in the low half), one copy per XCD
-        const uint32_t b1 = __shfl_down(b, 1, 64);
+        const uint32_t b1 = next_lane_in_row(b);   // read by even lanes only
         if ((tix() & 1) == 0) {
 #pragma unroll
             for (int c = 0; c < kCopies; ++c) st_word(p.out_w + c * p.xw_stride + (row >> 1), tag, b | (b1 << 16));

@@ -84,27 +84,87 @@ __device__ __forceinline__ void flag_error(uint32_t* err, bool bad, uint32_t bit
     if (__builtin_expect(bad, 0)) atomicOr(err, bit);
 }
 
-// Sum over the 64 lanes of a wave.
+// Cross-lane sums without the LDS crossbar.  A ds_bpermute (what a shuffle
+// compiles to) is an LDS round trip; these take VALU data-parallel
+// primitives (DPP) and gfx950's permlane swaps instead.  Each step pairs
+// the same lanes as the xor butterfly it replaces, and lane i and its
+// partner add the same two values (IEEE addition commutes), so every sum
+// keeps the bits of the butterfly:
+//   xor 1, xor 2: quad_perm [1,0,3,2] and [2,3,0,1];
+//   xor 8 within a 16-lane row: row_ror:8;
+//   xor 4: row_ror:4 once the values already agree across xor 8 (lane i
+//     then reads lane i+4 mod 16, which holds the value of lane i^4), or
+//     row_half_mirror once they agree within each quad (quad 0 <-> 1);
+//   xor 16, xor 32: v_permlane16_swap / v_permlane32_swap of the value with
+//     itself, which hands back the two halves of each pair.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppRor4 = 0x124, kDppRor8 = 0x128, kDppHalfMirror = 0x141,
+              kDppShl1 = 0x101;
+
+// v + v[lane ^ 16]
+__device__ __forceinline__ float add_xor16(float v) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+// v + v[lane ^ 32]
+__device__ __forceinline__ float add_xor32(float v) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// Sum over the 64 lanes of a wave (butterfly xor 32, 16, 8, 4, 2, 1).
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    v = add_xor32(v);
+    v = add_xor16(v);
+    v += dpp_f<kDppRor8>(v);
+    v += dpp_f<kDppRor4>(v);
+    v += dpp_f<kDppXor2>(v);
+    v += dpp_f<kDppXor1>(v);
     return v;
 }
 
-// Sum over the 16 lanes lane / 16 * 16 + 0..15 of a wave.
+// Sum over the 16 lanes lane / 16 * 16 + 0..15 of a wave (xor 1, 2, 4, 8).
 __device__ __forceinline__ float sum16(float v) {
-    v += __shfl_xor(v, 1, 64);
-    v += __shfl_xor(v, 2, 64);
-    v += __shfl_xor(v, 4, 64);
-    v += __shfl_xor(v, 8, 64);
+    v += dpp_f<kDppXor1>(v);
+    v += dpp_f<kDppXor2>(v);
+    v += dpp_f<kDppHalfMirror>(v);
+    v += dpp_f<kDppRor8>(v);
     return v;
 }
 
-// Sum over the four lanes lane%16 + 16*kb (kb = 0..3) of a wave.
+// Sum over the four lanes lane%16 + 16*kb (kb = 0..3) of a wave (xor 16, 32).
 __device__ __forceinline__ float sum_kb(float v) {
+    v = add_xor16(v);
+    v = add_xor32(v);
+    return v;
+}
+// The same sum through the LDS crossbar (ds_bpermute), for kernels that
+// measured faster with it; the bits are the same.
+__device__ __forceinline__ float sum_kb_bpermute(float v) {
     v += __shfl_xor(v, 16, 64);
     v += __shfl_xor(v, 32, 64);
     return v;
+}
+
+// Integer sum over the 4 (or, with EIGHT, 8) lanes of each aligned group.
+template <bool EIGHT>
+__device__ __forceinline__ int group_sum_i(int v) {
+    v += dpp_i<kDppXor1>(v);
+    v += dpp_i<kDppXor2>(v);
+    if constexpr (EIGHT) v += dpp_i<kDppHalfMirror>(v);
+    return v;
+}
+
+// v of lane + 1 within the lane's 16-lane row (lane 15 of a row reads 0).
+__device__ __forceinline__ uint32_t next_lane_in_row(uint32_t v) {
+    return (uint32_t)dpp_i<kDppShl1>((int)v);
 }
 
 __device__ __forceinline__ float gelu_tanh(float z) {

@@ -8,6 +8,9 @@ constexpr bool kOpaqueTid = true;
 constexpr bool kEarlySharedDown = true;
 constexpr bool kLateRoutedDown = true;
 constexpr bool kLateSharedGateUp = true;
+// The row totals' lane sums use permlane swaps: 555.7-556.2 us/token
+// against 560.1-560.6 through the LDS crossbar.
+constexpr bool kSwapKb = true;
 }
 }  // namespace mq
 
