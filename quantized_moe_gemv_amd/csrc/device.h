@@ -32,11 +32,21 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                            false);
 }
 
+// (a & m) | c in one VOP3 operation.  Left to itself the compiler uses two
+// VOP2 operations with literal constants (gfx9 VOP3 takes no literal); here
+// the mask comes from a scalar register and the exponent pattern from a
+// vector register (one scalar operand per VOP3 on gfx9).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
+    return r;
+}
+
 // Pair m (m = 0..3) of a DEV_V1 4-bit word as two bf16 values 128 + q:
 // the nibbles of columns 2m and 2m+1 sit at bits 4m and 16 + 4m, and OR-ing
 // them under the exponent of 128.0 (0x4300) gives 128 + q exactly.
 __device__ __forceinline__ uint32_t q4_pair(uint32_t w, int m) {
-    return ((w >> (4 * m)) & 0x000F000Fu) | 0x43004300u;
+    return and_or(m ? w >> (4 * m) : w, 0x000F000Fu, 0x43004300u);
 }
 
 // Partial dots of one lane over one 4-bit DEV_V1 block: rows 16*ms + lane%16
@@ -64,7 +74,7 @@ __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
 // Pair m of a DEV_V1 4-bit word as two fp16 values 1024 + q (the fp16
 // exponent of 1024.0 is 0x6400; its ten mantissa bits hold q exactly).
 __device__ __forceinline__ uint32_t q4_pair16(uint32_t w, int m) {
-    return ((w >> (4 * m)) & 0x000F000Fu) | 0x64006400u;
+    return and_or(m ? w >> (4 * m) : w, 0x000F000Fu, 0x64006400u);
 }
 
 // fp32 -> fp16 bits, round to nearest even.

@@ -437,16 +437,6 @@ __global__ __launch_bounds__(1024) void k_sort(Plan p) {
 // of the layer input in xso; the gate/up kernel stores the same pair of
 // every GeGLU row and 64-column group in hso for the down projection.
 //
-// (a & m) | c in one VOP3 operation.  Left to itself the compiler uses two
-// VOP2 operations with literal constants (gfx9 VOP3 takes no literal); here
-// the mask comes from a scalar register and the exponent pattern from a
-// vector register (one scalar operand per VOP3 on gfx9).
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
-    return r;
-}
-
 __device__ __forceinline__ half8_t codes8(uint32_t w) {
     const uint32_t t = w >> 8, e = 0x64006400u;
     u32x4_t v;
