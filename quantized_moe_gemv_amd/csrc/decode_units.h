@@ -198,7 +198,8 @@ struct Shared {
     float c4[1024];           // per 4-column quarter: sum of x * router_scale
     float red[kWaves][64];
     float red2[kWaves][kTilesD][32];   // per-wave row sums of a routed down unit
-    float hsum[16 * 4];
+    float hsx[16], hsa[16];   // per staged group: sum of the activations, of the stored operand
+    alignas(16) uint16_t hzero[8];       // zeros: the operand lanes that hold no token
     int32_t ids[kMaxTopK];
     float wts[kMaxTopK];
     float rc;                 // router input scale 1/sqrt(mean(x^2)+eps)/sqrt(H)
@@ -626,21 +627,24 @@ __device__ __forceinline__ void fetch_ids(const Plan& p, Shared& sh, uint32_t ta
 }
 
 // One source's activations (64 tagged words per group, from group g0, fp16
-// in the low half of the payload) into LDS, with each lane's column sums.
+// in the low half of the payload) into LDS as the matrix-core operand of
+// the token: the columns with (c & 2) != 0 divided by 16 (see codes8),
+// with each group's sums of the activations (hsx) and of the stored
+// operand (hsa).  ng <= kWaves: wave w converts group w.
 __device__ __forceinline__ void stage_h(const Plan& p, Shared& sh, const uint64_t* h, int g0, int ng, uint32_t tag) {
     gather_words(h + 64 * g0, ng * 64, tag, p.f_err, sh.gbuf, kGatherT0);
-    for (int q = tix(); q < ng * 64; q += kThreads) sh.h16[q] = (uint16_t)sh.gbuf[q];
-    __syncthreads();
-    for (int q = tix(); q < ng * 4; q += kThreads) {
-        const int gl = q >> 2, qb = q & 3;
-        const uint4 a0 = *(const uint4*)(sh.h16 + 64 * gl + 8 * qb);
-        const uint4 a1 = *(const uint4*)(sh.h16 + 64 * gl + 32 + 8 * qb);
-        const uint32_t w[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        float v = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v += f16_lo(w[i]) + f16_hi(w[i]);
-        sh.hsum[q] = v;
+    const int q = tix(), lane = q & 63, g = wave_id();
+    if (g < ng) {
+        const _Float16 x = __builtin_bit_cast(_Float16, (uint16_t)sh.gbuf[q]);
+        const _Float16 a = (lane & 2) ? x * (_Float16)0.0625f : x;
+        sh.h16[q] = __builtin_bit_cast(uint16_t, a);
+        const float sx = wave_sum((float)x), sa = wave_sum((float)a);
+        if (lane == 0) {
+            sh.hsx[g] = sx;
+            sh.hsa[g] = sa;
+        }
     }
+    if (q < 8) sh.hzero[q] = 0;
     __syncthreads();
 }
 
@@ -658,14 +662,37 @@ __device__ __forceinline__ void half_block_dot(const uint4& c, const uint4& xa, 
         for (int q = 0; q < 4; ++q) d[i >> 1] = dot2_bf16(q4_pair(w[i], q), xk[i & 1][q], d[i >> 1]);
 }
 
-// The same with fp16 activations: adds sum((1024 + q) * h) to d[r].
-__device__ __forceinline__ void half_block_dot16(const uint4& c, const uint4& ha, const uint4& hb, float d[2]) {
+// The token's staged activations as the A operand of
+// v_mfma_f32_16x16x32_f16 (16 tokens x 32 columns): the lanes of token 0
+// (lane % 16 == 0) read columns 32 kh + 8 (lane / 16) .. +7 of a group,
+// the others read zeros.
+struct TokOp {
+    const uint16_t* base;
+    int gstride, kh;
+};
+__device__ __forceinline__ TokOp tok_op(const Shared& sh) {
+    const int lane = tix() & 63;
+    const bool on = (lane & 15) == 0;
+    return {on ? sh.h16 + 8 * (lane >> 4) : sh.hzero, on ? 64 : 0, on ? 32 : 0};
+}
+
+// Rows 16 r + lane % 16 (r = 0, 1) of one 4-bit half block (the lane's
+// 16-byte code c: word 2 r + kh holds rows 16 r.., columns 32 kh + 8 (lane /
+// 16)..) against group g of the staged token, on the matrix cores with the
+// codes as the B operand (D[token][row]): lanes 0..15 of d[r] get
+// sum_c code_c a_c + neg over the group's 64 columns (neg = -1024 sum_c a_c
+// makes it sum_c q_c x_c).
+__device__ __forceinline__ void half_block_mma(const uint4& c, const TokOp& t, int g, float neg, float d[2]) {
+    const half8_t a0 = *(const half8_t*)(t.base + g * t.gstride);
+    const half8_t a1 = *(const half8_t*)(t.base + g * t.gstride + t.kh);
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-    const uint32_t hk[2][4] = {{ha.x, ha.y, ha.z, ha.w}, {hb.x, hb.y, hb.z, hb.w}};
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) d[i >> 1] = dot2_f16(q4_pair16(w[i], q), hk[i & 1][q], d[i >> 1]);
+    for (int r = 0; r < 2; ++r) {
+        float4_t acc = {neg, 0.f, 0.f, 0.f};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, codes8(w[2 * r]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, codes8(w[2 * r + 1]), acc, 0, 0, 0);
+        d[r] = acc[0];
+    }
 }
 
 // Row totals over the lanes and waves: v[r] holds rows 16*r + lane%16; after
@@ -676,6 +703,16 @@ __device__ __forceinline__ void reduce_rows(Shared& sh, const float* v, int nr) 
         const float s = row_sum_kb(v[r]);
         if (lane < 16) sh.red[wave][16 * r + lane] = s;
     }
+    __syncthreads();
+}
+
+// Row totals of a unit on the matrix cores: lanes 0..15 of v[r] already
+// hold the wave's part of rows 16*r + lane; after the call sh.red[w][row]
+// holds wave w's part of each row.
+__device__ __forceinline__ void store_rows(Shared& sh, const float* v, int nr) {
+    const int wave = wave_id(), lane = tix() & 63;
+    for (int r = 0; r < nr; ++r)
+        if (lane < 16) sh.red[wave][16 * r + lane] = v[r];
     __syncthreads();
 }
 
@@ -784,24 +821,23 @@ __device__ __forceinline__ void stage_sd(const Plan& p, Shared& sh, const Unit& 
 // The piece from its activations staged in LDS.
 __device__ __forceinline__ void sd_compute(const Plan& p, Shared& sh, const Unit& x, const Loads& L, uint32_t tag) {
     const int w0 = down_w0(p), nw = kWaves - w0;
-    const int wave = wave_id() - w0, lane = tix() & 63, kb = lane >> 4;
-    float acc[2] = {0.f, 0.f};    // rows 32*(wave & 1) + 16*r + lane%16 of the output tile
+    const int wave = wave_id() - w0;
+    const TokOp to = tok_op(sh);
+    float acc[2] = {0.f, 0.f};    // lanes 0..15: rows 32*(wave & 1) + 16*r + lane of the output tile
 #pragma unroll
     for (int m = 0; m < kItems; ++m) {
         const int it = wave + nw * m;
         if (wave >= 0 && it < 2 * x.ng) {
             const int gl = it >> 1;
-            const uint4 ha = *(const uint4*)(sh.h16 + 64 * gl + 8 * kb);
-            const uint4 hb = *(const uint4*)(sh.h16 + 64 * gl + 32 + 8 * kb);
-            const float hs = sh.hsum[gl * 4 + kb];
-            float d[2] = {0.f, 0.f};
-            half_block_dot16(L.c[m], ha, hb, d);
+            const float hx = sh.hsx[gl];
+            float d[2];
+            half_block_mma(L.c[m], to, gl, -1024.f * sh.hsa[gl], d);
             const uint32_t sw[2] = {L.s[m].x, L.s[m].y};
 #pragma unroll
-            for (int r = 0; r < 2; ++r) acc[r] += fmaf(bf16_lo(sw[r]), fmaf(-1024.f, hs, d[r]), bf16_hi(sw[r]) * hs);
+            for (int r = 0; r < 2; ++r) acc[r] += fmaf(bf16_lo(sw[r]), d[r], bf16_hi(sw[r]) * hx);
         }
     }
-    reduce_rows(sh, acc, 2);
+    store_rows(sh, acc, 2);
     uint64_t* dst = p.f_piece + ((int64_t)x.a * p.n_src + p.k + x.b) * 64;
     if (wave_id() == 0) st_word(dst + tix(), tag, __float_as_uint(row_total_par(sh, tix())));
     // no barrier: as at the end of run_rh
@@ -839,28 +875,26 @@ __device__ __forceinline__ void run_rdu(const Plan& p, Shared& sh, const DownUni
                                         uint32_t tag) {
     stage_h(p, sh, p.f_h + xcc_copy() * p.h_stride + (int64_t)d.b * p.I, 0, p.G_I, tag);
     const int w0 = down_w0(p), np = (kWaves - w0) / 2;
-    const int wave = wave_id(), lane = tix() & 63, kb = lane >> 4;
+    const int wave = wave_id(), lane = tix() & 63;
+    const TokOp to = tok_op(sh);
     const float wf = sh.wts[d.b];
-    float acc[kTilesD][2];
+    float acc[kTilesD][2];   // lanes 0..15: rows 32*(wave & 1) + 16*r + lane of tile t
 #pragma unroll
     for (int t = 0; t < kTilesD; ++t) acc[t][0] = acc[t][1] = 0.f;
 #pragma unroll
     for (int j = 0; j < kGroupsD; ++j) {
         const int g = ((wave - w0) >> 1) + np * j;
         if (wave >= w0 && g < p.G_I) {
-            const uint4 ha = *(const uint4*)(sh.h16 + 64 * g + 8 * kb);
-            const uint4 hb = *(const uint4*)(sh.h16 + 64 * g + 32 + 8 * kb);
-            const float hs = sh.hsum[g * 4 + kb];
+            const float hx = sh.hsx[g], neg = -1024.f * sh.hsa[g];
 #pragma unroll
             for (int t = 0; t < kTilesD; ++t)
                 if (t < d.nt) {
                     const int m = kGroupsD * t + j;
-                    float dd[2] = {0.f, 0.f};
-                    half_block_dot16(L.c[m], ha, hb, dd);
+                    float dd[2];
+                    half_block_mma(L.c[m], to, g, neg, dd);
                     const uint32_t sw[2] = {L.s[m].x, L.s[m].y};
 #pragma unroll
-                    for (int r = 0; r < 2; ++r)
-                        acc[t][r] += wf * fmaf(bf16_lo(sw[r]), fmaf(-1024.f, hs, dd[r]), bf16_hi(sw[r]) * hs);
+                    for (int r = 0; r < 2; ++r) acc[t][r] += wf * fmaf(bf16_lo(sw[r]), dd[r], bf16_hi(sw[r]) * hx);
                 }
         }
     }
@@ -868,10 +902,8 @@ __device__ __forceinline__ void run_rdu(const Plan& p, Shared& sh, const DownUni
     for (int t = 0; t < kTilesD; ++t)
         if (t < d.nt)
 #pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const float v = row_sum_kb(acc[t][r]);
-                if (lane < 16) sh.red2[wave][t][16 * r + lane] = v;
-            }
+            for (int r = 0; r < 2; ++r)
+                if (lane < 16) sh.red2[wave][t][16 * r + lane] = acc[t][r];
     __syncthreads();
     if (wave_id() == 0) {
         const int row = tix(), par = row >> 5;

@@ -32,14 +32,17 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                            false);
 }
 
-// (a & m) | c in one VOP3 operation.  Left to itself the compiler uses two
-// VOP2 operations with literal constants (gfx9 VOP3 takes no literal); here
-// the mask comes from a scalar register and the exponent pattern from a
-// vector register (one scalar operand per VOP3 on gfx9).
+// (a & m) | c in one v_and_or_b32.  With constant m and c the compiler uses
+// a VOP2 AND and a VOP2 OR with literals (gfx9 VOP3 takes no literal); OR-ed
+// plus a zero it cannot see through, the constants live in vector registers
+// (set once per kernel) and the compiler forms the VOP3.  The zero is the
+// work-item's y index: every launch of this library is one-dimensional.
+// (Inline assembly that writes a vector register is avoided on purpose: the
+// compiler may give it a register that a matrix-core operation still in
+// flight is about to write.)
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
-    return r;
+    const uint32_t z = __builtin_amdgcn_workitem_id_y();
+    return (a & (m + z)) | (c + z);
 }
 
 // Pair m (m = 0..3) of a DEV_V1 4-bit word as two bf16 values 128 + q:
@@ -65,17 +68,6 @@ __device__ __forceinline__ void q4_block_dot(const uint4& c0, const uint4& c1, c
 }
 
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-
-// c + a.lo*b.lo + a.hi*b.hi with fp16 pairs, fp32 accumulation.
-__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
-}
-
-// Pair m of a DEV_V1 4-bit word as two fp16 values 1024 + q (the fp16
-// exponent of 1024.0 is 0x6400; its ten mantissa bits hold q exactly).
-__device__ __forceinline__ uint32_t q4_pair16(uint32_t w, int m) {
-    return and_or(m ? w >> (4 * m) : w, 0x000F000Fu, 0x64006400u);
-}
 
 // fp32 -> fp16 bits, round to nearest even.
 __device__ __forceinline__ uint16_t f32_to_f16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
@@ -183,6 +175,26 @@ __device__ __forceinline__ float gelu_tanh(float z) {
 }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// The eight codes of a DEV_V1 4-bit word as eight fp16 operands, with four
+// AND-ORs under the fp16 exponent of 1024.0 (0x6400): columns c = 0, 1, 4, 5
+// of the eight come out as 1024 + q (the code in the low mantissa bits),
+// columns 2, 3, 6, 7 as 1024 + 16 q (the code four bits higher).  An
+// activation operand that holds the columns with (c & 2) != 0 divided by 16
+// (an exact power-of-two step) then gives, over a group of 64 columns with
+// a_c the stored activations,
+//     sum_c code_c a_c = sum_c q_c x_c + 1024 sum_c a_c.
+__device__ __forceinline__ half8_t codes8(uint32_t w) {
+    const uint32_t t = w >> 8, e = 0x64006400u;
+    u32x4_t v;
+    v[0] = and_or(w, 0x000F000Fu, e);
+    v[1] = and_or(w, 0x00F000F0u, e);
+    v[2] = and_or(t, 0x000F000Fu, e);
+    v[3] = and_or(t, 0x00F000F0u, e);
+    return __builtin_bit_cast(half8_t, v);
+}
 
 // 16-byte streaming load (non-temporal: the weights are read once per call).
 __device__ __forceinline__ uint4 ld_stream16(const void* p) {

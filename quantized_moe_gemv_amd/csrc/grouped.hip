@@ -15,10 +15,7 @@ namespace mq {
 
 __global__ void k_tail_grouped(Plan p);   // tail.hip
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef float float4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // Prefix sum of v[0 .. n) (n <= 1024), one value per thread of a 1024-thread
 // block: the thread's exclusive prefix in *excl_out, the total as the return
@@ -436,16 +433,7 @@ __global__ __launch_bounds__(1024) void k_sort(Plan p) {
 // Per token and group the front kernel stores (sum_c x_c, -1024 sum_c a_c)
 // of the layer input in xso; the gate/up kernel stores the same pair of
 // every GeGLU row and 64-column group in hso for the down projection.
-//
-__device__ __forceinline__ half8_t codes8(uint32_t w) {
-    const uint32_t t = w >> 8, e = 0x64006400u;
-    u32x4_t v;
-    v[0] = and_or(w, 0x000F000Fu, e);
-    v[1] = and_or(w, 0x00F000F0u, e);
-    v[2] = and_or(t, 0x000F000Fu, e);
-    v[3] = and_or(t, 0x00F000F0u, e);
-    return __builtin_bit_cast(half8_t, v);
-}
+// (codes8 is in device.h.)
 
 // fp16 scale and bias of a (scale | bias << 16) bf16 pair, and 16 * bias.
 struct Sb16 {
