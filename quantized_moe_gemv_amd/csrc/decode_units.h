@@ -192,7 +192,7 @@ struct Shared {
     float pes[256];           // per_expert_scale (1 when absent)
     float lbias[256];         // logit_bias (0 when absent)
     alignas(16) uint32_t gbuf[2048];     // gathered payloads (partial results of other units)
-    float xsum[64 * 4];       // x summed over each lane's 16 columns of a group (4-bit blocks)
+    alignas(16) float xsum[64 * 4];   // x summed over each lane's 16 columns of a group (4-bit blocks)
     float rsum[64 * 4];       // router input summed over each lane's 16 columns (8-bit blocks)
     float c8[512];            // per 8-column chunk: sum of x
     float c4[1024];           // per 4-column quarter: sum of x * router_scale
@@ -503,6 +503,7 @@ __device__ __forceinline__ void stage_token(const Plan& p, Shared& sh, const Tok
         sh.pes[t] = tl.pes;
         sh.lbias[t] = tl.lb;
     }
+    if (t < 8) sh.hzero[t] = 0;
     float ss = 0.f;
     if (t < nch) {
         *(uint4*)(sh.x + 8 * t) = v;
@@ -644,23 +645,10 @@ __device__ __forceinline__ void stage_h(const Plan& p, Shared& sh, const uint64_
             sh.hsa[g] = sa;
         }
     }
-    if (q < 8) sh.hzero[q] = 0;
     __syncthreads();
 }
 
 // ----------------------------------------------------------------- compute
-
-// Rows 16*r + lane%16 (r = 0, 1) of one 4-bit half block against the lane's
-// 16 input values (bf16 pairs xa for columns 8*(lane/16).., xb for +32):
-// adds sum((128 + q) * x) to d[r].
-__device__ __forceinline__ void half_block_dot(const uint4& c, const uint4& xa, const uint4& xb, float d[2]) {
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-    const uint32_t xk[2][4] = {{xa.x, xa.y, xa.z, xa.w}, {xb.x, xb.y, xb.z, xb.w}};
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) d[i >> 1] = dot2_bf16(q4_pair(w[i], q), xk[i & 1][q], d[i >> 1]);
-}
 
 // The token's staged activations as the A operand of
 // v_mfma_f32_16x16x32_f16 (16 tokens x 32 columns): the lanes of token 0
@@ -674,6 +662,30 @@ __device__ __forceinline__ TokOp tok_op(const Shared& sh) {
     const int lane = tix() & 63;
     const bool on = (lane & 15) == 0;
     return {on ? sh.h16 + 8 * (lane >> 4) : sh.hzero, on ? 64 : 0, on ? 32 : 0};
+}
+
+// The same operand over the staged token x (bf16), for the gate/up units.
+__device__ __forceinline__ TokOp tok_op_x(const Shared& sh) {
+    const int lane = tix() & 63;
+    const bool on = (lane & 15) == 0;
+    return {on ? sh.x + 8 * (lane >> 4) : sh.hzero, on ? 64 : 0, on ? 32 : 0};
+}
+
+// Rows 16 r + lane % 16 (r = 0, 1) of one 4-bit half block against group g
+// of the staged bf16 token, on the matrix cores with the codes as bf16
+// 128 + q (exact) in the B operand: lanes 0..15 of d[r] get
+// sum_c (128 + q_c) x_c + neg over the group's 64 columns.
+__device__ __forceinline__ void half_block_mma_bf16(const uint4& c, const TokOp& t, int g, float neg, float d[2]) {
+    const bf16x8_t a0 = *(const bf16x8_t*)(t.base + g * t.gstride);
+    const bf16x8_t a1 = *(const bf16x8_t*)(t.base + g * t.gstride + t.kh);
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        float4_t acc = {neg, 0.f, 0.f, 0.f};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, codes8_bf16(w[2 * r]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, codes8_bf16(w[2 * r + 1]), acc, 0, 0, 0);
+        d[r] = acc[0];
+    }
 }
 
 // Rows 16 r + lane % 16 (r = 0, 1) of one 4-bit half block (the lane's
@@ -779,24 +791,24 @@ __device__ __forceinline__ void run_router(const Plan& p, Shared& sh, const Unit
 // any partial exchange.
 __device__ __forceinline__ void run_rh(const Plan& p, Shared& sh, const Unit& x, const LoadsN<kItemsRH>& L,
                                        uint32_t tag) {
-    const int wave = wave_id(), lane = tix() & 63, kb = lane >> 4;
-    float acc[2] = {0.f, 0.f};    // rows 16*r + lane%16 of the wave's matrix (gate: even waves, up: odd)
+    const int wave = wave_id();
+    const TokOp to = tok_op_x(sh);
+    float acc[2] = {0.f, 0.f};    // lanes 0..15: rows 16*r + lane of the wave's matrix (gate: even waves, up: odd)
 #pragma unroll
     for (int m = 0; m < kItemsRH; ++m) {
         const int it = wave + kWaves * m;
         if (it < 2 * x.ng) {
             const int g = it >> 1;
-            const uint4 xa = *(const uint4*)(sh.x + 64 * g + 8 * kb);
-            const uint4 xb = *(const uint4*)(sh.x + 64 * g + 32 + 8 * kb);
-            const float xs = sh.xsum[g * 4 + kb];
-            float d[2] = {0.f, 0.f};
-            half_block_dot(L.c[m], xa, xb, d);
+            const float4 x4 = *(const float4*)(sh.xsum + 4 * g);
+            const float xs = (x4.x + x4.y) + (x4.z + x4.w);   // x over the group's 64 columns
+            float d[2];
+            half_block_mma_bf16(L.c[m], to, g, -128.f * xs, d);
             const uint32_t sw[2] = {L.s[m].x, L.s[m].y};
 #pragma unroll
-            for (int r = 0; r < 2; ++r) acc[r] += fmaf(bf16_lo(sw[r]), fmaf(-128.f, xs, d[r]), bf16_hi(sw[r]) * xs);
+            for (int r = 0; r < 2; ++r) acc[r] += fmaf(bf16_lo(sw[r]), d[r], bf16_hi(sw[r]) * xs);
         }
     }
-    reduce_rows(sh, acc, 2);
+    store_rows(sh, acc, 2);
     if (wave_id() == 0 && tix() < 32) {
         const int r = tix();
         const float h = gelu_tanh(row_total_par(sh, r)) * row_total_par(sh, 32 + r);

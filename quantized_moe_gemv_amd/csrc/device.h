@@ -8,6 +8,10 @@
 namespace mq {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
 
 // Index of the calling wave in its workgroup, as a wave-uniform (scalar)
 // value: branches on it are scalar branches, not exec-masked ones, so a
@@ -50,6 +54,15 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
 // them under the exponent of 128.0 (0x4300) gives 128 + q exactly.
 __device__ __forceinline__ uint32_t q4_pair(uint32_t w, int m) {
     return and_or(m ? w >> (4 * m) : w, 0x000F000Fu, 0x43004300u);
+}
+
+// The eight codes of a DEV_V1 4-bit word as eight bf16 operands 128 + q, in
+// column order (pair m holds columns 2m and 2m + 1).
+__device__ __forceinline__ bf16x8_t codes8_bf16(uint32_t w) {
+    u32x4_t v;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) v[m] = q4_pair(w, m);
+    return __builtin_bit_cast(bf16x8_t, v);
 }
 
 // Partial dots of one lane over one 4-bit DEV_V1 block: rows 16*ms + lane%16
@@ -173,10 +186,6 @@ __device__ __forceinline__ float gelu_tanh(float z) {
     const float k = 0.7978845608028654f;   // sqrt(2/pi)
     return 0.5f * z * (1.0f + tanhf(k * (z + 0.044715f * z * z * z)));
 }
-
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float float4_t __attribute__((ext_vector_type(4)));
 
 // The eight codes of a DEV_V1 4-bit word as eight fp16 operands, with four
 // AND-ORs under the fp16 exponent of 1024.0 (0x6400): columns c = 0, 1, 4, 5
