@@ -37,9 +37,9 @@
 
 namespace mq {
 // Internal linkage: each kernel file compiles its own copy, with its own
-// kOpaqueTid, kEarlySharedDown, kLateRoutedDown, kLateSharedGateUp and
-// kSwapKb (defined before this file is included; they change speed only,
-// never the arithmetic).
+// kOpaqueTid, kEarlySharedDown, kLateRoutedDown, kLateSharedGateUp, kSwapKb
+// and kSpareGateUpLoads (defined before this file is included; they change
+// speed only, never the arithmetic).
 namespace {
 
 // Sum over the four lanes of a row's column blocks (lane%16 + 16 kb): by
@@ -408,8 +408,12 @@ __device__ __forceinline__ void issue_loads(const Plan& p, const Shared& sh, con
     const int lc = oc + lane * 16, ls = os + (lane & 15) * 16;
 #pragma unroll
     for (int m = 0; m < N; ++m) {
-        if (wave + nw * m < n) {
-            const uint8_t* blk = wb + (int64_t)(nw / 2) * m * step;
+        // kSpareGateUpLoads: a gate/up unit's waves load every slot (the
+        // spare ones from the router's first block), so that every path
+        // issues the same number of loads and the compiler can wait for one
+        // item at a time
+        if ((kSpareGateUpLoads && (x.kind == U_SH || x.kind == U_RH)) || wave + nw * m < n) {
+            const uint8_t* blk = wave + nw * m < n ? wb + (int64_t)(nw / 2) * m * step : p.router_w;
             L.c[m] = ld_stream16(blk + lc);
             L.s[m] = *(const uint2*)(blk + ls);
         }

@@ -12,6 +12,10 @@ constexpr bool kLateSharedGateUp = false;
 // swaps this kernel measured 20.62-20.70 us per call against 20.03-20.06
 // (the stack launch the other way round).
 constexpr bool kSwapKb = false;
+// A gate/up unit loads all its wave slots (the spare ones from a block
+// already cached): 18.75 against 19.00 us per call; the stack launch is
+// faster without them (513 against 515 us/token).
+constexpr bool kSpareGateUpLoads = true;
 }
 }  // namespace mq
 

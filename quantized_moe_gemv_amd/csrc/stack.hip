@@ -11,6 +11,9 @@ constexpr bool kLateSharedGateUp = true;
 // The row totals' lane sums use permlane swaps: 555.7-556.2 us/token
 // against 560.1-560.6 through the LDS crossbar.
 constexpr bool kSwapKb = true;
+// A gate/up unit's waves skip the spare slots past its end (513 against
+// 515 us/token; the lone call is faster with them).
+constexpr bool kSpareGateUpLoads = false;
 }
 }  // namespace mq
 
