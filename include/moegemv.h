@@ -198,9 +198,11 @@ typedef struct {
     void* experts_ready;
 } mq_opts;
 
-/* Device scratch one call needs for up to max_tokens tokens.  The workspace
- * must be zero-filled once before its first use (the kernels leave their
- * counters at zero when they finish).  Returns 0 for invalid arguments. */
+/* Device scratch one call needs for up to max_tokens tokens (the library's
+ * own exchange buffers between its kernels and workgroups; the pages define
+ * no such buffer).  The workspace must be zero-filled once before its first
+ * use (the kernels leave their counters at zero when they finish).  Returns
+ * 0 for invalid arguments. */
 size_t mq_workspace_bytes(const mq_router* router, const mq_expert_pool* pool,
                           const mq_shared* shared, int32_t max_tokens);
 
@@ -305,20 +307,29 @@ mq_status moe_stack_forward(const mq_act* x, int32_t n_layers, const mq_router* 
  * workspace is zero-filled again.  workspace_bytes >= 1024. */
 mq_status mq_workspace_errors(const void* workspace, size_t workspace_bytes, uint32_t* errors, void* stream);
 
-/* Unit-weight RMS norm between stacked layers: out = bf16(x / sqrt(mean(x^2) + eps)).
- * x and out bf16 [T][H]; they may alias. */
+/* Unit-weight RMS norm between stacked layers: out = bf16(x / sqrt(mean(x^2) + eps))
+ * (the scale-free RMS norm of the "Decode" router listing, applied to the
+ * layer input as the stack harness does between layers; eps inside the
+ * root).  x and out bf16 [T][H]; they may alias.  MQ_ERR_* on invalid
+ * arguments, nothing written then. */
 mq_status mq_rmsnorm(const mq_act* x, mq_act* out, float eps, void* stream);
 
-/* Bytes of a matrix in `layout` (0 for unsupported arguments). */
+/* Bytes of a matrix in `layout` (0 for unsupported arguments): codes plus
+ * one BF16 scale and bias per group ("Why the runtime has this shape", 4th
+ * bullet; per-expert blob sizes as in "Resource split"). */
 size_t mq_packed_bytes(int32_t rows, int32_t cols, int32_t bits, int32_t group, int32_t layout);
 
 /* HOST: fill *pool's offsets and stride for experts packed back to back as
- * gate, up, down, each blob rounded up to page_bytes (a power of two >= 256).
+ * gate, up, down, each blob rounded up to page_bytes (a power of two >= 256)
+ * ("The .gturbo directory": fixed-stride page-aligned expert blobs;
+ * "Resource split": the page-rounded blob size).
  * base is left as given.  Returns the stride, 0 on invalid arguments. */
 int64_t mq_pool_layout(int32_t hidden, int32_t inter, int32_t bits, int32_t group,
                        int64_t page_bytes, mq_expert_pool* pool);
 
-/* HOST: canonical -> DEV_V1.  src describes HOST canonical arrays; dst is a
+/* HOST: canonical (MLX affine: packed codes, one BF16 scale and bias per
+ * group, "Why the runtime has this shape") -> DEV_V1, the same values in the
+ * matrix-core fragment order described above.  src describes HOST canonical arrays; dst is a
  * HOST buffer of dst_bytes >= mq_packed_bytes(.., MQ_LAYOUT_DEV_V1).  On
  * success *dst_desc (may be NULL) describes dst as a DEV_V1 tensor. */
 mq_status mq_pack(const mq_qtensor* src, void* dst, size_t dst_bytes, mq_qtensor* dst_desc);
@@ -328,7 +339,9 @@ mq_status mq_pack(const mq_qtensor* src, void* dst, size_t dst_bytes, mq_qtensor
  * the canonical sizes. */
 mq_status mq_unpack(const mq_qtensor* src, uint32_t* codes, uint16_t* scales, uint16_t* biases);
 
-/* Parity hooks: the GPU's reading of a DEV_V1 tensor.  codes_out uint8
+/* Parity hooks (test infrastructure, not a pages operation): the GPU's
+ * reading of a DEV_V1 tensor, w = scale * q + bias as in "Why the runtime
+ * has this shape".  codes_out uint8
  * [rows][cols] receives every code; w_out float [rows][cols] receives
  * scale * q + bias in fp32 (exact when the fp32 product is, e.g. for the
  * synthetic bias = -2^(bits-1) * scale). */
