@@ -54,7 +54,7 @@ struct Sizes {
 // the start of the workspace, at offsets that do not depend on the token
 // count, and no other kernel writes it.
 struct FusedCarve {
-    size_t rpart, act, piece, xw, tail, ctr, total;
+    size_t rpart, act, piece, xw, tail, ctr, epoch, total;
     int64_t h_stride, rpart_stride, xw_stride;   // in 8-byte words
 };
 
@@ -62,7 +62,8 @@ FusedCarve fused_carve(const Sizes& z) {
     FusedCarve f;
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
-    f.ctr = take((size_t)3 * kCtrStride * 4);   // c_done, epoch, error flag: first, at fixed offsets
+    f.ctr = take((size_t)3 * kCtrStride * 4);   // (unused), (unused), error flag: first, at fixed offsets
+    f.epoch = take((size_t)kFusedMaxWG * 4);    // one word per workgroup
     f.rpart_stride = (int64_t)up((size_t)(z.E + 15) / 16 * 8 * 16 * 8) / 8;
     f.rpart = take((size_t)8 * f.rpart_stride * 8);
     // one copy per XCD of the activations (shared then routed)
@@ -120,7 +121,7 @@ bool fused_ok(const Sizes& z, int cus) {
     // routed down slots run in tile ranges on the shared workgroups only when
     // the routed workgroups cannot take every slot (S < k)
     const bool ranges = std::min(z.n_rh / z.G_H, z.k) < z.k;
-    if (z.G_H > 48 || z.G_I > 12 || z.n_src > kFusedMaxSrc || m < 1 || r < 1) return false;
+    if (z.G_H > 48 || z.G_I > 12 || z.n_src > kFusedMaxSrc || m < 1 || r < 1 || cus > kFusedMaxWG) return false;
     if (z.H > kFusedMaxH || z.E > kFusedMaxE || z.k * z.I > kFusedMaxKI || z.Is > kFusedMaxIs) return false;
     if (z.ebits != 4) return false;
     return (!ranges || (z.G_H + r - 1) / r <= kFusedTilesD) && 2 * z.G_s <= m && (std::max(z.n_sd - z.n_rh, 0) + m - 1) / m <= kFusedSlotsSD &&
@@ -306,8 +307,7 @@ void fill_fused(Plan& p, const Sizes& z, uint8_t* ws) {
     p.f_tail = (uint64_t*)(ws + f.tail);
     p.xw_stride = f.xw_stride;
     uint32_t* ctr = (uint32_t*)(ws + f.ctr);
-    p.c_done = ctr;
-    p.f_epoch = ctr + kCtrStride;
+    p.f_epoch = (uint32_t*)(ws + f.epoch);
     p.f_err = ctr + 2 * kCtrStride;
     p.n_router = z.n_router;
     p.n_sd = z.n_sd;
@@ -489,6 +489,7 @@ static mq_status layer_forward(const mq_act* x, const mq_router* router, const m
     const bool fused =
         opts->path == MQ_PATH_FUSED || (opts->path == MQ_PATH_AUTO && T == 1 && !gemv_only && fused_ok(z, cus));
     p.n_rng = fused ? fused_ranges(z, cus) : 0;
+    p.nwg = fused ? cus : 0;
     p.in_eps = fused ? in_eps : 0.f;
     if (!fused && in_eps > 0.f) {   // normalise into the workspace, then run on that
         uint16_t* xn = (uint16_t*)(ws + c.xn);
@@ -678,6 +679,7 @@ extern "C" mq_status moe_stack_forward(const mq_act* x, int32_t n_layers, const 
     fill_layer(base, z, routers, pools, shared);
     fill_fused(base, z, ws);
     base.n_rng = fused_ranges(z, cus);
+    base.nwg = cus;
     base.x_stride = x->row_stride;
     base.out_stride = out->row_stride;
     base.out_f32 = out->dtype == MQ_DTYPE_F32;

@@ -203,7 +203,6 @@ struct Shared {
     int32_t ids[kMaxTopK];
     float wts[kMaxTopK];
     float rc;                 // router input scale 1/sqrt(mean(x^2)+eps)/sqrt(H)
-    uint32_t flag;
 };
 // First loading thread of the activation and output-sum gathers: waves 0
 // and 1 publish the units' results (the ids gather, after the router pieces
@@ -1067,19 +1066,19 @@ __device__ __forceinline__ void prefetch_args(const Plan& p) {
     asm volatile("" ::"s"(p.x), "s"(p.router_w), "s"(p.router_scale), "s"(p.pes), "s"(p.logit_bias),
                  "s"(p.f_epoch), "s"(p.pool_base), "s"(p.sh_gate), "s"(p.sh_up), "s"(p.sh_down));
     asm volatile("" ::"s"(p.f_rpart), "s"(p.f_hs), "s"(p.f_h), "s"(p.f_piece),
-                 "s"(p.f_err), "s"(p.c_done), "s"(p.out), "s"(p.ids_out), "s"(p.w_out), "s"(p.logits_out));
+                 "s"(p.f_err), "s"(p.out), "s"(p.ids_out), "s"(p.w_out), "s"(p.logits_out));
     asm volatile("" ::"s"(p.E), "s"(p.k), "s"(p.H), "s"(p.I), "s"(p.G_H), "s"(p.G_I), "s"(p.G_s), "s"(p.n_src),
                  "s"(p.n_router), "s"(p.n_rh), "s"(p.n_sd), "s"(p.n_sc), "s"(p.n_rng), "s"(p.eps));
     asm volatile("" ::"s"(p.x_w), "s"(p.out_w), "s"(p.xw_stride), "s"(p.in_eps));
     asm volatile("" ::"s"(p.h_stride), "s"(p.rpart_stride), "s"(p.expert_stride), "s"(p.gate_off), "s"(p.up_off),
-                 "s"(p.down_off), "s"(p.out_f32), "s"(gridDim.x));
+                 "s"(p.down_off), "s"(p.out_f32), "s"(p.nwg));
 }
 
 // One layer for one token: the workgroup's part of the unit order above.
 // Ends with every wave past its last use of the shared memory.
 template <bool TAIL>
 __device__ __forceinline__ void decode_layer(const Plan& p, Shared& sh, uint32_t tag, uint16_t* xraw) {
-    const int nwg = gridDim.x, w = blockIdx.x;
+    const int nwg = p.nwg, w = blockIdx.x;
     const Unit ur = unit_router(p, w - p.G_H);
     const Unit us = unit_sh(p, w - p.n_rh);
     const Unit rh = unit_rh(p, w);
@@ -1152,18 +1151,17 @@ __device__ __forceinline__ void decode_layer(const Plan& p, Shared& sh, uint32_t
     __syncthreads();
 }
 
-// The last workgroup to finish clears the done counter and advances the
-// epoch to the call's last tag.
-__device__ __forceinline__ void finish_call(const Plan& p, Shared& sh, uint32_t last_tag) {
-    __syncthreads();
-    if (tix() == 0) sh.flag = atomicAdd(p.c_done, 1u) + 1 == gridDim.x;
-    __syncthreads();
-    if (sh.flag) {
-        if (tix() == 0) {
-            __hip_atomic_store(p.c_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(p.f_epoch, last_tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
+// Tags: every workgroup keeps its own epoch word, the last tag it used.  A
+// call reads it at the start (tag = epoch + 1) and stores its last tag at
+// the end.  Every workgroup runs every call and calls on one workspace
+// follow each other in stream order, so all workgroups of a call read the
+// same epoch without any exchange, and no workgroup has to learn that the
+// others are done (a counter over all workgroups cost a round trip to one
+// contended address at the end of every call).
+__device__ __forceinline__ uint32_t first_tag(const Plan& p) { return ld_ctr(p.f_epoch + blockIdx.x) + 1; }
+
+__device__ __forceinline__ void finish_call(const Plan& p, uint32_t last_tag) {
+    if (tix() == 0) __hip_atomic_store(p.f_epoch + blockIdx.x, last_tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace

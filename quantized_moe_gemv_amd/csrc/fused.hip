@@ -34,9 +34,9 @@ __device__ __forceinline__ void decode_one(const Plan& p) {
         xraw = xraw_lds;
     }
     prefetch_args(p);
-    const uint32_t tag = ld_ctr(p.f_epoch) + 1;
+    const uint32_t tag = first_tag(p);
     decode_layer<TAIL>(p, sh, tag, xraw);
-    finish_call(p, sh, tag);
+    finish_call(p, tag);
 }
 
 __global__ __launch_bounds__(kThreads) void k_decode(Plan p) { decode_one<false>(p); }

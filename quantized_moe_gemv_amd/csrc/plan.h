@@ -12,6 +12,7 @@ constexpr int kMaxExperts = 256;
 constexpr int kDownSplits = 4;      // split of the down-projection source list (GEMV path)
 constexpr int kRouterPieces = 8;   // single-launch decode: column pieces of a 16-expert router slice
 constexpr int kCtrStride = 64;      // counters of the single-launch decode sit 256 bytes apart
+constexpr int kFusedMaxWG = 1024;   // largest grid of the single launch (compute units)
 // Sticky error bits kept in every workspace (read by mq_workspace_errors).
 constexpr uint32_t kErrWait = 1u;   // a bounded wait for another workgroup's result gave up
 constexpr uint32_t kErrRange = 2u;  // an fp16 activation overflowed (inf) or was NaN
@@ -88,10 +89,10 @@ struct Plan {
     const uint64_t* x_w;   // non-null: read the input row from here instead of x
     uint64_t* out_w;       // non-null: publish the output row here (out may then be null)
     int64_t xw_stride;
-    uint32_t* c_done;    // workgroups finished (cleared at the end of every call)
-    uint32_t* f_epoch;   // calls completed with this workspace
+    uint32_t* f_epoch;   // per workgroup of the single launch: the last tag it used (kFusedMaxWG words)
     uint32_t* f_err;     // non-zero once a bounded wait has given up
     int n_router, n_sd, n_sc, n_rh, n_rng, n_src;   // n_rng: tile ranges per routed down slot
+    int nwg;           // workgroups of the single launch (one per compute unit)
     int max_tiles;     // upper bound of scheduled (expert, token chunk) pairs
     int ntile;         // tokens per grouped chunk (32 or 128)
     int n_vs;          // virtual experts of the shared expert (0 without one)

@@ -32,13 +32,13 @@ namespace mq {
 // finite as in the single layer.
 __global__ __launch_bounds__(kThreads) void k_decode_stack(const Plan* __restrict__ plans, int n_layers) {
     __shared__ Shared sh;
-    const uint32_t base = ld_ctr(plans[0].f_epoch);
+    const uint32_t base = first_tag(plans[0]) - 1;
     for (int l = 0; l < n_layers; ++l) {
         const Plan& p = plans[l];
         prefetch_args(p);
         decode_layer<false>(p, sh, base + 1 + (uint32_t)l, nullptr);
     }
-    finish_call(plans[0], sh, base + (uint32_t)n_layers);
+    finish_call(plans[0], base + (uint32_t)n_layers);
 }
 
 // The same with every layer's tail applied in its output sums (a separate
@@ -46,13 +46,13 @@ __global__ __launch_bounds__(kThreads) void k_decode_stack(const Plan* __restric
 __global__ __launch_bounds__(kThreads) void k_decode_stack_tail(const Plan* __restrict__ plans, int n_layers) {
     __shared__ Shared sh;
     __shared__ alignas(16) uint16_t xraw[4096];   // each layer's input row as given (its tail's residual)
-    const uint32_t base = ld_ctr(plans[0].f_epoch);
+    const uint32_t base = first_tag(plans[0]) - 1;
     for (int l = 0; l < n_layers; ++l) {
         const Plan& p = plans[l];
         prefetch_args(p);
         decode_layer<true>(p, sh, base + 1 + (uint32_t)l, xraw);
     }
-    finish_call(plans[0], sh, base + (uint32_t)n_layers);
+    finish_call(plans[0], base + (uint32_t)n_layers);
 }
 
 // The per-layer arguments of a stack, written into the workspace by one
