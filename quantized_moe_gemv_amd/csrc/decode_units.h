@@ -37,9 +37,9 @@
 
 namespace mq {
 // Internal linkage: each kernel file compiles its own copy, with its own
-// kOpaqueTid, kEarlySharedDown, kLateRoutedDown, kLateSharedGateUp, kSwapKb
-// and kSpareGateUpLoads (defined before this file is included; they change
-// speed only, never the arithmetic).
+// kOpaqueTid, kEarlySharedDown, kLateRoutedDown, kLateSharedGateUp, kSwapKb,
+// kSpareGateUpLoads and kTokenFirst (defined before this file is included;
+// they change speed only, never the arithmetic).
 namespace {
 
 // Sum over the four lanes of a row's column blocks (lane%16 + 16 kb): by
@@ -1079,12 +1079,16 @@ __device__ __forceinline__ void prefetch_args(const Plan& p) {
 template <bool TAIL>
 __device__ __forceinline__ void decode_layer(const Plan& p, Shared& sh, uint32_t tag, uint16_t* xraw) {
     const int nwg = p.nwg, w = blockIdx.x;
+    // kTokenFirst: the token's loads go out before the unit assignments,
+    // whose integer divisions otherwise delay them
+    const bool need = w < p.n_rh || (w - p.G_H >= 0 && w - p.G_H < p.n_router) || (w - p.n_rh >= 0 && w - p.n_rh < 2 * p.G_s);
+    TokenLoads tl;
+    if constexpr (kTokenFirst) load_token(p, tl, need);
     const Unit ur = unit_router(p, w - p.G_H);
     const Unit us = unit_sh(p, w - p.n_rh);
     const Unit rh = unit_rh(p, w);
     const DownUnit du = unit_rdu(p, w, nwg);
-    TokenLoads tl;
-    load_token(p, tl, ur.kind == U_ROUTER || us.kind == U_SH || rh.kind == U_RH);
+    if constexpr (!kTokenFirst) load_token(p, tl, need);
     Loads lrt;
     LoadsN<kItemsRH> lsh;
     issue_loads(p, sh, ur, lrt);

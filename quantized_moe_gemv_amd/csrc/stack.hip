@@ -14,6 +14,8 @@ constexpr bool kSwapKb = true;
 // A gate/up unit's waves skip the spare slots past its end (513 against
 // 515 us/token; the lone call is faster with them).
 constexpr bool kSpareGateUpLoads = false;
+// The unit assignments before the token's loads (see fused.hip).
+constexpr bool kTokenFirst = false;
 }
 }  // namespace mq
 
