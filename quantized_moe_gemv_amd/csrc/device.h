@@ -80,13 +80,6 @@ __device__ __forceinline__ void q4_block_dot(const uint4& c0, const uint4& c1, c
     }
 }
 
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-
-// fp32 -> fp16 bits, round to nearest even.
-__device__ __forceinline__ uint16_t f32_to_f16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
-__device__ __forceinline__ float f16_lo(uint32_t v) { return (float)__builtin_bit_cast(f16x2_t, v)[0]; }
-__device__ __forceinline__ float f16_hi(uint32_t v) { return (float)__builtin_bit_cast(f16x2_t, v)[1]; }
-
 // True when an fp16 value is inf or NaN (all exponent bits set): the
 // conversion of an activation overflowed fp16's range (|v| >= 65520) or the
 // value was already NaN.
